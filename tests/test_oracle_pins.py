@@ -1,0 +1,331 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself:
+the published e2m1/e8m0 encodings (golden fixtures), hand-decoded packs,
+closed forms, library routines (torch, numpy), brute force on tiny inputs and
+exact invariants.  CPU only."""
+
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import synthetic
+from oracle import brute, ref
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_fixture(name):
+    rows = {}
+    with open(os.path.join(GOLDEN, name)) as fh:
+        for line in fh:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            key, *vals = line.split()
+            rows.setdefault(key, []).extend(vals)
+    return rows
+
+
+# ----------------------------------------------------------------- formats
+
+def test_e2m1_table_matches_published_encoding():
+    codes, values = [], []
+    with open(os.path.join(GOLDEN, "e2m1.txt")) as fh:
+        for line in fh:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                c, bits, v = line.split()
+                assert int(bits, 2) == int(c)
+                codes.append(int(c))
+                values.append(float(v))
+    assert codes == list(range(16))
+    got = ref.e2m1_to_f64(np.arange(16, dtype=np.uint8))
+    for c in range(16):
+        assert got[c] == values[c] and math.copysign(1, got[c]) == math.copysign(1, values[c])
+        b = brute.e2m1_value(c)      # bit-field decode, independent of the table
+        assert b == values[c] and math.copysign(1, b) == math.copysign(1, values[c])
+
+
+def test_e8m0_closed_form():
+    b = np.array([0, 1, 119, 123, 126, 127, 128, 254], dtype=np.uint8)
+    assert list(ref.e8m0_to_f64(b)) == [2.0 ** (int(v) - 127) for v in b]
+    assert ref.e8m0_to_f64(np.array([127], np.uint8))[0] == 1.0
+    with pytest.raises(ValueError):
+        ref.e8m0_to_f64(np.array([255], np.uint8))
+
+
+def test_mxfp4_hand_decoded_row():
+    fx = _read_fixture("mxfp4_row.txt")
+    codes = np.array([int(v, 16) for v in fx["bytes"]], np.uint8)[None, :]
+    scales = np.array([int(v) for v in fx["scales"]], np.uint8)[None, :]
+    want = np.array([float(v) for v in fx["values"]])
+    got = ref.dequant_mxfp4(codes, scales)[0]
+    assert got.shape == want.shape == (64,)
+    assert np.array_equal(got, want)
+    assert np.array_equal(np.signbit(got), np.signbit(want))          # code 8 is -0
+    mat = dict(fmt="mxfp4", codes=codes[None], scales=scales[None])
+    assert brute.dequant_row(mat, 0, 0, 64) == list(want)
+
+
+def test_q2_hand_decoded_row():
+    fx = _read_fixture("q2_row.txt")
+    codes = np.array([int(v, 16) for v in fx["bytes"]], np.uint8)[None, :]
+    sc = np.array([int(v, 16) for v in fx["scales"]], np.uint16)[None, :]
+    mn = np.array([int(v, 16) for v in fx["mins"]], np.uint16)[None, :]
+    want = np.array([float(v) for v in fx["values"]])
+    got = ref.dequant_q2(codes, sc, mn)[0]
+    assert np.array_equal(got, want)
+    mat = dict(fmt="q2", codes=codes[None], scales=sc[None], mins=mn[None])
+    assert brute.dequant_row(mat, 0, 0, 64) == list(want)
+
+
+def test_mxfp4_values_exact_in_bf16():
+    """Every e2m1 code times a scale 2**-8..2**-4 is a bf16 value, so MXFP4
+    weights can be widened to bf16 for matrix cores with no rounding."""
+    for s in range(119, 124):
+        for c in range(16):
+            v = brute.e2m1_value(c) * 2.0 ** (s - 127)
+            assert brute.round_bf16(v) == v
+
+
+def test_q2_values_exact_in_fp32():
+    """scale*q + min of fp16 scale/min is exact in float32 for the workload's
+    ranges, so a float32 dequantisation with one FMA loses nothing."""
+    rng = np.random.default_rng(7)
+    sc = rng.uniform(0.005, 0.02, 20000).astype(np.float16).astype(np.float64)
+    mn = rng.uniform(-0.04, 0.0, 20000).astype(np.float16).astype(np.float64)
+    for q in range(4):
+        w = sc * q + mn
+        assert np.array_equal(w.astype(np.float32).astype(np.float64), w)
+
+
+# ------------------------------------------------------------ bf16 rounding
+
+def test_round_bf16_matches_torch_on_float32_values():
+    rng = np.random.default_rng(3)
+    v = np.concatenate([
+        rng.standard_normal(20000) * 10.0 ** rng.integers(-30, 30, 20000),
+        # exact ties between two bf16 neighbours (low 16 bits = 0x8000)
+        ((rng.integers(0, 2 ** 31, 4000, dtype=np.uint64) & ~np.uint64(0xFFFF)) | np.uint64(0x8000))
+        .astype(np.uint32).view(np.float32).astype(np.float64),
+        np.array([0.0, -0.0, 1e-40, -1e-40, 1e-45, 3.3e38, -3.39e38]),
+    ]).astype(np.float32)
+    v = v[np.isfinite(v)]
+    want = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+    got = ref.round_bf16(v.astype(np.float64))
+    assert np.array_equal(got, want)
+    assert np.array_equal(np.signbit(got), np.signbit(want))
+
+
+def test_round_bf16_direct_from_float64():
+    # no double rounding: 1 + 2**-8 + 2**-30 is just above the tie -> rounds up
+    assert ref.round_bf16(np.array([1.0 + 2.0 ** -8 + 2.0 ** -30]))[0] == 1.0 + 2.0 ** -7
+    assert ref.round_bf16(np.array([1.0 + 2.0 ** -8]))[0] == 1.0              # tie -> even
+    assert ref.round_bf16(np.array([1.0 + 3 * 2.0 ** -8]))[0] == 1.0 + 2.0 ** -6  # tie -> even (up)
+    assert ref.round_bf16(np.array([3.4e38]))[0] == math.inf
+    # against the independent rational search on random float64 values
+    rng = np.random.default_rng(5)
+    v = rng.standard_normal(3000) * 10.0 ** rng.integers(-40, 38, 3000)
+    got = ref.round_bf16(v)
+    for a, b in zip(v, got):
+        assert brute.round_bf16(float(a)) == b
+
+
+# ------------------------------------------------------------------ routing
+
+def test_router_logits_closed_form():
+    T, d, E = 3, 64, 5
+    x = synthetic.to_bf16_bits(np.random.default_rng(1).standard_normal((T, d)).astype(np.float32))
+    xv = np.array([[brute.bf16_value(int(b)) for b in row] for row in x])
+    wr = np.zeros((E, d), np.float32)
+    for e in range(E):
+        wr[e, 3 * e] = 1.0                # one-hot rows pick x[:, 3e]
+        wr[e, 3 * e + 1] = -2.0
+    bias = np.arange(E, dtype=np.float32) * 0.25
+    got = ref.router_logits(x, wr, bias)
+    want = xv[:, 0:3 * E:3] - 2.0 * xv[:, 1:3 * E + 1:3] + bias[None, :]
+    assert np.array_equal(got, want)
+
+
+def test_topk_brute_force_with_ties():
+    rng = np.random.default_rng(11)
+    for trial in range(60):
+        E = 8
+        l = rng.integers(-3, 4, size=(3, E)).astype(np.float64) * 0.5   # many exact ties
+        if trial % 7 == 0:
+            l[:] = 0.0
+            l[0, 2] = -0.0
+        for k in (1, 2, 3, 8):
+            ids, w = ref.route_topk(l, k)
+            bids, bw = brute.route_topk(l, k)
+            assert ids.tolist() == bids
+            assert np.allclose(w, bw, rtol=0, atol=1e-15)
+
+
+def test_topk_tie_rules():
+    l = np.array([[1.0, 2.0, 2.0, 0.5], [0.0, -0.0, 0.0, -1.0]])
+    ids, _ = ref.route_topk(l, 2)
+    assert ids.tolist() == [[1, 2], [0, 1]]
+    with pytest.raises(ValueError):
+        ref.route_topk(np.array([[0.0, np.nan]]), 1)
+
+
+def test_topk_weights_sum_to_one_and_full_softmax():
+    rng = np.random.default_rng(12)
+    l = rng.standard_normal((50, 16)) * 3
+    for k in (1, 2, 5):
+        _, w = ref.route_topk(l, k)
+        assert np.all(np.abs(w.sum(1) - 1.0) < 1e-15)
+    ids, w = ref.route_topk(l, 16)                 # k = E: plain softmax
+    sm = torch.softmax(torch.from_numpy(l), dim=1).numpy()
+    assert np.allclose(np.take_along_axis(sm, ids.astype(np.int64), 1), w, rtol=1e-14, atol=0)
+
+
+# ----------------------------------------------------------------- dispatch
+
+def test_dispatch_against_brute_and_invariants():
+    rng = np.random.default_rng(13)
+    for T, E, k in [(1, 64, 2), (7, 8, 2), (33, 16, 3), (100, 5, 1), (0, 4, 2)]:
+        ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]) if T else np.zeros((0, k), np.int32)
+        off, perm, inv = ref.dispatch(ids, E)
+        boff, bperm, binv = brute.dispatch(ids.tolist(), E)
+        assert off.tolist() == boff and perm.tolist() == bperm and inv.tolist() == binv
+        assert off[0] == 0 and off[-1] == T * k and np.all(np.diff(off) >= 0)
+        assert sorted(perm.tolist()) == list(range(T * k))
+        assert np.array_equal(inv[perm], np.arange(T * k))
+        flat = ids.reshape(-1)
+        for e in range(E):
+            seg = perm[off[e]:off[e + 1]]
+            assert np.all(flat[seg] == e) and np.all(np.diff(seg) > 0)   # stable
+
+
+# ---------------------------------------------------------------------- FFN
+
+def _small_case(fmt, T=3, d=64, E=4, k=2, f=32, seed=0, **kw):
+    return synthetic.make_case(T, d, E, k, f, fmt, seed=seed, router="device", **kw)
+
+
+def _dense_weights_brute(mat, slot, n, K):
+    return np.array([brute.dequant_row(mat, slot, r, K) for r in range(n)])
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "q2"])
+def test_single_expert_is_dense_swiglu(fmt):
+    """E = 1, k = 1: the layer is a dense SwiGLU MLP (torch float64)."""
+    c = _small_case(fmt, T=5, d=64, E=1, k=1, f=32, seed=4)
+    r = ref.layer(c["x"], 1, c["gate"], c["up"], c["down"], w_router=c["w_router"])
+    x = torch.tensor([[brute.bf16_value(int(b)) for b in row] for row in c["x"]], dtype=torch.float64)
+    wg = torch.from_numpy(_dense_weights_brute(c["gate"], 0, 32, 64))
+    wu = torch.from_numpy(_dense_weights_brute(c["up"], 0, 32, 64))
+    wd = torch.from_numpy(_dense_weights_brute(c["down"], 0, 64, 32))
+    h = torch.nn.functional.silu(x @ wg.T) * (x @ wu.T)
+    act = torch.tensor([[brute.round_bf16(float(v)) for v in row] for row in h], dtype=torch.float64)
+    out = act @ wd.T
+    assert np.allclose(r["out"], out.numpy(), rtol=1e-12, atol=1e-12)
+    assert np.array_equal(r["w"], np.ones((5, 1)))
+
+
+def test_identity_experts_closed_form():
+    """Hand-built weights: gate = I, up = 2I, down = cyclic shift.  Then
+    out[t, n] = bf16(silu(x[t, n+1]) * 2 x[t, n+1]) (indices mod 32)."""
+    d = f = 32
+    E, k, T = 2, 1, 3
+    def eye_pack(code):
+        codes = np.zeros((E, d, d // 2), np.uint8)
+        for n in range(d):
+            codes[:, n, n // 2] |= code << (4 * (n % 2))
+        return dict(fmt="mxfp4", codes=codes, scales=np.full((E, d, 1), 127, np.uint8))
+    gate, up = eye_pack(2), eye_pack(4)           # e2m1 code 2 = 1.0, code 4 = 2.0
+    down = dict(fmt="mxfp4", codes=np.zeros((E, d, f // 2), np.uint8),
+                scales=np.full((E, d, 1), 127, np.uint8))
+    for n in range(d):
+        kk = (n + 1) % f
+        down["codes"][:, n, kk // 2] |= 2 << (4 * (kk % 2))
+    xv = np.array([[(i - 16) / 8.0 + 0.125 * t for i in range(d)] for t in range(T)], np.float32)
+    x = synthetic.to_bf16_bits(xv)
+    logits = np.array([[1.0, 0.0], [0.0, 1.0], [2.0, 2.0]], np.float32)
+    r = ref.layer(x, k, gate, up, down, logits=logits)
+    for t in range(T):
+        for n in range(d):
+            xi = float(xv[t, (n + 1) % d])
+            want = brute.round_bf16(xi / (1 + math.exp(-xi)) * 2 * xi)
+            assert r["out"][t, n] == want
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "q2"])
+def test_ref_matches_brute_small(fmt):
+    for seed, (T, d, E, k, f) in enumerate([(3, 64, 4, 2, 32), (6, 32, 8, 3, 64), (2, 96, 3, 3, 32)]):
+        c = _small_case(fmt, T=T, d=d, E=E, k=k, f=f, seed=seed, zipf=1.1 if seed == 1 else None)
+        r = ref.layer(c["x"], k, c["gate"], c["up"], c["down"], w_router=c["w_router"], bias=c["bias"])
+        b = brute.layer(c["x"], k, c["gate"], c["up"], c["down"], w_router=c["w_router"], bias=c["bias"])
+        assert np.allclose(r["logits"], b["logits"], rtol=0, atol=1e-14)
+        assert r["ids"].tolist() == b["ids"]
+        assert r["perm"].tolist() == b["perm"] and r["offsets"].tolist() == b["offsets"]
+        assert np.array_equal(r["act"], np.array(b["act"]))
+        scale = np.abs(np.array(b["out"])).max()
+        assert np.allclose(r["out"], b["out"], rtol=0, atol=1e-12 * scale)
+
+
+def test_ref_matches_brute_tiny_workload():
+    c = synthetic.workload(0)
+    r = ref.layer(c["x"], c["k"], c["gate"], c["up"], c["down"], logits=c["logits"])
+    b = brute.layer(c["x"], c["k"], c["gate"], c["up"], c["down"], logits=c["logits"])
+    assert r["ids"].tolist() == b["ids"] and r["perm"].tolist() == b["perm"]
+    assert np.array_equal(r["act"], np.array(b["act"]))
+    assert np.allclose(r["out"], b["out"], rtol=0, atol=1e-12 * np.abs(r["out"]).max())
+
+
+def test_k_equals_E_is_softmax_mixture():
+    c = _small_case("mxfp4", T=4, d=64, E=3, k=3, f=32, seed=9)
+    r = ref.layer(c["x"], 3, c["gate"], c["up"], c["down"], w_router=c["w_router"])
+    x = torch.tensor([[brute.bf16_value(int(b)) for b in row] for row in c["x"]], dtype=torch.float64)
+    p = torch.softmax(x @ torch.from_numpy(c["w_router"].astype(np.float64)).T, dim=1)
+    mix = torch.zeros((4, 64), dtype=torch.float64)
+    for e in range(3):
+        wg = torch.from_numpy(_dense_weights_brute(c["gate"], e, 32, 64))
+        wu = torch.from_numpy(_dense_weights_brute(c["up"], e, 32, 64))
+        wd = torch.from_numpy(_dense_weights_brute(c["down"], e, 64, 32))
+        h = torch.nn.functional.silu(x @ wg.T) * (x @ wu.T)
+        act = torch.tensor([[brute.round_bf16(float(v)) for v in row] for row in h], dtype=torch.float64)
+        mix += p[:, e:e + 1] * (act @ wd.T)
+    assert np.allclose(r["out"], mix.numpy(), rtol=1e-12, atol=1e-12 * float(mix.abs().max()))
+
+
+def test_token_permutation_invariance():
+    c = _small_case("mxfp4", T=9, d=64, E=6, k=2, f=32, seed=21)
+    r = ref.layer(c["x"], 2, c["gate"], c["up"], c["down"], w_router=c["w_router"])
+    pi = np.random.default_rng(0).permutation(9)
+    r2 = ref.layer(c["x"][pi], 2, c["gate"], c["up"], c["down"], w_router=c["w_router"])
+    assert np.array_equal(r2["ids"], r["ids"][pi])
+    assert np.allclose(r2["out"], r["out"][pi], rtol=0, atol=1e-13 * np.abs(r["out"]).max())
+
+
+def test_power_of_two_scale_invariance():
+    c = _small_case("mxfp4", T=4, d=64, E=4, k=2, f=32, seed=22)
+    base = ref.layer(c["x"], 2, c["gate"], c["up"], c["down"], w_router=c["w_router"])["out"]
+    for which in ("up", "down"):
+        m = dict(c[which])
+        m["scales"] = m["scales"] + np.uint8(1)
+        mats = {"gate": c["gate"], "up": c["up"], "down": c["down"], which: m}
+        out = ref.layer(c["x"], 2, mats["gate"], mats["up"], mats["down"], w_router=c["w_router"])["out"]
+        assert np.array_equal(out, 2.0 * base)
+    q = _small_case("q2", T=4, d=64, E=4, k=2, f=32, seed=23)
+    base = ref.layer(q["x"], 2, q["gate"], q["up"], q["down"], w_router=q["w_router"])["out"]
+    m = dict(q["down"])
+    # doubling an fp16 value = adding 1 to its exponent field (values are normal)
+    m["scales"] = m["scales"] + np.uint16(1 << 10)
+    m["mins"] = np.where(m["mins"] & 0x7FFF, m["mins"] + np.uint16(1 << 10), m["mins"]).astype(np.uint16)
+    out = ref.layer(q["x"], 2, q["gate"], q["up"], m, w_router=q["w_router"])["out"]
+    assert np.array_equal(out, 2.0 * base)
+
+
+def test_combine_order_and_weights():
+    y = np.arange(12, dtype=np.float64).reshape(6, 2)
+    inv = np.array([5, 0, 1, 4, 2, 3])
+    w = np.array([[0.25, 0.75], [0.5, 0.5], [1.0, 0.0]])
+    out = ref.combine(y, inv, w, 2)
+    want = np.array([0.25 * y[5] + 0.75 * y[0], 0.5 * y[1] + 0.5 * y[4], y[2]])
+    assert np.array_equal(out, want)
