@@ -1,0 +1,256 @@
+"""Benchmark of the routed MoE layer on one MI355X.
+
+A step is one pass of the whole layer -- router logits, top-k, dispatch,
+fused-dequant SwiGLU expert FFN, combine -- over one batch of tokens, with
+every input already resident in HBM.  Consecutive steps use different weight
+pools ("layers") and different token batches, cycling through enough pools
+that a layer's experts are evicted from the 256 MB Infinity Cache before the
+layer comes round again (as in a real decode pass over a deep MoE model).
+
+Prints ONE JSON line.  Default workload: decode, T=1, d=4096, E=64, k=2,
+f=2048, MXFP4 experts.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 0..4]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0         # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
+METRIC = "MoE layer tokens/s; decode weight-stream GB/s; prefill expert TFLOP/s"
+
+MX_BYTES_PER_EXPERT = lambda d, f: 3 * d * f // 2 + 3 * d * f // 32      # codes + e8m0 scales
+Q2_BYTES_PER_EXPERT = lambda d, f: 3 * d * f // 4 + 3 * d * f // 32 * 4  # codes + fp16 scale + min
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", type=int, default=1, choices=[0, 1, 2, 3, 4])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-steps", type=int, default=0,
+                   help="oracle steps timed on the host (0 = automatic)")
+    return p.parse_args()
+
+
+def make_pool(torch, w, gen, dev):
+    """One layer's experts on the device: uniform codes, scales as in the
+    synthetic recipe (e8m0 bytes 119..123; Q2 fp16 scale U[.005,.02], min U[-.04,0])."""
+    import quantized_routed_moe_amd as qm
+
+    E, d, f = w["E"], w["d"], w["f"]
+
+    def mat(n, K):
+        if w["fmt"] == "mxfp4":
+            codes = torch.randint(0, 256, (E, n, K // 2), dtype=torch.uint8, device=dev, generator=gen)
+            scales = torch.randint(119, 124, (E, n, K // 32), dtype=torch.uint8, device=dev, generator=gen)
+            return qm.QMat(codes, scales)
+        codes = torch.randint(0, 256, (E, n, K // 4), dtype=torch.uint8, device=dev, generator=gen)
+        sc = (torch.rand((E, n, K // 32), device=dev, generator=gen) * 0.015 + 0.005).half().view(torch.int16)
+        mn = (torch.rand((E, n, K // 32), device=dev, generator=gen) * -0.04).half().view(torch.int16)
+        return qm.QMat(codes, sc.contiguous(), mn.contiguous())
+
+    return qm.Experts(w["fmt"], mat(f, d), mat(f, d), mat(d, f), None, E)
+
+
+def cpu_baseline(c, steps):
+    """The oracle as it stands, timed on this host on `steps` seeded steps of
+    the same workload (input generation excluded)."""
+    import numpy as np
+
+    import synthetic
+    from oracle import ref
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        blas = 1
+    total, tokens = 0.0, 0
+    for i in range(steps):
+        case = synthetic.workload(c, seed_offset=17 + i)
+        t0 = time.perf_counter()
+        ref.layer(case["x"], case["k"], case["gate"], case["up"], case["down"], logits=case["logits"],
+                  w_router=case["w_router"], bias=case["bias"])
+        total += time.perf_counter() - t0
+        tokens += case["T"]
+    return dict(value=tokens / total, unit="tokens/s", cores=int(blas), kind="oracle",
+                sample=f"{steps} seeded step(s) of the workload ({tokens} tokens), NumPy float64 oracle, "
+                       f"{total:.1f} s of host time; input generation not timed")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(expert-parallel sharding is designed, not built)"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import quantized_routed_moe_amd as qm
+    import synthetic
+
+    c = args.workload
+    w = synthetic.WORKLOADS[c]
+    T, d, E, k, f = w["T"], w["d"], w["E"], w["k"], w["f"]
+    shape = qm.Shape(T, d, E, k, f)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1000 * c + 123)
+
+    per_expert = (MX_BYTES_PER_EXPERT if w["fmt"] == "mxfp4" else Q2_BYTES_PER_EXPERT)(d, f)
+    touched_guess = min(E, max(2, T * k)) * per_expert
+    n_pools = 1 + math.ceil(512 * 2 ** 20 / touched_guess)
+    n_pools = max(2, min(n_pools, 24))
+    pools = [make_pool(torch, w, gen, dev) for _ in range(n_pools)]
+    routers = []
+    for _ in range(n_pools):
+        if w["router"] == "given":
+            routers.append(None)
+        else:
+            wr = torch.randn((E, d), device=dev, generator=gen) / math.sqrt(d)
+            b = torch.from_numpy(synthetic.zipf_bias(E, w["zipf"])).to(dev) if w.get("zipf") else None
+            routers.append((wr.contiguous(), b))
+    n_x = 4 if T >= 1024 else 61
+    if w.get("correlated"):
+        base = torch.randn((n_x, 1, d), device=dev, generator=gen)
+        xs = (base + 0.3 * torch.randn((n_x, T, d), device=dev, generator=gen)).to(torch.bfloat16)
+    else:
+        xs = torch.randn((n_x, T, d), device=dev, generator=gen).to(torch.bfloat16)
+    xs = xs.view(torch.int16).contiguous()
+    given = torch.randn((n_x, T, E), device=dev, generator=gen) if w["router"] == "given" else None
+
+    logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    tw = torch.empty((T, k), dtype=torch.float32, device=dev)
+    offsets = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+    perm = torch.empty((T * k,), dtype=torch.int32, device=dev)
+    inv = torch.empty((T * k,), dtype=torch.int32, device=dev)
+    y = torch.empty((T * k, d), dtype=torch.float32, device=dev)
+    out = torch.empty((T, d), dtype=torch.float32, device=dev)
+    ws = qm.alloc_workspace(shape, layer=True, device=dev)
+
+    def step(i, ev=None):
+        p = i % n_pools
+        x = xs[i % n_x]
+        if given is not None:
+            logits.copy_(given[i % n_x])
+            wr, b = None, None
+        else:
+            wr, b = routers[p]
+        qm.moe_route_topk(shape, x, wr, b, logits, ids, tw)
+        qm.moe_dispatch(shape, ids, offsets, perm, inv, ws)
+        if ev is not None:
+            ev[0].record()
+        qm.moe_expert_ffn(shape, x, pools[p], offsets, perm, y, ws)
+        if ev is not None:
+            ev[1].record()
+        qm.moe_combine(shape, y, inv, tw, out)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ffn_ms = [a.elapsed_time(b) for a, b in evs]
+
+    # one-call path (moe_layer), same steps, for reference
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for i in range(K):
+        j = args.warmup + i
+        p = j % n_pools
+        wr, b = (None, None) if given is not None else routers[p]
+        if given is not None:
+            logits.copy_(given[j % n_x])
+        qm.moe_layer(shape, xs[j % n_x], wr, b, logits, pools[p], ids, tw, out, ws)
+    torch.cuda.synchronize()
+    layer_elapsed = time.perf_counter() - t1
+    assert qm.moe_read_device_status(ws) == 0
+
+    # activated experts per timed step (routing replayed untimed; it is deterministic)
+    U = []
+    for i in range(K):
+        j = args.warmup + i
+        p = j % n_pools
+        if given is not None:
+            logits.copy_(given[j % n_x])
+            wr, b = None, None
+        else:
+            wr, b = routers[p]
+        qm.moe_route_topk(shape, xs[j % n_x], wr, b, logits, ids, tw)
+        qm.moe_dispatch(shape, ids, offsets, perm, inv, ws)
+        U.append(int((offsets[1:] - offsets[:-1] > 0).sum().item()))
+    U_mean = float(np.mean(U))
+
+    weight_bytes = U_mean * per_expert
+    act_bytes = T * d * 2 + T * k * f * 2 * 2 + T * k * d * 4     # x read, act write+read, y write
+    ffn_bytes = weight_bytes + act_bytes
+    ffn_avg_s = float(np.mean(ffn_ms)) / 1e3
+    flops = 2.0 * T * k * 3 * d * f
+    gbps = ffn_bytes / ffn_avg_s / 1e9
+    tflops = flops / ffn_avg_s / 1e12
+
+    if T * k >= 1024:
+        roof = dict(bound="mfma", achieved=round(tflops, 2), peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), traffic=None)
+    else:
+        roof = dict(bound="hbm", achieved=round(gbps, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
+                    frac=round(gbps / HBM_PEAK_GBPS, 4), traffic=None)
+    roof["kernel"] = "moe_expert_ffn (gate/up + SwiGLU kernel, down kernel)"
+    roof["algorithmic_bytes_per_launch"] = round(ffn_bytes)
+    roof["avg_launch_ms"] = round(ffn_avg_s * 1e3, 5)
+
+    ms_per_step = elapsed / K * 1e3
+    res = {
+        "metric": METRIC,
+        "value": round(T * K / elapsed, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w['name']}: T={T} d={d} E={E} k={k} f={f} {w['fmt']}",
+                   "T": T, "d": d, "E": E, "k": k, "f": f, "format": w["fmt"],
+                   "weight_pools": n_pools, "parallelism": "none (1 GPU)"},
+        "weight_stream_GBps": round(gbps, 1),
+        "expert_TFLOPs": round(tflops, 3),
+        "active_experts_mean": U_mean,
+        "moe_layer_ms_per_step": round(layer_elapsed / K * 1e3, 5),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        n = args.cpu_sample_steps or {0: 200, 1: 6, 2: 4, 3: 1, 4: 3}[c]
+        res["cpu_baseline"] = cpu_baseline(c, n)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,185 @@
+/*
+ * moe.h -- C ABI of the quantized routed mixture-of-experts layer for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * What the layer computes (the pages describe it in prose only):
+ *   a router scores every token against E experts, keeps the top k, and a
+ *   block-sparse kernel streams only the activated experts' quantised
+ *   weights, dequantising them on the fly ("antirez ds4: DeepSeek Metal
+ *   inference", ainews.cool, section 技术深度解析 -- 64 fine-grained experts,
+ *   top-2 routing, custom dequantisation kernels); the routed count k is a
+ *   run-time choice (Anemll/ds4-ssd README, section "Experimental Pro
+ *   Support", --moe-expert-topk); experts come as native MXFP4 packs
+ *   (ds4-ssd README, section "Run SSD Sidecar Mode") or 2-bit asymmetric
+ *   packs ("DwarfStar 4 (ds4) | Mac Studio ... 完整指南", res.pawin.top,
+ *   section on q2 asymmetric quantisation).
+ *
+ *   1. logits[t][e] = sum_i float(x[t][i]) * w_router[e][i] + bias[e]     (fp32)
+ *   2. topk_ids[t][0..k) = the k largest logits, ordered by (logit desc,
+ *      expert id asc); topk_w[t][j] = softmax over the k selected logits
+ *   3. stable counting sort of the pairs p = t*k + j by topk_ids:
+ *      offsets[E+1], perm[r] = pair at sorted row r, inv[p] = row of pair p
+ *   4. for sorted row r of expert e, token t = perm[r] / k:
+ *      act[r][n] = bf16_rne( silu(Wg[e][n,:] . x[t]) * (Wu[e][n,:] . x[t]) )
+ *   5. y[r][m] = Wd[e][m,:] . act[r]                                          (fp32)
+ *   6. out[t][m] = sum_{j=0..k-1} topk_w[t][j] * y[inv[t*k+j]][m]  (j order) (fp32)
+ *
+ * Conventions for every entry point:
+ *   - Every data pointer is a DEVICE pointer (HBM of the current HIP
+ *     device) unless stated otherwise; `moe_shape` / `moe_experts` structs are
+ *     read on the host during the call and may be freed after it returns.
+ *   - bf16 and fp16 values are passed as their uint16 bit patterns.
+ *   - Row-major everywhere; the last index is contiguous.
+ *   - Alignment: x, y, out, logits, every pack pointer and ws must be 16-byte
+ *     aligned; int32 arrays 4-byte aligned.
+ *   - The caller owns and allocates every buffer (inputs, outputs and the
+ *     workspace).  The library allocates and frees nothing and keeps no
+ *     mutable global state: calls on different streams with different
+ *     buffers are independent.
+ *   - Every call only ENQUEUES work on `stream` and returns; buffers must stay
+ *     valid until the stream has passed that work.  Nothing synchronises the
+ *     host except moe_read_device_status.
+ *   - Host-side validation runs before any HIP call; a negative return code
+ *     means nothing was enqueued.  The library never prints, aborts or throws.
+ *   - T == 0 is valid and enqueues nothing.
+ *
+ * Shape limits: 1 <= k <= E <= 64; d and f positive multiples of 32;
+ * T >= 0; T*k*max(d, f) < 2^31.
+ */
+#ifndef QUANTIZED_ROUTED_MOE_AMD_MOE_H
+#define QUANTIZED_ROUTED_MOE_AMD_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes (return values). */
+enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_NULL = -1,        /* a required pointer is NULL */
+    MOE_ERR_SHAPE = -2,       /* shape outside the limits above */
+    MOE_ERR_FORMAT = -3,      /* unknown or mixed pack format, missing Q2 mins */
+    MOE_ERR_ALIGN = -4,       /* a pointer is not aligned as required */
+    MOE_ERR_WORKSPACE = -5,   /* ws_bytes < moe_workspace_bytes(shape) */
+    MOE_ERR_UNSUPPORTED = -6, /* valid request this build cannot serve */
+    MOE_ERR_HIP = -7,         /* a HIP call (launch, copy) failed */
+    MOE_ERR_DEVICE = -8       /* a kernel flagged bad device data (see below) */
+};
+
+/* Device status bits, OR-ed into the workspace header by the kernels. */
+enum moe_device_status_bits {
+    MOE_DEV_BAD_EXPERT_ID = 1, /* a topk id outside [0, E) reached moe_dispatch */
+    MOE_DEV_BAD_SLOT = 2       /* slot_of_expert[e] outside [0, num_slots) for a routed e */
+};
+
+typedef struct moe_shape {
+    int32_t T; /* tokens in the call */
+    int32_t d; /* hidden size (model dimension) */
+    int32_t E; /* routed experts */
+    int32_t k; /* experts per token (top-k) */
+    int32_t f; /* expert FFN (intermediate) size */
+} moe_shape;
+
+/* Expert weight pack formats. */
+enum moe_format {
+    /* MXFP4 (OCP Microscaling v1.0): 4-bit e2m1 codes, element 2i of a row in
+       the LOW nibble of byte i, element 2i+1 in the HIGH nibble (bit 3 of a
+       code is its sign); one e8m0 scale byte per 32 consecutive elements
+       along K (value 2^(byte-127); byte 255 is not allowed).
+       codes  uint8 [slots][n][K/2], scales uint8 [slots][n][K/32], mins unused. */
+    MOE_FMT_MXFP4 = 1,
+    /* 2-bit group-asymmetric: w = scale * q + min, q in {0,1,2,3}; element 4i+j
+       of a row is bits (2j, 2j+1) of byte i; one fp16 scale and one fp16 min per
+       32 consecutive elements along K.
+       codes uint8 [slots][n][K/4], scales/mins uint16 (fp16) [slots][n][K/32]. */
+    MOE_FMT_Q2G32 = 2
+};
+
+/* One quantised matrix, n rows of K elements, for every slot. */
+typedef struct moe_qmat {
+    int32_t fmt;        /* enum moe_format */
+    const void* codes;  /* device */
+    const void* scales; /* device */
+    const void* mins;   /* device; Q2 only, NULL for MXFP4 */
+} moe_qmat;
+
+/* The experts of one layer.  gate and up are n=f rows of K=d; down is n=d
+   rows of K=f.  All three use the same format.  Expert e lives in pack slot
+   slot_of_expert[e] (device int32 [E]) or, when slot_of_expert is NULL, in
+   slot e (then num_slots >= E is required).  A routed expert whose slot is
+   outside [0, num_slots) is not computed: its y rows are written as zeros and
+   MOE_DEV_BAD_SLOT is raised. */
+typedef struct moe_experts {
+    moe_qmat gate, up, down;
+    const int32_t* slot_of_expert;
+    int32_t num_slots;
+} moe_experts;
+
+/* Workspace bytes moe_dispatch / moe_expert_ffn / moe_layer need for `shape`
+   (a 256-byte header holding the device status word, then the bf16 SwiGLU
+   intermediate act[T*k][f]).  Returns 0 for an invalid shape.  The header
+   must be zeroed once before first use (moe_workspace_init does it). */
+size_t moe_workspace_bytes(const moe_shape* shape);
+
+/* Clears the workspace header (device status word) on `stream`. */
+int moe_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Steps 1-2.  x bf16 [T][d]; w_router fp32 [E][d]; bias fp32 [E] or NULL.
+   If w_router != NULL the logits are computed and written to logits fp32
+   [T][E]; if w_router == NULL, logits is an INPUT (given router logits) and
+   bias must be NULL.  Logits must be finite (NaN gives unspecified routing).
+   Out: topk_ids int32 [T][k] in selection order, topk_w fp32 [T][k].
+   Ties between equal logits go to the lower expert id; -0.0 == +0.0. */
+int moe_route_topk(const moe_shape* shape, const uint16_t* x, const float* w_router,
+                   const float* bias, float* logits, int32_t* topk_ids, float* topk_w,
+                   hipStream_t stream);
+
+/* Step 3.  topk_ids int32 [T][k] (any source).  Out: offsets int32 [E+1]
+   (offsets[0] = 0, offsets[E] = number of valid pairs = T*k when all ids are
+   valid), perm int32 [T*k], inv int32 [T*k].  Pairs of one expert keep
+   ascending pair order (stable).  Ids outside [0, E) raise
+   MOE_DEV_BAD_EXPERT_ID and are sorted after every valid pair.  Uses the
+   workspace header only. */
+int moe_dispatch(const moe_shape* shape, const int32_t* topk_ids, int32_t* offsets,
+                 int32_t* perm, int32_t* inv, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Steps 4-5.  x bf16 [T][d]; offsets/perm as produced by moe_dispatch.
+   Out: y fp32 [T*k][d] in sorted-row order (rows at or past offsets[E] are
+   zero).  The bf16 intermediate act lives in ws.  Only experts with at least
+   one row are read from HBM. */
+int moe_expert_ffn(const moe_shape* shape, const uint16_t* x, const moe_experts* experts,
+                   const int32_t* offsets, const int32_t* perm, float* y, void* ws,
+                   size_t ws_bytes, hipStream_t stream);
+
+/* Step 6.  y fp32 [T*k][d], inv int32 [T*k], topk_w fp32 [T][k].
+   Out: out fp32 [T][d].  Fixed summation order j = 0..k-1 (deterministic). */
+int moe_combine(const moe_shape* shape, const float* y, const int32_t* inv,
+                const float* topk_w, float* out, hipStream_t stream);
+
+/* Steps 1-6 in one call; identical (bit for bit) to moe_route_topk,
+   moe_dispatch, moe_expert_ffn and moe_combine in sequence.  offsets, perm,
+   inv and y are carved from `ws`, which must hold
+   moe_layer_workspace_bytes(shape) bytes. */
+size_t moe_layer_workspace_bytes(const moe_shape* shape);
+int moe_layer(const moe_shape* shape, const uint16_t* x, const float* w_router,
+              const float* bias, float* logits, const moe_experts* experts,
+              int32_t* topk_ids, float* topk_w, float* out, void* ws, size_t ws_bytes,
+              hipStream_t stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* moe_status_str(int status);
+
+/* Synchronises `stream`, then reads the workspace's device status word.
+   Returns MOE_OK, MOE_ERR_DEVICE (some bit set; *bits receives the word when
+   bits != NULL) or MOE_ERR_HIP.  The word stays set until moe_workspace_init. */
+int moe_read_device_status(const void* ws, uint32_t* bits, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QUANTIZED_ROUTED_MOE_AMD_MOE_H */

@@ -254,6 +254,33 @@ def expert_ffn(x_bits, k: int, offsets, perm, gate: dict, up: dict, down: dict,
     return act, y
 
 
+def expert_ffn_rows(x_bits, k: int, offsets, perm, rows, gate: dict, up: dict, down: dict,
+                    slot_of_expert=None):
+    """Steps 4 and 5 for a chosen subset of sorted rows only (same arithmetic
+    as ``expert_ffn``), for checking large calls on sampled outputs.
+
+    Returns act float64 [len(rows), f] and y float64 [len(rows), d].
+    """
+    x = bf16_bits_to_f64(x_bits)
+    offsets = np.asarray(offsets, dtype=np.int64)
+    perm = np.asarray(perm, dtype=np.int64)
+    rows = np.asarray(rows, dtype=np.int64)
+    expert_of_row = np.searchsorted(offsets, rows, side="right") - 1
+    f = gate["codes"].shape[-2]
+    d = down["codes"].shape[-2]
+    act = np.zeros((rows.size, f), dtype=np.float64)
+    y = np.zeros((rows.size, d), dtype=np.float64)
+    for e in np.unique(expert_of_row):
+        sel = np.nonzero(expert_of_row == e)[0]
+        slot = int(e) if slot_of_expert is None else int(slot_of_expert[e])
+        wg, wu, wd = dequant(gate, slot), dequant(up, slot), dequant(down, slot)
+        xt = x[perm[rows[sel]] // k]
+        a = round_bf16(silu(xt @ wg.T) * (xt @ wu.T))
+        act[sel] = a
+        y[sel] = a @ wd.T
+    return act, y
+
+
 def combine(y, inv, w, k: int):
     """Step 6: out[t] = sum_j w[t, j] * y[inv[t*k + j]], summed in j order."""
     y = np.asarray(y, dtype=np.float64)

@@ -1,0 +1,312 @@
+"""Python binding of the routed MoE layer's C ABI (``include/moe.h``).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of
+``libqrmoe.so``.  torch supplies device memory (tensors) and the stream
+(``torch.cuda.current_stream()``).  There is no fallback: if the library is
+missing or a call fails, an exception is raised.
+
+The functions keep the C names.  Outputs are caller-allocated tensors, as in
+the C ABI; ``layer()`` is a convenience wrapper that allocates them.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libqrmoe.so")
+
+MOE_OK = 0
+MOE_ERR_NULL = -1
+MOE_ERR_SHAPE = -2
+MOE_ERR_FORMAT = -3
+MOE_ERR_ALIGN = -4
+MOE_ERR_WORKSPACE = -5
+MOE_ERR_UNSUPPORTED = -6
+MOE_ERR_HIP = -7
+MOE_ERR_DEVICE = -8
+
+MOE_DEV_BAD_EXPERT_ID = 1
+MOE_DEV_BAD_SLOT = 2
+
+MOE_FMT_MXFP4 = 1
+MOE_FMT_Q2G32 = 2
+FORMATS = {"mxfp4": MOE_FMT_MXFP4, "q2": MOE_FMT_Q2G32}
+
+# Every symbol include/moe.h declares.
+EXPORTS = (
+    "moe_workspace_bytes", "moe_workspace_init", "moe_route_topk", "moe_dispatch",
+    "moe_expert_ffn", "moe_combine", "moe_layer_workspace_bytes", "moe_layer",
+    "moe_status_str", "moe_read_device_status",
+)
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {status_str(code)} ({code})")
+
+
+class moe_shape(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("f", ctypes.c_int32)]
+
+
+class moe_qmat(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int32), ("codes", ctypes.c_void_p),
+                ("scales", ctypes.c_void_p), ("mins", ctypes.c_void_p)]
+
+
+class moe_experts(ctypes.Structure):
+    _fields_ = [("gate", moe_qmat), ("up", moe_qmat), ("down", moe_qmat),
+                ("slot_of_expert", ctypes.c_void_p), ("num_slots", ctypes.c_int32)]
+
+
+_LIB = None
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_SZ = ctypes.c_size_t
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`"
+                " (there is no CPU fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        sig = {
+            "moe_workspace_bytes": (_SZ, [_P]),
+            "moe_layer_workspace_bytes": (_SZ, [_P]),
+            "moe_workspace_init": (_I, [_P, _SZ, _P]),
+            "moe_route_topk": (_I, [_P, _P, _P, _P, _P, _P, _P, _P]),
+            "moe_dispatch": (_I, [_P, _P, _P, _P, _P, _P, _SZ, _P]),
+            "moe_expert_ffn": (_I, [_P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+            "moe_combine": (_I, [_P, _P, _P, _P, _P, _P]),
+            "moe_layer": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+            "moe_status_str": (ctypes.c_char_p, [_I]),
+            "moe_read_device_status": (_I, [_P, _P, _P]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = L
+    return _LIB
+
+
+def status_str(code: int) -> str:
+    return lib().moe_status_str(int(code)).decode()
+
+
+# ------------------------------------------------------------------ helpers
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream) -> int:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return int(s.cuda_stream)
+
+
+def _ptr(t, dtype=None, name="tensor", allow_none=False) -> Optional[int]:
+    if t is None:
+        if allow_none:
+            return None
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    return t.data_ptr()
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != MOE_OK:
+        raise MoeError(rc, where)
+
+
+@dataclass(frozen=True)
+class Shape:
+    T: int
+    d: int
+    E: int
+    k: int
+    f: int
+
+    def c(self) -> moe_shape:
+        return moe_shape(self.T, self.d, self.E, self.k, self.f)
+
+
+@dataclass
+class QMat:
+    """One quantised matrix pack on the device (see include/moe.h)."""
+    codes: object
+    scales: object
+    mins: object = None
+
+
+@dataclass
+class Experts:
+    """The gate/up/down packs of one layer (device tensors)."""
+    fmt: str
+    gate: QMat
+    up: QMat
+    down: QMat
+    slot_of_expert: object = None
+    num_slots: int = 0
+
+    def c(self) -> moe_experts:
+        torch = _torch()
+        f = FORMATS[self.fmt]
+        u16 = (torch.uint16, torch.int16)
+
+        def q(m: QMat, name: str) -> moe_qmat:
+            codes = _ptr(m.codes, torch.uint8, f"{name}.codes")
+            if self.fmt == "mxfp4":
+                scales = _ptr(m.scales, torch.uint8, f"{name}.scales")
+                mins = None
+            else:
+                scales = _ptr(m.scales, u16, f"{name}.scales")
+                mins = _ptr(m.mins, u16, f"{name}.mins")
+            return moe_qmat(f, codes, scales, mins)
+
+        slots = self.num_slots or int(self.gate.codes.shape[0])
+        soe = _ptr(self.slot_of_expert, torch.int32, "slot_of_expert", allow_none=True)
+        return moe_experts(q(self.gate, "gate"), q(self.up, "up"), q(self.down, "down"), soe, slots)
+
+    @staticmethod
+    def from_arrays(fmt: str, gate: dict, up: dict, down: dict, device="cuda",
+                    slot_of_expert=None) -> "Experts":
+        """Copy host arrays (numpy; codes uint8, scales uint8 or uint16 fp16
+        bits, mins uint16) to device tensors."""
+        torch = _torch()
+
+        def dev(a):
+            if a is None:
+                return None
+            t = torch.from_numpy(a) if not isinstance(a, torch.Tensor) else a
+            if t.dtype == torch.uint16:
+                t = t.view(torch.int16)
+            return t.contiguous().to(device)
+
+        mk = lambda m: QMat(dev(m["codes"]), dev(m["scales"]), dev(m.get("mins")))
+        soe = None if slot_of_expert is None else dev(slot_of_expert).to(torch.int32)
+        return Experts(fmt, mk(gate), mk(up), mk(down), soe, int(gate["codes"].shape[0]))
+
+
+# ------------------------------------------------------------ C entry points
+
+def moe_workspace_bytes(shape: Shape) -> int:
+    return int(lib().moe_workspace_bytes(ctypes.byref(shape.c())))
+
+
+def moe_layer_workspace_bytes(shape: Shape) -> int:
+    return int(lib().moe_layer_workspace_bytes(ctypes.byref(shape.c())))
+
+
+def moe_workspace_init(ws, stream=None) -> None:
+    _check(lib().moe_workspace_init(_ptr(ws, name="ws"), ws.numel() * ws.element_size(), _stream(stream)),
+           "moe_workspace_init")
+
+
+def moe_route_topk(shape: Shape, x, w_router, bias, logits, topk_ids, topk_w, stream=None) -> None:
+    torch = _torch()
+    rc = lib().moe_route_topk(
+        ctypes.byref(shape.c()), _ptr(x, (torch.int16, torch.bfloat16, torch.uint16), "x", allow_none=True),
+        _ptr(w_router, torch.float32, "w_router", allow_none=True),
+        _ptr(bias, torch.float32, "bias", allow_none=True), _ptr(logits, torch.float32, "logits"),
+        _ptr(topk_ids, torch.int32, "topk_ids"), _ptr(topk_w, torch.float32, "topk_w"), _stream(stream))
+    _check(rc, "moe_route_topk")
+
+
+def moe_dispatch(shape: Shape, topk_ids, offsets, perm, inv, ws, stream=None) -> None:
+    torch = _torch()
+    rc = lib().moe_dispatch(
+        ctypes.byref(shape.c()), _ptr(topk_ids, torch.int32, "topk_ids"),
+        _ptr(offsets, torch.int32, "offsets"), _ptr(perm, torch.int32, "perm"),
+        _ptr(inv, torch.int32, "inv"), _ptr(ws, name="ws"), ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc, "moe_dispatch")
+
+
+def moe_expert_ffn(shape: Shape, x, experts: Experts, offsets, perm, y, ws, stream=None) -> None:
+    torch = _torch()
+    ex = experts.c()
+    rc = lib().moe_expert_ffn(
+        ctypes.byref(shape.c()), _ptr(x, (torch.int16, torch.bfloat16, torch.uint16), "x"),
+        ctypes.byref(ex), _ptr(offsets, torch.int32, "offsets"), _ptr(perm, torch.int32, "perm"),
+        _ptr(y, torch.float32, "y"), _ptr(ws, name="ws"), ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc, "moe_expert_ffn")
+
+
+def moe_combine(shape: Shape, y, inv, topk_w, out, stream=None) -> None:
+    torch = _torch()
+    rc = lib().moe_combine(
+        ctypes.byref(shape.c()), _ptr(y, torch.float32, "y"), _ptr(inv, torch.int32, "inv"),
+        _ptr(topk_w, torch.float32, "topk_w"), _ptr(out, torch.float32, "out"), _stream(stream))
+    _check(rc, "moe_combine")
+
+
+def moe_layer(shape: Shape, x, w_router, bias, logits, experts: Experts, topk_ids, topk_w, out, ws,
+              stream=None) -> None:
+    torch = _torch()
+    ex = experts.c()
+    rc = lib().moe_layer(
+        ctypes.byref(shape.c()), _ptr(x, (torch.int16, torch.bfloat16, torch.uint16), "x"),
+        _ptr(w_router, torch.float32, "w_router", allow_none=True),
+        _ptr(bias, torch.float32, "bias", allow_none=True), _ptr(logits, torch.float32, "logits"),
+        ctypes.byref(ex), _ptr(topk_ids, torch.int32, "topk_ids"), _ptr(topk_w, torch.float32, "topk_w"),
+        _ptr(out, torch.float32, "out"), _ptr(ws, name="ws"), ws.numel() * ws.element_size(),
+        _stream(stream))
+    _check(rc, "moe_layer")
+
+
+def moe_read_device_status(ws, stream=None) -> int:
+    """Synchronises the stream; returns the device status bits (0 = clean)."""
+    bits = ctypes.c_uint32(0)
+    rc = lib().moe_read_device_status(_ptr(ws, name="ws"), ctypes.byref(bits), _stream(stream))
+    if rc not in (MOE_OK, MOE_ERR_DEVICE):
+        raise MoeError(rc, "moe_read_device_status")
+    return int(bits.value)
+
+
+# --------------------------------------------------------------- conveniences
+
+def alloc_workspace(shape: Shape, layer: bool = False, device="cuda", stream=None):
+    """A zero-initialised workspace tensor for `shape` (header cleared)."""
+    torch = _torch()
+    n = moe_layer_workspace_bytes(shape) if layer else moe_workspace_bytes(shape)
+    if n == 0:
+        raise MoeError(MOE_ERR_SHAPE, "alloc_workspace")
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    moe_workspace_init(ws, stream)
+    return ws
+
+
+def layer(x, experts: Experts, k: int, *, w_router=None, bias=None, logits=None, ws=None, stream=None):
+    """Run the whole layer; returns (out, topk_ids, topk_w, logits)."""
+    torch = _torch()
+    T, d = x.shape
+    E = int(w_router.shape[0]) if w_router is not None else int(logits.shape[1])
+    f = int(experts.gate.codes.shape[1])
+    shape = Shape(T, d, E, k, f)
+    dev = x.device
+    if logits is None:
+        logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    out = torch.empty((T, d), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = alloc_workspace(shape, layer=True, device=dev, stream=stream)
+    moe_layer(shape, x, w_router, bias, logits, experts, ids, w, out, ws, stream)
+    return out, ids, w, logits

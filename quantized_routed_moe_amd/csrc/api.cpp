@@ -1,0 +1,266 @@
+// C ABI of the routed MoE layer: argument validation (entirely on the host,
+// before any HIP call), workspace carving and kernel launches.  See
+// include/moe.h for the contract of every entry point.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/moe.h"
+#include "kernels.hpp"
+
+namespace {
+
+using qrmoe::FfnArgs;
+
+constexpr size_t kHeader = 256;
+
+size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int check_shape(const moe_shape* s) {
+    if (!s) return MOE_ERR_NULL;
+    if (s->T < 0 || s->k < 1 || s->E < 1 || s->E > 64 || s->k > s->E) return MOE_ERR_SHAPE;
+    if (s->d < 32 || s->f < 32 || s->d % 32 || s->f % 32) return MOE_ERR_SHAPE;
+    const long long rows = static_cast<long long>(s->T) * s->k;
+    const long long wide = s->d > s->f ? s->d : s->f;
+    if (rows * wide >= (1ll << 31)) return MOE_ERR_SHAPE;
+    return MOE_OK;
+}
+
+size_t ffn_ws_bytes(const moe_shape& s) {
+    return kHeader + align256(static_cast<size_t>(s.T) * s.k * s.f * 2);
+}
+
+struct LayerCarve {
+    size_t offsets, perm, inv, y, total;
+};
+
+LayerCarve layer_carve(const moe_shape& s) {
+    LayerCarve c;
+    const size_t pairs = static_cast<size_t>(s.T) * s.k;
+    c.offsets = ffn_ws_bytes(s);
+    c.perm = c.offsets + align256(static_cast<size_t>(s.E + 1) * 4);
+    c.inv = c.perm + align256(pairs * 4);
+    c.y = c.inv + align256(pairs * 4);
+    c.total = c.y + align256(pairs * s.d * 4);
+    return c;
+}
+
+int check_qmat(const moe_qmat& m, int fmt) {
+    if (m.fmt != fmt) return MOE_ERR_FORMAT;
+    if (!m.codes || !m.scales) return MOE_ERR_NULL;
+    if (!aligned(m.codes, 16) || !aligned(m.scales, 16)) return MOE_ERR_ALIGN;
+    if (fmt == MOE_FMT_Q2G32) {
+        if (!m.mins) return MOE_ERR_FORMAT;
+        if (!aligned(m.mins, 16)) return MOE_ERR_ALIGN;
+    }
+    return MOE_OK;
+}
+
+int check_experts(const moe_shape& s, const moe_experts* ex) {
+    if (!ex) return MOE_ERR_NULL;
+    const int fmt = ex->gate.fmt;
+    if (fmt != MOE_FMT_MXFP4 && fmt != MOE_FMT_Q2G32) return MOE_ERR_FORMAT;
+    int rc;
+    if ((rc = check_qmat(ex->gate, fmt)) != MOE_OK) return rc;
+    if ((rc = check_qmat(ex->up, fmt)) != MOE_OK) return rc;
+    if ((rc = check_qmat(ex->down, fmt)) != MOE_OK) return rc;
+    if (ex->num_slots < 1) return MOE_ERR_SHAPE;
+    if (!ex->slot_of_expert && ex->num_slots < s.E) return MOE_ERR_SHAPE;
+    if (ex->slot_of_expert && !aligned(ex->slot_of_expert, 4)) return MOE_ERR_ALIGN;
+    return MOE_OK;
+}
+
+int hip_rc(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// ---- unchecked bodies (arguments already validated) ----
+
+int do_route(const moe_shape& s, const uint16_t* x, const float* wr, const float* bias, float* logits,
+             int32_t* ids, float* w, hipStream_t st) {
+    return hip_rc(qrmoe::launch_route(s, x, wr, bias, logits, ids, w, st));
+}
+
+int do_dispatch(const moe_shape& s, const int32_t* ids, int32_t* offsets, int32_t* perm, int32_t* inv,
+                void* ws, hipStream_t st) {
+    return hip_rc(qrmoe::launch_dispatch(s, ids, offsets, perm, inv, static_cast<uint32_t*>(ws), st));
+}
+
+int do_ffn(const moe_shape& s, const uint16_t* x, const moe_experts* ex, const int32_t* offsets,
+           const int32_t* perm, float* y, void* ws, hipStream_t st) {
+    FfnArgs a;
+    a.T = s.T; a.d = s.d; a.E = s.E; a.k = s.k; a.f = s.f;
+    a.x = x;
+    a.offsets = offsets;
+    a.perm = perm;
+    a.slot_of_expert = ex->slot_of_expert;
+    a.num_slots = ex->num_slots;
+    const moe_qmat* mats[3] = {&ex->gate, &ex->up, &ex->down};
+    for (int i = 0; i < 3; ++i) {
+        a.codes[i] = static_cast<const uint8_t*>(mats[i]->codes);
+        a.scales[i] = static_cast<const uint8_t*>(mats[i]->scales);
+        a.mins[i] = static_cast<const uint16_t*>(mats[i]->mins);
+    }
+    a.act = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + kHeader);
+    a.y = y;
+    a.status = static_cast<uint32_t*>(ws);
+    return hip_rc(qrmoe::launch_ffn(s, ex->gate.fmt, a, st));
+}
+
+int do_combine(const moe_shape& s, const float* y, const int32_t* inv, const float* w, float* out,
+               hipStream_t st) {
+    return hip_rc(qrmoe::launch_combine(s, y, inv, w, out, st));
+}
+
+int check_route_args(const moe_shape& s, const uint16_t* x, const float* wr, const float* bias,
+                     const float* logits, const int32_t* ids, const float* w) {
+    if (!logits || !ids || !w) return MOE_ERR_NULL;
+    if (wr && !x) return MOE_ERR_NULL;
+    if (!wr && bias) return MOE_ERR_UNSUPPORTED;
+    if ((x && !aligned(x, 16)) || (wr && !aligned(wr, 16)) || !aligned(logits, 16)) return MOE_ERR_ALIGN;
+    if ((bias && !aligned(bias, 4)) || !aligned(ids, 4) || !aligned(w, 4)) return MOE_ERR_ALIGN;
+    (void)s;
+    return MOE_OK;
+}
+
+int check_dispatch_args(const moe_shape& s, const int32_t* ids, const int32_t* offsets,
+                        const int32_t* perm, const int32_t* inv, const void* ws, size_t ws_bytes) {
+    if (!ids || !offsets || !perm || !inv || !ws) return MOE_ERR_NULL;
+    if (!aligned(ids, 4) || !aligned(offsets, 4) || !aligned(perm, 4) || !aligned(inv, 4) || !aligned(ws, 16))
+        return MOE_ERR_ALIGN;
+    if (ws_bytes < kHeader) return MOE_ERR_WORKSPACE;
+    (void)s;
+    return MOE_OK;
+}
+
+int check_ffn_args(const moe_shape& s, const uint16_t* x, const moe_experts* ex, const int32_t* offsets,
+                   const int32_t* perm, const float* y, const void* ws, size_t ws_bytes) {
+    if (!x || !offsets || !perm || !y || !ws) return MOE_ERR_NULL;
+    int rc = check_experts(s, ex);
+    if (rc != MOE_OK) return rc;
+    if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ws, 16)) return MOE_ERR_ALIGN;
+    if (!aligned(offsets, 4) || !aligned(perm, 4)) return MOE_ERR_ALIGN;
+    if (ws_bytes < ffn_ws_bytes(s)) return MOE_ERR_WORKSPACE;
+    return MOE_OK;
+}
+
+int check_combine_args(const float* y, const int32_t* inv, const float* w, const float* out) {
+    if (!y || !inv || !w || !out) return MOE_ERR_NULL;
+    if (!aligned(y, 16) || !aligned(out, 16) || !aligned(inv, 4) || !aligned(w, 4)) return MOE_ERR_ALIGN;
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_bytes(const moe_shape* shape) {
+    if (check_shape(shape) != MOE_OK) return 0;
+    return ffn_ws_bytes(*shape);
+}
+
+size_t moe_layer_workspace_bytes(const moe_shape* shape) {
+    if (check_shape(shape) != MOE_OK) return 0;
+    return layer_carve(*shape).total;
+}
+
+int moe_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (!ws) return MOE_ERR_NULL;
+    if (!aligned(ws, 16)) return MOE_ERR_ALIGN;
+    if (ws_bytes < kHeader) return MOE_ERR_WORKSPACE;
+    return hip_rc(qrmoe::launch_clear_header(static_cast<uint32_t*>(ws), stream));
+}
+
+int moe_route_topk(const moe_shape* shape, const uint16_t* x, const float* w_router, const float* bias,
+                   float* logits, int32_t* topk_ids, float* topk_w, hipStream_t stream) {
+    int rc = check_shape(shape);
+    if (rc != MOE_OK) return rc;
+    if (shape->T == 0) return MOE_OK;
+    rc = check_route_args(*shape, x, w_router, bias, logits, topk_ids, topk_w);
+    if (rc != MOE_OK) return rc;
+    return do_route(*shape, x, w_router, bias, logits, topk_ids, topk_w, stream);
+}
+
+int moe_dispatch(const moe_shape* shape, const int32_t* topk_ids, int32_t* offsets, int32_t* perm,
+                 int32_t* inv, void* ws, size_t ws_bytes, hipStream_t stream) {
+    int rc = check_shape(shape);
+    if (rc != MOE_OK) return rc;
+    if (shape->T == 0) return MOE_OK;
+    rc = check_dispatch_args(*shape, topk_ids, offsets, perm, inv, ws, ws_bytes);
+    if (rc != MOE_OK) return rc;
+    return do_dispatch(*shape, topk_ids, offsets, perm, inv, ws, stream);
+}
+
+int moe_expert_ffn(const moe_shape* shape, const uint16_t* x, const moe_experts* experts,
+                   const int32_t* offsets, const int32_t* perm, float* y, void* ws, size_t ws_bytes,
+                   hipStream_t stream) {
+    int rc = check_shape(shape);
+    if (rc != MOE_OK) return rc;
+    if (shape->T == 0) return MOE_OK;
+    rc = check_ffn_args(*shape, x, experts, offsets, perm, y, ws, ws_bytes);
+    if (rc != MOE_OK) return rc;
+    return do_ffn(*shape, x, experts, offsets, perm, y, ws, stream);
+}
+
+int moe_combine(const moe_shape* shape, const float* y, const int32_t* inv, const float* topk_w,
+                float* out, hipStream_t stream) {
+    int rc = check_shape(shape);
+    if (rc != MOE_OK) return rc;
+    if (shape->T == 0) return MOE_OK;
+    rc = check_combine_args(y, inv, topk_w, out);
+    if (rc != MOE_OK) return rc;
+    return do_combine(*shape, y, inv, topk_w, out, stream);
+}
+
+int moe_layer(const moe_shape* shape, const uint16_t* x, const float* w_router, const float* bias,
+              float* logits, const moe_experts* experts, int32_t* topk_ids, float* topk_w, float* out,
+              void* ws, size_t ws_bytes, hipStream_t stream) {
+    int rc = check_shape(shape);
+    if (rc != MOE_OK) return rc;
+    if (shape->T == 0) return MOE_OK;
+    const moe_shape& s = *shape;
+    if (!ws || !out) return MOE_ERR_NULL;
+    if (!aligned(ws, 16) || !aligned(out, 16)) return MOE_ERR_ALIGN;
+    const LayerCarve c = layer_carve(s);
+    if (ws_bytes < c.total) return MOE_ERR_WORKSPACE;
+    char* base = static_cast<char*>(ws);
+    int32_t* offsets = reinterpret_cast<int32_t*>(base + c.offsets);
+    int32_t* perm = reinterpret_cast<int32_t*>(base + c.perm);
+    int32_t* inv = reinterpret_cast<int32_t*>(base + c.inv);
+    float* y = reinterpret_cast<float*>(base + c.y);
+    if ((rc = check_route_args(s, x, w_router, bias, logits, topk_ids, topk_w)) != MOE_OK) return rc;
+    if (!x) return MOE_ERR_NULL;
+    if ((rc = check_ffn_args(s, x, experts, offsets, perm, y, ws, ws_bytes)) != MOE_OK) return rc;
+    if ((rc = do_route(s, x, w_router, bias, logits, topk_ids, topk_w, stream)) != MOE_OK) return rc;
+    if ((rc = do_dispatch(s, topk_ids, offsets, perm, inv, ws, stream)) != MOE_OK) return rc;
+    if ((rc = do_ffn(s, x, experts, offsets, perm, y, ws, stream)) != MOE_OK) return rc;
+    return do_combine(s, y, inv, topk_w, out, stream);
+}
+
+const char* moe_status_str(int status) {
+    switch (status) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_NULL: return "MOE_ERR_NULL: a required pointer is NULL";
+        case MOE_ERR_SHAPE: return "MOE_ERR_SHAPE: shape outside the supported limits";
+        case MOE_ERR_FORMAT: return "MOE_ERR_FORMAT: unknown or mixed pack format, or Q2 pack without mins";
+        case MOE_ERR_ALIGN: return "MOE_ERR_ALIGN: pointer not aligned as required";
+        case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace too small";
+        case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: request not supported";
+        case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP call failed";
+        case MOE_ERR_DEVICE: return "MOE_ERR_DEVICE: a kernel flagged bad device data";
+        default: return "unknown moe status";
+    }
+}
+
+int moe_read_device_status(const void* ws, uint32_t* bits, hipStream_t stream) {
+    if (!ws) return MOE_ERR_NULL;
+    if (!aligned(ws, 16)) return MOE_ERR_ALIGN;
+    uint32_t word = 0;
+    if (hipMemcpyAsync(&word, ws, sizeof(word), hipMemcpyDeviceToHost, stream) != hipSuccess) return MOE_ERR_HIP;
+    if (hipStreamSynchronize(stream) != hipSuccess) return MOE_ERR_HIP;
+    if (bits) *bits = word;
+    return word ? MOE_ERR_DEVICE : MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,45 @@
+// Weighted combine: out[t] = sum_j w[t][j] * y[inv[t*k + j]], summed in
+// j order (deterministic; no atomics).  One workgroup per token, four floats
+// per thread per pass over d.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace qrmoe {
+
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
+                                                       const int32_t* __restrict__ inv,
+                                                       const float* __restrict__ w,
+                                                       float* __restrict__ out, int d, int k) {
+    const int t = blockIdx.x;
+    const int d4 = d / 4;
+    for (int i = threadIdx.x; i < d4; i += blockDim.x) {
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int j = 0; j < k; ++j) {
+            const float wj = w[static_cast<size_t>(t) * k + j];
+            const int r = inv[static_cast<size_t>(t) * k + j];
+            const float4 v = reinterpret_cast<const float4*>(y + static_cast<size_t>(r) * d)[i];
+            acc.x = fmaf(wj, v.x, acc.x);
+            acc.y = fmaf(wj, v.y, acc.y);
+            acc.z = fmaf(wj, v.z, acc.z);
+            acc.w = fmaf(wj, v.w, acc.w);
+        }
+        reinterpret_cast<float4*>(out + static_cast<size_t>(t) * d)[i] = acc;
+    }
+}
+
+__global__ void clear_header_kernel(uint32_t* header) {
+    if (threadIdx.x < kWsHeader / 4) header[threadIdx.x] = 0u;
+}
+
+hipError_t launch_combine(const moe_shape& s, const float* y, const int32_t* inv, const float* w,
+                          float* out, hipStream_t st) {
+    combine_kernel<<<s.T, 256, 0, st>>>(y, inv, w, out, s.d, s.k);
+    return hipGetLastError();
+}
+
+hipError_t launch_clear_header(uint32_t* header, hipStream_t st) {
+    clear_header_kernel<<<1, 64, 0, st>>>(header);
+    return hipGetLastError();
+}
+
+}  // namespace qrmoe

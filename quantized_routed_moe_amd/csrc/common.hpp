@@ -1,0 +1,124 @@
+// Device helpers shared by the gfx950 kernels of the routed MoE layer:
+// number formats (bf16, e2m1 / e8m0, 2-bit groups), MFMA operand types and
+// small wave64 utilities.  Everything here is written for CDNA4 (gfx950),
+// wave64 only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace qrmoe {
+
+constexpr int kWave = 64;
+constexpr int kMaxExperts = 64;
+constexpr int kGroup = 32;             // elements per quantisation group (MX block)
+constexpr size_t kWsHeader = 256;      // workspace header: device status word
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- bf16
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round-to-nearest-even float -> bf16 bit pattern (NaN stays NaN, quietened).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
+    uint32_t u = __float_as_uint(v);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+// IEEE binary16 bit pattern (low 16 bits) -> float (exact).
+__device__ __forceinline__ float fp16_to_f32(uint32_t bits) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits & 0xffffu)));
+}
+
+// Two bf16 (as one dword: low half = element 0) -> two floats.
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// ---------------------------------------------------------------- MXFP4
+
+// e8m0 byte -> float 2^(b-127).  Bytes 1..254 give normal floats exactly;
+// byte 0 (2^-127) is a float32 subnormal and is built separately.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
+    return b ? __uint_as_float(b << 23) : __uint_as_float(0x00400000u);
+}
+
+// Eight e2m1 codes (one dword, element 0 in the low nibble) times the block
+// scale -> eight bf16 in MFMA operand order.  Uses the gfx950 scaled
+// conversion, which applies the scale exactly (the product is representable
+// in bf16 for every code and every scale whose result is a normal bf16).
+__device__ __forceinline__ bf16x8 mxfp4x8_to_bf16(uint32_t codes, float scale) {
+    bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0);
+    bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1);
+    bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2);
+    bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3);
+    bf16x8 r;
+    r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+    r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+    return r;
+}
+
+// ---------------------------------------------------------------- MFMA
+
+// D = A(16x32) * B(32x16) + C, bf16 inputs, fp32 accumulate.
+// Lane l supplies A[l%16][8*(l/16) + 0..7] and B[8*(l/16) + 0..7][l%16];
+// it receives C[4*(l/16) + 0..3][l%16].
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// D = A(32x16) * B(16x32) + C.  Lane l supplies A[l%32][8*(l/32) + 0..7] and
+// B[8*(l/32) + 0..7][l%32]; it receives C[8*(i/4) + 4*(l/32) + i%4][l%32] in
+// element i (0..15).
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 bf16x8_from_u32x4(u32x4 v) {
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ bf16x8 bf16x8_zero() {
+    return __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+}
+
+// ---------------------------------------------------------------- misc
+
+__device__ __forceinline__ float silu_mul(float g, float u) {
+    // silu(g) * u = g / (1 + exp(-g)) * u
+    return g / (1.0f + expf(-g)) * u;
+}
+
+__device__ __forceinline__ void raise_status(uint32_t* status, uint32_t bit) {
+    atomicOr(status, bit);
+}
+
+// Active-expert lookup from offsets[E+1]: every lane of the calling wave
+// receives the id of the `a`-th expert (in id order) that owns at least one
+// row, or -1 if fewer than a+1 experts are active.  E <= 64.
+__device__ __forceinline__ int nth_active_expert(const int32_t* __restrict__ offsets, int E, int a) {
+    const int lane = threadIdx.x & (kWave - 1);
+    int cnt = 0;
+    if (lane < E) cnt = offsets[lane + 1] - offsets[lane];
+    const uint64_t mask = __ballot(cnt > 0);
+    const uint64_t below = lane ? (mask & ((~0ull) >> (64 - lane))) : 0ull;
+    const bool hit = cnt > 0 && __popcll(below) == a;
+    const uint64_t hitmask = __ballot(hit);
+    return hitmask ? __ffsll(static_cast<unsigned long long>(hitmask)) - 1 : -1;
+}
+
+__host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+}  // namespace qrmoe

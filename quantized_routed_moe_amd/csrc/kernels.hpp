@@ -1,0 +1,36 @@
+// Internal launch interface between the C ABI (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace qrmoe {
+
+// Everything the expert-FFN kernels read, resolved on the host.
+struct FfnArgs {
+    int T, d, E, k, f;
+    const uint16_t* x;            // bf16 [T][d]
+    const int32_t* offsets;       // [E+1]
+    const int32_t* perm;          // [T*k]
+    const int32_t* slot_of_expert;  // [E] or null
+    int num_slots;
+    const uint8_t* codes[3];      // gate, up, down
+    const uint8_t* scales[3];     // MXFP4: e8m0 bytes; Q2: fp16 bits
+    const uint16_t* mins[3];      // Q2 only
+    uint16_t* act;                // bf16 [T*k][f] (workspace)
+    float* y;                     // fp32 [T*k][d]
+    uint32_t* status;             // workspace header
+};
+
+hipError_t launch_route(const moe_shape& s, const uint16_t* x, const float* wr, const float* bias,
+                        float* logits, int32_t* ids, float* w, hipStream_t st);
+hipError_t launch_dispatch(const moe_shape& s, const int32_t* ids, int32_t* offsets, int32_t* perm,
+                           int32_t* inv, uint32_t* status, hipStream_t st);
+hipError_t launch_ffn(const moe_shape& s, int fmt, const FfnArgs& a, hipStream_t st);
+hipError_t launch_combine(const moe_shape& s, const float* y, const int32_t* inv, const float* w,
+                          float* out, hipStream_t st);
+hipError_t launch_clear_header(uint32_t* header, hipStream_t st);
+
+}  // namespace qrmoe

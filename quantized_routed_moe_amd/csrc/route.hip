@@ -1,0 +1,177 @@
+// Router logits and top-k selection with renormalised softmax weights.
+//
+// The router scores every token against every expert in full float32
+// precision (the ds4 guide, section "避坑指南", reports that quantised routers
+// collapse quality); the top-k experts per token are kept ("antirez ds4:
+// DeepSeek Metal inference", section 技术深度解析: top-2 of 64).
+//
+// Kernels:
+//   router_rows_kernel  small T: one workgroup per expert streams W_r[e] once
+//                       and dots it with every token (T <= kRowsMaxT).
+//   router_mfma_kernel  large T: fp32 MFMA tiles, 16 tokens x 16 experts per
+//                       wave, four waves cover 64 experts.
+//   topk_kernel         one wave64 per token, lane = expert.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace qrmoe {
+
+constexpr int kRowsMaxT = 8;
+constexpr int kRowsThreads = 256;
+
+// logits[t][e] for t in [t0, t0 + nt), one expert per workgroup.
+// Thread i handles elements 8*i .. 8*i+7 of each 8*256-element chunk of d.
+__global__ __launch_bounds__(kRowsThreads) void router_rows_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ bias,
+    float* __restrict__ logits, int T, int d, int E) {
+    const int e = blockIdx.x;
+    const int t0 = blockIdx.y * kRowsMaxT;
+    const int nt = min(kRowsMaxT, T - t0);
+    const float* wrow = wr + static_cast<size_t>(e) * d;
+    float acc[kRowsMaxT];
+#pragma unroll
+    for (int j = 0; j < kRowsMaxT; ++j) acc[j] = 0.f;
+    for (int i = threadIdx.x * 8; i < d; i += kRowsThreads * 8) {
+        const float4 w0 = *reinterpret_cast<const float4*>(wrow + i);
+        const float4 w1 = *reinterpret_cast<const float4*>(wrow + i + 4);
+#pragma unroll
+        for (int j = 0; j < kRowsMaxT; ++j) {
+            if (j < nt) {
+                const u32x4 xv = *reinterpret_cast<const u32x4*>(x + static_cast<size_t>(t0 + j) * d + i);
+                float s = acc[j];
+                s = fmaf(bf16lo(xv[0]), w0.x, s);
+                s = fmaf(bf16hi(xv[0]), w0.y, s);
+                s = fmaf(bf16lo(xv[1]), w0.z, s);
+                s = fmaf(bf16hi(xv[1]), w0.w, s);
+                s = fmaf(bf16lo(xv[2]), w1.x, s);
+                s = fmaf(bf16hi(xv[2]), w1.y, s);
+                s = fmaf(bf16lo(xv[3]), w1.z, s);
+                s = fmaf(bf16hi(xv[3]), w1.w, s);
+                acc[j] = s;
+            }
+        }
+    }
+    // wave reduction (fixed butterfly), then across the 4 waves in wave order
+    __shared__ float part[kRowsThreads / kWave][kRowsMaxT];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int j = 0; j < kRowsMaxT; ++j) {
+        float s = acc[j];
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+        if (lane == 0) part[wave][j] = s;
+    }
+    __syncthreads();
+    if (threadIdx.x < nt) {
+        const int j = threadIdx.x;
+        float s = part[0][j];
+#pragma unroll
+        for (int w = 1; w < kRowsThreads / kWave; ++w) s += part[w][j];
+        if (bias) s += bias[e];
+        logits[static_cast<size_t>(t0 + j) * E + e] = s;
+    }
+}
+
+// Large-T router.  Workgroup = 4 waves = 16 tokens x 64 experts; wave w owns
+// experts 16w .. 16w+15.  fp32 MFMA 16x16x4: in MFMA s of a 16-wide K step,
+// lane group g (= lane / 16) supplies element k0 + 4g + s, so each lane reads
+// 4 consecutive floats of W_r and 4 consecutive bf16 of x per K step.
+typedef float f32x1v __attribute__((ext_vector_type(1)));
+__global__ __launch_bounds__(256) void router_mfma_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ bias,
+    float* __restrict__ logits, int T, int d, int E) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int t0 = blockIdx.x * 16;
+    const int e0 = wave * 16;
+    if (e0 >= E) return;
+    const int row = lane & 15, g = lane >> 4;
+    const int tok = t0 + row;
+    const int ex = e0 + row;
+    const bool tok_ok = tok < T, ex_ok = ex < E;
+    const uint16_t* xr = x + static_cast<size_t>(tok_ok ? tok : 0) * d + 4 * g;
+    const float* wrow = wr + static_cast<size_t>(ex_ok ? ex : 0) * d + 4 * g;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int k0 = 0; k0 < d; k0 += 16) {
+        float4 wv = ex_ok ? *reinterpret_cast<const float4*>(wrow + k0) : make_float4(0.f, 0.f, 0.f, 0.f);
+        u32x2 xv = tok_ok ? *reinterpret_cast<const u32x2*>(xr + k0) : u32x2{0u, 0u};
+        // A = x (16 tokens x 4), B = W_r^T (4 x 16 experts)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16lo(xv[0]), wv.x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16hi(xv[0]), wv.y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16lo(xv[1]), wv.z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16hi(xv[1]), wv.w, acc, 0, 0, 0);
+    }
+    // acc[i] = C[token 4g + i][expert row]
+    if (ex_ok) {
+        const float b = bias ? bias[ex] : 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = t0 + 4 * g + i;
+            if (t < T) logits[static_cast<size_t>(t) * E + ex] = acc[i] + b;
+        }
+    }
+}
+
+// Sortable key of a finite float: larger float -> larger unsigned key; -0 and
+// +0 share the key of +0.
+__device__ __forceinline__ uint32_t float_key(float v) {
+    uint32_t u = __float_as_uint(v);
+    if ((u & 0x7fffffffu) == 0u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// One wave per token; lane e holds expert e's logit.  k rounds of a 64-bit
+// wave max over (key(logit) << 32 | 63 - e) pick experts in (logit desc, id
+// asc) order.  The softmax over the selected logits is taken against the
+// first (largest) one and summed in selection order.
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits,
+                                                    int32_t* __restrict__ ids,
+                                                    float* __restrict__ w, int T, int E, int k) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * (blockDim.x / kWave) + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const float l = lane < E ? logits[static_cast<size_t>(t) * E + lane] : 0.f;
+    uint64_t key = lane < E ? ((static_cast<uint64_t>(float_key(l)) << 32) | static_cast<uint32_t>(63 - lane)) : 0ull;
+    int my_sel = -1;       // lane j < k: expert chosen in round j
+    float my_l = 0.f;      // its logit
+    float lmax = 0.f;
+    for (int j = 0; j < k; ++j) {
+        uint64_t m = key;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            const uint64_t other = __shfl_xor(m, o);
+            m = other > m ? other : m;
+        }
+        const int e = 63 - static_cast<int>(m & 63u);
+        const float le = __shfl(l, e);
+        if (j == 0) lmax = le;
+        if (lane == j) { my_sel = e; my_l = le; }
+        if (lane == e) key = 0ull;
+    }
+    float ex = lane < k ? expf(my_l - lmax) : 0.f;
+    // sum in selection order (lane 0, 1, ..., k-1)
+    float sum = 0.f;
+    for (int j = 0; j < k; ++j) sum += __shfl(ex, j);
+    if (lane < k) {
+        ids[static_cast<size_t>(t) * k + lane] = my_sel;
+        w[static_cast<size_t>(t) * k + lane] = ex / sum;
+    }
+}
+
+hipError_t launch_route(const moe_shape& s, const uint16_t* x, const float* wr, const float* bias,
+                        float* logits, int32_t* ids, float* w, hipStream_t st) {
+    if (wr) {
+        if (s.T <= 4 * kRowsMaxT) {
+            dim3 grid(s.E, ceil_div(s.T, kRowsMaxT));
+            router_rows_kernel<<<grid, kRowsThreads, 0, st>>>(x, wr, bias, logits, s.T, s.d, s.E);
+        } else {
+            router_mfma_kernel<<<ceil_div(s.T, 16), 256, 0, st>>>(x, wr, bias, logits, s.T, s.d, s.E);
+        }
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    topk_kernel<<<ceil_div(s.T, 4), 256, 0, st>>>(logits, ids, w, s.T, s.E, s.k);
+    return hipGetLastError();
+}
+
+}  // namespace qrmoe

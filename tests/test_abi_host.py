@@ -1,0 +1,144 @@
+"""The C-ABI library on the host (no GPU needed): it loads, exports every
+symbol include/moe.h declares, and rejects every invalid request with the
+documented status code before making any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_routed_moe_amd as qm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+A16 = 0x10000          # fake, 16-byte aligned "device" addresses (never dereferenced)
+
+
+def _declared_symbols():
+    text = open(os.path.join(ROOT, "include", "moe.h")).read()
+    return sorted(set(re.findall(r"^(?:size_t|int|const char\s*\*)\s+(moe_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    syms = _declared_symbols()
+    assert len(syms) == 10
+    assert sorted(qm.EXPORTS) == syms
+    L = ctypes.CDLL(qm.LIB_PATH)
+    for s in syms:
+        assert hasattr(L, s), s
+
+
+def test_status_strings():
+    codes = [qm.MOE_OK, qm.MOE_ERR_NULL, qm.MOE_ERR_SHAPE, qm.MOE_ERR_FORMAT, qm.MOE_ERR_ALIGN,
+             qm.MOE_ERR_WORKSPACE, qm.MOE_ERR_UNSUPPORTED, qm.MOE_ERR_HIP, qm.MOE_ERR_DEVICE]
+    names = [qm.status_str(c) for c in codes]
+    assert len(set(names)) == len(codes)
+    for c, n in zip(codes, names):
+        assert n.startswith("MOE_")
+    assert "unknown" in qm.status_str(-99)
+
+
+def _shape(T=4, d=256, E=8, k=2, f=128):
+    return qm.moe_shape(T, d, E, k, f)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(k=0), dict(k=9), dict(E=65, k=2), dict(E=0), dict(d=48), dict(f=100), dict(d=0),
+    dict(T=-1), dict(T=1 << 20, d=4096, k=8),
+])
+def test_shape_validation(bad):
+    s = _shape(**bad)
+    assert qm.lib().moe_workspace_bytes(ctypes.byref(s)) == 0
+    assert qm.lib().moe_layer_workspace_bytes(ctypes.byref(s)) == 0
+    rc = qm.lib().moe_combine(ctypes.byref(s), A16, A16, A16, A16, None)
+    assert rc == qm.MOE_ERR_SHAPE
+
+
+def test_workspace_sizes():
+    s = _shape(T=5, d=4096, E=64, k=2, f=2048)
+    # 256-byte header + bf16 act[T*k][f] rounded up to 256
+    assert qm.lib().moe_workspace_bytes(ctypes.byref(s)) == 256 + 5 * 2 * 2048 * 2
+    lw = qm.lib().moe_layer_workspace_bytes(ctypes.byref(s))
+    al = lambda v: (v + 255) // 256 * 256
+    assert lw == 256 + al(5 * 2 * 2048 * 2) + al(65 * 4) + 2 * al(10 * 4) + al(10 * 4096 * 4)
+
+
+def test_null_shape_and_zero_tokens():
+    assert qm.lib().moe_combine(None, A16, A16, A16, A16, None) == qm.MOE_ERR_NULL
+    # T == 0 is valid and enqueues nothing, whatever the pointers
+    s = _shape(T=0)
+    assert qm.lib().moe_combine(ctypes.byref(s), None, None, None, None, None) == qm.MOE_OK
+    assert qm.lib().moe_layer(ctypes.byref(s), *([None] * 9), 0, None) == qm.MOE_OK
+
+
+def _experts(fmt=qm.MOE_FMT_MXFP4, mins=None, slots=8, soe=None, **over):
+    q = lambda: qm.moe_qmat(fmt, A16, A16, mins)
+    e = qm.moe_experts(q(), q(), q(), soe, slots)
+    for k, v in over.items():
+        setattr(e, k, v)
+    return e
+
+
+def _ffn(s, ex, x=A16, offsets=A16, perm=A16, y=A16, ws=A16, ws_bytes=1 << 30):
+    return qm.lib().moe_expert_ffn(ctypes.byref(s), x, ctypes.byref(ex) if ex is not None else None,
+                                   offsets, perm, y, ws, ws_bytes, None)
+
+
+def test_ffn_validation():
+    s = _shape()
+    assert _ffn(s, None) == qm.MOE_ERR_NULL
+    assert _ffn(s, _experts(), x=None) == qm.MOE_ERR_NULL
+    assert _ffn(s, _experts(), y=None) == qm.MOE_ERR_NULL
+    assert _ffn(s, _experts(fmt=7)) == qm.MOE_ERR_FORMAT
+    mixed = _experts()
+    mixed.down = qm.moe_qmat(qm.MOE_FMT_Q2G32, A16, A16, A16)
+    assert _ffn(s, mixed) == qm.MOE_ERR_FORMAT
+    assert _ffn(s, _experts(fmt=qm.MOE_FMT_Q2G32, mins=None)) == qm.MOE_ERR_FORMAT
+    assert _ffn(s, _experts(slots=7)) == qm.MOE_ERR_SHAPE            # identity map needs E slots
+    assert _ffn(s, _experts(slots=0, soe=A16)) == qm.MOE_ERR_SHAPE
+    assert _ffn(s, _experts(), x=A16 + 8) == qm.MOE_ERR_ALIGN
+    assert _ffn(s, _experts(), y=A16 + 4) == qm.MOE_ERR_ALIGN
+    bad = _experts()
+    bad.up = qm.moe_qmat(qm.MOE_FMT_MXFP4, A16 + 2, A16, None)
+    assert _ffn(s, bad) == qm.MOE_ERR_ALIGN
+    assert _ffn(s, _experts(fmt=qm.MOE_FMT_Q2G32, mins=A16 + 8)) == qm.MOE_ERR_ALIGN
+    assert _ffn(s, _experts(soe=A16 + 2, slots=4)) == qm.MOE_ERR_ALIGN
+    need = qm.lib().moe_workspace_bytes(ctypes.byref(s))
+    assert _ffn(s, _experts(), ws_bytes=need - 1) == qm.MOE_ERR_WORKSPACE
+    assert _ffn(s, _experts(), ws=None) == qm.MOE_ERR_NULL
+
+
+def test_route_dispatch_combine_validation():
+    s = _shape()
+    L = qm.lib()
+    # given logits (no router) cannot take a bias
+    assert L.moe_route_topk(ctypes.byref(s), A16, None, A16, A16, A16, A16, None) == qm.MOE_ERR_UNSUPPORTED
+    assert L.moe_route_topk(ctypes.byref(s), None, A16, None, A16, A16, A16, None) == qm.MOE_ERR_NULL
+    assert L.moe_route_topk(ctypes.byref(s), A16, A16, None, None, A16, A16, None) == qm.MOE_ERR_NULL
+    assert L.moe_route_topk(ctypes.byref(s), A16 + 2, A16, None, A16, A16, A16, None) == qm.MOE_ERR_ALIGN
+    assert L.moe_route_topk(ctypes.byref(s), A16, A16, None, A16, A16 + 2, A16, None) == qm.MOE_ERR_ALIGN
+    assert L.moe_dispatch(ctypes.byref(s), None, A16, A16, A16, A16, 1 << 20, None) == qm.MOE_ERR_NULL
+    assert L.moe_dispatch(ctypes.byref(s), A16, A16, A16 + 1, A16, A16, 1 << 20, None) == qm.MOE_ERR_ALIGN
+    assert L.moe_dispatch(ctypes.byref(s), A16, A16, A16, A16, A16, 100, None) == qm.MOE_ERR_WORKSPACE
+    assert L.moe_combine(ctypes.byref(s), A16, A16, None, A16, None) == qm.MOE_ERR_NULL
+    assert L.moe_combine(ctypes.byref(s), A16, A16, A16, A16 + 4, None) == qm.MOE_ERR_ALIGN
+    assert L.moe_workspace_init(None, 256, None) == qm.MOE_ERR_NULL
+    assert L.moe_workspace_init(A16, 100, None) == qm.MOE_ERR_WORKSPACE
+    assert L.moe_read_device_status(None, None, None) == qm.MOE_ERR_NULL
+
+
+def test_layer_validation():
+    s = _shape()
+    L = qm.lib()
+    ex = _experts()
+    need = L.moe_layer_workspace_bytes(ctypes.byref(s))
+    args = lambda **o: [ctypes.byref(s), o.get("x", A16), o.get("wr", A16), o.get("bias", None),
+                        o.get("logits", A16), ctypes.byref(o.get("ex", ex)), o.get("ids", A16),
+                        o.get("w", A16), o.get("out", A16), o.get("ws", A16), o.get("wsb", need), None]
+    assert L.moe_layer(*args(ws=None)) == qm.MOE_ERR_NULL
+    assert L.moe_layer(*args(out=None)) == qm.MOE_ERR_NULL
+    assert L.moe_layer(*args(wsb=need - 1)) == qm.MOE_ERR_WORKSPACE
+    assert L.moe_layer(*args(x=None)) == qm.MOE_ERR_NULL
+    assert L.moe_layer(*args(ex=_experts(fmt=3))) == qm.MOE_ERR_FORMAT
+    assert L.moe_layer(*args(wr=None, bias=A16)) == qm.MOE_ERR_UNSUPPORTED

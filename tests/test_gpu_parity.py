@@ -1,0 +1,187 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle: the five
+workloads at their full sizes, ragged shapes spanning several tiles, and the
+degenerate cases of routing and dispatch."""
+
+import numpy as np
+import pytest
+import torch
+
+import quantized_routed_moe_amd as qm
+import synthetic
+from gpu_util import (assert_close, check_against_oracle, device_case, run_layer, run_steps)
+from oracle import ref
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+@pytest.mark.parametrize("c", [0, 1, 2, 4])
+def test_workload_full(c):
+    case = synthetic.workload(c)
+    _say(f"workload {c}: T={case['T']} d={case['d']} E={case['E']} k={case['k']} f={case['f']} {case['fmt']}")
+    dc = device_case(case)
+    g = run_steps(dc)
+    assert g["status"] == 0
+    info = check_against_oracle(case, g)
+    _say(f"  parity ok {info}")
+    lay = run_layer(dc)
+    for n in ("out", "ids", "w", "logits"):
+        assert np.array_equal(lay[n], g[n]), f"moe_layer differs from the four calls in {n}"
+
+
+def test_workload_prefill_sampled():
+    case = synthetic.workload(3)
+    _say("workload 3 (prefill chunk T=2048), sampled rows")
+    dc = device_case(case)
+    g = run_steps(dc)
+    assert g["status"] == 0
+    rng = np.random.default_rng(0)
+    toks = rng.choice(case["T"], size=40, replace=False)
+    rows = np.sort(np.array([g["inv"][t * case["k"] + j] for t in toks for j in range(case["k"])]))
+    info = check_against_oracle(case, g, rows=rows)
+    _say(f"  parity ok {info}")
+    lay = run_layer(dc)
+    assert np.array_equal(lay["out"], g["out"])
+
+
+SHAPES = [
+    # T, d, E, k, f        (d, f multiples of 32 but not of 128: ragged K steps)
+    (37, 384, 16, 3, 224),
+    (3, 96, 4, 2, 64),
+    (100, 512, 64, 8, 256),
+    (17, 256, 8, 8, 128),
+    (1, 32, 1, 1, 32),
+    (64, 1024, 32, 2, 512),
+]
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "q2"])
+@pytest.mark.parametrize("shape", SHAPES)
+def test_ragged_shapes(fmt, shape):
+    T, d, E, k, f = shape
+    case = synthetic.make_case(T, d, E, k, f, fmt, seed=hash((fmt,) + shape) % 1000, zipf=1.1)
+    _say(f"shape {shape} {fmt}")
+    g = run_steps(device_case(case))
+    assert g["status"] == 0
+    check_against_oracle(case, g)
+
+
+def _given(case, logits):
+    case = dict(case)
+    case["logits"] = np.asarray(logits, dtype=np.float32)
+    case["w_router"] = None
+    case["bias"] = None
+    return case
+
+
+def test_one_expert_takes_every_token():
+    base = synthetic.make_case(40, 256, 8, 2, 128, "mxfp4", seed=3)
+    lg = np.random.default_rng(1).standard_normal((40, 8)).astype(np.float32)
+    lg[:, 5] = 50.0
+    case = _given(base, lg)
+    g = run_steps(device_case(case))
+    check_against_oracle(case, g)
+    assert np.all(g["ids"][:, 0] == 5)
+
+
+def test_exact_ties_and_signed_zero():
+    base = synthetic.make_case(6, 128, 8, 3, 64, "mxfp4", seed=4)
+    lg = np.zeros((6, 8), np.float32)
+    lg[1] = [1, 1, 1, 1, 2, 2, 0, 0]
+    lg[2] = [-0.0, 0.0, -0.0, 0.0, -1, -1, -1, -1]
+    lg[3] = [0.5, -0.0, 0.5, 0.0, 0.5, -2, 3, 0.5]
+    lg[4] = np.float32(1e-30) * np.arange(8)
+    lg[5] = -np.arange(8, dtype=np.float32)
+    case = _given(base, lg)
+    g = run_steps(device_case(case))
+    check_against_oracle(case, g)
+    assert g["ids"][0].tolist() == [0, 1, 2]
+    assert g["ids"][2].tolist() == [0, 1, 2]
+    assert g["ids"][3].tolist() == [6, 0, 2]
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "q2"])
+def test_single_expert_and_full_fanout(fmt):
+    c1 = synthetic.make_case(9, 128, 1, 1, 64, fmt, seed=5)
+    check_against_oracle(c1, run_steps(device_case(c1)))
+    c2 = synthetic.make_case(9, 128, 8, 8, 64, fmt, seed=6)
+    g = run_steps(device_case(c2))
+    check_against_oracle(c2, g)
+    assert np.all(np.sort(g["ids"], axis=1) == np.arange(8))
+
+
+def test_zero_tokens_is_a_noop():
+    s = qm.Shape(0, 256, 8, 2, 128)
+    t = torch.empty(0, device="cuda")
+    qm.moe_combine(s, t.float(), t.int(), t.float(), t.float())
+
+
+def test_slot_indirection():
+    case = synthetic.make_case(12, 256, 8, 2, 128, "mxfp4", seed=7, slots=11)
+    soe = np.array([10, 3, 0, 7, 1, 9, 2, 5], np.int32)
+    case["slot_of_expert"] = soe
+    g = run_steps(device_case(case))
+    assert g["status"] == 0
+    check_against_oracle(case, g)
+
+
+def test_bad_slot_raises_status_and_zeroes_rows():
+    case = synthetic.make_case(12, 256, 8, 2, 128, "mxfp4", seed=8, slots=8)
+    lg = np.random.default_rng(2).standard_normal((12, 8)).astype(np.float32)
+    lg[:, 6] = 9.0                          # every token routes to expert 6
+    case = _given(case, lg)
+    case["slot_of_expert"] = np.array([0, 1, 2, 3, 4, 5, 99, 7], np.int32)
+    g = run_steps(device_case(case))
+    assert g["status"] == qm.MOE_DEV_BAD_SLOT
+    rows6 = np.arange(g["offsets"][6], g["offsets"][7])
+    assert rows6.size == 12 and np.all(g["y"][rows6] == 0.0)
+
+
+def test_dispatch_bad_ids():
+    s = qm.Shape(5, 64, 4, 2, 32)
+    ids = torch.tensor([[0, 1], [7, 2], [3, -1], [1, 0], [2, 3]], dtype=torch.int32, device="cuda")
+    offsets = torch.empty(5, dtype=torch.int32, device="cuda")
+    perm = torch.empty(10, dtype=torch.int32, device="cuda")
+    inv = torch.empty(10, dtype=torch.int32, device="cuda")
+    ws = qm.alloc_workspace(s)
+    qm.moe_dispatch(s, ids, offsets, perm, inv, ws)
+    assert qm.moe_read_device_status(ws) == qm.MOE_DEV_BAD_EXPERT_ID
+    off, pm, iv = offsets.cpu().numpy(), perm.cpu().numpy(), inv.cpu().numpy()
+    assert off.tolist() == [0, 2, 4, 6, 8]
+    assert pm.tolist() == [0, 7, 1, 6, 3, 8, 4, 9, 2, 5]
+    assert np.array_equal(iv[pm], np.arange(10))
+
+
+def test_determinism_and_token_permutation():
+    case = synthetic.make_case(29, 512, 16, 2, 256, "mxfp4", seed=9, zipf=1.1)
+    dc = device_case(case)
+    a, b = run_steps(dc), run_steps(dc)
+    for n in ("logits", "ids", "w", "perm", "y", "out", "act"):
+        assert np.array_equal(a[n], b[n]), n
+    pi = np.random.default_rng(3).permutation(29)
+    case2 = dict(case)
+    case2["x"] = case["x"][pi]
+    c = run_steps(device_case(case2))
+    assert np.array_equal(c["ids"], a["ids"][pi])
+    assert np.array_equal(c["out"], a["out"][pi])
+
+
+@pytest.mark.parametrize("c", [1, 4])
+def test_power_of_two_scaling(c):
+    """+1 on every down-projection scale exponent doubles the output exactly."""
+    case = synthetic.workload(c)
+    a = run_steps(device_case(case))
+    case2 = dict(case)
+    d2 = dict(case["down"])
+    if case["fmt"] == "mxfp4":
+        d2["scales"] = d2["scales"] + np.uint8(1)
+    else:
+        # x2 in binary16 is exact (normal and subnormal values alike)
+        d2["scales"] = (d2["scales"].view(np.float16) * np.float16(2)).view(np.uint16)
+        d2["mins"] = (d2["mins"].view(np.float16) * np.float16(2)).view(np.uint16)
+    case2["down"] = d2
+    b = run_steps(device_case(case2))
+    assert np.array_equal(b["out"], 2.0 * a["out"])

@@ -315,9 +315,9 @@ def test_power_of_two_scale_invariance():
     q = _small_case("q2", T=4, d=64, E=4, k=2, f=32, seed=23)
     base = ref.layer(q["x"], 2, q["gate"], q["up"], q["down"], w_router=q["w_router"])["out"]
     m = dict(q["down"])
-    # doubling an fp16 value = adding 1 to its exponent field (values are normal)
-    m["scales"] = m["scales"] + np.uint16(1 << 10)
-    m["mins"] = np.where(m["mins"] & 0x7FFF, m["mins"] + np.uint16(1 << 10), m["mins"]).astype(np.uint16)
+    # x2 in binary16 is exact (normal and subnormal values alike)
+    m["scales"] = (m["scales"].view(np.float16) * np.float16(2)).view(np.uint16)
+    m["mins"] = (m["mins"].view(np.float16) * np.float16(2)).view(np.uint16)
     out = ref.layer(q["x"], 2, q["gate"], q["up"], m, w_router=q["w_router"])["out"]
     assert np.array_equal(out, 2.0 * base)
 
