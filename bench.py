@@ -145,36 +145,69 @@ def main():
     out = torch.empty((T, d), dtype=torch.float32, device=dev)
     ws = qm.alloc_workspace(shape, layer=True, device=dev)
 
-    def step(i, ev=None):
-        p = i % n_pools
-        x = xs[i % n_x]
-        if given is not None:
-            logits.copy_(given[i % n_x])
-            wr, b = None, None
-        else:
-            wr, b = routers[p]
-        qm.moe_route_topk(shape, x, wr, b, logits, ids, tw)
-        qm.moe_dispatch(shape, ids, offsets, perm, inv, ws)
+    # Raw C-ABI calls with precomputed arguments keep the host far ahead of
+    # the GPU, so HIP event pairs measure kernels, not launch latency.
+    import ctypes
+    L = qm.lib()
+    hip = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+    stream = torch.cuda.current_stream().cuda_stream
+    sc = shape.c()
+    sh = ctypes.byref(sc)
+    ex_c = [p_.c() for p_ in pools]
+    ex_ref = [ctypes.byref(e) for e in ex_c]
+    xb, xstride = xs.data_ptr(), T * d * 2
+    lg_p, ids_p, tw_p = logits.data_ptr(), ids.data_ptr(), tw.data_ptr()
+    off_p, perm_p, inv_p = offsets.data_ptr(), perm.data_ptr(), inv.data_ptr()
+    y_p, out_p, ws_p, ws_n = y.data_ptr(), out.data_ptr(), ws.data_ptr(), ws.numel()
+    ffn_ws_n = qm.moe_workspace_bytes(shape)
+    wr_p = [None if r is None else r[0].data_ptr() for r in routers]
+    b_p = [None if (r is None or r[1] is None) else r[1].data_ptr() for r in routers]
+    given_p = None if given is None else given.data_ptr()
+
+    def set_logits(j):
+        if given is not None:    # given router logits are an input: copy them in
+            hip.hipMemcpyAsync(ctypes.c_void_p(lg_p), ctypes.c_void_p(given_p + (j % n_x) * T * E * 4),
+                               ctypes.c_size_t(T * E * 4), 3, ctypes.c_void_p(stream))
+
+    def step(j, ev=None):
+        p = j % n_pools
+        xp = xb + (j % n_x) * xstride
+        set_logits(j)
+        rc = L.moe_route_topk(sh, xp, wr_p[p], b_p[p], lg_p, ids_p, tw_p, stream)
+        rc |= L.moe_dispatch(sh, ids_p, off_p, perm_p, inv_p, ws_p, ws_n, stream)
         if ev is not None:
-            ev[0].record()
-        qm.moe_expert_ffn(shape, x, pools[p], offsets, perm, y, ws)
+            hip.hipEventRecord(ev[0], ctypes.c_void_p(stream))
+        rc |= L.moe_expert_ffn(sh, xp, ex_ref[p], off_p, perm_p, y_p, ws_p, ffn_ws_n, stream)
         if ev is not None:
-            ev[1].record()
-        qm.moe_combine(shape, y, inv, tw, out)
+            hip.hipEventRecord(ev[1], ctypes.c_void_p(stream))
+        rc |= L.moe_combine(sh, y_p, inv_p, tw_p, out_p, stream)
+        if rc:
+            raise RuntimeError("a C-ABI call failed")
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
     K = args.steps
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    evs = []
+    for _ in range(K):
+        a_, b_ = ctypes.c_void_p(), ctypes.c_void_p()
+        hip.hipEventCreate(ctypes.byref(a_))
+        hip.hipEventCreate(ctypes.byref(b_))
+        evs.append((a_, b_))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
         step(args.warmup + i, evs[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    ffn_ms = [a.elapsed_time(b) for a, b in evs]
+    ffn_ms = []
+    for a_, b_ in evs:
+        ms = ctypes.c_float()
+        hip.hipEventElapsedTime(ctypes.byref(ms), a_, b_)
+        ffn_ms.append(ms.value)
+        hip.hipEventDestroy(a_)
+        hip.hipEventDestroy(b_)
 
     # one-call path (moe_layer), same steps, for reference
     torch.cuda.synchronize()
@@ -182,10 +215,10 @@ def main():
     for i in range(K):
         j = args.warmup + i
         p = j % n_pools
-        wr, b = (None, None) if given is not None else routers[p]
-        if given is not None:
-            logits.copy_(given[j % n_x])
-        qm.moe_layer(shape, xs[j % n_x], wr, b, logits, pools[p], ids, tw, out, ws)
+        set_logits(j)
+        if L.moe_layer(sh, xb + (j % n_x) * xstride, wr_p[p], b_p[p], lg_p, ex_ref[p], ids_p, tw_p, out_p,
+                       ws_p, ws_n, stream):
+            raise RuntimeError("moe_layer failed")
     torch.cuda.synchronize()
     layer_elapsed = time.perf_counter() - t1
     assert qm.moe_read_device_status(ws) == 0
@@ -195,13 +228,9 @@ def main():
     for i in range(K):
         j = args.warmup + i
         p = j % n_pools
-        if given is not None:
-            logits.copy_(given[j % n_x])
-            wr, b = None, None
-        else:
-            wr, b = routers[p]
-        qm.moe_route_topk(shape, xs[j % n_x], wr, b, logits, ids, tw)
-        qm.moe_dispatch(shape, ids, offsets, perm, inv, ws)
+        set_logits(j)
+        L.moe_route_topk(sh, xb + (j % n_x) * xstride, wr_p[p], b_p[p], lg_p, ids_p, tw_p, stream)
+        L.moe_dispatch(sh, ids_p, off_p, perm_p, inv_p, ws_p, ws_n, stream)
         U.append(int((offsets[1:] - offsets[:-1] > 0).sum().item()))
     U_mean = float(np.mean(U))
 

@@ -281,6 +281,25 @@ def expert_ffn_rows(x_bits, k: int, offsets, perm, rows, gate: dict, up: dict, d
     return act, y
 
 
+def expert_down(act, offsets, down: dict, rows=None, slot_of_expert=None):
+    """Step 5 alone, on a GIVEN bf16 intermediate: y_r = W_d[e] act_r in
+    float64 for the sorted rows `rows` (all rows when None).  Used to check
+    the down projection of a device given the act it produced itself, so
+    that a one-ulp difference at the bf16 rounding point of step 4 is not
+    mistaken for an error of step 5."""
+    offsets = np.asarray(offsets, dtype=np.int64)
+    act = np.asarray(act, dtype=np.float64)
+    rows = np.arange(int(offsets[-1])) if rows is None else np.asarray(rows, dtype=np.int64)
+    expert_of_row = np.searchsorted(offsets, rows, side="right") - 1
+    d = down["codes"].shape[-2]
+    y = np.zeros((rows.size, d), dtype=np.float64)
+    for e in np.unique(expert_of_row):
+        sel = np.nonzero(expert_of_row == e)[0]
+        slot = int(e) if slot_of_expert is None else int(slot_of_expert[e])
+        y[sel] = act[sel] @ dequant(down, slot).T
+    return y
+
+
 def combine(y, inv, w, k: int):
     """Step 6: out[t] = sum_j w[t, j] * y[inv[t*k + j]], summed in j order."""
     y = np.asarray(y, dtype=np.float64)

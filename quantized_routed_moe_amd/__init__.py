@@ -75,6 +75,9 @@ def lib() -> ctypes.CDLL:
     """The loaded HIP library (raises if it has not been built)."""
     global _LIB
     if _LIB is None:
+        # torch first: its HIP runtime is the one the library must share
+        # (stream handles and device pointers come from it).
+        _torch()
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(
                 f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`"

@@ -65,7 +65,9 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_kernel(
         }
         const int rank = __popcll(same & lt_mask);
         const bool leader = (same >> lane) == 1ull;     // highest lane of its group
-        for (int i = tid; i < kDispWaves * (E + 1); i += kDispThreads) (&wcnt[0][0])[i] = 0;
+        // clear every [wave][expert] count: a wave that holds no pair of
+        // expert e never writes wcnt[wave][e], and the scan below reads it
+        for (int i = tid; i < kDispWaves * (kMaxExperts + 1); i += kDispThreads) (&wcnt[0][0])[i] = 0;
         __syncthreads();
         if (valid && leader) wcnt[wave][e] = __popcll(same);
         __syncthreads();

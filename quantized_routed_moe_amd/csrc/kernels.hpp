@@ -29,6 +29,8 @@ hipError_t launch_route(const moe_shape& s, const uint16_t* x, const float* wr, 
 hipError_t launch_dispatch(const moe_shape& s, const int32_t* ids, int32_t* offsets, int32_t* perm,
                            int32_t* inv, uint32_t* status, hipStream_t st);
 hipError_t launch_ffn(const moe_shape& s, int fmt, const FfnArgs& a, hipStream_t st);
+bool grouped_supported(const moe_shape& s, int fmt);
+hipError_t launch_ffn_grouped(const moe_shape& s, const FfnArgs& a, hipStream_t st);
 hipError_t launch_combine(const moe_shape& s, const float* y, const int32_t* inv, const float* w,
                           float* out, hipStream_t st);
 hipError_t launch_clear_header(uint32_t* header, hipStream_t st);

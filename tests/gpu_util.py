@@ -107,11 +107,18 @@ def assert_act_close(got, want, what="act"):
                                  f"rms(act)={rms:.4g}; got vs want: {detail}")
 
 
-def check_against_oracle(case: dict, g: dict, *, rows=None, check_logits=True) -> dict:
+def check_against_oracle(case: dict, g: dict, *, rows=None, check_logits=True, strict=False) -> dict:
     """Compare device results `g` (from run_steps) with the oracle.
 
     Routing is judged on the device's float32 logits (bit-exact ids, perm,
     inv, offsets); the float64 oracle logits must agree within LOGIT_ABS.
+    act is compared with the oracle's act (ACT_FLIP_FRAC / one ulp).  y is
+    compared with the oracle's down projection of the DEVICE act, and out
+    with the oracle's combine of that y, at REL_L2 / ELEM_RMS: fp32 and
+    float64 sums round to bf16 differently on ~1e-3 of the act elements,
+    and one such ulp on a large activation moves a y element by more than
+    5e-3*rms on some shapes.  With strict=True (the five workloads) the
+    device out must ALSO meet REL_L2 / ELEM_RMS against the pure oracle.
     With `rows`, the FFN is checked on those sorted rows only."""
     k, E = case["k"], case["E"]
     info = {}
@@ -134,21 +141,27 @@ def check_against_oracle(case: dict, g: dict, *, rows=None, check_logits=True) -
     if rows is None:
         act, y = ref.expert_ffn(case["x"], k, offsets, perm, case["gate"], case["up"], case["down"], soe)
         assert_act_close(g["act"], act)
-        assert_close(g["y"], y, "y")
-        out = ref.combine(y, inv, w, k)
-        assert_close(g["out"], out, "out")
+        y_dev_act = ref.expert_down(g["act"], offsets, case["down"], slot_of_expert=soe)
+        assert_close(g["y"], y_dev_act, "y (given device act)")
+        assert_close(g["out"], ref.combine(y_dev_act, inv, w, k), "out (given device act)")
+        if strict:
+            assert_close(g["out"], ref.combine(y, inv, w, k), "out")
     else:
         act, y = ref.expert_ffn_rows(case["x"], k, offsets, perm, rows, case["gate"], case["up"],
                                      case["down"], soe)
         assert_act_close(g["act"][rows], act)
-        assert_close(g["y"][rows], y, "y (sampled rows)")
+        y_dev_act = ref.expert_down(g["act"][rows], offsets, case["down"], rows=rows, slot_of_expert=soe)
+        assert_close(g["y"][rows], y_dev_act, "y (sampled rows, given device act)")
+        if strict:
+            assert_close(g["y"][rows], y, "y (sampled rows)")
         # combine checked on tokens whose every pair was sampled
         rowset = set(int(r) for r in rows)
         toks = [t for t in range(case["T"]) if all(int(inv[t * k + j]) in rowset for j in range(k))]
         if toks:
-            ymap = {int(r): y[i] for i, r in enumerate(rows)}
+            ymap = {int(r): y_dev_act[i] for i, r in enumerate(rows)}
             out = np.stack([sum(w[t, j] * ymap[int(inv[t * k + j])] for j in range(k)) for t in toks])
             assert_close(g["out"][toks], out, "out (sampled tokens)")
         info["sampled_tokens"] = len(toks)
     info["active_experts"] = int(np.sum(np.diff(offsets) > 0))
+    info["act_flips"] = int(np.sum(g["act"][rows if rows is not None else slice(None)] != act))
     return info
