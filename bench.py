@@ -42,7 +42,23 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-steps", type=int, default=0,
                    help="oracle steps timed on the host (0 = automatic)")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="instead of the layer: copy MIB MiB device-to-device 5 times (a plain copy "
+                        "of known size, to scale the FETCH_SIZE / WRITE_SIZE counters)")
     return p.parse_args()
+
+
+def copy_calibration(mib: int) -> None:
+    import torch
+
+    n = mib * 2 ** 20
+    src = torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "copies": 5}), flush=True)
 
 
 def make_pool(torch, w, gen, dev):
@@ -93,6 +109,9 @@ def cpu_baseline(c, steps):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
                                    "(expert-parallel sharding is designed, not built)"}))

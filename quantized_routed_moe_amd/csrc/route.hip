@@ -9,7 +9,7 @@
 //   router_rows_kernel  small T: one workgroup per expert streams W_r[e] once
 //                       and dots it with every token (T <= kRowsMaxT).
 //   router_mfma_kernel  large T: fp32 MFMA tiles, 16 tokens x 16 experts per
-//                       wave, four waves cover 64 experts.
+//                       workgroup, eight waves splitting K.
 //   topk_kernel         one wave64 per token, lane = expert.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -72,43 +72,63 @@ __global__ __launch_bounds__(kRowsThreads) void router_rows_kernel(
     }
 }
 
-// Large-T router.  Workgroup = 4 waves = 16 tokens x 64 experts; wave w owns
-// experts 16w .. 16w+15.  fp32 MFMA 16x16x4: in MFMA s of a 16-wide K step,
-// lane group g (= lane / 16) supplies element k0 + 4g + s, so each lane reads
-// 4 consecutive floats of W_r and 4 consecutive bf16 of x per K step.
-typedef float f32x1v __attribute__((ext_vector_type(1)));
-__global__ __launch_bounds__(256) void router_mfma_kernel(
+// Large-T router.  Workgroup = 8 waves = 16 tokens x 16 experts; the waves
+// split K and their partial tiles are summed in LDS in wave order.  fp32 MFMA
+// 16x16x4: in MFMA s of a 16-wide K step, lane group g (= lane / 16) supplies
+// element k0 + 4g + s, so each lane reads 4 consecutive floats of W_r and 4
+// consecutive bf16 of x per step.  A wave issues the loads of kRouterUnroll
+// steps before their MFMAs; the loads are unconditional (addresses clamped,
+// values masked), which keeps every load of a batch in flight at once.
+constexpr int kRouterWaves = 8;
+constexpr int kRouterUnroll = 16;
+
+__global__ __launch_bounds__(kRouterWaves * 64) void router_mfma_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ bias,
     float* __restrict__ logits, int T, int d, int E) {
+    __shared__ __align__(16) f32x4 red[kRouterWaves][kWave];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int t0 = blockIdx.x * 16;
-    const int e0 = wave * 16;
-    if (e0 >= E) return;
+    const int t0 = blockIdx.x * 16, e0 = blockIdx.y * 16;
     const int row = lane & 15, g = lane >> 4;
-    const int tok = t0 + row;
-    const int ex = e0 + row;
+    const int tok = t0 + row, ex = e0 + row;
     const bool tok_ok = tok < T, ex_ok = ex < E;
     const uint16_t* xr = x + static_cast<size_t>(tok_ok ? tok : 0) * d + 4 * g;
     const float* wrow = wr + static_cast<size_t>(ex_ok ? ex : 0) * d + 4 * g;
+    const int S = d / 16;
+    const int s_beg = (S * wave) / kRouterWaves, s_end = (S * (wave + 1)) / kRouterWaves;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int k0 = 0; k0 < d; k0 += 16) {
-        float4 wv = ex_ok ? *reinterpret_cast<const float4*>(wrow + k0) : make_float4(0.f, 0.f, 0.f, 0.f);
-        u32x2 xv = tok_ok ? *reinterpret_cast<const u32x2*>(xr + k0) : u32x2{0u, 0u};
-        // A = x (16 tokens x 4), B = W_r^T (4 x 16 experts)
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16lo(xv[0]), wv.x, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16hi(xv[0]), wv.y, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16lo(xv[1]), wv.z, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16hi(xv[1]), wv.w, acc, 0, 0, 0);
-    }
-    // acc[i] = C[token 4g + i][expert row]
-    if (ex_ok) {
-        const float b = bias ? bias[ex] : 0.f;
+    for (int sb = s_beg; sb < s_end; sb += kRouterUnroll) {
+        float4 wv[kRouterUnroll];
+        u32x2 xv[kRouterUnroll];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = t0 + 4 * g + i;
-            if (t < T) logits[static_cast<size_t>(t) * E + ex] = acc[i] + b;
+        for (int u = 0; u < kRouterUnroll; ++u) {
+            const int s = min(sb + u, s_end - 1);
+            wv[u] = *reinterpret_cast<const float4*>(wrow + 16 * s);
+            xv[u] = *reinterpret_cast<const u32x2*>(xr + 16 * s);
         }
+#pragma unroll
+        for (int u = 0; u < kRouterUnroll; ++u) {
+            // the lane's A value (its token row) and B value (its expert
+            // column) are masked separately
+            const bool ok = sb + u < s_end;
+            const float4 w = ok && ex_ok ? wv[u] : make_float4(0.f, 0.f, 0.f, 0.f);
+            const u32x2 xx = ok && tok_ok ? xv[u] : u32x2{0u, 0u};
+            // A = x (16 tokens x 4), B = W_r^T (4 x 16 experts)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16lo(xx[0]), w.x, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16hi(xx[0]), w.y, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16lo(xx[1]), w.z, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16hi(xx[1]), w.w, acc, 0, 0, 0);
+        }
+    }
+    red[wave][lane] = acc;
+    __syncthreads();
+    // acc[i] of lane l = C[token 4(l/16) + i][expert l%16]
+    for (int idx = threadIdx.x; idx < 256; idx += kRouterWaves * 64) {
+        const int l = idx >> 2, i = idx & 3;
+        float v = red[0][l][i];
+#pragma unroll
+        for (int w = 1; w < kRouterWaves; ++w) v += red[w][l][i];
+        const int t = t0 + 4 * (l >> 4) + i, e = e0 + (l & 15);
+        if (t < T && e < E) logits[static_cast<size_t>(t) * E + e] = v + (bias ? bias[e] : 0.f);
     }
 }
 
@@ -165,7 +185,8 @@ hipError_t launch_route(const moe_shape& s, const uint16_t* x, const float* wr, 
             dim3 grid(s.E, ceil_div(s.T, kRowsMaxT));
             router_rows_kernel<<<grid, kRowsThreads, 0, st>>>(x, wr, bias, logits, s.T, s.d, s.E);
         } else {
-            router_mfma_kernel<<<ceil_div(s.T, 16), 256, 0, st>>>(x, wr, bias, logits, s.T, s.d, s.E);
+            router_mfma_kernel<<<dim3(ceil_div(s.T, 16), ceil_div(s.E, 16)), kRouterWaves * 64, 0, st>>>(
+                x, wr, bias, logits, s.T, s.d, s.E);
         }
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;

@@ -57,10 +57,11 @@ SHAPES = [
     (17, 256, 8, 8, 128),
     (1, 32, 1, 1, 32),
     (64, 1024, 32, 2, 512),
-    # T*k >= 256 with d % 256 == 0 and f % 128 == 0: the LDS-tiled grouped path
-    (300, 256, 8, 2, 128),
-    (700, 512, 16, 2, 256),
-    (257, 1024, 64, 4, 384),
+    # T*k >= 256 with d % 512 == 0 and f % 256 == 0: the LDS-tiled grouped path
+    # (MXFP4); Q2 takes the skinny path at these sizes
+    (300, 512, 8, 2, 256),
+    (700, 1024, 16, 2, 512),
+    (257, 512, 64, 4, 768),
 ]
 
 
