@@ -19,8 +19,11 @@ LIB = os.path.join(HERE, "libqrmoe.so")
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming v_pk_{add,mul,fma}_f32.
+# -ffp-contract=off: every fused multiply-add is written out (fmaf, MFMA);
+# a product and a sum written separately are rounded separately, which the
+# combine relies on to equal the scatter-add fused into the down projection.
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
-          "-Wno-unused-variable", "-Wno-unused-but-set-variable",
+          "-Wno-unused-variable", "-Wno-unused-but-set-variable", "-ffp-contract=off",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 

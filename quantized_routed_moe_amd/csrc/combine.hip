@@ -1,6 +1,8 @@
 // Weighted combine: out[t] = sum_j w[t][j] * y[inv[t*k + j]], summed in
 // j order (deterministic; no atomics).  One workgroup per token, four floats
-// per thread per pass over d.
+// per thread per pass over d.  Products and sums are rounded separately (no
+// fused multiply-add), so for k <= 2 the result equals the scatter-add of
+// the weighted expert outputs that moe_layer fuses into the down projection.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -18,10 +20,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
             const float wj = w[static_cast<size_t>(t) * k + j];
             const int r = inv[static_cast<size_t>(t) * k + j];
             const float4 v = reinterpret_cast<const float4*>(y + static_cast<size_t>(r) * d)[i];
-            acc.x = fmaf(wj, v.x, acc.x);
-            acc.y = fmaf(wj, v.y, acc.y);
-            acc.z = fmaf(wj, v.z, acc.z);
-            acc.w = fmaf(wj, v.w, acc.w);
+            acc.x = __fadd_rn(acc.x, __fmul_rn(wj, v.x));
+            acc.y = __fadd_rn(acc.y, __fmul_rn(wj, v.y));
+            acc.z = __fadd_rn(acc.z, __fmul_rn(wj, v.z));
+            acc.w = __fadd_rn(acc.w, __fmul_rn(wj, v.w));
         }
         reinterpret_cast<float4*>(out + static_cast<size_t>(t) * d)[i] = acc;
     }

@@ -15,6 +15,7 @@ constexpr int kWave = 64;
 constexpr int kMaxExperts = 64;
 constexpr int kGroup = 32;             // elements per quantisation group (MX block)
 constexpr size_t kWsHeader = 256;      // workspace header: device status word
+constexpr int kLastBlockCounter = 16;  // header word (byte 64): last-workgroup counter of fused routing
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));

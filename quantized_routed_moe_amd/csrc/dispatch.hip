@@ -13,83 +13,17 @@
 // and stable.  Ids outside [0, E) go to an extra bucket E after all valid
 // pairs and raise MOE_DEV_BAD_EXPERT_ID.
 #include "common.hpp"
+#include "dispatch_dev.hpp"
 #include "kernels.hpp"
 
 namespace qrmoe {
 
 constexpr int kDispThreads = 1024;
-constexpr int kDispWaves = kDispThreads / kWave;
 
 __global__ __launch_bounds__(kDispThreads) void dispatch_kernel(
     const int32_t* __restrict__ ids, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
     int32_t* __restrict__ inv, uint32_t* __restrict__ status, int n_pairs, int E) {
-    __shared__ int cnt[kMaxExperts + 1];
-    __shared__ int base[kMaxExperts + 1];
-    __shared__ int wcnt[kDispWaves][kMaxExperts + 1];
-    __shared__ int bad;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    if (tid <= E) cnt[tid] = 0;
-    if (tid == 0) bad = 0;
-    __syncthreads();
-    for (int p = tid; p < n_pairs; p += kDispThreads) {
-        int e = ids[p];
-        if (e < 0 || e >= E) { e = E; bad = 1; }
-        atomicAdd(&cnt[e], 1);
-    }
-    __syncthreads();
-    if (tid == 0) {
-        int run = 0;
-        for (int e = 0; e <= E; ++e) {
-            base[e] = run;
-            offsets[e] = run;     // offsets[E] = number of valid pairs
-            run += cnt[e];
-        }
-        if (bad) raise_status(status, MOE_DEV_BAD_EXPERT_ID);
-    }
-    __syncthreads();
-    const uint64_t lt_mask = lane ? ((~0ull) >> (64 - lane)) : 0ull;
-    for (int p0 = 0; p0 < n_pairs; p0 += kDispThreads) {
-        const int p = p0 + tid;
-        const bool valid = p < n_pairs;
-        int e = E + 1;                                   // padding lanes: matches no real id
-        if (valid) {
-            e = ids[p];
-            if (e < 0 || e >= E) e = E;
-        }
-        // lanes with the same e: AND of per-bit agreement masks (e < 128)
-        uint64_t same = ~0ull;
-#pragma unroll
-        for (int b = 0; b < 7; ++b) {
-            const uint64_t ones = __ballot((e >> b) & 1);
-            same &= ((e >> b) & 1) ? ones : ~ones;
-        }
-        const int rank = __popcll(same & lt_mask);
-        const bool leader = (same >> lane) == 1ull;     // highest lane of its group
-        // clear every [wave][expert] count: a wave that holds no pair of
-        // expert e never writes wcnt[wave][e], and the scan below reads it
-        for (int i = tid; i < kDispWaves * (kMaxExperts + 1); i += kDispThreads) (&wcnt[0][0])[i] = 0;
-        __syncthreads();
-        if (valid && leader) wcnt[wave][e] = __popcll(same);
-        __syncthreads();
-        if (tid <= E) {                                  // exclusive scan over waves
-            int run = 0;
-            for (int w = 0; w < kDispWaves; ++w) {
-                const int c = wcnt[w][tid];
-                wcnt[w][tid] = run;
-                run += c;
-            }
-            cnt[tid] = run;                              // this tile's total for expert tid
-        }
-        __syncthreads();
-        if (valid) {
-            const int r = base[e] + wcnt[wave][e] + rank;
-            perm[r] = p;
-            inv[p] = r;
-        }
-        __syncthreads();
-        if (tid <= E) base[tid] += cnt[tid];
-        __syncthreads();
-    }
+    dispatch_block<kDispThreads>(ids, offsets, perm, inv, status, n_pairs, E);
 }
 
 hipError_t launch_dispatch(const moe_shape& s, const int32_t* ids, int32_t* offsets, int32_t* perm,

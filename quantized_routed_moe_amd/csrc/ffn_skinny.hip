@@ -95,8 +95,18 @@ __device__ __forceinline__ void run_item(const FfnArgs& a, int slot, int n0, int
                     v[m] = s;
                 }
                 const int n = n0 + nn;
-                if constexpr (MODE == 0) a.act[static_cast<size_t>(rr) * a.f + n] = f32_to_bf16_rne(silu_mul(v[0], v[NM - 1]));
-                else a.y[static_cast<size_t>(rr) * a.d + n] = v[0];
+                if constexpr (MODE == 0) {
+                    a.act[static_cast<size_t>(rr) * a.f + n] = f32_to_bf16_rne(silu_mul(v[0], v[NM - 1]));
+                } else {
+                    a.y[static_cast<size_t>(rr) * a.d + n] = v[0];
+                    if (a.fuse_combine) {
+                        // scatter-add of the weighted expert output; with at
+                        // most two addends on a zeroed out the sum does not
+                        // depend on their order (it equals the combine kernel's)
+                        const int p = a.perm[rr];
+                        atomicAdd(a.out + static_cast<size_t>(p / a.k) * a.d + n, __fmul_rn(a.topk_w[p], v[0]));
+                    }
+                }
             }
         }
         __syncthreads();
@@ -189,8 +199,12 @@ static hipError_t launch_two(const moe_shape& s, const FfnArgs& a, hipStream_t s
 // Token rows (T*k) from which the LDS-tiled grouped GEMM takes over.
 constexpr int kGroupedMinRows = 256;
 
+bool ffn_uses_grouped(const moe_shape& s, int fmt) {
+    return s.T * s.k >= kGroupedMinRows && grouped_supported(s, fmt);
+}
+
 hipError_t launch_ffn(const moe_shape& s, int fmt, const FfnArgs& a, hipStream_t st) {
-    if (s.T * s.k >= kGroupedMinRows && grouped_supported(s, fmt)) return launch_ffn_grouped(s, a, st);
+    if (ffn_uses_grouped(s, fmt)) return launch_ffn_grouped(s, a, st);
     return fmt == MOE_FMT_MXFP4 ? launch_two<MOE_FMT_MXFP4>(s, a, st) : launch_two<MOE_FMT_Q2G32>(s, a, st);
 }
 

@@ -22,6 +22,11 @@ struct FfnArgs {
     uint16_t* act;                // bf16 [T*k][f] (workspace)
     float* y;                     // fp32 [T*k][d]
     uint32_t* status;             // workspace header
+    // moe_layer with k <= 2 only: the down projection also scatter-adds
+    // w[p] * y[r] into out (zeroed beforehand), replacing the combine kernel
+    const float* topk_w;          // [T*k]
+    float* out;                   // [T][d]
+    int fuse_combine;
 };
 
 hipError_t launch_route(const moe_shape& s, const uint16_t* x, const float* wr, const float* bias,
@@ -30,6 +35,11 @@ hipError_t launch_dispatch(const moe_shape& s, const int32_t* ids, int32_t* offs
                            int32_t* inv, uint32_t* status, hipStream_t st);
 hipError_t launch_ffn(const moe_shape& s, int fmt, const FfnArgs& a, hipStream_t st);
 bool grouped_supported(const moe_shape& s, int fmt);
+bool ffn_uses_grouped(const moe_shape& s, int fmt);
+bool small_fused_supported(const moe_shape& s);
+hipError_t launch_route_small_fused(const moe_shape& s, const uint16_t* x, const float* wr, const float* bias,
+                                   float* logits, int32_t* ids, float* w, int32_t* offsets, int32_t* perm,
+                                   int32_t* inv, float* out, uint32_t* header, hipStream_t st);
 hipError_t launch_ffn_grouped(const moe_shape& s, const FfnArgs& a, hipStream_t st);
 hipError_t launch_combine(const moe_shape& s, const float* y, const int32_t* inv, const float* w,
                           float* out, hipStream_t st);

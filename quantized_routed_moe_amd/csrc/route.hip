@@ -12,6 +12,7 @@
 //                       workgroup, eight waves splitting K.
 //   topk_kernel         one wave64 per token, lane = expert.
 #include "common.hpp"
+#include "dispatch_dev.hpp"
 #include "kernels.hpp"
 
 namespace qrmoe {
@@ -19,13 +20,13 @@ namespace qrmoe {
 constexpr int kRowsMaxT = 8;
 constexpr int kRowsThreads = 256;
 
-// logits[t][e] for t in [t0, t0 + nt), one expert per workgroup.
-// Thread i handles elements 8*i .. 8*i+7 of each 8*256-element chunk of d.
-__global__ __launch_bounds__(kRowsThreads) void router_rows_kernel(
-    const uint16_t* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ bias,
-    float* __restrict__ logits, int T, int d, int E) {
-    const int e = blockIdx.x;
-    const int t0 = blockIdx.y * kRowsMaxT;
+// logits[t][e] for t in [t0, t0 + nt) of one expert, by one workgroup of
+// kRowsThreads threads.  Thread i handles elements 8*i .. 8*i+7 of each
+// 8*256-element chunk of d; the partial sums are reduced by a fixed butterfly
+// in each wave, then across the waves in wave order.
+__device__ __forceinline__ void router_rows_block(const uint16_t* __restrict__ x, const float* __restrict__ wr,
+                                                  const float* __restrict__ bias, float* __restrict__ logits,
+                                                  int e, int t0, int T, int d, int E) {
     const int nt = min(kRowsMaxT, T - t0);
     const float* wrow = wr + static_cast<size_t>(e) * d;
     float acc[kRowsMaxT];
@@ -51,7 +52,6 @@ __global__ __launch_bounds__(kRowsThreads) void router_rows_kernel(
             }
         }
     }
-    // wave reduction (fixed butterfly), then across the 4 waves in wave order
     __shared__ float part[kRowsThreads / kWave][kRowsMaxT];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -70,6 +70,12 @@ __global__ __launch_bounds__(kRowsThreads) void router_rows_kernel(
         if (bias) s += bias[e];
         logits[static_cast<size_t>(t0 + j) * E + e] = s;
     }
+}
+
+__global__ __launch_bounds__(kRowsThreads) void router_rows_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ bias,
+    float* __restrict__ logits, int T, int d, int E) {
+    router_rows_block(x, wr, bias, logits, blockIdx.x, blockIdx.y * kRowsMaxT, T, d, E);
 }
 
 // Large-T router.  Workgroup = 8 waves = 16 tokens x 16 experts; the waves
@@ -140,17 +146,14 @@ __device__ __forceinline__ uint32_t float_key(float v) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// One wave per token; lane e holds expert e's logit.  k rounds of a 64-bit
-// wave max over (key(logit) << 32 | 63 - e) pick experts in (logit desc, id
-// asc) order.  The softmax over the selected logits is taken against the
-// first (largest) one and summed in selection order.
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits,
-                                                    int32_t* __restrict__ ids,
-                                                    float* __restrict__ w, int T, int E, int k) {
+// Top-k of one token by one wave; lane e holds expert e's logit.  k rounds of
+// a 64-bit wave max over (key(logit) << 32 | 63 - e) pick experts in (logit
+// desc, id asc) order.  The softmax over the selected logits is taken against
+// the first (largest) one and summed in selection order.
+__device__ __forceinline__ void topk_wave(const float* __restrict__ lrow, int32_t* __restrict__ ids,
+                                          float* __restrict__ w, int E, int k) {
     const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * (blockDim.x / kWave) + (threadIdx.x >> 6);
-    if (t >= T) return;
-    const float l = lane < E ? logits[static_cast<size_t>(t) * E + lane] : 0.f;
+    const float l = lane < E ? lrow[lane] : 0.f;
     uint64_t key = lane < E ? ((static_cast<uint64_t>(float_key(l)) << 32) | static_cast<uint32_t>(63 - lane)) : 0ull;
     int my_sel = -1;       // lane j < k: expert chosen in round j
     float my_l = 0.f;      // its logit
@@ -168,14 +171,69 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
         if (lane == j) { my_sel = e; my_l = le; }
         if (lane == e) key = 0ull;
     }
-    float ex = lane < k ? expf(my_l - lmax) : 0.f;
-    // sum in selection order (lane 0, 1, ..., k-1)
-    float sum = 0.f;
+    const float ex = lane < k ? expf(my_l - lmax) : 0.f;
+    float sum = 0.f;       // selection order: lane 0, 1, ..., k-1
     for (int j = 0; j < k; ++j) sum += __shfl(ex, j);
     if (lane < k) {
-        ids[static_cast<size_t>(t) * k + lane] = my_sel;
-        w[static_cast<size_t>(t) * k + lane] = ex / sum;
+        ids[lane] = my_sel;
+        w[lane] = ex / sum;
     }
+}
+
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits,
+                                                    int32_t* __restrict__ ids,
+                                                    float* __restrict__ w, int T, int E, int k) {
+    const int t = blockIdx.x * (blockDim.x / kWave) + (threadIdx.x >> 6);
+    if (t >= T) return;
+    topk_wave(logits + static_cast<size_t>(t) * E, ids + static_cast<size_t>(t) * k,
+              w + static_cast<size_t>(t) * k, E, k);
+}
+
+// Small-T fused routing for moe_layer: one workgroup per expert computes its
+// logits (or, with given logits, a single workgroup); the last workgroup to
+// finish -- found with an atomic counter in the workspace header, after a
+// release fence by every workgroup and an acquire fence by the last -- runs
+// the top-k of every token, the dispatch, and zeroes `out` for the
+// scatter-add combine.  The counter is reset by that last workgroup, so the
+// next call finds it at zero.  Arithmetic is that of router_rows_block,
+// topk_wave and dispatch_block, so results equal the separate kernels'.
+__global__ __launch_bounds__(kRowsThreads) void route_small_fused_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ bias,
+    float* __restrict__ logits, int32_t* __restrict__ ids, float* __restrict__ w, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ perm, int32_t* __restrict__ inv, float* __restrict__ out, uint32_t* __restrict__ header,
+    int T, int d, int E, int k) {
+    __shared__ int last;
+    if (wr) router_rows_block(x, wr, bias, logits, blockIdx.x, 0, T, d, E);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t* counter = header + kLastBlockCounter;
+        const uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        last = prev == gridDim.x - 1;
+        if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!last) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // see every workgroup's logits
+    const int wave = threadIdx.x >> 6;
+    for (int t = wave; t < T; t += kRowsThreads / kWave)
+        topk_wave(logits + static_cast<size_t>(t) * E, ids + static_cast<size_t>(t) * k,
+                  w + static_cast<size_t>(t) * k, E, k);
+    if (out) {
+        float4* o4 = reinterpret_cast<float4*>(out);
+        for (int i = threadIdx.x; i < T * d / 4; i += kRowsThreads) o4[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    __syncthreads();
+    dispatch_block<kRowsThreads>(ids, offsets, perm, inv, header, T * k, E);
+}
+
+bool small_fused_supported(const moe_shape& s) { return s.T <= kRowsMaxT; }
+
+hipError_t launch_route_small_fused(const moe_shape& s, const uint16_t* x, const float* wr, const float* bias,
+                                   float* logits, int32_t* ids, float* w, int32_t* offsets, int32_t* perm,
+                                   int32_t* inv, float* out, uint32_t* header, hipStream_t st) {
+    route_small_fused_kernel<<<wr ? s.E : 1, kRowsThreads, 0, st>>>(x, wr, bias, logits, ids, w, offsets, perm, inv,
+                                                                   out, header, s.T, s.d, s.E, s.k);
+    return hipGetLastError();
 }
 
 hipError_t launch_route(const moe_shape& s, const uint16_t* x, const float* wr, const float* bias,
