@@ -26,14 +26,23 @@ __device__ __forceinline__ void dispatch_block(const int32_t* __restrict__ ids, 
         atomicAdd(&cnt[e], 1);
     }
     __syncthreads();
-    if (tid == 0) {
-        int run = 0;
-        for (int e = 0; e <= E; ++e) {
-            base[e] = run;
-            offsets[e] = run;     // offsets[E] = number of valid pairs
-            run += cnt[e];
+    if (wave == 0) {           // exclusive scan of the counts over a wave (E <= 64)
+        const int c = lane < E ? cnt[lane] : 0;
+        int incl = c;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int v = __shfl_up(incl, o);
+            if (lane >= o) incl += v;
         }
-        if (bad) raise_status(status, MOE_DEV_BAD_EXPERT_ID);
+        if (lane < E) {
+            base[lane] = incl - c;
+            offsets[lane] = incl - c;
+        }
+        if (lane == 63) {      // lanes >= E hold 0, so this is the number of valid pairs
+            base[E] = incl;
+            offsets[E] = incl;
+        }
+        if (lane == 0 && bad) raise_status(status, MOE_DEV_BAD_EXPERT_ID);
     }
     __syncthreads();
     const uint64_t lt_mask = lane ? ((~0ull) >> (64 - lane)) : 0ull;

@@ -18,12 +18,13 @@
 namespace qrmoe {
 
 constexpr int kRowsMaxT = 8;
-constexpr int kRowsThreads = 256;
+constexpr int kRowsThreads = 512;
 
 // logits[t][e] for t in [t0, t0 + nt) of one expert, by one workgroup of
 // kRowsThreads threads.  Thread i handles elements 8*i .. 8*i+7 of each
-// 8*256-element chunk of d; the partial sums are reduced by a fixed butterfly
-// in each wave, then across the waves in wave order.
+// 8*512-element chunk of d (one chunk at d = 4096: one round of loads); the
+// partial sums are reduced by a fixed butterfly in each wave, then across
+// the waves in wave order.
 __device__ __forceinline__ void router_rows_block(const uint16_t* __restrict__ x, const float* __restrict__ wr,
                                                   const float* __restrict__ bias, float* __restrict__ logits,
                                                   int e, int t0, int T, int d, int E) {
@@ -32,6 +33,7 @@ __device__ __forceinline__ void router_rows_block(const uint16_t* __restrict__ x
     float acc[kRowsMaxT];
 #pragma unroll
     for (int j = 0; j < kRowsMaxT; ++j) acc[j] = 0.f;
+#pragma unroll 2
     for (int i = threadIdx.x * 8; i < d; i += kRowsThreads * 8) {
         const float4 w0 = *reinterpret_cast<const float4*>(wrow + i);
         const float4 w1 = *reinterpret_cast<const float4*>(wrow + i + 4);
@@ -203,6 +205,7 @@ __global__ __launch_bounds__(kRowsThreads) void route_small_fused_kernel(
     int32_t* __restrict__ perm, int32_t* __restrict__ inv, float* __restrict__ out, uint32_t* __restrict__ header,
     int T, int d, int E, int k) {
     __shared__ int last;
+    __shared__ int32_t sids[kRowsMaxT * kMaxExperts];   // T*k ids of the last workgroup
     if (wr) router_rows_block(x, wr, bias, logits, blockIdx.x, 0, T, d, E);
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -214,16 +217,17 @@ __global__ __launch_bounds__(kRowsThreads) void route_small_fused_kernel(
     __syncthreads();
     if (!last) return;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // see every workgroup's logits
+    // top-k into LDS (the dispatch reads it there), weights to global
     const int wave = threadIdx.x >> 6;
     for (int t = wave; t < T; t += kRowsThreads / kWave)
-        topk_wave(logits + static_cast<size_t>(t) * E, ids + static_cast<size_t>(t) * k,
-                  w + static_cast<size_t>(t) * k, E, k);
+        topk_wave(logits + static_cast<size_t>(t) * E, sids + t * k, w + static_cast<size_t>(t) * k, E, k);
     if (out) {
         float4* o4 = reinterpret_cast<float4*>(out);
         for (int i = threadIdx.x; i < T * d / 4; i += kRowsThreads) o4[i] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
     __syncthreads();
-    dispatch_block<kRowsThreads>(ids, offsets, perm, inv, header, T * k, E);
+    for (int i = threadIdx.x; i < T * k; i += kRowsThreads) ids[i] = sids[i];
+    dispatch_block<kRowsThreads>(sids, offsets, perm, inv, header, T * k, E);
 }
 
 bool small_fused_supported(const moe_shape& s) { return s.T <= kRowsMaxT; }
