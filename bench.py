@@ -74,16 +74,20 @@ def make_pool(torch, w, gen, dev):
     E, d, f = w["E"], w["d"], w["f"]
 
     def mat(n, K):
+        # drawn in the row layout, then re-laid into the tile layout the
+        # kernels read (moe_pack_qmat); the row copy is dropped
         if w["fmt"] == "mxfp4":
             codes = torch.randint(0, 256, (E, n, K // 2), dtype=torch.uint8, device=dev, generator=gen)
             scales = torch.randint(119, 124, (E, n, K // 32), dtype=torch.uint8, device=dev, generator=gen)
-            return qm.QMat(codes, scales)
-        codes = torch.randint(0, 256, (E, n, K // 4), dtype=torch.uint8, device=dev, generator=gen)
-        sc = (torch.rand((E, n, K // 32), device=dev, generator=gen) * 0.015 + 0.005).half().view(torch.int16)
-        mn = (torch.rand((E, n, K // 32), device=dev, generator=gen) * -0.04).half().view(torch.int16)
-        return qm.QMat(codes, sc.contiguous(), mn.contiguous())
+            rows = qm.QMat(codes, scales, None, qm.MOE_LAYOUT_ROWS)
+        else:
+            codes = torch.randint(0, 256, (E, n, K // 4), dtype=torch.uint8, device=dev, generator=gen)
+            sc = (torch.rand((E, n, K // 32), device=dev, generator=gen) * 0.015 + 0.005).half().view(torch.int16)
+            mn = (torch.rand((E, n, K // 32), device=dev, generator=gen) * -0.04).half().view(torch.int16)
+            rows = qm.QMat(codes, sc.contiguous(), mn.contiguous(), qm.MOE_LAYOUT_ROWS)
+        return qm.pack_qmat(w["fmt"], rows, E, n, K)
 
-    return qm.Experts(w["fmt"], mat(f, d), mat(f, d), mat(d, f), None, E)
+    return qm.Experts(w["fmt"], mat(f, d), mat(f, d), mat(d, f), None, E, d, f)
 
 
 def cpu_baseline(c, steps):

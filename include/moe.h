@@ -62,7 +62,7 @@ enum moe_status {
     MOE_OK = 0,
     MOE_ERR_NULL = -1,        /* a required pointer is NULL */
     MOE_ERR_SHAPE = -2,       /* shape outside the limits above */
-    MOE_ERR_FORMAT = -3,      /* unknown or mixed pack format, missing Q2 mins */
+    MOE_ERR_FORMAT = -3,      /* unknown, mixed or mislaid pack format / layout */
     MOE_ERR_ALIGN = -4,       /* a pointer is not aligned as required */
     MOE_ERR_WORKSPACE = -5,   /* ws_bytes < moe_workspace_bytes(shape) */
     MOE_ERR_UNSUPPORTED = -6, /* valid request this build cannot serve */
@@ -84,31 +84,82 @@ typedef struct moe_shape {
     int32_t f; /* expert FFN (intermediate) size */
 } moe_shape;
 
-/* Expert weight pack formats. */
+/* Expert weight pack formats (the quantisation of one row; the layout of the
+   rows in memory is given separately by enum moe_layout). */
 enum moe_format {
     /* MXFP4 (OCP Microscaling v1.0): 4-bit e2m1 codes, element 2i of a row in
        the LOW nibble of byte i, element 2i+1 in the HIGH nibble (bit 3 of a
        code is its sign); one e8m0 scale byte per 32 consecutive elements
-       along K (value 2^(byte-127); byte 255 is not allowed).
-       codes  uint8 [slots][n][K/2], scales uint8 [slots][n][K/32], mins unused. */
+       along K (value 2^(byte-127); byte 255 is not allowed). */
     MOE_FMT_MXFP4 = 1,
     /* 2-bit group-asymmetric: w = scale * q + min, q in {0,1,2,3}; element 4i+j
        of a row is bits (2j, 2j+1) of byte i; one fp16 scale and one fp16 min per
-       32 consecutive elements along K.
-       codes uint8 [slots][n][K/4], scales/mins uint16 (fp16) [slots][n][K/32]. */
+       32 consecutive elements along K. */
     MOE_FMT_Q2G32 = 2
+};
+
+/* Memory layouts of a quantised matrix of n rows x K elements per slot
+   (n a multiple of 16, K a multiple of 32; G = K/32 groups per row).
+
+   MOE_LAYOUT_ROWS -- the interchange layout (input of moe_pack_qmat only):
+     MXFP4: codes uint8 [slots][n][K/2], scales uint8 [slots][n][G], mins NULL.
+     Q2:    codes uint8 [slots][n][K/4], scales and mins fp16 bits
+            uint16 [slots][n][G].
+
+   MOE_LAYOUT_TILES -- the layout the expert FFN reads (moe_pack_qmat writes
+   it).  Rows are cut into tiles of 16 and K into steps of 128 elements (four
+   groups; S = ceil(K/128) steps, the groups past G of the last step are
+   padding).  One (tile, step) block holds 64 "pieces"; piece L covers row
+   16*tile + L%16.  Blocks are stored [slots][n/16][S] (step fastest), so
+   one piece array of a block is contiguous and a 64-lane wave reads a
+   whole block in one instruction.
+     MXFP4: piece L = group 4*step + L/16 of its row:
+            codes  [slots][n/16][S][64][16 B]  the group's 16 code bytes
+                                                (padding: 0)
+            scales [slots][n/16][S][64] uint8  its e8m0 scale (padding: 127)
+            mins   NULL
+     Q2:    codes  [slots][n/16][S][64][8 B]   for j = 0..3, bytes 2g and
+                                                2g+1 (g = L/16) of the 8 code
+                                                bytes of group 4*step+j, j
+                                                ascending (padding: 0) --
+                                                elements 8g..8g+7 of each of
+                                                the step's four groups
+            scales [slots][n/16][S][64] uint32  fp16 scale | fp16 min << 16 of
+                                                group 4*step + L/16 (padding 0)
+            mins   NULL (the mins live in scales)
+   Sizes: moe_qmat_bytes. */
+enum moe_layout {
+    MOE_LAYOUT_ROWS = 0,
+    MOE_LAYOUT_TILES = 1
 };
 
 /* One quantised matrix, n rows of K elements, for every slot. */
 typedef struct moe_qmat {
     int32_t fmt;        /* enum moe_format */
+    int32_t layout;     /* enum moe_layout */
     const void* codes;  /* device */
     const void* scales; /* device */
-    const void* mins;   /* device; Q2 only, NULL for MXFP4 */
+    const void* mins;   /* device; Q2 in MOE_LAYOUT_ROWS only, else NULL */
 } moe_qmat;
 
+/* Bytes of each array of a (fmt, layout) matrix of `slots` x n x K (any of
+   the out pointers may be NULL).  Returns the total, or 0 (all outputs 0)
+   when the request is invalid: unknown fmt or layout, slots < 1, n not a
+   positive multiple of 16, K not a positive multiple of 32. */
+size_t moe_qmat_bytes(int32_t fmt, int32_t layout, int32_t slots, int32_t n, int32_t K,
+                      size_t* codes_bytes, size_t* scales_bytes, size_t* mins_bytes);
+
+/* Re-lays `src` (MOE_LAYOUT_ROWS) into `dst` (MOE_LAYOUT_TILES, same fmt,
+   arrays of moe_qmat_bytes size, caller-allocated, not overlapping src) on
+   `stream`: a bit-exact copy of every code, scale and min.  Meant to run once
+   when the weights are loaded.  Errors: MOE_ERR_NULL, MOE_ERR_FORMAT (fmt or
+   layout mismatch), MOE_ERR_SHAPE (as moe_qmat_bytes), MOE_ERR_ALIGN (codes
+   16-byte, scales and mins 4-byte aligned), MOE_ERR_HIP. */
+int moe_pack_qmat(const moe_qmat* src, const moe_qmat* dst, int32_t slots, int32_t n, int32_t K,
+                  hipStream_t stream);
+
 /* The experts of one layer.  gate and up are n=f rows of K=d; down is n=d
-   rows of K=f.  All three use the same format.  Expert e lives in pack slot
+   rows of K=f.  All three use the same format and MOE_LAYOUT_TILES.  Expert e lives in pack slot
    slot_of_expert[e] (device int32 [E]) or, when slot_of_expert is NULL, in
    slot e (then num_slots >= E is required).  A routed expert whose slot is
    outside [0, num_slots) is not computed: its y rows are written as zeros and

@@ -16,6 +16,8 @@ import os
 from dataclasses import dataclass
 from typing import Optional
 
+import numpy as np
+
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqrmoe.so")
 
@@ -36,11 +38,14 @@ MOE_FMT_MXFP4 = 1
 MOE_FMT_Q2G32 = 2
 FORMATS = {"mxfp4": MOE_FMT_MXFP4, "q2": MOE_FMT_Q2G32}
 
+MOE_LAYOUT_ROWS = 0
+MOE_LAYOUT_TILES = 1
+
 # Every symbol include/moe.h declares.
 EXPORTS = (
     "moe_workspace_bytes", "moe_workspace_init", "moe_route_topk", "moe_dispatch",
     "moe_expert_ffn", "moe_combine", "moe_layer_workspace_bytes", "moe_layer",
-    "moe_status_str", "moe_read_device_status",
+    "moe_status_str", "moe_read_device_status", "moe_qmat_bytes", "moe_pack_qmat",
 )
 
 
@@ -56,7 +61,7 @@ class moe_shape(ctypes.Structure):
 
 
 class moe_qmat(ctypes.Structure):
-    _fields_ = [("fmt", ctypes.c_int32), ("codes", ctypes.c_void_p),
+    _fields_ = [("fmt", ctypes.c_int32), ("layout", ctypes.c_int32), ("codes", ctypes.c_void_p),
                 ("scales", ctypes.c_void_p), ("mins", ctypes.c_void_p)]
 
 
@@ -94,6 +99,8 @@ def lib() -> ctypes.CDLL:
             "moe_layer": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
             "moe_status_str": (ctypes.c_char_p, [_I]),
             "moe_read_device_status": (_I, [_P, _P, _P]),
+            "moe_qmat_bytes": (_SZ, [_I, _I, _I, _I, _I, _P, _P, _P]),
+            "moe_pack_qmat": (_I, [_P, _P, _I, _I, _I, _P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -153,62 +160,108 @@ class Shape:
 
 @dataclass
 class QMat:
-    """One quantised matrix pack on the device (see include/moe.h)."""
+    """One quantised matrix on the device: n rows of K elements per slot, in
+    MOE_LAYOUT_ROWS (codes/scales/mins as in include/moe.h) or
+    MOE_LAYOUT_TILES (codes/scales; mins None)."""
     codes: object
     scales: object
     mins: object = None
+    layout: int = MOE_LAYOUT_TILES
+
+    def c(self, fmt: int, name: str = "qmat") -> moe_qmat:
+        torch = _torch()
+        codes = _ptr(self.codes, torch.uint8, f"{name}.codes")
+        scales = _ptr(self.scales, name=f"{name}.scales")
+        mins = _ptr(self.mins, name=f"{name}.mins", allow_none=True)
+        return moe_qmat(fmt, self.layout, codes, scales, mins)
 
 
 @dataclass
 class Experts:
-    """The gate/up/down packs of one layer (device tensors)."""
+    """The gate/up/down packs of one layer (device tensors, tile layout);
+    d = hidden size, f = expert FFN size."""
     fmt: str
     gate: QMat
     up: QMat
     down: QMat
     slot_of_expert: object = None
     num_slots: int = 0
+    d: int = 0
+    f: int = 0
 
     def c(self) -> moe_experts:
         torch = _torch()
-        f = FORMATS[self.fmt]
-        u16 = (torch.uint16, torch.int16)
-
-        def q(m: QMat, name: str) -> moe_qmat:
-            codes = _ptr(m.codes, torch.uint8, f"{name}.codes")
-            if self.fmt == "mxfp4":
-                scales = _ptr(m.scales, torch.uint8, f"{name}.scales")
-                mins = None
-            else:
-                scales = _ptr(m.scales, u16, f"{name}.scales")
-                mins = _ptr(m.mins, u16, f"{name}.mins")
-            return moe_qmat(f, codes, scales, mins)
-
-        slots = self.num_slots or int(self.gate.codes.shape[0])
+        fmt = FORMATS[self.fmt]
         soe = _ptr(self.slot_of_expert, torch.int32, "slot_of_expert", allow_none=True)
-        return moe_experts(q(self.gate, "gate"), q(self.up, "up"), q(self.down, "down"), soe, slots)
+        return moe_experts(self.gate.c(fmt, "gate"), self.up.c(fmt, "up"), self.down.c(fmt, "down"), soe,
+                           self.num_slots)
 
     @staticmethod
     def from_arrays(fmt: str, gate: dict, up: dict, down: dict, device="cuda",
                     slot_of_expert=None) -> "Experts":
-        """Copy host arrays (numpy; codes uint8, scales uint8 or uint16 fp16
-        bits, mins uint16) to device tensors."""
+        """Row-layout host arrays (numpy; codes uint8 [slots][n][..], scales
+        uint8 or uint16 fp16 bits, mins uint16) -> tile-layout device packs
+        (copied to the device, then re-laid by moe_pack_qmat)."""
         torch = _torch()
+        slots, f = int(gate["codes"].shape[0]), int(gate["codes"].shape[1])
+        d = 32 * int(gate["scales"].shape[2])
+        soe = None
+        if slot_of_expert is not None:
+            soe = torch.from_numpy(np.ascontiguousarray(slot_of_expert, dtype=np.int32)).to(device)
+        return Experts(fmt, pack_arrays(fmt, gate, f, d, device), pack_arrays(fmt, up, f, d, device),
+                       pack_arrays(fmt, down, d, f, device), soe, slots, d, f)
 
-        def dev(a):
-            if a is None:
-                return None
-            t = torch.from_numpy(a) if not isinstance(a, torch.Tensor) else a
-            if t.dtype == torch.uint16:
-                t = t.view(torch.int16)
-            return t.contiguous().to(device)
 
-        mk = lambda m: QMat(dev(m["codes"]), dev(m["scales"]), dev(m.get("mins")))
-        soe = None if slot_of_expert is None else dev(slot_of_expert).to(torch.int32)
-        return Experts(fmt, mk(gate), mk(up), mk(down), soe, int(gate["codes"].shape[0]))
+def _dev(a, device):
+    torch = _torch()
+    if a is None:
+        return None
+    t = torch.from_numpy(np.ascontiguousarray(a)) if not isinstance(a, torch.Tensor) else a
+    if t.dtype == torch.uint16:
+        t = t.view(torch.int16)
+    return t.contiguous().to(device)
+
+
+def pack_arrays(fmt: str, m: dict, n: int, K: int, device="cuda", stream=None) -> QMat:
+    """One row-layout matrix (host arrays) -> a tile-layout QMat on the device."""
+    src = QMat(_dev(m["codes"], device), _dev(m["scales"], device), _dev(m.get("mins"), device),
+               MOE_LAYOUT_ROWS)
+    slots = int(m["codes"].shape[0])
+    return pack_qmat(fmt, src, slots, n, K, stream)
+
+
+def pack_qmat(fmt: str, src: QMat, slots: int, n: int, K: int, stream=None) -> QMat:
+    """Allocate a tile-layout matrix and fill it from the row-layout `src`
+    (device tensors) with moe_pack_qmat."""
+    torch = _torch()
+    cb, sb, _ = moe_qmat_bytes(fmt, MOE_LAYOUT_TILES, slots, n, K)
+    if cb == 0:
+        raise MoeError(MOE_ERR_SHAPE, "pack_qmat")
+    dev = src.codes.device
+    dst = QMat(torch.empty(cb, dtype=torch.uint8, device=dev), torch.empty(sb, dtype=torch.uint8, device=dev),
+               None, MOE_LAYOUT_TILES)
+    moe_pack_qmat(fmt, src, dst, slots, n, K, stream)
+    return dst
 
 
 # ------------------------------------------------------------ C entry points
+
+def moe_qmat_bytes(fmt, layout: int, slots: int, n: int, K: int):
+    """(codes, scales, mins) byte sizes of a matrix; zeros if invalid."""
+    f = FORMATS.get(fmt, fmt) if isinstance(fmt, str) else fmt
+    c, s_, m = ctypes.c_size_t(0), ctypes.c_size_t(0), ctypes.c_size_t(0)
+    lib().moe_qmat_bytes(int(f), int(layout), int(slots), int(n), int(K), ctypes.byref(c), ctypes.byref(s_),
+                         ctypes.byref(m))
+    return int(c.value), int(s_.value), int(m.value)
+
+
+def moe_pack_qmat(fmt, src: QMat, dst: QMat, slots: int, n: int, K: int, stream=None) -> None:
+    f = FORMATS[fmt] if isinstance(fmt, str) else fmt
+    s_ = src.c(f, "src")
+    d_ = dst.c(f, "dst")
+    _check(lib().moe_pack_qmat(ctypes.byref(s_), ctypes.byref(d_), int(slots), int(n), int(K), _stream(stream)),
+           "moe_pack_qmat")
+
 
 def moe_workspace_bytes(shape: Shape) -> int:
     return int(lib().moe_workspace_bytes(ctypes.byref(shape.c())))
@@ -301,7 +354,7 @@ def layer(x, experts: Experts, k: int, *, w_router=None, bias=None, logits=None,
     torch = _torch()
     T, d = x.shape
     E = int(w_router.shape[0]) if w_router is not None else int(logits.shape[1])
-    f = int(experts.gate.codes.shape[1])
+    f = experts.f
     shape = Shape(T, d, E, k, f)
     dev = x.device
     if logits is None:

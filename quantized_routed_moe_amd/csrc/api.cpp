@@ -48,14 +48,32 @@ LayerCarve layer_carve(const moe_shape& s) {
     return c;
 }
 
-int check_qmat(const moe_qmat& m, int fmt) {
-    if (m.fmt != fmt) return MOE_ERR_FORMAT;
-    if (!m.codes || !m.scales) return MOE_ERR_NULL;
-    if (!aligned(m.codes, 16) || !aligned(m.scales, 16)) return MOE_ERR_ALIGN;
-    if (fmt == MOE_FMT_Q2G32) {
-        if (!m.mins) return MOE_ERR_FORMAT;
-        if (!aligned(m.mins, 16)) return MOE_ERR_ALIGN;
+// Array sizes of one (fmt, layout) matrix; false when the request is invalid.
+bool qmat_sizes(int fmt, int layout, int slots, int n, int K, size_t* codes, size_t* scales, size_t* mins) {
+    *codes = *scales = *mins = 0;
+    if (fmt != MOE_FMT_MXFP4 && fmt != MOE_FMT_Q2G32) return false;
+    if (layout != MOE_LAYOUT_ROWS && layout != MOE_LAYOUT_TILES) return false;
+    if (slots < 1 || n < 16 || n % 16 || K < 32 || K % 32) return false;
+    const size_t rows = static_cast<size_t>(slots) * n;
+    const size_t groups = rows * (K / 32);
+    if (layout == MOE_LAYOUT_ROWS) {
+        *codes = fmt == MOE_FMT_MXFP4 ? rows * (K / 2) : rows * (K / 4);
+        *scales = fmt == MOE_FMT_MXFP4 ? groups : groups * 2;
+        *mins = fmt == MOE_FMT_MXFP4 ? 0 : groups * 2;
+    } else {
+        const size_t pieces = static_cast<size_t>(slots) * (n / 16) * ((K + 127) / 128) * 64;
+        *codes = pieces * (fmt == MOE_FMT_MXFP4 ? 16 : 8);
+        *scales = pieces * (fmt == MOE_FMT_MXFP4 ? 1 : 4);
     }
+    return true;
+}
+
+// A matrix the expert FFN can read: tile layout, every pointer 16-byte aligned.
+int check_qmat(const moe_qmat& m, int fmt) {
+    if (m.fmt != fmt || m.layout != MOE_LAYOUT_TILES) return MOE_ERR_FORMAT;
+    if (!m.codes || !m.scales) return MOE_ERR_NULL;
+    if (m.mins) return MOE_ERR_FORMAT;
+    if (!aligned(m.codes, 16) || !aligned(m.scales, 16)) return MOE_ERR_ALIGN;
     return MOE_OK;
 }
 
@@ -101,7 +119,6 @@ int do_ffn(const moe_shape& s, const uint16_t* x, const moe_experts* ex, const i
     for (int i = 0; i < 3; ++i) {
         a.codes[i] = static_cast<const uint8_t*>(mats[i]->codes);
         a.scales[i] = static_cast<const uint8_t*>(mats[i]->scales);
-        a.mins[i] = static_cast<const uint16_t*>(mats[i]->mins);
     }
     a.act = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + kHeader);
     a.y = y;
@@ -167,6 +184,35 @@ size_t moe_workspace_bytes(const moe_shape* shape) {
 size_t moe_layer_workspace_bytes(const moe_shape* shape) {
     if (check_shape(shape) != MOE_OK) return 0;
     return layer_carve(*shape).total;
+}
+
+size_t moe_qmat_bytes(int32_t fmt, int32_t layout, int32_t slots, int32_t n, int32_t K, size_t* codes_bytes,
+                      size_t* scales_bytes, size_t* mins_bytes) {
+    size_t c, s, m;
+    qmat_sizes(fmt, layout, slots, n, K, &c, &s, &m);
+    if (codes_bytes) *codes_bytes = c;
+    if (scales_bytes) *scales_bytes = s;
+    if (mins_bytes) *mins_bytes = m;
+    return c + s + m;
+}
+
+int moe_pack_qmat(const moe_qmat* src, const moe_qmat* dst, int32_t slots, int32_t n, int32_t K,
+                  hipStream_t stream) {
+    if (!src || !dst) return MOE_ERR_NULL;
+    if (src->fmt != dst->fmt || src->layout != MOE_LAYOUT_ROWS || dst->layout != MOE_LAYOUT_TILES)
+        return MOE_ERR_FORMAT;
+    size_t c, s, m;
+    if (!qmat_sizes(src->fmt, MOE_LAYOUT_ROWS, slots, n, K, &c, &s, &m)) {
+        return src->fmt != MOE_FMT_MXFP4 && src->fmt != MOE_FMT_Q2G32 ? MOE_ERR_FORMAT : MOE_ERR_SHAPE;
+    }
+    const bool q2 = src->fmt == MOE_FMT_Q2G32;
+    if (!src->codes || !src->scales || !dst->codes || !dst->scales || (q2 && !src->mins)) return MOE_ERR_NULL;
+    if (dst->mins || (!q2 && src->mins)) return MOE_ERR_FORMAT;
+    if (!aligned(src->codes, 16) || !aligned(dst->codes, 16) || !aligned(src->scales, 4) ||
+        !aligned(dst->scales, 4) || (q2 && !aligned(src->mins, 4)))
+        return MOE_ERR_ALIGN;
+    return hip_rc(qrmoe::launch_pack(src->fmt, src->codes, src->scales, src->mins, const_cast<void*>(dst->codes),
+                                     const_cast<void*>(dst->scales), slots, n, K, stream));
 }
 
 int moe_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream) {
@@ -259,7 +305,7 @@ const char* moe_status_str(int status) {
         case MOE_OK: return "MOE_OK";
         case MOE_ERR_NULL: return "MOE_ERR_NULL: a required pointer is NULL";
         case MOE_ERR_SHAPE: return "MOE_ERR_SHAPE: shape outside the supported limits";
-        case MOE_ERR_FORMAT: return "MOE_ERR_FORMAT: unknown or mixed pack format, or Q2 pack without mins";
+        case MOE_ERR_FORMAT: return "MOE_ERR_FORMAT: unknown, mixed or mislaid pack format or layout";
         case MOE_ERR_ALIGN: return "MOE_ERR_ALIGN: pointer not aligned as required";
         case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace too small";
         case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: request not supported";

@@ -16,15 +16,18 @@
 // column tile holding only padding rows (past the expert's last row) is
 // skipped, so a partial tile costs MFMA work in proportion to its rows.
 //
-// Operands in LDS: the weight tile stays in its raw MXFP4 form (32 code bytes
-// + 2 scale bytes per row and K step, the two 16-byte halves swapped on rows
-// 8..15 mod 16); a wave dequantises its own A fragment (gfx950 scaled fp4 ->
-// bf16 conversion) right after reading it.  The token tile is bf16 with its
-// 16-byte chunks XOR-swizzled by (row mod 8).  Both keep the 16 rows one
-// ds_read_b128 phase touches in distinct banks.  K is
-// permuted inside a step so that in sub-step kk lane half h (= lane/32) takes
-// elements 32h + 8kk .. +8: a lane then reads one whole 32-element group (16
-// code bytes, one scale) of the weight row and 64 contiguous bytes of the
+// Operands in LDS: the weight tile stays in its raw MXFP4 form, exactly as
+// the tile layout stores it (include/moe.h, MOE_LAYOUT_TILES): a 64-element
+// K step of a 16-row tile is half of one layout block, 32 pieces of 16 code
+// bytes + 32 scale bytes, contiguous in HBM, so each thread copies whole
+// pieces and each wave load instruction reads full cache lines.  A wave
+// dequantises its own A fragment (gfx950 scaled fp4 -> bf16 conversion)
+// right after reading it; the 64 lanes of that read cover two pieces arrays
+// of 512 contiguous bytes (no bank conflicts).  The token tile is bf16 with
+// its 16-byte chunks XOR-swizzled by (row mod 8).  K is permuted inside a
+// step so that in sub-step kk lane half h (= lane/32) takes elements
+// 32h + 8kk .. +8: a lane then reads one whole 32-element group (one piece:
+// 16 code bytes, one scale) of the weight row and 64 contiguous bytes of the
 // token row per step.
 //
 // Pipeline: global loads run four K steps ahead into a 4-slot register ring;
@@ -55,8 +58,8 @@ constexpr int kGWaves = 8;
 constexpr int kGThreads = kGWaves * 64;
 
 struct GSlot {
-    u32x4 w[2];     // 32 code bytes of this thread's weight row for the step
-    uint32_t sc;    // its two e8m0 scale bytes
+    u32x4 w[2];     // pieces p and 16+p of this thread's tile for the step
+    uint32_t sc;    // the scale bytes of pieces 2p and 2p+1
     u32x4 x[2];     // 32 bytes of this thread's token row quarter
 };
 
@@ -64,8 +67,8 @@ __device__ __forceinline__ int xswz(int row, int chunk) { return row * 128 + ((c
 
 template <int MODE>
 __global__ __launch_bounds__(kGThreads) void ffn_grouped_kernel(FfnArgs a) {
-    __shared__ __align__(16) uint8_t wl[2][kGN * 32];   // raw codes [row][32 B]
-    __shared__ __align__(16) uint16_t sl[2][kGN];       // two e8m0 bytes per row
+    __shared__ __align__(16) uint8_t wl[2][kGN * 32];   // codes [tile][piece][16 B]
+    __shared__ __align__(16) uint8_t sl[2][kGN * 2];    // e8m0 [tile][piece]
     __shared__ __align__(16) uint8_t xl[2][kGM * 128];  // bf16 tokens [row][64], swizzled
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -105,42 +108,45 @@ __global__ __launch_bounds__(kGThreads) void ffn_grouped_kernel(FfnArgs a) {
         return;
     }
 
-    // ---- per-thread load roles: weight row `tid` of the tile; token row
-    // tid/4, quarter tid%4 (16 bf16) of the step's 64 K elements.
+    // ---- per-thread load roles: pieces p and 16+p (p = tid%16) of 16-row
+    // tile tid/16 of the workgroup's 32; token row tid/4, quarter tid%4 (16
+    // bf16) of the step's 64 K elements.
+    const int wt = tid >> 4, wp = tid & 15;
     const uint8_t* wcodes;
     const uint8_t* wscales;
     {
-        int mat = 2, row = nt * kGN + tid;
+        int mat = 2, tile = nt * (kGN / 16) + wt;
         if (MODE == 0) {
-            mat = tid < kGN / 2 ? 0 : 1;
-            row = nt * (kGN / 2) + (tid & (kGN / 2 - 1));
+            mat = wt < kGN / 32 ? 0 : 1;
+            tile = nt * (kGN / 32) + (wt & (kGN / 32 - 1));
         }
-        const size_t grow = static_cast<size_t>(slot) * N + row;
-        wcodes = a.codes[mat] + grow * (K / 2);
-        wscales = a.scales[mat] + grow * (K / 32);
+        const size_t blk = (static_cast<size_t>(slot) * (N / 16) + tile) * (K / 128);
+        wcodes = a.codes[mat] + blk * 64 * 16 + wp * 16;
+        wscales = a.scales[mat] + blk * 64 + 2 * wp;
     }
     const int xj = tid >> 2, xq = tid & 3;
     const bool xok = xj < nvalid;
     const uint16_t* xrow;    // padding rows read row 0 (always valid) and store zeros
     if (MODE == 0) xrow = a.x + static_cast<size_t>(xok ? a.perm[r_base + xj] / a.k : 0) * a.d;
     else xrow = a.act + static_cast<size_t>(xok ? r_base + xj : r_base) * a.f;
-    const int wsw = (tid >> 3) & 1;      // weight-row half swap (bank spread)
 
+    // step s of 64 elements = half s%2 of layout block s/2 (pieces 32*(s%2) ..)
     auto gload = [&](GSlot& g, int s) {
         s = min(s, S - 1);
-        const u32x4* cp = reinterpret_cast<const u32x4*>(wcodes + s * (kGK / 2));
+        const size_t half = static_cast<size_t>(s >> 1) * 64 + 32 * (s & 1);
+        const u32x4* cp = reinterpret_cast<const u32x4*>(wcodes + half * 16);
         g.w[0] = cp[0];
-        g.w[1] = cp[1];
-        g.sc = *reinterpret_cast<const uint16_t*>(wscales + s * 2);
+        g.w[1] = cp[16];
+        g.sc = *reinterpret_cast<const uint16_t*>(wscales + half);
         const u32x4* xp = reinterpret_cast<const u32x4*>(xrow + s * kGK + xq * 16);
         g.x[0] = xp[0];
         g.x[1] = xp[1];
     };
     auto lstore = [&](int buf, const GSlot& g) {
-        u32x4* wd = reinterpret_cast<u32x4*>(wl[buf] + tid * 32);
-        wd[wsw] = g.w[0];
-        wd[wsw ^ 1] = g.w[1];
-        sl[buf][tid] = static_cast<uint16_t>(g.sc);
+        u32x4* wd = reinterpret_cast<u32x4*>(wl[buf] + wt * 512 + wp * 16);
+        wd[0] = g.w[0];
+        wd[16] = g.w[1];
+        *reinterpret_cast<uint16_t*>(&sl[buf][wt * 32 + 2 * wp]) = static_cast<uint16_t>(g.sc);
         const u32x4 z = {0u, 0u, 0u, 0u};
         *reinterpret_cast<u32x4*>(xl[buf] + xswz(xj, 2 * xq)) = xok ? g.x[0] : z;
         *reinterpret_cast<u32x4*>(xl[buf] + xswz(xj, 2 * xq + 1)) = xok ? g.x[1] : z;
@@ -158,12 +164,15 @@ __global__ __launch_bounds__(kGThreads) void ffn_grouped_kernel(FfnArgs a) {
     const int rt1 = MODE == 0 ? kGN / 2 + 32 * wave : 64 * wave + 32;
     const int r32 = lane & 31, h = lane >> 5;
 
+    // LDS piece index of weight row rt + r32, local group h
+    const int pc0 = (rt0 / 16 + (r32 >> 4)) * 32 + 16 * h + (r32 & 15);
+    const int pc1 = (rt1 / 16 + (r32 >> 4)) * 32 + 16 * h + (r32 & 15);
     auto compute = [&](int buf) {
         const uint8_t* wb = wl[buf];
-        const u32x4 c0 = *reinterpret_cast<const u32x4*>(wb + (rt0 + r32) * 32 + 16 * (h ^ ((r32 >> 3) & 1)));
-        const u32x4 c1 = *reinterpret_cast<const u32x4*>(wb + (rt1 + r32) * 32 + 16 * (h ^ ((r32 >> 3) & 1)));
-        const float s0 = e8m0_to_f32((sl[buf][rt0 + r32] >> (8 * h)) & 0xffu);
-        const float s1 = e8m0_to_f32((sl[buf][rt1 + r32] >> (8 * h)) & 0xffu);
+        const u32x4 c0 = *reinterpret_cast<const u32x4*>(wb + pc0 * 16);
+        const u32x4 c1 = *reinterpret_cast<const u32x4*>(wb + pc1 * 16);
+        const float s0 = e8m0_to_f32(sl[buf][pc0]);
+        const float s1 = e8m0_to_f32(sl[buf][pc1]);
         const uint8_t* xb = xl[buf];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {

@@ -4,10 +4,11 @@
 // inference", section 技术深度解析: the block-sparse routed-expert kernel loads
 // only the activated experts' weights and dequantises them on the fly).
 //
-// Work item = (active expert, tile of 16 weight rows); the waves of a
-// workgroup split K and their partial tiles are summed in LDS in a fixed wave
-// order (deterministic).  The active expert of an item is found on the device
-// from offsets[E+1]; there is no host round trip.
+// The active expert of a work item is found on the device from offsets[E+1];
+// there is no host round trip.
+//
+// Weights come in the tile layout, so every weight load of a wave reads one
+// contiguous 16-row x 128-element block (1 KB of MXFP4 codes).
 //
 // Two launches: gate/up + SwiGLU (act to the workspace), then down (y).  A
 // single persistent kernel with a grid barrier between the projections was
@@ -19,98 +20,33 @@
 
 namespace qrmoe {
 
-template <int MODE>
-struct ModeDims {
-    static constexpr int NM = MODE == 0 ? 2 : 1;
+// The `ai`-th active expert (in id order) of offsets[E+1], its sorted rows
+// [r0, r1) and its pack slot, from one load per lane (lane e reads
+// offsets[e], offsets[e+1] and slot_of_expert[e]) and wave shuffles.  Every
+// lane of the wave receives the result; e = -1 when fewer than ai+1 experts
+// are active.
+struct Item {
+    int e, r0, r1, slot;
 };
 
-// One work item: 16 weight rows starting at n0 of expert slot `slot`, all of
-// the expert's token rows [r0, r1).  Wave w of KW handles K steps
-// [S*w/KW, S*(w+1)/KW).  `pre` (when has_pre) holds this wave's first weight
-// chunk, loaded earlier.
-template <int FMT, int MODE, int KW>
-__device__ __forceinline__ void run_item(const FfnArgs& a, int slot, int n0, int r0, int r1,
-                                         f32x4 (*red)[ModeDims<MODE>::NM][kWave], Q2Lds* q2,
-                                         const WChunk<FMT> (&pre)[ModeDims<MODE>::NM], bool has_pre) {
-    constexpr int NM = ModeDims<MODE>::NM;
-    const int N = MODE == 0 ? a.f : a.d;
-    const int K = MODE == 0 ? a.d : a.f;
-    const int G = K / kGroup;
-    const int S = ceil_div(G, 4);
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int row = lane & 15, g = lane >> 4;
-    const int s_beg = (S * wave) / KW, s_end = (S * (wave + 1)) / KW;
-    const int nk = ceil_div(s_end - s_beg, kCap);
-
-    WRow wr[NM];
-#pragma unroll
-    for (int m = 0; m < NM; ++m) {
-        const int mat = MODE == 0 ? m : 2;
-        wr[m] = wrow<FMT>(a.codes[mat], a.scales[mat], a.mins[mat], static_cast<size_t>(slot) * N + n0 + row, K);
+__device__ __forceinline__ Item find_item(const FfnArgs& a, int ai) {
+    const int lane = threadIdx.x & 63;
+    int lo = 0, hi = 0, sl = lane;
+    if (lane < a.E) {
+        lo = a.offsets[lane];
+        hi = a.offsets[lane + 1];
+        if (a.slot_of_expert) sl = a.slot_of_expert[lane];
     }
-    WChunk<FMT> w[NM];
-    if (nk == 1) {
-#pragma unroll
-        for (int m = 0; m < NM; ++m) {
-            if (has_pre) w[m] = pre[m];
-            else load_w<FMT>(w[m], wr[m], s_beg, s_end, G, g);
-        }
-    }
-    for (int c0 = r0; c0 < r1; c0 += 16) {
-        const int r = c0 + row;
-        const bool colok = r < r1;
-        const uint16_t* brow;
-        if (MODE == 0) brow = a.x + static_cast<size_t>(colok ? a.perm[r] / a.k : 0) * a.d;
-        else brow = a.act + static_cast<size_t>(colok ? r : 0) * a.f;
-        f32x4 acc[NM];
-#pragma unroll
-        for (int m = 0; m < NM; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int kc = 0; kc < nk; ++kc) {
-            const int s0 = s_beg + kc * kCap;
-            if (nk > 1) {
-#pragma unroll
-                for (int m = 0; m < NM; ++m) {
-                    if (has_pre && kc == 0 && c0 == r0) w[m] = pre[m];
-                    else load_w<FMT>(w[m], wr[m], s0, s_end, G, g);
-                }
-            }
-            u32x4 bv[kCap][4];
-            load_b<FMT>(bv, brow, colok, s0, s_end, G, g);
-            mma_chunk<FMT, NM>(acc, w, bv, q2 + wave * NM);
-        }
-#pragma unroll
-        for (int m = 0; m < NM; ++m) red[wave][m][lane] = acc[m];
-        __syncthreads();
-        for (int idx = tid; idx < 16 * 16; idx += KW * kWave) {
-            const int col = idx >> 4, nn = idx & 15;
-            const int src = col + 16 * (nn >> 2), i = nn & 3;
-            const int rr = c0 + col;
-            if (rr < r1) {
-                float v[NM];
-#pragma unroll
-                for (int m = 0; m < NM; ++m) {
-                    float s = red[0][m][src][i];
-#pragma unroll
-                    for (int ww = 1; ww < KW; ++ww) s += red[ww][m][src][i];
-                    v[m] = s;
-                }
-                const int n = n0 + nn;
-                if constexpr (MODE == 0) {
-                    a.act[static_cast<size_t>(rr) * a.f + n] = f32_to_bf16_rne(silu_mul(v[0], v[NM - 1]));
-                } else {
-                    a.y[static_cast<size_t>(rr) * a.d + n] = v[0];
-                    if (a.fuse_combine) {
-                        // scatter-add of the weighted expert output; with at
-                        // most two addends on a zeroed out the sum does not
-                        // depend on their order (it equals the combine kernel's)
-                        const int p = a.perm[rr];
-                        atomicAdd(a.out + static_cast<size_t>(p / a.k) * a.d + n, __fmul_rn(a.topk_w[p], v[0]));
-                    }
-                }
-            }
-        }
-        __syncthreads();
-    }
+    const uint64_t mask = __ballot(hi > lo);
+    const uint64_t below = mask & ((1ull << lane) - 1ull);
+    const uint64_t hit = __ballot(((mask >> lane) & 1ull) && __popcll(below) == ai);
+    Item it;
+    it.e = hit ? __ffsll(static_cast<unsigned long long>(hit)) - 1 : -1;
+    const int src = it.e < 0 ? 0 : it.e;
+    it.r0 = __shfl(lo, src);
+    it.r1 = __shfl(hi, src);
+    it.slot = __shfl(sl, src);
+    return it;
 }
 
 // Zero y rows [r0, r1) x [n0, n0+16) (down tiles of an expert whose slot is invalid).
@@ -128,54 +64,128 @@ __device__ __forceinline__ void zero_y_tail(const FfnArgs& a) {
         base[i] = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
-struct ItemRef {
-    int e, slot, r0, r1, n0;
-    bool slot_ok;
-};
-
-// Work item `item` of a projection with `ntiles` 16-row tiles per expert.
-__device__ __forceinline__ ItemRef item_ref(const FfnArgs& a, int item, int ntiles) {
-    ItemRef it;
-    const int ai = item / ntiles;
-    it.n0 = (item % ntiles) * 16;
-    it.e = nth_active_expert(a.offsets, a.E, ai);
-    it.r0 = it.r1 = it.slot = 0;
-    it.slot_ok = false;
-    if (it.e < 0) return it;
-    it.r0 = a.offsets[it.e];
-    it.r1 = a.offsets[it.e + 1];
-    it.slot = a.slot_of_expert ? a.slot_of_expert[it.e] : it.e;
-    it.slot_ok = it.slot >= 0 && it.slot < a.num_slots;
-    return it;
-}
-
-__device__ __forceinline__ int active_count(const int32_t* offsets, int E) {
-    const int lane = threadIdx.x & 63;
-    const int cnt = lane < E ? offsets[lane + 1] - offsets[lane] : 0;
-    return __popcll(__ballot(cnt > 0));
-}
-
-// ------------------------------------------------------------ two launches
-
+// Work item = (active expert, tile of 16 weight rows); block = KW waves that
+// split the K steps; their partial tiles are summed in LDS in wave order.
+//  MODE 0: gate and up + SwiGLU -> act (bf16).  MODE 1: down -> y (fp32), or
+//          with fuse_combine the weighted scatter-add into out instead.
+// Column c of a 16-row column tile is sorted row c0 + c: MODE 0 reads
+// x[perm[r]/k], MODE 1 reads act[r]; padding columns read a valid row and
+// are zeroed.  Loads are ordered so that nothing waits on the weight stream
+// before the multiply: vmcnt retires loads in issue order, so the row index
+// an address needs (perm) is loaded before the weights.  (Taking the T <= 16
+// tokens themselves as the columns, which drops that index load, measured no
+// faster at T = 1 and slower at T = 5 and 16, where most columns then load
+// token rows the expert does not own.)
 template <int FMT, int MODE, int KW>
 __global__ __launch_bounds__(KW * 64) void ffn_skinny_kernel(FfnArgs a) {
-    constexpr int NM = ModeDims<MODE>::NM;
+    constexpr int NM = MODE == 0 ? 2 : 1;
     __shared__ __align__(16) f32x4 red[KW][NM][kWave];
     __shared__ __align__(16) Q2Lds q2[FMT == MOE_FMT_Q2G32 ? KW * NM : 1];
+    __shared__ int row_tok[16];     // fused combine: token of the row
+    __shared__ float row_w[16];     // fused combine: routing weight of the row
     if (MODE == 1 && blockIdx.x == gridDim.x - 1) {
         zero_y_tail(a);
         return;
     }
-    const int ntiles = (MODE == 0 ? a.f : a.d) / 16;
-    const ItemRef it = item_ref(a, blockIdx.x, ntiles);
+    const int N = MODE == 0 ? a.f : a.d;
+    const int K = MODE == 0 ? a.d : a.f;
+    const int G = K / kGroup, S = ceil_div(K, kStepK), NT = N / 16;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int row = lane & 15, g = lane >> 4;
+    const int s_beg = (S * wave) / KW, s_end = (S * (wave + 1)) / KW;
+    const int nk = ceil_div(s_end - s_beg, kCap);
+    const bool fused = MODE == 1 && a.fuse_combine;
+
+    const int n0 = (blockIdx.x % NT) * 16;
+    const Item it = find_item(a, blockIdx.x / NT);
     if (it.e < 0) return;
-    if (!it.slot_ok) {
-        if (threadIdx.x == 0 && it.n0 == 0) raise_status(a.status, MOE_DEV_BAD_SLOT);
-        if (MODE == 1) zero_y_tile(a, it.n0, it.r0, it.r1);
+    if (it.slot < 0 || it.slot >= a.num_slots) {
+        if (tid == 0 && n0 == 0) raise_status(a.status, MOE_DEV_BAD_SLOT);
+        if (MODE == 1) zero_y_tile(a, n0, it.r0, it.r1);
         return;
     }
-    WChunk<FMT> none[NM];
-    run_item<FMT, MODE, KW>(a, it.slot, it.n0, it.r0, it.r1, red, q2, none, false);
+
+    // Row data of the first column tile, ahead of the weight loads.
+    int r = it.r0 + row;
+    bool colok = r < it.r1;
+    int pr = colok && (MODE == 0 || fused) ? a.perm[r] : 0;
+    const uint16_t* brow = MODE == 0 ? a.x + static_cast<size_t>(pr / a.k) * a.d
+                                     : a.act + static_cast<size_t>(colok ? r : it.r0) * a.f;
+
+    WTile wt[NM];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+        const int mat = MODE == 0 ? m : 2;
+        wt[m] = wtile<FMT>(a.codes[mat], a.scales[mat], static_cast<size_t>(it.slot) * NT + n0 / 16, S, lane);
+    }
+    WChunk<FMT> w[NM];
+    if (nk > 0) {
+#pragma unroll
+        for (int m = 0; m < NM; ++m) load_w<FMT>(w[m], wt[m], s_beg, s_end);
+    }
+    u32x4 bv[kCap][4];
+    if (nk > 0) load_b<FMT>(bv, brow, colok, s_beg, G, g);
+    float wr = fused && colok ? a.topk_w[pr] : 0.f;   // queued behind the weights
+
+    const int ncol = ceil_div(it.r1 - it.r0, 16);
+    for (int ct = 0; ct < ncol; ++ct) {
+        const int c0 = it.r0 + 16 * ct;
+        if (ct > 0) {
+            r = c0 + row;
+            colok = r < it.r1;
+            pr = colok && (MODE == 0 || fused) ? a.perm[r] : 0;
+            brow = MODE == 0 ? a.x + static_cast<size_t>(pr / a.k) * a.d
+                             : a.act + static_cast<size_t>(colok ? r : it.r0) * a.f;
+            wr = fused && colok ? a.topk_w[pr] : 0.f;
+        }
+        f32x4 acc[NM];
+#pragma unroll
+        for (int m = 0; m < NM; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int kc = 0; kc < nk; ++kc) {
+            const int s0 = s_beg + kc * kCap;
+            if (kc > 0 || ct > 0) {
+                if (nk > 1) {
+#pragma unroll
+                    for (int m = 0; m < NM; ++m) load_w<FMT>(w[m], wt[m], s0, s_end);
+                }
+                load_b<FMT>(bv, brow, colok, s0, G, g);
+            }
+            mma_chunk<FMT, NM>(acc, w, bv, min(kCap, s_end - s0), q2 + wave * NM);
+        }
+#pragma unroll
+        for (int m = 0; m < NM; ++m) red[wave][m][lane] = acc[m];
+        if (fused && wave == 0 && lane < 16) {
+            row_tok[lane] = pr / a.k;
+            row_w[lane] = wr;
+        }
+        __syncthreads();
+        const int R = min(16, it.r1 - c0);
+        for (int idx = tid; idx < R * 16; idx += KW * kWave) {
+            const int cc = idx >> 4, nn = idx & 15;
+            const int src = cc + 16 * (nn >> 2), i = nn & 3;
+            float v[NM];
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                float sum = red[0][m][src][i];
+#pragma unroll
+                for (int ww = 1; ww < KW; ++ww) sum += red[ww][m][src][i];
+                v[m] = sum;
+            }
+            const size_t rr = static_cast<size_t>(c0 + cc);
+            const int n = n0 + nn;
+            if constexpr (MODE == 0) {
+                a.act[rr * a.f + n] = f32_to_bf16_rne(silu_mul(v[0], v[NM - 1]));
+            } else if (fused) {
+                // scatter-add of the weighted expert output; with at most two
+                // addends on a zeroed out the sum does not depend on their
+                // order (it equals the combine kernel's)
+                atomicAdd(a.out + static_cast<size_t>(row_tok[cc]) * a.d + n, __fmul_rn(row_w[cc], v[0]));
+            } else {
+                a.y[rr * a.d + n] = v[0];
+            }
+        }
+        __syncthreads();
+    }
 }
 
 // ------------------------------------------------------------ launch

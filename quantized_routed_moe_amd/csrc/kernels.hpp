@@ -16,9 +16,8 @@ struct FfnArgs {
     const int32_t* perm;          // [T*k]
     const int32_t* slot_of_expert;  // [E] or null
     int num_slots;
-    const uint8_t* codes[3];      // gate, up, down
-    const uint8_t* scales[3];     // MXFP4: e8m0 bytes; Q2: fp16 bits
-    const uint16_t* mins[3];      // Q2 only
+    const uint8_t* codes[3];      // gate, up, down: tile layout (MOE_LAYOUT_TILES)
+    const uint8_t* scales[3];     // MXFP4: e8m0 byte per piece; Q2: fp16 scale | fp16 min << 16
     uint16_t* act;                // bf16 [T*k][f] (workspace)
     float* y;                     // fp32 [T*k][d]
     uint32_t* status;             // workspace header
@@ -44,5 +43,7 @@ hipError_t launch_ffn_grouped(const moe_shape& s, const FfnArgs& a, hipStream_t 
 hipError_t launch_combine(const moe_shape& s, const float* y, const int32_t* inv, const float* w,
                           float* out, hipStream_t st);
 hipError_t launch_clear_header(uint32_t* header, hipStream_t st);
+hipError_t launch_pack(int fmt, const void* src_codes, const void* src_scales, const void* src_mins, void* dst_codes,
+                       void* dst_scales, int slots, int n, int K, hipStream_t st);
 
 }  // namespace qrmoe

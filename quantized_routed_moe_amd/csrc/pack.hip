@@ -1,0 +1,77 @@
+// Re-layout of quantised expert matrices from rows (n x K per slot) into the
+// tile layout the expert-FFN kernels stream: 16-row tiles x 128-element K
+// steps, each (tile, step) block a contiguous array of 64 pieces in the order
+// the lanes of a wave consume them (include/moe.h, enum moe_layout).  A pure
+// gather: every code, scale and min is copied bit for bit.  Runs once when
+// the weights are loaded.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace qrmoe {
+
+// One thread per piece.  pieces = slots * (n/16) * S * 64, S = ceil(K/128).
+template <int FMT>
+__global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ src_codes,
+                                                   const uint8_t* __restrict__ src_scales,
+                                                   const uint16_t* __restrict__ src_mins,
+                                                   uint8_t* __restrict__ dst_codes, uint8_t* __restrict__ dst_scales,
+                                                   int n, int K, size_t pieces) {
+    const int G = K / kGroup;
+    const int S = ceil_div(K, 128);
+    const int NT = n / 16;
+    for (size_t p = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; p < pieces;
+         p += static_cast<size_t>(gridDim.x) * blockDim.x) {
+        const int L = static_cast<int>(p & 63);
+        const size_t blk = p >> 6;                       // (slot * NT + tile) * S + step
+        const int s = static_cast<int>(blk % S);
+        const size_t ti = blk / S;                       // slot * NT + tile
+        const size_t slot = ti / NT;
+        const int row = static_cast<int>(ti % NT) * 16 + (L & 15);
+        const int g = L >> 4;
+        const size_t grow = slot * n + row;
+        const int gi = 4 * s + g;                        // group of this piece's scale
+        if constexpr (FMT == MOE_FMT_MXFP4) {
+            u32x4 c = {0u, 0u, 0u, 0u};
+            uint8_t sc = 127;
+            if (gi < G) {
+                c = *reinterpret_cast<const u32x4*>(src_codes + grow * (K / 2) + static_cast<size_t>(gi) * 16);
+                sc = src_scales[grow * G + gi];
+            }
+            *reinterpret_cast<u32x4*>(dst_codes + p * 16) = c;
+            dst_scales[p] = sc;
+        } else {
+            // bytes 2g, 2g+1 of each of the step's four groups
+            const uint16_t* row16 = reinterpret_cast<const uint16_t*>(src_codes + grow * (K / 4));
+            uint32_t h[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int gj = 4 * s + j;
+                h[j] = gj < G ? row16[gj * 4 + g] : 0u;
+            }
+            *reinterpret_cast<u32x2*>(dst_codes + p * 8) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+            uint32_t sm = 0u;
+            if (gi < G) {
+                const uint16_t* sc16 = reinterpret_cast<const uint16_t*>(src_scales);
+                sm = static_cast<uint32_t>(sc16[grow * G + gi]) | (static_cast<uint32_t>(src_mins[grow * G + gi]) << 16);
+            }
+            reinterpret_cast<uint32_t*>(dst_scales)[p] = sm;
+        }
+    }
+}
+
+hipError_t launch_pack(int fmt, const void* src_codes, const void* src_scales, const void* src_mins, void* dst_codes,
+                       void* dst_scales, int slots, int n, int K, hipStream_t st) {
+    const size_t pieces = static_cast<size_t>(slots) * (n / 16) * ceil_div(K, 128) * 64;
+    const size_t want = (pieces + 255) / 256;
+    const int blocks = static_cast<int>(want < 65536 ? want : 65536);
+    const auto* sc = static_cast<const uint8_t*>(src_codes);
+    const auto* ss = static_cast<const uint8_t*>(src_scales);
+    const auto* sm = static_cast<const uint16_t*>(src_mins);
+    auto* dc = static_cast<uint8_t*>(dst_codes);
+    auto* ds = static_cast<uint8_t*>(dst_scales);
+    if (fmt == MOE_FMT_MXFP4) pack_kernel<MOE_FMT_MXFP4><<<blocks, 256, 0, st>>>(sc, ss, sm, dc, ds, n, K, pieces);
+    else pack_kernel<MOE_FMT_Q2G32><<<blocks, 256, 0, st>>>(sc, ss, sm, dc, ds, n, K, pieces);
+    return hipGetLastError();
+}
+
+}  // namespace qrmoe

@@ -22,7 +22,7 @@ def _declared_symbols():
 
 def test_library_exports_every_declared_symbol():
     syms = _declared_symbols()
-    assert len(syms) == 10
+    assert len(syms) == 12
     assert sorted(qm.EXPORTS) == syms
     L = ctypes.CDLL(qm.LIB_PATH)
     for s in syms:
@@ -72,8 +72,11 @@ def test_null_shape_and_zero_tokens():
     assert qm.lib().moe_layer(ctypes.byref(s), *([None] * 9), 0, None) == qm.MOE_OK
 
 
-def _experts(fmt=qm.MOE_FMT_MXFP4, mins=None, slots=8, soe=None, **over):
-    q = lambda: qm.moe_qmat(fmt, A16, A16, mins)
+TILES, ROWS = qm.MOE_LAYOUT_TILES, qm.MOE_LAYOUT_ROWS
+
+
+def _experts(fmt=qm.MOE_FMT_MXFP4, mins=None, slots=8, soe=None, layout=TILES, **over):
+    q = lambda: qm.moe_qmat(fmt, layout, A16, A16, mins)
     e = qm.moe_experts(q(), q(), q(), soe, slots)
     for k, v in over.items():
         setattr(e, k, v)
@@ -92,17 +95,21 @@ def test_ffn_validation():
     assert _ffn(s, _experts(), y=None) == qm.MOE_ERR_NULL
     assert _ffn(s, _experts(fmt=7)) == qm.MOE_ERR_FORMAT
     mixed = _experts()
-    mixed.down = qm.moe_qmat(qm.MOE_FMT_Q2G32, A16, A16, A16)
+    mixed.down = qm.moe_qmat(qm.MOE_FMT_Q2G32, TILES, A16, A16, None)
     assert _ffn(s, mixed) == qm.MOE_ERR_FORMAT
-    assert _ffn(s, _experts(fmt=qm.MOE_FMT_Q2G32, mins=None)) == qm.MOE_ERR_FORMAT
+    # the kernels read the tile layout only; its Q2 mins live in scales
+    assert _ffn(s, _experts(layout=ROWS)) == qm.MOE_ERR_FORMAT
+    assert _ffn(s, _experts(fmt=qm.MOE_FMT_Q2G32, mins=A16)) == qm.MOE_ERR_FORMAT
+    assert _ffn(s, _experts(fmt=qm.MOE_FMT_Q2G32, mins=None), ws=None) == qm.MOE_ERR_NULL
     assert _ffn(s, _experts(slots=7)) == qm.MOE_ERR_SHAPE            # identity map needs E slots
     assert _ffn(s, _experts(slots=0, soe=A16)) == qm.MOE_ERR_SHAPE
     assert _ffn(s, _experts(), x=A16 + 8) == qm.MOE_ERR_ALIGN
     assert _ffn(s, _experts(), y=A16 + 4) == qm.MOE_ERR_ALIGN
     bad = _experts()
-    bad.up = qm.moe_qmat(qm.MOE_FMT_MXFP4, A16 + 2, A16, None)
+    bad.up = qm.moe_qmat(qm.MOE_FMT_MXFP4, TILES, A16 + 2, A16, None)
     assert _ffn(s, bad) == qm.MOE_ERR_ALIGN
-    assert _ffn(s, _experts(fmt=qm.MOE_FMT_Q2G32, mins=A16 + 8)) == qm.MOE_ERR_ALIGN
+    bad.up = qm.moe_qmat(qm.MOE_FMT_MXFP4, TILES, A16, A16 + 8, None)
+    assert _ffn(s, bad) == qm.MOE_ERR_ALIGN
     assert _ffn(s, _experts(soe=A16 + 2, slots=4)) == qm.MOE_ERR_ALIGN
     need = qm.lib().moe_workspace_bytes(ctypes.byref(s))
     assert _ffn(s, _experts(), ws_bytes=need - 1) == qm.MOE_ERR_WORKSPACE
@@ -142,3 +149,47 @@ def test_layer_validation():
     assert L.moe_layer(*args(x=None)) == qm.MOE_ERR_NULL
     assert L.moe_layer(*args(ex=_experts(fmt=3))) == qm.MOE_ERR_FORMAT
     assert L.moe_layer(*args(wr=None, bias=A16)) == qm.MOE_ERR_UNSUPPORTED
+
+
+def _qbytes(fmt, layout, slots, n, K):
+    c, sc, m = ctypes.c_size_t(7), ctypes.c_size_t(7), ctypes.c_size_t(7)
+    tot = qm.lib().moe_qmat_bytes(fmt, layout, slots, n, K, ctypes.byref(c), ctypes.byref(sc), ctypes.byref(m))
+    return tot, c.value, sc.value, m.value
+
+
+def test_qmat_bytes():
+    MX, Q2 = qm.MOE_FMT_MXFP4, qm.MOE_FMT_Q2G32
+    # row layout: the packed data itself
+    assert _qbytes(MX, ROWS, 64, 2048, 4096) == (64 * 2048 * (2048 + 128),) + (64 * 2048 * 2048, 64 * 2048 * 128, 0)
+    assert _qbytes(Q2, ROWS, 3, 16, 96)[1:] == (3 * 16 * 24, 3 * 16 * 3 * 2, 3 * 16 * 3 * 2)
+    # tile layout: (slots * n/16 * ceil(K/128)) blocks of 64 pieces; no padding when 128 | K
+    assert _qbytes(MX, TILES, 64, 2048, 4096)[1:] == (64 * 2048 * 2048, 64 * 2048 * 128, 0)
+    assert _qbytes(MX, TILES, 2, 32, 160)[1:] == (2 * 2 * 2 * 64 * 16, 2 * 2 * 2 * 64, 0)
+    assert _qbytes(Q2, TILES, 3, 16, 96)[1:] == (3 * 1 * 1 * 64 * 8, 3 * 1 * 1 * 64 * 4, 0)
+    for bad in [(5, TILES, 1, 16, 32), (MX, 2, 1, 16, 32), (MX, TILES, 0, 16, 32), (MX, TILES, 1, 24, 32),
+                (MX, TILES, 1, 16, 48), (MX, ROWS, 1, 0, 32), (Q2, TILES, 1, 16, 0)]:
+        assert _qbytes(*bad) == (0, 0, 0, 0), bad
+
+
+def test_pack_validation():
+    L = qm.lib()
+    MX, Q2 = qm.MOE_FMT_MXFP4, qm.MOE_FMT_Q2G32
+    pk = lambda src, dst, n=32, K=128, slots=2: L.moe_pack_qmat(
+        None if src is None else ctypes.byref(src), None if dst is None else ctypes.byref(dst), slots, n, K, None)
+    rows = lambda fmt=MX, c=A16, sc=A16, mn=None: qm.moe_qmat(fmt, ROWS, c, sc, mn)
+    tiles = lambda fmt=MX, c=A16, sc=A16, mn=None: qm.moe_qmat(fmt, TILES, c, sc, mn)
+    assert pk(None, tiles()) == qm.MOE_ERR_NULL
+    assert pk(rows(), None) == qm.MOE_ERR_NULL
+    assert pk(tiles(), tiles()) == qm.MOE_ERR_FORMAT            # source must be the row layout
+    assert pk(rows(), rows()) == qm.MOE_ERR_FORMAT              # destination must be the tile layout
+    assert pk(rows(MX), tiles(Q2)) == qm.MOE_ERR_FORMAT         # same format on both sides
+    assert pk(rows(9), tiles(9)) == qm.MOE_ERR_FORMAT
+    assert pk(rows(), tiles(), n=24) == qm.MOE_ERR_SHAPE
+    assert pk(rows(), tiles(), K=48) == qm.MOE_ERR_SHAPE
+    assert pk(rows(), tiles(), slots=0) == qm.MOE_ERR_SHAPE
+    assert pk(rows(Q2), tiles(Q2)) == qm.MOE_ERR_NULL           # Q2 rows need mins
+    assert pk(rows(MX, mn=A16), tiles()) == qm.MOE_ERR_FORMAT
+    assert pk(rows(Q2, mn=A16), tiles(Q2, mn=A16)) == qm.MOE_ERR_FORMAT
+    assert pk(rows(c=A16 + 4), tiles()) == qm.MOE_ERR_ALIGN
+    assert pk(rows(), tiles(sc=A16 + 2)) == qm.MOE_ERR_ALIGN
+    assert pk(rows(Q2, mn=A16 + 2), tiles(Q2)) == qm.MOE_ERR_ALIGN

@@ -10,7 +10,8 @@ import torch
 
 import quantized_routed_moe_amd as qm
 import synthetic
-from gpu_util import (assert_close, check_against_oracle, device_case, run_layer, run_steps)
+from gpu_util import (assert_act_close, assert_close, check_against_oracle, device_case, run_layer,
+                      run_steps)
 from oracle import ref
 
 pytestmark = pytest.mark.gpu
@@ -264,3 +265,78 @@ def test_layer_repeated_on_one_workspace():
         assert np.array_equal(o, outs[0])
     g = run_steps(dc)
     assert np.array_equal(outs[0], g["out"])
+
+
+# ---------------------------------------------------------------- tile layout
+
+def _tiles_mxfp4(codes, scales):
+    """The tile layout of include/moe.h restated with numpy reshapes:
+    block (slot, tile, step), piece L = 16 g + r holds group 4 step + g of row
+    16 tile + r; padding groups have zero codes and scale byte 127."""
+    slots, n, half = codes.shape
+    G, S, NT = half // 16, -(-half // 64), n // 16
+    cg = np.zeros((slots, n, 4 * S, 16), np.uint8)
+    cg[:, :, :G] = codes.reshape(slots, n, G, 16)
+    sg = np.full((slots, n, 4 * S), 127, np.uint8)
+    sg[:, :, :G] = scales
+    c = cg.reshape(slots, NT, 16, S, 4, 16).transpose(0, 1, 3, 4, 2, 5)
+    s = sg.reshape(slots, NT, 16, S, 4).transpose(0, 1, 3, 4, 2)
+    return c.reshape(-1), s.reshape(-1)
+
+
+def _tiles_q2(codes, scales, mins):
+    """Q2: piece L = 16 g + r holds, for j = 0..3, bytes 2g, 2g+1 of group
+    4 step + j of row 16 tile + r; its scale word is (scale | min << 16) of
+    group 4 step + g (zero for padding)."""
+    slots, n, quarter = codes.shape
+    G, S, NT = quarter // 8, -(-quarter // 32), n // 16
+    cg = np.zeros((slots, n, 4 * S, 8), np.uint8)
+    cg[:, :, :G] = codes.reshape(slots, n, G, 8)
+    c = cg.reshape(slots, NT, 16, S, 4, 4, 2).transpose(0, 1, 3, 5, 2, 4, 6)
+    sm = np.zeros((slots, n, 4 * S), np.uint32)
+    sm[:, :, :G] = scales.astype(np.uint32) | (mins.astype(np.uint32) << 16)
+    s = sm.reshape(slots, NT, 16, S, 4).transpose(0, 1, 3, 4, 2)
+    return c.reshape(-1), np.ascontiguousarray(s.reshape(-1)).view(np.uint8)
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "q2"])
+@pytest.mark.parametrize("n,K", [(48, 224), (16, 32), (32, 512)])
+def test_pack_layout(fmt, n, K):
+    rng = np.random.default_rng(n * 7 + K)
+    m = synthetic.make_matrix(fmt, 3, n, K, rng)
+    q = qm.pack_arrays(fmt, m, n, K)
+    got_c, got_s = q.codes.cpu().numpy(), q.scales.cpu().numpy()
+    if fmt == "mxfp4":
+        want_c, want_s = _tiles_mxfp4(m["codes"], m["scales"])
+    else:
+        want_c, want_s = _tiles_q2(m["codes"], m["scales"], m["mins"])
+    assert np.array_equal(got_c, want_c)
+    assert np.array_equal(got_s, want_s)
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "q2"])
+def test_repeated_ids_within_a_token(fmt):
+    """moe_dispatch takes ids from any source: tokens that name expert 3 twice
+    give it 20 rows of 12 tokens (two 16-row column tiles, the second ragged)."""
+    T, d, E, k, f = 12, 256, 8, 2, 160
+    case = synthetic.make_case(T, d, E, k, f, fmt, seed=21)
+    dc = device_case(case)
+    ids = np.full((T, k), 3, np.int32)
+    ids[::3, 1] = 5
+    s = dc["shape"]
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    perm = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    inv = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    y = torch.full((T * k, d), float("nan"), dtype=torch.float32, device="cuda")
+    ws = qm.alloc_workspace(s)
+    qm.moe_dispatch(s, torch.from_numpy(ids).cuda(), offsets, perm, inv, ws)
+    qm.moe_expert_ffn(s, dc["x"], dc["experts"], offsets, perm, y, ws)
+    assert qm.moe_read_device_status(ws) == 0
+    off, pm, _ = ref.dispatch(ids, E)
+    assert np.array_equal(offsets.cpu().numpy(), off) and off[4] - off[3] == 20
+    assert np.array_equal(perm.cpu().numpy(), pm)
+    act_dev = ws[256:256 + T * k * f * 2].view(torch.int16).view(torch.bfloat16).float().reshape(T * k, f)
+    act_dev = act_dev.cpu().numpy()
+    act, _ = ref.expert_ffn(case["x"], k, off, pm, case["gate"], case["up"], case["down"])
+    assert_act_close(act_dev, act)
+    assert_close(y.cpu().numpy(), ref.expert_down(act_dev, off, case["down"]), "y (given device act)")
