@@ -34,6 +34,18 @@ HBM_PEAK_GBPS = 8000.0         # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
 METRIC = "MoE layer tokens/s; decode weight-stream GB/s; prefill expert TFLOP/s"
 
+# HBM bytes per moe_expert_ffn call from rocprofv3 counter runs of the current
+# FFN kernels (--pmc FETCH_SIZE, then --pmc WRITE_SIZE, one dispatch each;
+# FETCH_SIZE x 2.0 and WRITE_SIZE x 1.0 KiB, the factors a plain 256 MiB copy
+# reads), summed over the kernels of the call.  Workloads 3 and 4 route a
+# different number of experts each step: theirs is the average of the counted
+# steps.  Must be re-measured (or removed) whenever an FFN kernel changes.
+MEASURED_FFN_TRAFFIC = {
+    1: (2 * (8787.4 + 4428.6) + (8.0 + 32.0)) * 1024,
+    3: (2 * (280324.6 + 163505.5 + 12.0) + (16397.3 + 65545.1)) * 1024,
+    4: (2 * (27544.7 + 14033.6) + (128.0 + 512.0)) * 1024,
+}
+
 MX_BYTES_PER_EXPERT = lambda d, f: 3 * d * f // 2 + 3 * d * f // 32      # codes + e8m0 scales
 Q2_BYTES_PER_EXPERT = lambda d, f: 3 * d * f // 4 + 3 * d * f // 32 * 4  # codes + fp16 scale + min
 
@@ -275,12 +287,15 @@ def main():
     gbps = ffn_bytes / ffn_avg_s / 1e9
     tflops = flops / ffn_avg_s / 1e12
 
+    traffic = MEASURED_FFN_TRAFFIC.get(c)
+    traffic = None if traffic is None else round(traffic)
     if T * k >= 1024:
         roof = dict(bound="mfma", achieved=round(tflops, 2), peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), traffic=None)
+                    frac=round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), traffic=traffic)
     else:
         roof = dict(bound="hbm", achieved=round(gbps, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
-                    frac=round(gbps / HBM_PEAK_GBPS, 4), traffic=None)
+                    frac=round(gbps / HBM_PEAK_GBPS, 4), traffic=traffic)
+    roof["traffic_unit"] = "HBM bytes per call (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
     roof["kernel"] = "moe_expert_ffn (gate/up + SwiGLU kernel, down kernel)"
     roof["algorithmic_bytes_per_launch"] = round(ffn_bytes)
     roof["avg_launch_ms"] = round(ffn_avg_s * 1e3, 5)
