@@ -61,11 +61,16 @@ def run_steps(dc: dict) -> dict:
     return res
 
 
-def run_layer(dc: dict) -> dict:
+def run_layer(dc: dict, ws=None) -> dict:
+    """moe_layer in one call; the workspace's device status must stay clean."""
     s = dc["shape"]
     logits = dc["logits_in"].clone() if dc["logits_in"] is not None else None
+    if ws is None:
+        ws = qm.alloc_workspace(s, layer=True, device=dc["x"].device)
     out, ids, w, lg = qm.layer(dc["x"], dc["experts"], s.k, w_router=dc["w_router"], bias=dc["bias"],
-                               logits=logits)
+                               logits=logits, ws=ws)
+    status = qm.moe_read_device_status(ws)
+    assert status == 0, f"device status {status:#x}"
     return dict(out=out.cpu().numpy(), ids=ids.cpu().numpy(), w=w.cpu().numpy(), logits=lg.cpu().numpy())
 
 

@@ -250,8 +250,9 @@ def test_layer_small_T_fused_path_equals_steps(shape, fmt):
 
 
 def test_layer_repeated_on_one_workspace():
-    """Back-to-back moe_layer calls sharing one workspace (the fused routing's
-    last-workgroup counter must come back to zero) give identical results."""
+    """Back-to-back moe_layer calls sharing one workspace give identical
+    results: the fused routing's last-workgroup counter (header word 16) comes
+    back to zero after every call."""
     case = synthetic.workload(1)
     dc = device_case(case)
     s = dc["shape"]
@@ -261,6 +262,8 @@ def test_layer_repeated_on_one_workspace():
         out, ids, w, lg = qm.layer(dc["x"], dc["experts"], s.k, w_router=dc["w_router"], bias=dc["bias"], ws=ws)
         outs.append(out.cpu().numpy())
     assert qm.moe_read_device_status(ws) == 0
+    words = ws[:256].view(torch.int32).cpu().numpy()
+    assert not words[16:32].any(), words[16:32]
     for o in outs[1:]:
         assert np.array_equal(o, outs[0])
     g = run_steps(dc)
