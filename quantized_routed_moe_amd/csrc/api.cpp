@@ -105,10 +105,9 @@ int do_dispatch(const moe_shape& s, const int32_t* ids, int32_t* offsets, int32_
     return hip_rc(qrmoe::launch_dispatch(s, ids, offsets, perm, inv, static_cast<uint32_t*>(ws), st));
 }
 
-int do_ffn(const moe_shape& s, const uint16_t* x, const moe_experts* ex, const int32_t* offsets,
-           const int32_t* perm, float* y, void* ws, hipStream_t st, const float* fused_w = nullptr,
-           float* fused_out = nullptr) {
-    FfnArgs a;
+FfnArgs ffn_args(const moe_shape& s, const uint16_t* x, const moe_experts* ex, const int32_t* offsets,
+                 const int32_t* perm, float* y, void* ws) {
+    FfnArgs a{};
     a.T = s.T; a.d = s.d; a.E = s.E; a.k = s.k; a.f = s.f;
     a.x = x;
     a.offsets = offsets;
@@ -123,10 +122,12 @@ int do_ffn(const moe_shape& s, const uint16_t* x, const moe_experts* ex, const i
     a.act = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + kHeader);
     a.y = y;
     a.status = static_cast<uint32_t*>(ws);
-    a.topk_w = fused_w;
-    a.out = fused_out;
-    a.fuse_combine = fused_out != nullptr;
-    return hip_rc(qrmoe::launch_ffn(s, ex->gate.fmt, a, st));
+    return a;
+}
+
+int do_ffn(const moe_shape& s, const uint16_t* x, const moe_experts* ex, const int32_t* offsets,
+           const int32_t* perm, float* y, void* ws, hipStream_t st) {
+    return hip_rc(qrmoe::launch_ffn(s, ex->gate.fmt, ffn_args(s, x, ex, offsets, perm, y, ws), st));
 }
 
 int do_combine(const moe_shape& s, const float* y, const int32_t* inv, const float* w, float* out,
@@ -282,16 +283,27 @@ int moe_layer(const moe_shape* shape, const uint16_t* x, const float* w_router, 
     if ((rc = check_route_args(s, x, w_router, bias, logits, topk_ids, topk_w)) != MOE_OK) return rc;
     if (!x) return MOE_ERR_NULL;
     if ((rc = check_ffn_args(s, x, experts, offsets, perm, y, ws, ws_bytes)) != MOE_OK) return rc;
-    // Small T: routing, top-k and dispatch in one launch; with k <= 2 the
-    // combine is a scatter-add inside the down projection.  Same arithmetic
-    // as the separate entry points, so the results are identical.
-    if (qrmoe::small_fused_supported(s)) {
-        const bool fuse_combine = s.k <= 2 && !qrmoe::ffn_uses_grouped(s, experts->gate.fmt);
-        rc = hip_rc(qrmoe::launch_route_small_fused(s, x, w_router, bias, logits, topk_ids, topk_w, offsets, perm, inv,
-                                                    fuse_combine ? out : nullptr, static_cast<uint32_t*>(ws), stream));
-        if (rc != MOE_OK) return rc;
-        if ((rc = do_ffn(s, x, experts, offsets, perm, y, ws, stream, topk_w, fuse_combine ? out : nullptr)) != MOE_OK)
+    // Small batches (T <= 8, T*k <= 64): the router launch computes only the
+    // logits; every workgroup of the gate/up launch routes the batch itself
+    // (top-k and dispatch in LDS) and its workgroup 0 writes the routing
+    // outputs; with k <= 2 the combine is a scatter-add inside the down
+    // launch.  Same arithmetic as the separate entry points, so the results
+    // are identical.
+    if (qrmoe::routed_ffn_supported(s, experts->gate.fmt)) {
+        if (w_router && (rc = hip_rc(qrmoe::launch_router_logits(s, x, w_router, bias, logits, stream))) != MOE_OK)
             return rc;
+        const bool fuse_combine = s.k <= 2;
+        FfnArgs a = ffn_args(s, x, experts, offsets, perm, y, ws);
+        a.topk_w = topk_w;
+        a.out = fuse_combine ? out : nullptr;
+        a.fuse_combine = fuse_combine;
+        a.logits = logits;
+        a.ids_out = topk_ids;
+        a.w_out = topk_w;
+        a.offsets_out = offsets;
+        a.perm_out = perm;
+        a.inv_out = inv;
+        if ((rc = hip_rc(qrmoe::launch_ffn_routed(s, experts->gate.fmt, a, stream))) != MOE_OK) return rc;
         return fuse_combine ? MOE_OK : do_combine(s, y, inv, topk_w, out, stream);
     }
     if ((rc = do_route(s, x, w_router, bias, logits, topk_ids, topk_w, stream)) != MOE_OK) return rc;

@@ -102,6 +102,59 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
     return g / (1.0f + expf(-g)) * u;
 }
 
+// v of lane `src` (a wave-uniform index) in every lane.
+__device__ __forceinline__ int lane_value(int v, int src) { return __builtin_amdgcn_readlane(v, src); }
+__device__ __forceinline__ float lane_value(float v, int src) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
+}
+
+// One step of a wave max over DPP: every lane the control moves data into
+// takes max(own, moved); the others keep their value.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_max_u64(uint64_t v) {
+    const int lo = static_cast<int>(static_cast<uint32_t>(v));
+    const int hi = static_cast<int>(static_cast<uint32_t>(v >> 32));
+    const uint32_t mlo = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(lo, lo, CTRL, ROW_MASK, 0xf, false));
+    const uint32_t mhi = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(hi, hi, CTRL, ROW_MASK, 0xf, false));
+    const uint64_t m = (static_cast<uint64_t>(mhi) << 32) | mlo;
+    return m > v ? m : v;
+}
+
+// Maximum of a 64-bit value over the 64 lanes, returned to every lane.  Row
+// shifts by 1, 2, 4, 8 leave each row's maximum in its lane 15; row
+// broadcasts 15 and 31 carry those into lane 63, which is then read out.
+// Register-to-register (DPP), no LDS round trips.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+    v = dpp_max_u64<0x111, 0xf>(v);   // row_shr:1
+    v = dpp_max_u64<0x112, 0xf>(v);   // row_shr:2
+    v = dpp_max_u64<0x114, 0xf>(v);   // row_shr:4
+    v = dpp_max_u64<0x118, 0xf>(v);   // row_shr:8
+    v = dpp_max_u64<0x142, 0xa>(v);   // row_bcast:15 into rows 1 and 3
+    v = dpp_max_u64<0x143, 0xc>(v);   // row_bcast:31 into rows 2 and 3
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v)), 63));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v >> 32)), 63));
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add_f32(float v) {
+    const int b = __float_as_int(v);
+    // lanes the control moves no data into receive 0 (old = 0) and keep v
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, b, CTRL, ROW_MASK, 0xf, false));
+}
+
+// Sum of a float over the 64 lanes in a fixed order (the shifts and
+// broadcasts of wave_max_u64), returned to every lane.
+__device__ __forceinline__ float wave_sum_f32(float v) {
+    v = dpp_add_f32<0x111, 0xf>(v);   // row_shr:1
+    v = dpp_add_f32<0x112, 0xf>(v);   // row_shr:2
+    v = dpp_add_f32<0x114, 0xf>(v);   // row_shr:4
+    v = dpp_add_f32<0x118, 0xf>(v);   // row_shr:8
+    v = dpp_add_f32<0x142, 0xa>(v);   // row_bcast:15 into rows 1 and 3
+    v = dpp_add_f32<0x143, 0xc>(v);   // row_bcast:31 into rows 2 and 3
+    return lane_value(v, 63);
+}
+
 __device__ __forceinline__ void raise_status(uint32_t* status, uint32_t bit) {
     atomicOr(status, bit);
 }

@@ -17,8 +17,15 @@
 #include "common.hpp"
 #include "ffn_tile.hpp"
 #include "kernels.hpp"
+#include "topk_dev.hpp"
 
 namespace qrmoe {
+
+// Waves per workgroup (K split): gate/up K = d, down K = f.  With d = 4096 /
+// f = 2048 every wave holds its whole K slice (4 steps) in registers, so all
+// of a workgroup's weight loads are in flight at once.
+constexpr int kGateUpWaves = 8;
+constexpr int kDownWaves = 4;
 
 // The `ai`-th active expert (in id order) of offsets[E+1], its sorted rows
 // [r0, r1) and its pack slot, from one load per lane (lane e reads
@@ -29,6 +36,20 @@ struct Item {
     int e, r0, r1, slot;
 };
 
+__device__ __forceinline__ Item pick_item(int lo, int hi, int sl, int ai) {
+    const int lane = threadIdx.x & 63;
+    const uint64_t mask = __ballot(hi > lo);
+    const uint64_t below = mask & ((1ull << lane) - 1ull);
+    const uint64_t hit = __ballot(((mask >> lane) & 1ull) && __popcll(below) == ai);
+    Item it;
+    it.e = hit ? __ffsll(static_cast<unsigned long long>(hit)) - 1 : -1;
+    const int src = it.e < 0 ? 0 : it.e;
+    it.r0 = lane_value(lo, src);
+    it.r1 = lane_value(hi, src);
+    it.slot = lane_value(sl, src);
+    return it;
+}
+
 __device__ __forceinline__ Item find_item(const FfnArgs& a, int ai) {
     const int lane = threadIdx.x & 63;
     int lo = 0, hi = 0, sl = lane;
@@ -37,16 +58,7 @@ __device__ __forceinline__ Item find_item(const FfnArgs& a, int ai) {
         hi = a.offsets[lane + 1];
         if (a.slot_of_expert) sl = a.slot_of_expert[lane];
     }
-    const uint64_t mask = __ballot(hi > lo);
-    const uint64_t below = mask & ((1ull << lane) - 1ull);
-    const uint64_t hit = __ballot(((mask >> lane) & 1ull) && __popcll(below) == ai);
-    Item it;
-    it.e = hit ? __ffsll(static_cast<unsigned long long>(hit)) - 1 : -1;
-    const int src = it.e < 0 ? 0 : it.e;
-    it.r0 = __shfl(lo, src);
-    it.r1 = __shfl(hi, src);
-    it.slot = __shfl(sl, src);
-    return it;
+    return pick_item(lo, hi, sl, ai);
 }
 
 // Zero y rows [r0, r1) x [n0, n0+16) (down tiles of an expert whose slot is invalid).
@@ -76,17 +88,16 @@ __device__ __forceinline__ void zero_y_tail(const FfnArgs& a) {
 // tokens themselves as the columns, which drops that index load, measured no
 // faster at T = 1 and slower at T = 5 and 16, where most columns then load
 // token rows the expert does not own.)
+//
+// `it` is the item's expert, rows and slot, `n0` its first weight row; `perm`
+// is the sorted-row -> pair map (global, or the workgroup's own LDS copy).
 template <int FMT, int MODE, int KW>
-__global__ __launch_bounds__(KW * 64) void ffn_skinny_kernel(FfnArgs a) {
+__device__ __forceinline__ void skinny_body(const FfnArgs& a, const Item& it, int n0, const int32_t* perm) {
     constexpr int NM = MODE == 0 ? 2 : 1;
     __shared__ __align__(16) f32x4 red[KW][NM][kWave];
     __shared__ __align__(16) Q2Lds q2[FMT == MOE_FMT_Q2G32 ? KW * NM : 1];
     __shared__ int row_tok[16];     // fused combine: token of the row
     __shared__ float row_w[16];     // fused combine: routing weight of the row
-    if (MODE == 1 && blockIdx.x == gridDim.x - 1) {
-        zero_y_tail(a);
-        return;
-    }
     const int N = MODE == 0 ? a.f : a.d;
     const int K = MODE == 0 ? a.d : a.f;
     const int G = K / kGroup, S = ceil_div(K, kStepK), NT = N / 16;
@@ -96,21 +107,12 @@ __global__ __launch_bounds__(KW * 64) void ffn_skinny_kernel(FfnArgs a) {
     const int nk = ceil_div(s_end - s_beg, kCap);
     const bool fused = MODE == 1 && a.fuse_combine;
 
-    const int n0 = (blockIdx.x % NT) * 16;
-    const Item it = find_item(a, blockIdx.x / NT);
-    if (it.e < 0) return;
-    if (it.slot < 0 || it.slot >= a.num_slots) {
-        if (tid == 0 && n0 == 0) raise_status(a.status, MOE_DEV_BAD_SLOT);
-        if (MODE == 1) zero_y_tile(a, n0, it.r0, it.r1);
-        return;
-    }
-
-    // Row data of the first column tile, ahead of the weight loads.
+    // Row index of the first column tile, loaded ahead of the weights; it is
+    // only used (the x row address) after the weight loads are issued, so the
+    // wait for it does not hold them back.
     int r = it.r0 + row;
     bool colok = r < it.r1;
-    int pr = colok && (MODE == 0 || fused) ? a.perm[r] : 0;
-    const uint16_t* brow = MODE == 0 ? a.x + static_cast<size_t>(pr / a.k) * a.d
-                                     : a.act + static_cast<size_t>(colok ? r : it.r0) * a.f;
+    int pr = colok && (MODE == 0 || fused) ? perm[r] : 0;
 
     WTile wt[NM];
 #pragma unroll
@@ -118,13 +120,17 @@ __global__ __launch_bounds__(KW * 64) void ffn_skinny_kernel(FfnArgs a) {
         const int mat = MODE == 0 ? m : 2;
         wt[m] = wtile<FMT>(a.codes[mat], a.scales[mat], static_cast<size_t>(it.slot) * NT + n0 / 16, S, lane);
     }
+    // Unconditional (a wave with no K steps loads step 0 and ignores it): a
+    // load under a branch makes the wait for `pr` below cover the weights too.
     WChunk<FMT> w[NM];
-    if (nk > 0) {
 #pragma unroll
-        for (int m = 0; m < NM; ++m) load_w<FMT>(w[m], wt[m], s_beg, s_end);
-    }
+    for (int m = 0; m < NM; ++m) load_w<FMT>(w[m], wt[m], s_beg, s_end);
+    // keep the use of `pr` (and its wait) below the weight loads
+    __builtin_amdgcn_sched_barrier(0);
+    const uint16_t* brow = MODE == 0 ? a.x + static_cast<size_t>(pr / a.k) * a.d
+                                     : a.act + static_cast<size_t>(colok ? r : it.r0) * a.f;
     u32x4 bv[kCap][4];
-    if (nk > 0) load_b<FMT>(bv, brow, colok, s_beg, G, g);
+    load_b<FMT>(bv, brow, colok, s_beg, G, g);
     float wr = fused && colok ? a.topk_w[pr] : 0.f;   // queued behind the weights
 
     const int ncol = ceil_div(it.r1 - it.r0, 16);
@@ -133,7 +139,7 @@ __global__ __launch_bounds__(KW * 64) void ffn_skinny_kernel(FfnArgs a) {
         if (ct > 0) {
             r = c0 + row;
             colok = r < it.r1;
-            pr = colok && (MODE == 0 || fused) ? a.perm[r] : 0;
+            pr = colok && (MODE == 0 || fused) ? perm[r] : 0;
             brow = MODE == 0 ? a.x + static_cast<size_t>(pr / a.k) * a.d
                              : a.act + static_cast<size_t>(colok ? r : it.r0) * a.f;
             wr = fused && colok ? a.topk_w[pr] : 0.f;
@@ -188,13 +194,106 @@ __global__ __launch_bounds__(KW * 64) void ffn_skinny_kernel(FfnArgs a) {
     }
 }
 
+// An item whose expert has no valid slot is skipped: its y rows read as zero
+// and MOE_DEV_BAD_SLOT is raised.
+template <int FMT, int MODE, int KW>
+__device__ __forceinline__ void run_item(const FfnArgs& a, const Item& it, int n0, const int32_t* perm) {
+    if (it.e < 0) return;
+    if (it.slot < 0 || it.slot >= a.num_slots) {
+        if (threadIdx.x == 0 && n0 == 0) raise_status(a.status, MOE_DEV_BAD_SLOT);
+        if (MODE == 1) zero_y_tile(a, n0, it.r0, it.r1);
+        return;
+    }
+    skinny_body<FMT, MODE, KW>(a, it, n0, perm);
+}
+
+// The last workgroup of the down launch zeroes the y rows past offsets[E].
+template <int FMT, int MODE, int KW>
+__global__ __launch_bounds__(KW * 64) void ffn_skinny_kernel(FfnArgs a) {
+    if (MODE == 1 && blockIdx.x == gridDim.x - 1) {
+        zero_y_tail(a);
+        return;
+    }
+    const int NT = (MODE == 0 ? a.f : a.d) / 16;
+    run_item<FMT, MODE, KW>(a, find_item(a, blockIdx.x / NT), (blockIdx.x % NT) * 16, a.perm);
+}
+
+// ------------------------------------------------------------ routed gate/up
+
+// Routing of a batch of at most kRoutedMaxPairs pairs, held in LDS.
+constexpr int kRoutedMaxPairs = 64;
+struct SmallRouting {
+    int32_t ids[kRoutedMaxPairs];
+    float w[kRoutedMaxPairs];
+    int32_t perm[kRoutedMaxPairs];
+    int32_t inv[kRoutedMaxPairs];
+    int32_t offsets[kMaxExperts + 1];
+};
+
+// Stable counting sort of n <= 64 pairs by expert id, by one wave: pair p
+// (lane p) goes to row (pairs with a smaller id) + (pairs with its id and a
+// smaller index); offsets[x] = pairs with an id below x.  The same
+// permutation as the dispatch kernel's for valid ids.
+__device__ __forceinline__ void wave_dispatch(SmallRouting& r, int n, int E) {
+    const int lane = threadIdx.x & 63;
+    const int e = lane < n ? r.ids[lane] : 0x7fffffff;
+    int before = 0, tie = 0, below_lane = 0;
+    for (int q = 0; q < n; ++q) {
+        const int eq = lane_value(e, q);
+        before += eq < e;
+        tie += (eq == e) & (q < lane);
+        below_lane += eq < lane;
+    }
+    if (lane < n) {
+        r.perm[before + tie] = lane;
+        r.inv[lane] = before + tie;
+    }
+    if (lane < E) r.offsets[lane] = below_lane;
+    if (lane == 0) r.offsets[E] = n;
+}
+
+// Gate/up launch of moe_layer for small batches: every workgroup routes the
+// whole batch from the logits itself (top-k by one wave per token, then the
+// one-wave counting sort: a few hundred instructions), so no routing launch
+// and no read of routing results from HBM precede its weight loads.
+// Workgroup 0 also writes ids, w, offsets, perm and inv and zeroes `out` for
+// the down launch's scatter-add.  Arithmetic as topk_kernel and the dispatch
+// kernel, so every output is identical.
+template <int FMT>
+__global__ __launch_bounds__(kGateUpWaves * 64) void ffn_gate_up_routed_kernel(FfnArgs a) {
+    __shared__ SmallRouting r;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int T = a.T, E = a.E, k = a.k, n = a.T * a.k;
+    int sl = lane;      // slot of expert `lane`, read before the routing is known
+    if (lane < E && a.slot_of_expert) sl = a.slot_of_expert[lane];
+    if (wave < T) topk_wave(a.logits + static_cast<size_t>(wave) * E, r.ids + wave * k, r.w + wave * k, E, k);
+    __syncthreads();
+    if (wave == 0) wave_dispatch(r, n, E);
+    __syncthreads();
+    if (blockIdx.x == 0) {
+        for (int i = tid; i < n; i += blockDim.x) {
+            a.ids_out[i] = r.ids[i];
+            a.w_out[i] = r.w[i];
+            a.perm_out[i] = r.perm[i];
+            a.inv_out[i] = r.inv[i];
+        }
+        for (int i = tid; i <= E; i += blockDim.x) a.offsets_out[i] = r.offsets[i];
+        if (a.fuse_combine) {
+            float4* o4 = reinterpret_cast<float4*>(a.out);
+            for (int i = tid; i < T * a.d / 4; i += blockDim.x) o4[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    }
+    int lo = 0, hi = 0;
+    if (lane < E) {
+        lo = r.offsets[lane];
+        hi = r.offsets[lane + 1];
+    }
+    const int NT = a.f / 16;
+    run_item<FMT, 0, kGateUpWaves>(a, pick_item(lo, hi, sl, blockIdx.x / NT), (blockIdx.x % NT) * 16, r.perm);
+}
+
 // ------------------------------------------------------------ launch
 
-// Waves per workgroup (K split): gate/up K = d, down K = f.  With d = 4096 /
-// f = 2048 every wave holds its whole K slice (4 steps) in registers, so all
-// of a workgroup's weight loads are in flight at once.
-constexpr int kGateUpWaves = 8;
-constexpr int kDownWaves = 4;
 
 template <int FMT>
 static hipError_t launch_two(const moe_shape& s, const FfnArgs& a, hipStream_t st) {
@@ -211,6 +310,24 @@ constexpr int kGroupedMinRows = 256;
 
 bool ffn_uses_grouped(const moe_shape& s, int fmt) {
     return s.T * s.k >= kGroupedMinRows && grouped_supported(s, fmt);
+}
+
+bool routed_ffn_supported(const moe_shape& s, int fmt) {
+    return s.T <= kGateUpWaves && s.T * s.k <= kRoutedMaxPairs && !ffn_uses_grouped(s, fmt);
+}
+
+template <int FMT>
+static hipError_t launch_two_routed(const moe_shape& s, const FfnArgs& a, hipStream_t st) {
+    const int umax = s.E < s.T * s.k ? s.E : s.T * s.k;
+    ffn_gate_up_routed_kernel<FMT><<<umax * (s.f / 16), kGateUpWaves * 64, 0, st>>>(a);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    ffn_skinny_kernel<FMT, 1, kDownWaves><<<umax * (s.d / 16) + 1, kDownWaves * 64, 0, st>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_ffn_routed(const moe_shape& s, int fmt, const FfnArgs& a, hipStream_t st) {
+    return fmt == MOE_FMT_MXFP4 ? launch_two_routed<MOE_FMT_MXFP4>(s, a, st) : launch_two_routed<MOE_FMT_Q2G32>(s, a, st);
 }
 
 hipError_t launch_ffn(const moe_shape& s, int fmt, const FfnArgs& a, hipStream_t st) {

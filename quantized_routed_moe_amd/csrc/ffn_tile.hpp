@@ -59,13 +59,13 @@ __device__ __forceinline__ WTile wtile(const uint8_t* codes, const uint8_t* scal
 }
 
 // Loads steps [s0, s0 + kCap) of the tile; steps at or past s1 reload step
-// s1 - 1 (s1 > s0), so every load is issued unconditionally and the values are
-// simply not used.
+// s1 - 1 (step 0 when the range is empty), so every load is issued
+// unconditionally and the surplus values are simply not used.
 template <int FMT>
 __device__ __forceinline__ void load_w(WChunk<FMT>& w, const WTile& t, int s0, int s1) {
 #pragma unroll
     for (int u = 0; u < kCap; ++u) {
-        const size_t s = static_cast<size_t>(min(s0 + u, s1 - 1));
+        const size_t s = static_cast<size_t>(max(min(s0 + u, s1 - 1), 0));
         if constexpr (FMT == MOE_FMT_MXFP4) {
             w.c[u] = *reinterpret_cast<const u32x4*>(t.codes + s * kWave * 16);
             w.s[u] = t.scales[s * kWave];

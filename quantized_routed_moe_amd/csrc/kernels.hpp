@@ -26,6 +26,15 @@ struct FfnArgs {
     const float* topk_w;          // [T*k]
     float* out;                   // [T][d]
     int fuse_combine;
+    // moe_layer with T <= 8 and T*k <= 64 only: the gate/up launch routes the
+    // batch itself from the logits [T][E] (every workgroup, in LDS); its
+    // workgroup 0 writes the routing outputs (same buffers as offsets/perm).
+    const float* logits;
+    int32_t* ids_out;
+    float* w_out;
+    int32_t* offsets_out;
+    int32_t* perm_out;
+    int32_t* inv_out;
 };
 
 hipError_t launch_route(const moe_shape& s, const uint16_t* x, const float* wr, const float* bias,
@@ -35,10 +44,13 @@ hipError_t launch_dispatch(const moe_shape& s, const int32_t* ids, int32_t* offs
 hipError_t launch_ffn(const moe_shape& s, int fmt, const FfnArgs& a, hipStream_t st);
 bool grouped_supported(const moe_shape& s, int fmt);
 bool ffn_uses_grouped(const moe_shape& s, int fmt);
-bool small_fused_supported(const moe_shape& s);
-hipError_t launch_route_small_fused(const moe_shape& s, const uint16_t* x, const float* wr, const float* bias,
-                                   float* logits, int32_t* ids, float* w, int32_t* offsets, int32_t* perm,
-                                   int32_t* inv, float* out, uint32_t* header, hipStream_t st);
+// Router logits only (no top-k), T <= 32.
+hipError_t launch_router_logits(const moe_shape& s, const uint16_t* x, const float* wr, const float* bias,
+                                float* logits, hipStream_t st);
+// moe_layer for small batches: the skinny FFN whose gate/up launch routes the
+// batch from a.logits (see FfnArgs).
+bool routed_ffn_supported(const moe_shape& s, int fmt);
+hipError_t launch_ffn_routed(const moe_shape& s, int fmt, const FfnArgs& a, hipStream_t st);
 hipError_t launch_ffn_grouped(const moe_shape& s, const FfnArgs& a, hipStream_t st);
 hipError_t launch_combine(const moe_shape& s, const float* y, const int32_t* inv, const float* w,
                           float* out, hipStream_t st);

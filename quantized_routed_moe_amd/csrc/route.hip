@@ -12,8 +12,8 @@
 //                       workgroup, eight waves splitting K.
 //   topk_kernel         one wave64 per token, lane = expert.
 #include "common.hpp"
-#include "dispatch_dev.hpp"
 #include "kernels.hpp"
+#include "topk_dev.hpp"
 
 namespace qrmoe {
 
@@ -23,7 +23,8 @@ constexpr int kRowsThreads = 512;
 // logits[t][e] for t in [t0, t0 + nt) of one expert, by one workgroup of
 // kRowsThreads threads.  Thread i handles elements 8*i .. 8*i+7 of each
 // 8*512-element chunk of d (one chunk at d = 4096: one round of loads); the
-// partial sums are reduced by a fixed butterfly in each wave, then across
+// partial sums are reduced in a fixed order within each wave (DPP shifts and
+// broadcasts, wave_sum_f32), then across
 // the waves in wave order.
 __device__ __forceinline__ void router_rows_block(const uint16_t* __restrict__ x, const float* __restrict__ wr,
                                                   const float* __restrict__ bias, float* __restrict__ logits,
@@ -58,10 +59,10 @@ __device__ __forceinline__ void router_rows_block(const uint16_t* __restrict__ x
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
     for (int j = 0; j < kRowsMaxT; ++j) {
-        float s = acc[j];
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
-        if (lane == 0) part[wave][j] = s;
+        if (j < nt) {
+            const float s = wave_sum_f32(acc[j]);
+            if (lane == 0) part[wave][j] = s;
+        }
     }
     __syncthreads();
     if (threadIdx.x < nt) {
@@ -140,48 +141,6 @@ __global__ __launch_bounds__(kRouterWaves * 64) void router_mfma_kernel(
     }
 }
 
-// Sortable key of a finite float: larger float -> larger unsigned key; -0 and
-// +0 share the key of +0.
-__device__ __forceinline__ uint32_t float_key(float v) {
-    uint32_t u = __float_as_uint(v);
-    if ((u & 0x7fffffffu) == 0u) u = 0u;
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// Top-k of one token by one wave; lane e holds expert e's logit.  k rounds of
-// a 64-bit wave max over (key(logit) << 32 | 63 - e) pick experts in (logit
-// desc, id asc) order.  The softmax over the selected logits is taken against
-// the first (largest) one and summed in selection order.
-__device__ __forceinline__ void topk_wave(const float* __restrict__ lrow, int32_t* __restrict__ ids,
-                                          float* __restrict__ w, int E, int k) {
-    const int lane = threadIdx.x & 63;
-    const float l = lane < E ? lrow[lane] : 0.f;
-    uint64_t key = lane < E ? ((static_cast<uint64_t>(float_key(l)) << 32) | static_cast<uint32_t>(63 - lane)) : 0ull;
-    int my_sel = -1;       // lane j < k: expert chosen in round j
-    float my_l = 0.f;      // its logit
-    float lmax = 0.f;
-    for (int j = 0; j < k; ++j) {
-        uint64_t m = key;
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            const uint64_t other = __shfl_xor(m, o);
-            m = other > m ? other : m;
-        }
-        const int e = 63 - static_cast<int>(m & 63u);
-        const float le = __shfl(l, e);
-        if (j == 0) lmax = le;
-        if (lane == j) { my_sel = e; my_l = le; }
-        if (lane == e) key = 0ull;
-    }
-    const float ex = lane < k ? expf(my_l - lmax) : 0.f;
-    float sum = 0.f;       // selection order: lane 0, 1, ..., k-1
-    for (int j = 0; j < k; ++j) sum += __shfl(ex, j);
-    if (lane < k) {
-        ids[lane] = my_sel;
-        w[lane] = ex / sum;
-    }
-}
-
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits,
                                                     int32_t* __restrict__ ids,
                                                     float* __restrict__ w, int T, int E, int k) {
@@ -191,52 +150,10 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
               w + static_cast<size_t>(t) * k, E, k);
 }
 
-// Small-T fused routing for moe_layer: one workgroup per expert computes its
-// logits (or, with given logits, a single workgroup); the last workgroup to
-// finish -- found with an atomic counter in the workspace header, after a
-// release fence by every workgroup and an acquire fence by the last -- runs
-// the top-k of every token, the dispatch, and zeroes `out` for the
-// scatter-add combine.  The counter is reset by that last workgroup, so the
-// next call finds it at zero.  Arithmetic is that of router_rows_block,
-// topk_wave and dispatch_block, so results equal the separate kernels'.
-__global__ __launch_bounds__(kRowsThreads) void route_small_fused_kernel(
-    const uint16_t* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ bias,
-    float* __restrict__ logits, int32_t* __restrict__ ids, float* __restrict__ w, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ perm, int32_t* __restrict__ inv, float* __restrict__ out, uint32_t* __restrict__ header,
-    int T, int d, int E, int k) {
-    __shared__ int last;
-    __shared__ int32_t sids[kRowsMaxT * kMaxExperts];   // T*k ids of the last workgroup
-    if (wr) router_rows_block(x, wr, bias, logits, blockIdx.x, 0, T, d, E);
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t* counter = header + kLastBlockCounter;
-        const uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        last = prev == gridDim.x - 1;
-        if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    if (!last) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // see every workgroup's logits
-    // top-k into LDS (the dispatch reads it there), weights to global
-    const int wave = threadIdx.x >> 6;
-    for (int t = wave; t < T; t += kRowsThreads / kWave)
-        topk_wave(logits + static_cast<size_t>(t) * E, sids + t * k, w + static_cast<size_t>(t) * k, E, k);
-    if (out) {
-        float4* o4 = reinterpret_cast<float4*>(out);
-        for (int i = threadIdx.x; i < T * d / 4; i += kRowsThreads) o4[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    __syncthreads();
-    for (int i = threadIdx.x; i < T * k; i += kRowsThreads) ids[i] = sids[i];
-    dispatch_block<kRowsThreads>(sids, offsets, perm, inv, header, T * k, E);
-}
-
-bool small_fused_supported(const moe_shape& s) { return s.T <= kRowsMaxT; }
-
-hipError_t launch_route_small_fused(const moe_shape& s, const uint16_t* x, const float* wr, const float* bias,
-                                   float* logits, int32_t* ids, float* w, int32_t* offsets, int32_t* perm,
-                                   int32_t* inv, float* out, uint32_t* header, hipStream_t st) {
-    route_small_fused_kernel<<<wr ? s.E : 1, kRowsThreads, 0, st>>>(x, wr, bias, logits, ids, w, offsets, perm, inv,
-                                                                   out, header, s.T, s.d, s.E, s.k);
+hipError_t launch_router_logits(const moe_shape& s, const uint16_t* x, const float* wr, const float* bias,
+                                float* logits, hipStream_t st) {
+    dim3 grid(s.E, ceil_div(s.T, kRowsMaxT));
+    router_rows_kernel<<<grid, kRowsThreads, 0, st>>>(x, wr, bias, logits, s.T, s.d, s.E);
     return hipGetLastError();
 }
 
@@ -244,8 +161,8 @@ hipError_t launch_route(const moe_shape& s, const uint16_t* x, const float* wr, 
                         float* logits, int32_t* ids, float* w, hipStream_t st) {
     if (wr) {
         if (s.T <= 4 * kRowsMaxT) {
-            dim3 grid(s.E, ceil_div(s.T, kRowsMaxT));
-            router_rows_kernel<<<grid, kRowsThreads, 0, st>>>(x, wr, bias, logits, s.T, s.d, s.E);
+            const hipError_t err = launch_router_logits(s, x, wr, bias, logits, st);
+            if (err != hipSuccess) return err;
         } else {
             router_mfma_kernel<<<dim3(ceil_div(s.T, 16), ceil_div(s.E, 16)), kRouterWaves * 64, 0, st>>>(
                 x, wr, bias, logits, s.T, s.d, s.E);
