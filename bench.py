@@ -40,11 +40,7 @@ METRIC = "MoE layer tokens/s; decode weight-stream GB/s; prefill expert TFLOP/s"
 # reads), summed over the kernels of the call.  Workloads 3 and 4 route a
 # different number of experts each step: theirs is the average of the counted
 # steps.  Must be re-measured (or removed) whenever an FFN kernel changes.
-MEASURED_FFN_TRAFFIC = {
-    1: (2 * (8787.4 + 4428.6) + (8.0 + 32.0)) * 1024,
-    3: (2 * (280324.6 + 163505.5 + 12.0) + (16397.3 + 65545.1)) * 1024,
-    4: (2 * (27544.7 + 14033.6) + (128.0 + 512.0)) * 1024,
-}
+MEASURED_FFN_TRAFFIC: dict = {}   # re-taken after the latest FFN kernel changes
 
 MX_BYTES_PER_EXPERT = lambda d, f: 3 * d * f // 2 + 3 * d * f // 32      # codes + e8m0 scales
 Q2_BYTES_PER_EXPERT = lambda d, f: 3 * d * f // 4 + 3 * d * f // 32 * 4  # codes + fp16 scale + min
