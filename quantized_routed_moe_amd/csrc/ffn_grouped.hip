@@ -24,7 +24,7 @@
 // dequantises its own A fragment (gfx950 scaled fp4 -> bf16 conversion)
 // right after reading it; the 64 lanes of that read cover two pieces arrays
 // of 512 contiguous bytes (no bank conflicts).  The token tile is bf16 with
-// its 16-byte chunks XOR-swizzled by (row mod 8).  K is permuted inside a
+// its 16-byte chunks XOR-swizzled by (row / 2 mod 8) (see xswz).  K is permuted inside a
 // step so that in sub-step kk lane half h (= lane/32) takes elements
 // 32h + 8kk .. +8: a lane then reads one whole 32-element group (one piece:
 // 16 code bytes, one scale) of the weight row and 64 contiguous bytes of the
@@ -63,7 +63,14 @@ struct GSlot {
     u32x4 x[2];     // 32 bytes of this thread's token row quarter
 };
 
-__device__ __forceinline__ int xswz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+// Byte offset of 16-byte chunk `chunk` (0..7) of token row `row` (128 B) in
+// the token tile.  gfx950's LDS serves 256 B per cycle (64 four-byte banks),
+// i.e. one ds_read_b128 phase is 16 lanes; XOR-ing the chunk with
+// (row / 2) % 8 puts any 16 consecutive rows at the same logical chunk into
+// 16 distinct bank groups (row parity picks the half of the 256 B, the
+// swizzled chunk the 16 B within it).  (The XOR with row % 8, right for
+// 128 B per cycle, left a 2-way conflict on every read: rows r and r+8.)
+__device__ __forceinline__ int xswz(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
 
 template <int MODE>
 __global__ __launch_bounds__(kGThreads) void ffn_grouped_kernel(FfnArgs a) {
@@ -159,7 +166,8 @@ __global__ __launch_bounds__(kGThreads) void ffn_grouped_kernel(FfnArgs a) {
         for (int t = 0; t < 4; ++t)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[m][t][i] = 0.f;
-    const int ntt = ceil_div(nvalid, 32);
+    // uniform in the workgroup: scalar branches on the column tiles below
+    const int ntt = __builtin_amdgcn_readfirstlane(ceil_div(nvalid, 32));
     const int rt0 = MODE == 0 ? 32 * wave : 64 * wave;
     const int rt1 = MODE == 0 ? kGN / 2 + 32 * wave : 64 * wave + 32;
     const int r32 = lane & 31, h = lane >> 5;

@@ -90,8 +90,12 @@ __device__ __forceinline__ void zero_y_tail(const FfnArgs& a) {
 // token rows the expert does not own.)
 //
 // `it` is the item's expert, rows and slot, `n0` its first weight row; `perm`
-// is the sorted-row -> pair map (global, or the workgroup's own LDS copy).
-template <int FMT, int MODE, int KW>
+// is the sorted-row -> pair map (global, or with PERM_LDS the workgroup's own
+// LDS copy).  When the token rows' addresses need no global load (the down
+// projection reads act[r]; PERM_LDS) the token operand is loaded first: it
+// is small and cached, and with it in place the multiplies of the first
+// steps start as soon as those steps' weights arrive.
+template <int FMT, int MODE, int KW, bool PERM_LDS>
 __device__ __forceinline__ void skinny_body(const FfnArgs& a, const Item& it, int n0, const int32_t* perm) {
     constexpr int NM = MODE == 0 ? 2 : 1;
     __shared__ __align__(16) f32x4 red[KW][NM][kWave];
@@ -107,12 +111,19 @@ __device__ __forceinline__ void skinny_body(const FfnArgs& a, const Item& it, in
     const int nk = ceil_div(s_end - s_beg, kCap);
     const bool fused = MODE == 1 && a.fuse_combine;
 
-    // Row index of the first column tile, loaded ahead of the weights; it is
-    // only used (the x row address) after the weight loads are issued, so the
-    // wait for it does not hold them back.
+    // Row index of the first column tile, loaded ahead of the weights.
     int r = it.r0 + row;
     bool colok = r < it.r1;
     int pr = colok && (MODE == 0 || fused) ? perm[r] : 0;
+    constexpr bool b_first = MODE == 1 || PERM_LDS;
+    const uint16_t* brow = nullptr;
+    u32x4 bv[kCap][4];
+    if constexpr (b_first) {
+        brow = MODE == 0 ? a.x + static_cast<size_t>(pr / a.k) * a.d
+                         : a.act + static_cast<size_t>(colok ? r : it.r0) * a.f;
+        load_b<FMT>(bv, brow, colok, s_beg, G, g);
+        __builtin_amdgcn_sched_barrier(0);
+    }
 
     WTile wt[NM];
 #pragma unroll
@@ -125,12 +136,12 @@ __device__ __forceinline__ void skinny_body(const FfnArgs& a, const Item& it, in
     WChunk<FMT> w[NM];
 #pragma unroll
     for (int m = 0; m < NM; ++m) load_w<FMT>(w[m], wt[m], s_beg, s_end);
-    // keep the use of `pr` (and its wait) below the weight loads
-    __builtin_amdgcn_sched_barrier(0);
-    const uint16_t* brow = MODE == 0 ? a.x + static_cast<size_t>(pr / a.k) * a.d
-                                     : a.act + static_cast<size_t>(colok ? r : it.r0) * a.f;
-    u32x4 bv[kCap][4];
-    load_b<FMT>(bv, brow, colok, s_beg, G, g);
+    if constexpr (!b_first) {
+        // keep the use of `pr` (a global load: its wait) below the weight loads
+        __builtin_amdgcn_sched_barrier(0);
+        brow = a.x + static_cast<size_t>(pr / a.k) * a.d;
+        load_b<FMT>(bv, brow, colok, s_beg, G, g);
+    }
     float wr = fused && colok ? a.topk_w[pr] : 0.f;   // queued behind the weights
 
     const int ncol = ceil_div(it.r1 - it.r0, 16);
@@ -196,7 +207,7 @@ __device__ __forceinline__ void skinny_body(const FfnArgs& a, const Item& it, in
 
 // An item whose expert has no valid slot is skipped: its y rows read as zero
 // and MOE_DEV_BAD_SLOT is raised.
-template <int FMT, int MODE, int KW>
+template <int FMT, int MODE, int KW, bool PERM_LDS = false>
 __device__ __forceinline__ void run_item(const FfnArgs& a, const Item& it, int n0, const int32_t* perm) {
     if (it.e < 0) return;
     if (it.slot < 0 || it.slot >= a.num_slots) {
@@ -204,7 +215,7 @@ __device__ __forceinline__ void run_item(const FfnArgs& a, const Item& it, int n
         if (MODE == 1) zero_y_tile(a, n0, it.r0, it.r1);
         return;
     }
-    skinny_body<FMT, MODE, KW>(a, it, n0, perm);
+    skinny_body<FMT, MODE, KW, PERM_LDS>(a, it, n0, perm);
 }
 
 // The last workgroup of the down launch zeroes the y rows past offsets[E].
@@ -289,7 +300,7 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void ffn_gate_up_routed_kernel(F
         hi = r.offsets[lane + 1];
     }
     const int NT = a.f / 16;
-    run_item<FMT, 0, kGateUpWaves>(a, pick_item(lo, hi, sl, blockIdx.x / NT), (blockIdx.x % NT) * 16, r.perm);
+    run_item<FMT, 0, kGateUpWaves, true>(a, pick_item(lo, hi, sl, blockIdx.x / NT), (blockIdx.x % NT) * 16, r.perm);
 }
 
 // ------------------------------------------------------------ launch
