@@ -12,31 +12,39 @@
 //    so silu(g)*u is formed in registers and act = bf16_rne(.) is stored.
 //  * MODE 1 (down): weight rows [m0, m0+512) of W_d; wave w owns rows
 //    [m0+64w, m0+64w+64); y is stored in fp32.
-// Every wave covers all 128 token rows (four 32-wide MFMA column tiles); a
-// column tile holding only padding rows (past the expert's last row) is
-// skipped, so a partial tile costs MFMA work in proportion to its rows.
+// Every wave covers all 128 token rows (four 32-wide MFMA column tiles); the
+// K loop is instantiated for the number of column tiles that hold a valid
+// row (1..4), so a partial tile costs MFMA work in proportion to its rows and
+// the inner loop has no branches.
 //
-// Operands in LDS: the weight tile stays in its raw MXFP4 form, exactly as
-// the tile layout stores it (include/moe.h, MOE_LAYOUT_TILES): a 64-element
-// K step of a 16-row tile is half of one layout block, 32 pieces of 16 code
-// bytes + 32 scale bytes, contiguous in HBM, so each thread copies whole
-// pieces and each wave load instruction reads full cache lines.  A wave
-// dequantises its own A fragment (gfx950 scaled fp4 -> bf16 conversion)
-// right after reading it; the 64 lanes of that read cover two pieces arrays
-// of 512 contiguous bytes (no bank conflicts).  The token tile is bf16 with
-// its 16-byte chunks XOR-swizzled by (row / 2 mod 8) (see xswz).  K is permuted inside a
-// step so that in sub-step kk lane half h (= lane/32) takes elements
-// 32h + 8kk .. +8: a lane then reads one whole 32-element group (one piece:
-// 16 code bytes, one scale) of the weight row and 64 contiguous bytes of the
-// token row per step.
+// Operands in LDS, four stages deep, filled by direct global -> LDS loads
+// (gfx950 global_load_lds, 16 bytes per lane: lane i of an instruction lands
+// at the instruction's LDS base + 16 i, from an address of its own choice):
+//  * weights: the raw MXFP4 pieces of the tile layout (include/moe.h): a
+//    64-element step of a 16-row tile is half of one layout block, 32 pieces
+//    of 16 code bytes, contiguous in HBM and copied as is; the 32 scale bytes
+//    with it (16 bytes per lane from lanes 0..7 of each wave: with 1-, 2- or
+//    4-byte lanes the LDS destination advances 4 bytes per lane, so a
+//    2-byte copy would not be contiguous);
+//  * tokens: bf16 rows of 128 B (64 elements) whose 16-byte chunks are stored
+//    XOR-swizzled by (row / 2) mod 8 -- each lane fetches the global chunk
+//    that belongs at its LDS position.  gfx950's LDS serves 256 B per cycle
+//    (16 lanes of a ds_read_b128), and the swizzle puts any 16 consecutive
+//    rows at one logical chunk in 16 distinct bank groups.
+// A wave dequantises its own A fragment (gfx950 scaled fp4 -> bf16
+// conversion) right after reading it.  K is permuted inside a step so that in
+// sub-step kk lane half h (= lane/32) takes elements 32h + 8kk .. +8: a lane
+// then reads one whole 32-element group (one piece: 16 code bytes, one scale)
+// of the weight row and 64 contiguous bytes of the token row per step.
 //
-// Pipeline: global loads run four K steps ahead into a 4-slot register ring;
-// after step s is multiplied, the slot of step s+1 is written to the other
-// LDS buffer.  Every load is issued unconditionally (past-the-end steps
-// reload the last step, padding token rows reload row 0 and are zeroed when
-// written to LDS) and the loop is unrolled by the ring depth, so the compiler
-// can wait for exactly the step it needs (s_waitcnt vmcnt(N)) instead of
-// draining every prefetch.
+// Pipeline: every wave issues the same five LDS-bound loads per stage, three
+// stages ahead; before computing stage s it waits (vmcnt) until only the two
+// younger stages are in flight, and one barrier per stage makes every wave's
+// copy visible and frees the buffer of stage s-1 for stage s+3.  No register
+// ring and no LDS store pass: the registers go to the accumulators and to the
+// B fragments, which are all read at the start of a stage so that their LDS
+// latency overlaps the multiplies.  Padding token rows (past the expert's
+// last row) load a valid row; their output columns are never stored.
 //
 // Schedule: work units (expert, m-tile, n-tile) are enumerated with the n-tile
 // fastest and unit = workgroup id.  Workgroup ids are dealt round-robin over
@@ -46,6 +54,8 @@
 // of hot experts are spread evenly over all XCDs (handing out contiguous
 // ranges of units per XCD instead put a whole hot expert on one XCD and was
 // measured ~1.5x slower).  Units are derived from offsets on the device.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -56,27 +66,30 @@ constexpr int kGN = 512;        // weight rows per tile
 constexpr int kGK = 64;         // K per step
 constexpr int kGWaves = 8;
 constexpr int kGThreads = kGWaves * 64;
+constexpr int kStages = 4;
+constexpr int kStageW = kGN * 32;            // 32 tiles x 32 pieces x 16 B
+constexpr int kStageS = kGN * 2;             // 32 tiles x 32 scale bytes
+constexpr int kStageX = kGM * 128;           // 128 token rows x 64 bf16
+constexpr int kStageBytes = kStageW + kStageS + kStageX;
+constexpr int kLoadsPerStage = 5;            // per wave: 2 weight, 1 scale, 2 token
+constexpr int kLoadsPerStageNoX = 3;         // a wave whose token rows no column tile reads
 
-struct GSlot {
-    u32x4 w[2];     // pieces p and 16+p of this thread's tile for the step
-    uint32_t sc;    // the scale bytes of pieces 2p and 2p+1
-    u32x4 x[2];     // 32 bytes of this thread's token row quarter
-};
+typedef __attribute__((address_space(3))) void lds_void;
 
 // Byte offset of 16-byte chunk `chunk` (0..7) of token row `row` (128 B) in
-// the token tile.  gfx950's LDS serves 256 B per cycle (64 four-byte banks),
-// i.e. one ds_read_b128 phase is 16 lanes; XOR-ing the chunk with
-// (row / 2) % 8 puts any 16 consecutive rows at the same logical chunk into
-// 16 distinct bank groups (row parity picks the half of the 256 B, the
-// swizzled chunk the 16 B within it).  (The XOR with row % 8, right for
-// 128 B per cycle, left a 2-way conflict on every read: rows r and r+8.)
+// the token tile (see the swizzle above).
 __device__ __forceinline__ int xswz(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
+
+// s_waitcnt vmcnt(N), leaving the other counters alone.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
 template <int MODE>
 __global__ __launch_bounds__(kGThreads) void ffn_grouped_kernel(FfnArgs a) {
-    __shared__ __align__(16) uint8_t wl[2][kGN * 32];   // codes [tile][piece][16 B]
-    __shared__ __align__(16) uint8_t sl[2][kGN * 2];    // e8m0 [tile][piece]
-    __shared__ __align__(16) uint8_t xl[2][kGM * 128];  // bf16 tokens [row][64], swizzled
+    __shared__ __align__(16) uint8_t lds[kStages][kStageBytes];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int N = MODE == 0 ? a.f : a.d;
@@ -100,7 +113,7 @@ __global__ __launch_bounds__(kGThreads) void ffn_grouped_kernel(FfnArgs a) {
     const int excl = incl - mt;
     const uint64_t below = __ballot(mt > 0 && excl * NT <= unit);
     const int e = 63 - __clzll(static_cast<long long>(below));
-    const int e_excl = __shfl(excl, e), e_mt = __shfl(mt, e);
+    const int e_excl = __shfl(excl, e);
     const int local = unit - e_excl * NT;
     const int mti = local / NT, nt = local % NT;
     const int r_base = a.offsets[e] + mti * kGM;
@@ -115,48 +128,58 @@ __global__ __launch_bounds__(kGThreads) void ffn_grouped_kernel(FfnArgs a) {
         return;
     }
 
-    // ---- per-thread load roles: pieces p and 16+p (p = tid%16) of 16-row
-    // tile tid/16 of the workgroup's 32; token row tid/4, quarter tid%4 (16
-    // bf16) of the step's 64 K elements.
-    const int wt = tid >> 4, wp = tid & 15;
-    const uint8_t* wcodes;
-    const uint8_t* wscales;
-    {
-        int mat = 2, tile = nt * (kGN / 16) + wt;
+    // ---- load roles of this lane (per stage: 2 weight, 1 scale, 2 token
+    // instructions per wave)
+    auto tile_base = [&](int tt, int& mat) {     // layout tile index of workgroup tile tt (0..31)
+        mat = 2;
+        int tile = nt * (kGN / 16) + tt;
         if (MODE == 0) {
-            mat = wt < kGN / 32 ? 0 : 1;
-            tile = nt * (kGN / 32) + (wt & (kGN / 32 - 1));
+            mat = tt < kGN / 32 ? 0 : 1;
+            tile = nt * (kGN / 32) + (tt & (kGN / 32 - 1));
         }
-        const size_t blk = (static_cast<size_t>(slot) * (N / 16) + tile) * (K / 128);
-        wcodes = a.codes[mat] + blk * 64 * 16 + wp * 16;
-        wscales = a.scales[mat] + blk * 64 + 2 * wp;
-    }
-    const int xj = tid >> 2, xq = tid & 3;
-    const bool xok = xj < nvalid;
-    const uint16_t* xrow;    // padding rows read row 0 (always valid) and store zeros
-    if (MODE == 0) xrow = a.x + static_cast<size_t>(xok ? a.perm[r_base + xj] / a.k : 0) * a.d;
-    else xrow = a.act + static_cast<size_t>(xok ? r_base + xj : r_base) * a.f;
-
-    // step s of 64 elements = half s%2 of layout block s/2 (pieces 32*(s%2) ..)
-    auto gload = [&](GSlot& g, int s) {
-        s = min(s, S - 1);
-        const size_t half = static_cast<size_t>(s >> 1) * 64 + 32 * (s & 1);
-        const u32x4* cp = reinterpret_cast<const u32x4*>(wcodes + half * 16);
-        g.w[0] = cp[0];
-        g.w[1] = cp[16];
-        g.sc = *reinterpret_cast<const uint16_t*>(wscales + half);
-        const u32x4* xp = reinterpret_cast<const u32x4*>(xrow + s * kGK + xq * 16);
-        g.x[0] = xp[0];
-        g.x[1] = xp[1];
+        return (static_cast<size_t>(slot) * (N / 16) + tile) * (K / 128);
     };
-    auto lstore = [&](int buf, const GSlot& g) {
-        u32x4* wd = reinterpret_cast<u32x4*>(wl[buf] + wt * 512 + wp * 16);
-        wd[0] = g.w[0];
-        wd[16] = g.w[1];
-        *reinterpret_cast<uint16_t*>(&sl[buf][wt * 32 + 2 * wp]) = static_cast<uint16_t>(g.sc);
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4*>(xl[buf] + xswz(xj, 2 * xq)) = xok ? g.x[0] : z;
-        *reinterpret_cast<u32x4*>(xl[buf] + xswz(xj, 2 * xq + 1)) = xok ? g.x[1] : z;
+    const uint8_t* wsrc[2];      // piece (lane & 31) of tile 4w + 2i + (lane >> 5), step 0
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        int mat;
+        const size_t blk = tile_base(4 * wave + 2 * i + (lane >> 5), mat);
+        wsrc[i] = a.codes[mat] + blk * 64 * 16 + (lane & 31) * 16;
+    }
+    const uint8_t* ssrc;         // lanes 0..7: scale bytes 16 (lane & 1) .. +16 of tile 4w + (lane >> 1)
+    {
+        int mat;
+        const size_t blk = tile_base(4 * wave + ((lane >> 1) & 3), mat);
+        ssrc = a.scales[mat] + blk * 64 + 16 * (lane & 1);
+    }
+    const uint16_t* xsrc[2];     // token row 16w + 8i + (lane >> 3), global chunk for LDS chunk lane & 7
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int row = 16 * wave + 8 * i + (lane >> 3);
+        const int rr = r_base + (row < nvalid ? row : 0);
+        const uint16_t* rowp = MODE == 0 ? a.x + static_cast<size_t>(a.perm[rr] / a.k) * a.d
+                                         : a.act + static_cast<size_t>(rr) * a.f;
+        xsrc[i] = rowp + (((lane & 7) ^ ((row >> 1) & 7)) << 3);
+    }
+    // Token rows at or past 32 * (live column tiles) are never read: the waves
+    // that own them (rows 16w .. 16w+15) copy no token rows at all.
+    const int ntt = __builtin_amdgcn_readfirstlane(ceil_div(nvalid, 32));
+    const bool x_live = 16 * wave < 32 * ntt;
+    auto issue = [&](int s) {    // stage s -> LDS buffer s % kStages
+        uint8_t* base = lds[s % kStages];
+        const size_t half = static_cast<size_t>(s >> 1) * 1024 + (s & 1) * 512;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            __builtin_amdgcn_global_load_lds(wsrc[i] + half, (lds_void*)(base + (4 * wave + 2 * i) * 512), 16, 0, 0);
+        if (lane < 8)
+            __builtin_amdgcn_global_load_lds(ssrc + (s >> 1) * 64 + (s & 1) * 32,
+                                             (lds_void*)(base + kStageW + 4 * wave * 32), 16, 0, 0);
+        if (x_live) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                __builtin_amdgcn_global_load_lds(xsrc[i] + s * kGK,
+                                                 (lds_void*)(base + kStageW + kStageS + (16 * wave + 8 * i) * 128), 16, 0, 0);
+        }
     };
 
     f32x16 acc[2][4];
@@ -166,58 +189,75 @@ __global__ __launch_bounds__(kGThreads) void ffn_grouped_kernel(FfnArgs a) {
         for (int t = 0; t < 4; ++t)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[m][t][i] = 0.f;
-    // uniform in the workgroup: scalar branches on the column tiles below
-    const int ntt = __builtin_amdgcn_readfirstlane(ceil_div(nvalid, 32));
     const int rt0 = MODE == 0 ? 32 * wave : 64 * wave;
     const int rt1 = MODE == 0 ? kGN / 2 + 32 * wave : 64 * wave + 32;
     const int r32 = lane & 31, h = lane >> 5;
-
     // LDS piece index of weight row rt + r32, local group h
     const int pc0 = (rt0 / 16 + (r32 >> 4)) * 32 + 16 * h + (r32 & 15);
     const int pc1 = (rt1 / 16 + (r32 >> 4)) * 32 + 16 * h + (r32 & 15);
-    auto compute = [&](int buf) {
-        const uint8_t* wb = wl[buf];
-        const u32x4 c0 = *reinterpret_cast<const u32x4*>(wb + pc0 * 16);
-        const u32x4 c1 = *reinterpret_cast<const u32x4*>(wb + pc1 * 16);
-        const float s0 = e8m0_to_f32(sl[buf][pc0]);
-        const float s1 = e8m0_to_f32(sl[buf][pc1]);
-        const uint8_t* xb = xl[buf];
+
+    auto kloop = [&](auto ntt_c) {
+        constexpr int NTT = decltype(ntt_c)::value;
+        for (int s = 0; s < S; ++s) {
+            // stage s is in LDS once at most the two younger stages are in
+            // flight (each wave counts its own loads per stage)
+            if (x_live) {
+                if (s + 2 < S) wait_vmcnt<2 * kLoadsPerStage>();
+                else if (s + 1 < S) wait_vmcnt<kLoadsPerStage>();
+                else wait_vmcnt<0>();
+            } else {
+                if (s + 2 < S) wait_vmcnt<2 * kLoadsPerStageNoX>();
+                else if (s + 1 < S) wait_vmcnt<kLoadsPerStageNoX>();
+                else wait_vmcnt<0>();
+            }
+            __builtin_amdgcn_s_barrier();
+            if (s + 3 < S) issue(s + 3);
+            const uint8_t* wb = lds[s % kStages];
+            const uint8_t* sb = wb + kStageW;
+            const uint8_t* xb = sb + kStageS;
+            // weight operand first, then the token fragments one sub-step
+            // ahead of the multiplies that use them (the scheduling barriers
+            // keep the compiler from sinking each read next to its use, which
+            // exposed the full LDS latency on every MFMA pair)
+            const u32x4 c0 = *reinterpret_cast<const u32x4*>(wb + pc0 * 16);
+            const u32x4 c1 = *reinterpret_cast<const u32x4*>(wb + pc1 * 16);
+            const uint32_t sc0 = sb[pc0], sc1 = sb[pc1];
+            u32x4 bcur[NTT], bnext[NTT];
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const bf16x8 a0 = mxfp4x8_to_bf16(c0[kk], s0);
-            const bf16x8 a1 = mxfp4x8_to_bf16(c1[kk], s1);
+            for (int t = 0; t < NTT; ++t) bcur[t] = *reinterpret_cast<const u32x4*>(xb + xswz(32 * t + r32, 4 * h));
+            const float s0 = e8m0_to_f32(sc0);
+            const float s1 = e8m0_to_f32(sc1);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                if (t < ntt) {
-                    const bf16x8 b = *reinterpret_cast<const bf16x8*>(xb + xswz(32 * t + r32, 4 * h + kk));
+            for (int kk = 0; kk < 4; ++kk) {
+                if (kk < 3) {
+#pragma unroll
+                    for (int t = 0; t < NTT; ++t)
+                        bnext[t] = *reinterpret_cast<const u32x4*>(xb + xswz(32 * t + r32, 4 * h + kk + 1));
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                const bf16x8 a0 = mxfp4x8_to_bf16(c0[kk], s0);
+                const bf16x8 a1 = mxfp4x8_to_bf16(c1[kk], s1);
+#pragma unroll
+                for (int t = 0; t < NTT; ++t) {
+                    const bf16x8 b = bf16x8_from_u32x4(bcur[t]);
                     acc[0][t] = mfma32x32x16(a0, b, acc[0][t]);
                     acc[1][t] = mfma32x32x16(a1, b, acc[1][t]);
                 }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int t = 0; t < NTT; ++t) bcur[t] = bnext[t];
             }
         }
     };
 
-    // Iteration s: multiply LDS buffer s%2, write ring slot (s+1)%4 (step s+1,
-    // loaded four iterations earlier) into LDS buffer (s+1)%2, then refill
-    // ring slot s%4 with step s+4.  S is a multiple of 4.
-    GSlot g0, g1, g2, g3;
-    gload(g0, 0);
-    gload(g1, 1);
-    gload(g2, 2);
-    gload(g3, 3);
-    lstore(0, g0);
-    __syncthreads();
-    auto iter = [&](int s, GSlot& mine, GSlot& next, int buf) {
-        compute(buf);
-        lstore(buf ^ 1, next);
-        gload(mine, s + 4);
-        __syncthreads();
-    };
-    for (int s = 0; s < S; s += 4) {
-        iter(s, g0, g1, 0);
-        iter(s + 1, g1, g2, 1);
-        iter(s + 2, g2, g3, 0);
-        iter(s + 3, g3, g0, 1);
+    issue(0);
+    issue(1);
+    issue(2);
+    switch (ntt) {
+        case 1: kloop(std::integral_constant<int, 1>{}); break;
+        case 2: kloop(std::integral_constant<int, 2>{}); break;
+        case 3: kloop(std::integral_constant<int, 3>{}); break;
+        default: kloop(std::integral_constant<int, 4>{}); break;
     }
 
     // ---- epilogue.  Lane l holds, for element i, weight row
