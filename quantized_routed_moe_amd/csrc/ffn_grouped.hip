@@ -97,25 +97,46 @@ __global__ __launch_bounds__(kGThreads) void ffn_grouped_kernel(FfnArgs a) {
     const int NT = MODE == 0 ? a.f / (kGN / 2) : a.d / kGN;
     const int S = K / kGK;
 
-    // ---- schedule: expert / m-tile / n-tile of this workgroup
+    // ---- schedule: expert / m-tile / n-tile of this workgroup.  Units run
+    // longest first: every full 128-row m-tile (expert-major, n-tile
+    // fastest), then the partial m-tiles (at most one per expert) by
+    // decreasing row count (ties: lower expert id first), so the shortest
+    // units fill the end of the launch.
     int cnt = 0;
     if (lane < a.E) cnt = a.offsets[lane + 1] - a.offsets[lane];
-    const int mt = ceil_div(cnt, kGM);
-    int incl = mt;
+    const int full = cnt / kGM;          // full m-tiles of expert `lane`
+    const int rem = cnt % kGM;           // rows of its partial m-tile (0: none)
+    int incl = full;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
         const int v = __shfl_up(incl, o);
         if (lane >= o) incl += v;
     }
-    const int total_units = __shfl(incl, 63) * NT;
+    const int n_full = lane_value(incl, 63);
+    const uint64_t has_part = __ballot(rem > 0);
+    const int total_units = (n_full + __popcll(has_part)) * NT;
     const int unit = blockIdx.x;
     if (unit >= total_units) return;
-    const int excl = incl - mt;
-    const uint64_t below = __ballot(mt > 0 && excl * NT <= unit);
-    const int e = 63 - __clzll(static_cast<long long>(below));
-    const int e_excl = __shfl(excl, e);
-    const int local = unit - e_excl * NT;
-    const int mti = local / NT, nt = local % NT;
+    int e, mti, nt;
+    if (unit < n_full * NT) {
+        const int q = unit / NT;
+        nt = unit % NT;
+        const int excl = incl - full;
+        const uint64_t below = __ballot(full > 0 && excl <= q);
+        e = 63 - __clzll(static_cast<long long>(below));
+        mti = q - lane_value(excl, e);
+    } else {
+        const int q = (unit - n_full * NT) / NT;
+        nt = (unit - n_full * NT) % NT;
+        int rank = 0;                    // partial tiles longer than this lane's, or as long with a lower id
+        for (int j = 0; j < 64; ++j) {
+            const int rj = lane_value(rem, j);
+            rank += (rj > rem) || (rj == rem && j < lane);
+        }
+        const uint64_t hit = __ballot(rem > 0 && rank == q);
+        e = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+        mti = lane_value(full, e);
+    }
     const int r_base = a.offsets[e] + mti * kGM;
     const int nvalid = min(kGM, a.offsets[e + 1] - r_base);
     const int slot = a.slot_of_expert ? a.slot_of_expert[e] : e;
