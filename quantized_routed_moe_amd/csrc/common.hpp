@@ -175,4 +175,15 @@ __device__ __forceinline__ int nth_active_expert(const int32_t* __restrict__ off
 
 __host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// s_waitcnt vmcnt(N), leaving the other counters alone (gfx950 encoding:
+// vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// LDS pointee type of the global -> LDS load builtin.
+typedef __attribute__((address_space(3))) void lds_void;
+
 }  // namespace qrmoe

@@ -74,18 +74,9 @@ constexpr int kStageBytes = kStageW + kStageS + kStageX;
 constexpr int kLoadsPerStage = 5;            // per wave: 2 weight, 1 scale, 2 token
 constexpr int kLoadsPerStageNoX = 3;         // a wave whose token rows no column tile reads
 
-typedef __attribute__((address_space(3))) void lds_void;
-
 // Byte offset of 16-byte chunk `chunk` (0..7) of token row `row` (128 B) in
 // the token tile (see the swizzle above).
 __device__ __forceinline__ int xswz(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
-
-// s_waitcnt vmcnt(N), leaving the other counters alone.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 template <int MODE>
 __global__ __launch_bounds__(kGThreads) void ffn_grouped_kernel(FfnArgs a) {

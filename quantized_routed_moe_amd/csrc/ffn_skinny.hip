@@ -80,50 +80,45 @@ __device__ __forceinline__ void zero_y_tail(const FfnArgs& a) {
 // split the K steps; their partial tiles are summed in LDS in wave order.
 //  MODE 0: gate and up + SwiGLU -> act (bf16).  MODE 1: down -> y (fp32), or
 //          with fuse_combine the weighted scatter-add into out instead.
-// Column c of a 16-row column tile is sorted row c0 + c: MODE 0 reads
-// x[perm[r]/k], MODE 1 reads act[r]; padding columns read a valid row and
-// are zeroed.  Loads are ordered so that nothing waits on the weight stream
-// before the multiply: vmcnt retires loads in issue order, so the row index
-// an address needs (perm) is loaded before the weights.  (Taking the T <= 16
-// tokens themselves as the columns, which drops that index load, measured no
-// faster at T = 1 and slower at T = 5 and 16, where most columns then load
-// token rows the expert does not own.)
+// The expert's sorted rows are taken RB at a time (a column pass): column c
+// of a pass is sorted row c0 + c; MODE 0 stages x[perm[r]/k], MODE 1 act[r]
+// (ffn_tile.hpp).  The weights of a wave's K slice stay in registers across
+// the passes when the slice fits one chunk.
+//
+// Load order: vmcnt retires loads in issue order.  When the token rows'
+// addresses need no global load (the down projection reads act[r]; PERM_LDS)
+// the token rows are staged first (small and cached), so the multiplies of
+// the first steps start as soon as those steps' weights arrive.  Otherwise
+// the weights go first and the row indices (perm) are read behind them.
+// (Taking the T <= 16 tokens themselves as the columns, which drops that
+// index load, measured no faster at T = 1 and slower at T = 5 and 16, where
+// most columns then load token rows the expert does not own.)
 //
 // `it` is the item's expert, rows and slot, `n0` its first weight row; `perm`
 // is the sorted-row -> pair map (global, or with PERM_LDS the workgroup's own
-// LDS copy).  When the token rows' addresses need no global load (the down
-// projection reads act[r]; PERM_LDS) the token operand is loaded first: it
-// is small and cached, and with it in place the multiplies of the first
-// steps start as soon as those steps' weights arrive.
-template <int FMT, int MODE, int KW, bool PERM_LDS>
+// LDS copy).
+template <int FMT, int MODE, int KW, int RB, bool PERM_LDS>
 __device__ __forceinline__ void skinny_body(const FfnArgs& a, const Item& it, int n0, const int32_t* perm) {
     constexpr int NM = MODE == 0 ? 2 : 1;
-    __shared__ __align__(16) f32x4 red[KW][NM][kWave];
+    // Per wave: RB staged token rows; after the pass's multiplies the same
+    // bytes hold the wave's partial tiles for the reduction.
+    constexpr int kRegion = RB * kBRowBytes > NM * kWave * 16 ? RB * kBRowBytes : NM * kWave * 16;
+    __shared__ __align__(16) uint8_t region[KW][kRegion];
     __shared__ __align__(16) Q2Lds q2[FMT == MOE_FMT_Q2G32 ? KW * NM : 1];
-    __shared__ int row_tok[16];     // fused combine: token of the row
-    __shared__ float row_w[16];     // fused combine: routing weight of the row
+    __shared__ int row_tok[RB];     // fused combine: token of the row
+    __shared__ float row_w[RB];     // fused combine: routing weight of the row
     const int N = MODE == 0 ? a.f : a.d;
     const int K = MODE == 0 ? a.d : a.f;
-    const int G = K / kGroup, S = ceil_div(K, kStepK), NT = N / 16;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int row = lane & 15, g = lane >> 4;
+    const int S = ceil_div(K, kStepK), NT = N / 16;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: K-slice branches stay scalar
+    const int col = lane & 15;
     const int s_beg = (S * wave) / KW, s_end = (S * (wave + 1)) / KW;
     const int nk = ceil_div(s_end - s_beg, kCap);
     const bool fused = MODE == 1 && a.fuse_combine;
-
-    // Row index of the first column tile, loaded ahead of the weights.
-    int r = it.r0 + row;
-    bool colok = r < it.r1;
-    int pr = colok && (MODE == 0 || fused) ? perm[r] : 0;
+    uint8_t* mine = region[wave];
+    const uint8_t* brow = mine + (col < RB ? col : RB - 1) * kBRowBytes;
     constexpr bool b_first = MODE == 1 || PERM_LDS;
-    const uint16_t* brow = nullptr;
-    u32x4 bv[kCap][4];
-    if constexpr (b_first) {
-        brow = MODE == 0 ? a.x + static_cast<size_t>(pr / a.k) * a.d
-                         : a.act + static_cast<size_t>(colok ? r : it.r0) * a.f;
-        load_b<FMT>(bv, brow, colok, s_beg, G, g);
-        __builtin_amdgcn_sched_barrier(0);
-    }
 
     WTile wt[NM];
 #pragma unroll
@@ -131,61 +126,97 @@ __device__ __forceinline__ void skinny_body(const FfnArgs& a, const Item& it, in
         const int mat = MODE == 0 ? m : 2;
         wt[m] = wtile<FMT>(a.codes[mat], a.scales[mat], static_cast<size_t>(it.slot) * NT + n0 / 16, S, lane);
     }
-    // Unconditional (a wave with no K steps loads step 0 and ignores it): a
-    // load under a branch makes the wait for `pr` below cover the weights too.
     WChunk<FMT> w[NM];
-#pragma unroll
-    for (int m = 0; m < NM; ++m) load_w<FMT>(w[m], wt[m], s_beg, s_end);
-    if constexpr (!b_first) {
-        // keep the use of `pr` (a global load: its wait) below the weight loads
-        __builtin_amdgcn_sched_barrier(0);
-        brow = a.x + static_cast<size_t>(pr / a.k) * a.d;
-        load_b<FMT>(bv, brow, colok, s_beg, G, g);
-    }
-    float wr = fused && colok ? a.topk_w[pr] : 0.f;   // queued behind the weights
+    f32x4 acc[NM];
+    int pr = 0;             // MODE 0: pair of this lane's column in the current pass
+    int tokc[RB];           // fused combine: token and routing weight of each column
+    float wc[RB];
 
-    const int ncol = ceil_div(it.r1 - it.r0, 16);
-    for (int ct = 0; ct < ncol; ++ct) {
-        const int c0 = it.r0 + 16 * ct;
-        if (ct > 0) {
-            r = c0 + row;
-            colok = r < it.r1;
-            pr = colok && (MODE == 0 || fused) ? perm[r] : 0;
-            brow = MODE == 0 ? a.x + static_cast<size_t>(pr / a.k) * a.d
-                             : a.act + static_cast<size_t>(colok ? r : it.r0) * a.f;
-            wr = fused && colok ? a.topk_w[pr] : 0.f;
-        }
-        f32x4 acc[NM];
+    // MODE 0: pair of column `col` of the pass at c0 (a valid row for every
+    // lane), issued before the weights so that waiting for it never waits
+    // for them.
+    auto load_pr = [&](int c0) {
+        if constexpr (MODE == 0) pr = perm[min(c0 + col, it.r1 - 1)];
+    };
+    // Fused combine: token and weight of each column, by scalar loads
+    // (wave-uniform addresses), issued once the pass's vector loads are in
+    // flight; the scalar counter is independent of the vector one.
+    auto load_fused = [&](int c0) {
+        if constexpr (MODE == 1) {
+            if (!fused) return;
+            typedef const __attribute__((address_space(4))) int32_t* cint;
+            typedef const __attribute__((address_space(4))) float* cfloat;
+            int p[RB];
 #pragma unroll
-        for (int m = 0; m < NM; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int kc = 0; kc < nk; ++kc) {
-            const int s0 = s_beg + kc * kCap;
-            if (kc > 0 || ct > 0) {
-                if (nk > 1) {
+            for (int c = 0; c < RB; ++c) p[c] = ((cint)perm)[min(c0 + c, it.r1 - 1)];
 #pragma unroll
-                    for (int m = 0; m < NM; ++m) load_w<FMT>(w[m], wt[m], s0, s_end);
-                }
-                load_b<FMT>(bv, brow, colok, s0, G, g);
+            for (int c = 0; c < RB; ++c) {
+                wc[c] = ((cfloat)a.topk_w)[p[c]];
+                tokc[c] = p[c] / a.k;
             }
-            mma_chunk<FMT, NM>(acc, w, bv, min(kCap, s_end - s0), q2 + wave * NM);
         }
+    };
+    // Issues the loads of chunk kc of the pass at c0 (the weights too when
+    // `weights`) and waits until the staged token rows have landed.
+    auto issue = [&](int c0, int kc, bool weights) {
+        const int nreal = min(RB, it.r1 - c0);
+        const int s0 = s_beg + kc * kCap;
+        // staged row c: sorted row min(c0 + c, r1 - 1) (pr is clamped alike)
+        auto src_row = [&](int c) -> const uint16_t* {
+            if constexpr (MODE == 0) return a.x + static_cast<size_t>(lane_value(pr, c) / a.k) * a.d;
+            else return a.act + static_cast<size_t>(c0 + min(c, nreal - 1)) * a.f;
+        };
+        if constexpr (b_first) {
+            stage_rows<RB>(mine, src_row, s0 * kStepK, K);
+            // keep the weight loads behind the staged rows
+            __builtin_amdgcn_sched_barrier(0);
+            if (weights) {
 #pragma unroll
-        for (int m = 0; m < NM; ++m) red[wave][m][lane] = acc[m];
-        if (fused && wave == 0 && lane < 16) {
-            row_tok[lane] = pr / a.k;
-            row_w[lane] = wr;
+                for (int m = 0; m < NM; ++m) load_w<FMT>(w[m], wt[m], s0, s_end);
+                // the staged rows are older than every load issued after them
+                wait_vmcnt<NM * kWLoads<FMT>>();
+            } else {
+                wait_vmcnt<0>();
+            }
+        } else {
+            if (weights) {
+#pragma unroll
+                for (int m = 0; m < NM; ++m) load_w<FMT>(w[m], wt[m], s0, s_end);
+            }
+            // keep the row addresses (a wait for perm) below the weight loads
+            __builtin_amdgcn_sched_barrier(0);
+            stage_rows<RB>(mine, src_row, s0 * kStepK, K);
+            wait_vmcnt<0>();
+        }
+    };
+    auto multiply = [&](int kc) {
+        mma_chunk<FMT, NM>(acc, w, brow, min(kCap, s_end - (s_beg + kc * kCap)), q2 + wave * NM);
+    };
+    // Sums the waves' partial tiles of the pass at c0 in wave order and
+    // stores its columns.
+    auto finish = [&](int c0) {
+        const int nreal = min(RB, it.r1 - c0);
+        // each wave's own multiplies are done: its staged rows are free
+        f32x4* red = reinterpret_cast<f32x4*>(mine);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) red[m * kWave + lane] = acc[m];
+        if (fused && wave == 0 && lane == 0) {
+#pragma unroll
+            for (int c = 0; c < RB; ++c) {
+                row_tok[c] = tokc[c];
+                row_w[c] = wc[c];
+            }
         }
         __syncthreads();
-        const int R = min(16, it.r1 - c0);
-        for (int idx = tid; idx < R * 16; idx += KW * kWave) {
+        for (int idx = tid; idx < nreal * 16; idx += KW * kWave) {
             const int cc = idx >> 4, nn = idx & 15;
             const int src = cc + 16 * (nn >> 2), i = nn & 3;
             float v[NM];
 #pragma unroll
             for (int m = 0; m < NM; ++m) {
-                float sum = red[0][m][src][i];
+                float sum = reinterpret_cast<const f32x4*>(region[0])[m * kWave + src][i];
 #pragma unroll
-                for (int ww = 1; ww < KW; ++ww) sum += red[ww][m][src][i];
+                for (int ww = 1; ww < KW; ++ww) sum += reinterpret_cast<const f32x4*>(region[ww])[m * kWave + src][i];
                 v[m] = sum;
             }
             const size_t rr = static_cast<size_t>(c0 + cc);
@@ -202,12 +233,43 @@ __device__ __forceinline__ void skinny_body(const FfnArgs& a, const Item& it, in
             }
         }
         __syncthreads();
+    };
+    auto zero_acc = [&] {
+#pragma unroll
+        for (int m = 0; m < NM; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    };
+
+    // First pass, first chunk: straight-line loads and multiplies, so the
+    // waits before the multiplies count exactly the loads in flight.
+    load_pr(it.r0);
+    issue(it.r0, 0, true);
+    load_fused(it.r0);
+    zero_acc();
+    multiply(0);
+    for (int kc = 1; kc < nk; ++kc) {
+        issue(it.r0, kc, true);
+        multiply(kc);
+    }
+    finish(it.r0);
+    // Later passes (more rows than RB): the weights stay in registers when
+    // the K slice is one chunk.
+    for (int c0 = it.r0 + RB; c0 < it.r1; c0 += RB) {
+        load_pr(c0);
+        issue(c0, 0, nk > 1);
+        load_fused(c0);
+        zero_acc();
+        multiply(0);
+        for (int kc = 1; kc < nk; ++kc) {
+            issue(c0, kc, true);
+            multiply(kc);
+        }
+        finish(c0);
     }
 }
 
 // An item whose expert has no valid slot is skipped: its y rows read as zero
 // and MOE_DEV_BAD_SLOT is raised.
-template <int FMT, int MODE, int KW, bool PERM_LDS = false>
+template <int FMT, int MODE, int KW, int RB, bool PERM_LDS = false>
 __device__ __forceinline__ void run_item(const FfnArgs& a, const Item& it, int n0, const int32_t* perm) {
     if (it.e < 0) return;
     if (it.slot < 0 || it.slot >= a.num_slots) {
@@ -215,18 +277,18 @@ __device__ __forceinline__ void run_item(const FfnArgs& a, const Item& it, int n
         if (MODE == 1) zero_y_tile(a, n0, it.r0, it.r1);
         return;
     }
-    skinny_body<FMT, MODE, KW, PERM_LDS>(a, it, n0, perm);
+    skinny_body<FMT, MODE, KW, RB, PERM_LDS>(a, it, n0, perm);
 }
 
 // The last workgroup of the down launch zeroes the y rows past offsets[E].
-template <int FMT, int MODE, int KW>
+template <int FMT, int MODE, int KW, int RB>
 __global__ __launch_bounds__(KW * 64) void ffn_skinny_kernel(FfnArgs a) {
     if (MODE == 1 && blockIdx.x == gridDim.x - 1) {
         zero_y_tail(a);
         return;
     }
     const int NT = (MODE == 0 ? a.f : a.d) / 16;
-    run_item<FMT, MODE, KW>(a, find_item(a, blockIdx.x / NT), (blockIdx.x % NT) * 16, a.perm);
+    run_item<FMT, MODE, KW, RB>(a, find_item(a, blockIdx.x / NT), (blockIdx.x % NT) * 16, a.perm);
 }
 
 // ------------------------------------------------------------ routed gate/up
@@ -268,9 +330,9 @@ __device__ __forceinline__ void wave_dispatch(SmallRouting& r, int n, int E) {
 // one-wave counting sort: a few hundred instructions), so no routing launch
 // and no read of routing results from HBM precede its weight loads.
 // Workgroup 0 also writes ids, w, offsets, perm and inv and zeroes `out` for
-// the down launch's scatter-add.  Arithmetic as topk_kernel and the dispatch
+// the down launch's scatter-add, after its own item.  Arithmetic as topk_kernel and the dispatch
 // kernel, so every output is identical.
-template <int FMT>
+template <int FMT, int RB>
 __global__ __launch_bounds__(kGateUpWaves * 64) void ffn_gate_up_routed_kernel(FfnArgs a) {
     __shared__ SmallRouting r;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -281,6 +343,15 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void ffn_gate_up_routed_kernel(F
     __syncthreads();
     if (wave == 0) wave_dispatch(r, n, E);
     __syncthreads();
+    int lo = 0, hi = 0;
+    if (lane < E) {
+        lo = r.offsets[lane];
+        hi = r.offsets[lane + 1];
+    }
+    const int NT = a.f / 16;
+    run_item<FMT, 0, kGateUpWaves, RB, true>(a, pick_item(lo, hi, sl, blockIdx.x / NT), (blockIdx.x % NT) * 16, r.perm);
+    // after the item: no stores ahead of its loads (the down launch is the
+    // first reader of these)
     if (blockIdx.x == 0) {
         for (int i = tid; i < n; i += blockDim.x) {
             a.ids_out[i] = r.ids[i];
@@ -294,26 +365,39 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void ffn_gate_up_routed_kernel(F
             for (int i = tid; i < T * a.d / 4; i += blockDim.x) o4[i] = make_float4(0.f, 0.f, 0.f, 0.f);
         }
     }
-    int lo = 0, hi = 0;
-    if (lane < E) {
-        lo = r.offsets[lane];
-        hi = r.offsets[lane + 1];
-    }
-    const int NT = a.f / 16;
-    run_item<FMT, 0, kGateUpWaves, true>(a, pick_item(lo, hi, sl, blockIdx.x / NT), (blockIdx.x % NT) * 16, r.perm);
 }
 
 // ------------------------------------------------------------ launch
 
+// Token rows staged per column pass.  An expert owns at most T rows when a
+// token's k ids are distinct (more only with repeated ids, which take extra
+// passes), so RB follows T; 16 rows of 1 KB per wave fill most of the LDS.
+static int staged_rows(int T) { return T <= 1 ? 1 : T <= 2 ? 2 : T <= 4 ? 4 : T <= 16 ? 8 : 16; }
 
-template <int FMT>
-static hipError_t launch_two(const moe_shape& s, const FfnArgs& a, hipStream_t st) {
+template <int FMT, int RB>
+static hipError_t launch_two_rb(const moe_shape& s, const FfnArgs& a, hipStream_t st, bool routed) {
     const int umax = s.E < s.T * s.k ? s.E : s.T * s.k;
-    ffn_skinny_kernel<FMT, 0, kGateUpWaves><<<umax * (s.f / 16), kGateUpWaves * 64, 0, st>>>(a);
+    if (routed) {
+        if constexpr (RB <= kGateUpWaves)
+            ffn_gate_up_routed_kernel<FMT, RB><<<umax * (s.f / 16), kGateUpWaves * 64, 0, st>>>(a);
+    } else {
+        ffn_skinny_kernel<FMT, 0, kGateUpWaves, RB><<<umax * (s.f / 16), kGateUpWaves * 64, 0, st>>>(a);
+    }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    ffn_skinny_kernel<FMT, 1, kDownWaves><<<umax * (s.d / 16) + 1, kDownWaves * 64, 0, st>>>(a);
+    ffn_skinny_kernel<FMT, 1, kDownWaves, RB><<<umax * (s.d / 16) + 1, kDownWaves * 64, 0, st>>>(a);
     return hipGetLastError();
+}
+
+template <int FMT>
+static hipError_t launch_two(const moe_shape& s, const FfnArgs& a, hipStream_t st, bool routed) {
+    switch (staged_rows(s.T)) {
+        case 1: return launch_two_rb<FMT, 1>(s, a, st, routed);
+        case 2: return launch_two_rb<FMT, 2>(s, a, st, routed);
+        case 4: return launch_two_rb<FMT, 4>(s, a, st, routed);
+        case 8: return launch_two_rb<FMT, 8>(s, a, st, routed);
+        default: return launch_two_rb<FMT, 16>(s, a, st, routed);
+    }
 }
 
 // Token rows (T*k) from which the LDS-tiled grouped GEMM takes over.
@@ -327,23 +411,13 @@ bool routed_ffn_supported(const moe_shape& s, int fmt) {
     return s.T <= kGateUpWaves && s.T * s.k <= kRoutedMaxPairs && !ffn_uses_grouped(s, fmt);
 }
 
-template <int FMT>
-static hipError_t launch_two_routed(const moe_shape& s, const FfnArgs& a, hipStream_t st) {
-    const int umax = s.E < s.T * s.k ? s.E : s.T * s.k;
-    ffn_gate_up_routed_kernel<FMT><<<umax * (s.f / 16), kGateUpWaves * 64, 0, st>>>(a);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    ffn_skinny_kernel<FMT, 1, kDownWaves><<<umax * (s.d / 16) + 1, kDownWaves * 64, 0, st>>>(a);
-    return hipGetLastError();
-}
-
 hipError_t launch_ffn_routed(const moe_shape& s, int fmt, const FfnArgs& a, hipStream_t st) {
-    return fmt == MOE_FMT_MXFP4 ? launch_two_routed<MOE_FMT_MXFP4>(s, a, st) : launch_two_routed<MOE_FMT_Q2G32>(s, a, st);
+    return fmt == MOE_FMT_MXFP4 ? launch_two<MOE_FMT_MXFP4>(s, a, st, true) : launch_two<MOE_FMT_Q2G32>(s, a, st, true);
 }
 
 hipError_t launch_ffn(const moe_shape& s, int fmt, const FfnArgs& a, hipStream_t st) {
     if (ffn_uses_grouped(s, fmt)) return launch_ffn_grouped(s, a, st);
-    return fmt == MOE_FMT_MXFP4 ? launch_two<MOE_FMT_MXFP4>(s, a, st) : launch_two<MOE_FMT_Q2G32>(s, a, st);
+    return fmt == MOE_FMT_MXFP4 ? launch_two<MOE_FMT_MXFP4>(s, a, st, false) : launch_two<MOE_FMT_Q2G32>(s, a, st, false);
 }
 
 }  // namespace qrmoe

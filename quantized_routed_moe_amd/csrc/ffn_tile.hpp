@@ -1,7 +1,7 @@
 // Building blocks of the skinny expert-FFN kernels (few token rows per
 // expert): one wave computes a 16 (weight rows) x 16 (token columns) output
 // tile over a slice of K on the 16x16x32 bf16 matrix cores, with the weights
-// dequantised in registers.
+// dequantised in registers and the token operand read from LDS.
 //
 // Weights are in the tile layout (include/moe.h, MOE_LAYOUT_TILES): for a
 // 16-row tile, K step s (128 elements, four 32-element groups) is a block of
@@ -10,7 +10,10 @@
 // every cache line it touches is consumed whole.
 //  * MXFP4: lane (row = L%16, g = L/16) holds group 4s+g of its row (16 code
 //    bytes, one scale).  MFMA j of the step takes elements 8j..8j+7 of that
-//    group; the token operand supplies the same elements of its row.
+//    group; the token operand supplies the same elements of its row.  The
+//    scale bytes of four consecutive steps are 256 contiguous bytes: one
+//    dword per lane fetches them all and a lane permute hands each lane its
+//    own byte, so a chunk costs one scale load instead of four.
 //  * Q2: each MFMA covers ONE group (4s+j), all four lane groups supplying
 //    slices of it, because the per-group scale and min must be applied to the
 //    group's partial sum.  The tile layout already hands lane (row, g) the
@@ -21,6 +24,14 @@
 //    The offset 1 keeps the cancellation between C and xs small.  The
 //    per-(row, group) scale pairs pass through a wave-private LDS area so that
 //    each lane finds the four rows its accumulator holds.
+//
+// Token operand: the wave copies the K slice of each real token row of the
+// column pass (kCap steps = 512 bf16 = 1 KB per row) straight from global
+// memory into its own LDS rows (gfx950 global_load_lds, 16 bytes per lane),
+// one instruction per row, and reads the MFMA fragments from there.
+// Padding columns read a staged copy of some row and their outputs are never
+// stored; MFMA columns do not mix.  Elements past K read a clamped,
+// finite address and meet padding weights, which are exactly zero.
 #pragma once
 
 #include "common.hpp"
@@ -29,6 +40,10 @@ namespace qrmoe {
 
 constexpr int kCap = 4;        // K steps held in registers per chunk
 constexpr int kStepK = 128;    // K elements per step of the tile layout
+// One staged token row in LDS: kCap steps of bf16 plus 16 bytes, so that the
+// rows read by the 16 lanes of one ds_read_b128 phase start in distinct
+// 16-byte bank groups (row stride 1040 B = 260 banks = 4 mod 64).
+constexpr int kBRowBytes = kCap * kStepK * 2 + 16;
 
 template <int FMT> struct PieceBytes;
 template <> struct PieceBytes<MOE_FMT_MXFP4> { static constexpr int codes = 16, scales = 1; };
@@ -37,14 +52,18 @@ template <> struct PieceBytes<MOE_FMT_Q2G32> { static constexpr int codes = 8, s
 template <int FMT> struct WChunk;
 template <> struct WChunk<MOE_FMT_MXFP4> {
     u32x4 c[kCap];        // 32 e2m1 codes of group 4s+g
-    uint32_t s[kCap];     // its e8m0 scale byte
+    uint32_t sraw;        // dword `lane` of the chunk's 256 scale bytes
 };
 template <> struct WChunk<MOE_FMT_Q2G32> {
     u32x2 c[kCap];        // elements 8g..8g+7 of groups 4s..4s+3, 2 bytes each
     uint32_t sm[kCap];    // fp16 scale | fp16 min << 16 of (row, group 4s+g)
 };
 
-// This lane's piece of step 0 of one 16-row tile of one matrix.
+// Weight loads per chunk and matrix (code blocks + scale loads).
+template <int FMT> constexpr int kWLoads = FMT == MOE_FMT_MXFP4 ? kCap + 1 : 2 * kCap;
+
+// One 16-row tile of one matrix: this lane's code piece of step 0 and the
+// tile's scale bytes of step 0.
 struct WTile {
     const uint8_t* codes;
     const uint8_t* scales;
@@ -54,8 +73,8 @@ struct WTile {
 template <int FMT>
 __device__ __forceinline__ WTile wtile(const uint8_t* codes, const uint8_t* scales, size_t tile_index, int S,
                                        int lane) {
-    const size_t piece = tile_index * S * kWave + lane;
-    return WTile{codes + piece * PieceBytes<FMT>::codes, scales + piece * PieceBytes<FMT>::scales};
+    const size_t block = tile_index * S * kWave;
+    return WTile{codes + (block + lane) * PieceBytes<FMT>::codes, scales + block * PieceBytes<FMT>::scales};
 }
 
 // Loads steps [s0, s0 + kCap) of the tile; steps at or past s1 reload step
@@ -63,36 +82,47 @@ __device__ __forceinline__ WTile wtile(const uint8_t* codes, const uint8_t* scal
 // unconditionally and the surplus values are simply not used.
 template <int FMT>
 __device__ __forceinline__ void load_w(WChunk<FMT>& w, const WTile& t, int s0, int s1) {
+    const int lane = threadIdx.x & 63;
+    if constexpr (FMT == MOE_FMT_MXFP4) {
+        // bytes [64 s, 64 s + 64) are the scales of step s; lane L takes the
+        // dword holding pieces 4(L%16)..4(L%16)+3 of step s0 + L/16.  Issued
+        // first: every step needs it.
+        const size_t s = static_cast<size_t>(max(min(s0 + (lane >> 4), s1 - 1), 0));
+        w.sraw = *reinterpret_cast<const uint32_t*>(t.scales + s * kWave + 4 * (lane & 15));
+    }
 #pragma unroll
     for (int u = 0; u < kCap; ++u) {
         const size_t s = static_cast<size_t>(max(min(s0 + u, s1 - 1), 0));
         if constexpr (FMT == MOE_FMT_MXFP4) {
             w.c[u] = *reinterpret_cast<const u32x4*>(t.codes + s * kWave * 16);
-            w.s[u] = t.scales[s * kWave];
         } else {
+            w.sm[u] = *reinterpret_cast<const uint32_t*>(t.scales + (s * kWave + lane) * 4);
             w.c[u] = *reinterpret_cast<const u32x2*>(t.codes + s * kWave * 8);
-            w.sm[u] = *reinterpret_cast<const uint32_t*>(t.scales + s * kWave * 4);
         }
     }
 }
 
-// Token operand (bf16) of steps [s0, s0 + kCap) for this lane's column:
-// brow is a readable row of K elements (a valid row even when the column is
-// padding); elements of padding columns and of groups past G read as zero.
-template <int FMT>
-__device__ __forceinline__ void load_b(u32x4 (&b)[kCap][4], const uint16_t* brow, bool colok, int s0, int G, int g) {
+// Scale byte of this lane's piece in step u of the chunk (MXFP4).
+__device__ __forceinline__ uint32_t mx_scale_byte(uint32_t sraw, int u) {
+    const int lane = threadIdx.x & 63;
+    const uint32_t v = static_cast<uint32_t>(
+        __builtin_amdgcn_ds_bpermute((16 * u + (lane >> 2)) << 2, static_cast<int>(sraw)));
+    return (v >> (8 * (lane & 3))) & 0xffu;
+}
+
+// Copies K elements [e0, e0 + kCap*kStepK) of RB token rows into the wave's
+// LDS rows (row c at dst + c * kBRowBytes), one global_load_lds per row.
+// Lane i moves elements e0 + 8i .. e0 + 8i + 7, clamped to the last eight
+// elements of the row.  `src(c)` is row c's first element; rows past the
+// pass's real rows repeat its last one: a fixed number of loads, so every
+// wait count after them is known at compile time.
+template <int RB, typename Src>
+__device__ __forceinline__ void stage_rows(uint8_t* dst, Src src, int e0, int K) {
+    const int lane = threadIdx.x & 63;
+    const int e = min(e0 + 8 * lane, K - 8);
 #pragma unroll
-    for (int u = 0; u < kCap; ++u) {
-        const int s = s0 + u;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int gi = FMT == MOE_FMT_MXFP4 ? 4 * s + g : 4 * s + j;
-            const int e0 = FMT == MOE_FMT_MXFP4 ? 8 * j : 8 * g;
-            const bool ok = colok && gi < G;
-            const u32x4 v = *reinterpret_cast<const u32x4*>(brow + min(gi, G - 1) * kGroup + e0);
-            b[u][j] = ok ? v : u32x4{0u, 0u, 0u, 0u};
-        }
-    }
+    for (int c = 0; c < RB; ++c)
+        __builtin_amdgcn_global_load_lds(src(c) + e, (lds_void*)(dst + c * kBRowBytes), 16, 0, 0);
 }
 
 // Wave-private LDS area for the Q2 scale pairs of one 16-row tile step.
@@ -101,10 +131,11 @@ struct Q2Lds {
 };
 
 // acc[m] += W_m(16 rows, steps [0, nsteps) of the chunk) x B(chunk, 16
-// columns), for NM matrices that share the token operand.
+// columns), for NM matrices that share the token operand.  `brow` is this
+// lane's staged token row (column lane % 16).
 template <int FMT, int NM>
-__device__ __forceinline__ void mma_chunk(f32x4 (&acc)[NM], const WChunk<FMT> (&w)[NM],
-                                          const u32x4 (&b)[kCap][4], int nsteps, Q2Lds* q2 /* [NM], Q2 only */) {
+__device__ __forceinline__ void mma_chunk(f32x4 (&acc)[NM], const WChunk<FMT> (&w)[NM], const uint8_t* brow,
+                                          int nsteps, Q2Lds* q2 /* [NM], Q2 only */) {
     const int lane = threadIdx.x & 63;
     const int row = lane & 15, g = lane >> 4;
 #pragma unroll
@@ -113,10 +144,11 @@ __device__ __forceinline__ void mma_chunk(f32x4 (&acc)[NM], const WChunk<FMT> (&
         if constexpr (FMT == MOE_FMT_MXFP4) {
             float scl[NM];
 #pragma unroll
-            for (int m = 0; m < NM; ++m) scl[m] = e8m0_to_f32(w[m].s[u] & 0xffu);
+            for (int m = 0; m < NM; ++m) scl[m] = e8m0_to_f32(mx_scale_byte(w[m].sraw, u));
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const bf16x8 bb = bf16x8_from_u32x4(b[u][j]);
+                // elements 128u + 32g + 8j .. +7 of the row
+                const bf16x8 bb = *reinterpret_cast<const bf16x8*>(brow + 256 * u + 64 * g + 16 * j);
 #pragma unroll
                 for (int m = 0; m < NM; ++m)
                     acc[m] = mfma16x16x32(mxfp4x8_to_bf16(w[m].c[u][j], scl[m]), bb, acc[m]);
@@ -132,7 +164,8 @@ __device__ __forceinline__ void mma_chunk(f32x4 (&acc)[NM], const WChunk<FMT> (&
             const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const bf16x8 bb = bf16x8_from_u32x4(b[u][j]);
+                // elements 128u + 32j + 8g .. +7 of the row (group 4s+j)
+                const bf16x8 bb = *reinterpret_cast<const bf16x8*>(brow + 256 * u + 64 * j + 16 * g);
                 const f32x4 xs = mfma16x16x32(ones, bb, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
                 for (int m = 0; m < NM; ++m) {
