@@ -118,14 +118,21 @@ enum moe_format {
                                                 (padding: 0)
             scales [slots][n/16][S][64] uint8  its e8m0 scale (padding: 127)
             mins   NULL
-     Q2:    codes  [slots][n/16][S][64][8 B]   for j = 0..3, bytes 2g and
-                                                2g+1 (g = L/16) of the 8 code
-                                                bytes of group 4*step+j, j
-                                                ascending (padding: 0) --
-                                                elements 8g..8g+7 of each of
-                                                the step's four groups
-            scales [slots][n/16][S][64] uint32  fp16 scale | fp16 min << 16 of
-                                                group 4*step + L/16 (padding 0)
+     Q2:    codes  [slots][n/16][S][64][8 B]   elements 8g..8g+7 (g = L/16)
+                                                of each of the step's four
+                                                groups (padding: 0), as two
+                                                little-endian uint32; word t
+                                                holds groups a = 4*step+2t and
+                                                b = a+1: bits 0-7 elements
+                                                8g, 8g+2, 8g+4, 8g+6 of a (2
+                                                bits each, ascending), bits
+                                                8-15 the same of b, bits 16-23
+                                                elements 8g+1, +3, +5, +7 of
+                                                a, bits 24-31 the same of b
+            scales [slots][n/16][S][16][4] uint32  row-major: word (r, j) =
+                                                fp16 scale | fp16 min << 16 of
+                                                row 16*tile + r, group
+                                                4*step + j (padding 0)
             mins   NULL (the mins live in scales)
    Sizes: moe_qmat_bytes. */
 enum moe_layout {

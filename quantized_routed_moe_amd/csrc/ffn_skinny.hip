@@ -104,7 +104,6 @@ __device__ __forceinline__ void skinny_body(const FfnArgs& a, const Item& it, in
     // bytes hold the wave's partial tiles for the reduction.
     constexpr int kRegion = RB * kBRowBytes > NM * kWave * 16 ? RB * kBRowBytes : NM * kWave * 16;
     __shared__ __align__(16) uint8_t region[KW][kRegion];
-    __shared__ __align__(16) Q2Lds q2[FMT == MOE_FMT_Q2G32 ? KW * NM : 1];
     __shared__ int row_tok[RB];     // fused combine: token of the row
     __shared__ float row_w[RB];     // fused combine: routing weight of the row
     const int N = MODE == 0 ? a.f : a.d;
@@ -190,7 +189,7 @@ __device__ __forceinline__ void skinny_body(const FfnArgs& a, const Item& it, in
         }
     };
     auto multiply = [&](int kc) {
-        mma_chunk<FMT, NM>(acc, w, brow, min(kCap, s_end - (s_beg + kc * kCap)), q2 + wave * NM);
+        mma_chunk<FMT, NM>(acc, w, brow, min(kCap, s_end - (s_beg + kc * kCap)));
     };
     // Sums the waves' partial tiles of the pass at c0 in wave order and
     // stores its columns.
@@ -209,8 +208,9 @@ __device__ __forceinline__ void skinny_body(const FfnArgs& a, const Item& it, in
         }
         __syncthreads();
         for (int idx = tid; idx < nreal * 16; idx += KW * kWave) {
+            // column cc, weight row nn: lane nn + 16 (cc / 4), element cc % 4
             const int cc = idx >> 4, nn = idx & 15;
-            const int src = cc + 16 * (nn >> 2), i = nn & 3;
+            const int src = nn + 16 * (cc >> 2), i = cc & 3;
             float v[NM];
 #pragma unroll
             for (int m = 0; m < NM; ++m) {
@@ -282,7 +282,7 @@ __device__ __forceinline__ void run_item(const FfnArgs& a, const Item& it, int n
 
 // The last workgroup of the down launch zeroes the y rows past offsets[E].
 template <int FMT, int MODE, int KW, int RB>
-__global__ __launch_bounds__(KW * 64) void ffn_skinny_kernel(FfnArgs a) {
+__global__ __launch_bounds__(KW * 64) __attribute__((amdgpu_waves_per_eu(4))) void ffn_skinny_kernel(FfnArgs a) {
     if (MODE == 1 && blockIdx.x == gridDim.x - 1) {
         zero_y_tail(a);
         return;
@@ -333,7 +333,7 @@ __device__ __forceinline__ void wave_dispatch(SmallRouting& r, int n, int E) {
 // the down launch's scatter-add, after its own item.  Arithmetic as topk_kernel and the dispatch
 // kernel, so every output is identical.
 template <int FMT, int RB>
-__global__ __launch_bounds__(kGateUpWaves * 64) void ffn_gate_up_routed_kernel(FfnArgs a) {
+__global__ __launch_bounds__(kGateUpWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void ffn_gate_up_routed_kernel(FfnArgs a) {
     __shared__ SmallRouting r;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int T = a.T, E = a.E, k = a.k, n = a.T * a.k;

@@ -1,7 +1,11 @@
 // Building blocks of the skinny expert-FFN kernels (few token rows per
-// expert): one wave computes a 16 (weight rows) x 16 (token columns) output
+// expert): one wave computes a 16 (token columns) x 16 (weight rows) output
 // tile over a slice of K on the 16x16x32 bf16 matrix cores, with the weights
-// dequantised in registers and the token operand read from LDS.
+// dequantised in registers and the token operand read from LDS.  The tokens
+// are the MFMA's A operand and the weights its B operand, so lane l receives
+// the outputs of weight row l%16 for tokens 4(l/16) .. 4(l/16)+3: every
+// per-row quantity (a Q2 group's scale and min) is uniform over a lane's
+// four outputs.
 //
 // Weights are in the tile layout (include/moe.h, MOE_LAYOUT_TILES): for a
 // 16-row tile, K step s (128 elements, four 32-element groups) is a block of
@@ -16,21 +20,23 @@
 //    own byte, so a chunk costs one scale load instead of four.
 //  * Q2: each MFMA covers ONE group (4s+j), all four lane groups supplying
 //    slices of it, because the per-group scale and min must be applied to the
-//    group's partial sum.  The tile layout already hands lane (row, g) the
-//    codes of elements 8g..8g+7 of each of the four groups.  A = bf16(1 + q/4)
-//    is exact (bit pattern 0x3F80 | q<<5); with C = sum (1+q/4) x and
-//    xs = sum x (a second MFMA against a ones operand) the group contributes
+//    group's partial sum.  The tile layout hands lane (row, g) the codes of
+//    elements 8g..8g+7 of each of the four groups, even elements and odd
+//    elements in separate bytes, so that one shift and one and-or turn a
+//    pair of codes into two bf16 values 1 + q/4 (bit pattern 0x3F80 | q<<5,
+//    exact).  With C = sum (1+q/4) x and xs = sum x (a second MFMA against a
+//    ones operand) the group contributes
 //        (4*scale)*C + (min - 4*scale)*xs == sum (scale*q + min) x.
-//    The offset 1 keeps the cancellation between C and xs small.  The
-//    per-(row, group) scale pairs pass through a wave-private LDS area so that
-//    each lane finds the four rows its accumulator holds.
+//    The offset 1 keeps the cancellation between C and xs small.  A lane
+//    loads the four (scale, min) words of its own row for the step (16
+//    contiguous bytes of the row-major scale block).
 //
 // Token operand: the wave copies the K slice of each real token row of the
 // column pass (kCap steps = 512 bf16 = 1 KB per row) straight from global
 // memory into its own LDS rows (gfx950 global_load_lds, 16 bytes per lane),
 // one instruction per row, and reads the MFMA fragments from there.
 // Padding columns read a staged copy of some row and their outputs are never
-// stored; MFMA columns do not mix.  Elements past K read a clamped,
+// stored; MFMA rows and columns do not mix.  Elements past K read a clamped,
 // finite address and meet padding weights, which are exactly zero.
 #pragma once
 
@@ -55,15 +61,15 @@ template <> struct WChunk<MOE_FMT_MXFP4> {
     uint32_t sraw;        // dword `lane` of the chunk's 256 scale bytes
 };
 template <> struct WChunk<MOE_FMT_Q2G32> {
-    u32x2 c[kCap];        // elements 8g..8g+7 of groups 4s..4s+3, 2 bytes each
-    uint32_t sm[kCap];    // fp16 scale | fp16 min << 16 of (row, group 4s+g)
+    u32x2 c[kCap];        // elements 8g..8g+7 of groups 4s..4s+3 (dword t: groups 4s+2t, 4s+2t+1)
+    u32x4 sm[kCap];       // fp16 scale | fp16 min << 16 of (row, group 4s+j), j = 0..3
 };
 
 // Weight loads per chunk and matrix (code blocks + scale loads).
 template <int FMT> constexpr int kWLoads = FMT == MOE_FMT_MXFP4 ? kCap + 1 : 2 * kCap;
 
 // One 16-row tile of one matrix: this lane's code piece of step 0 and the
-// tile's scale bytes of step 0.
+// tile's scale block of step 0.
 struct WTile {
     const uint8_t* codes;
     const uint8_t* scales;
@@ -96,7 +102,8 @@ __device__ __forceinline__ void load_w(WChunk<FMT>& w, const WTile& t, int s0, i
         if constexpr (FMT == MOE_FMT_MXFP4) {
             w.c[u] = *reinterpret_cast<const u32x4*>(t.codes + s * kWave * 16);
         } else {
-            w.sm[u] = *reinterpret_cast<const uint32_t*>(t.scales + (s * kWave + lane) * 4);
+            // row-major scale block: the four words of row L%16
+            w.sm[u] = *reinterpret_cast<const u32x4*>(t.scales + s * kWave * 4 + 16 * (lane & 15));
             w.c[u] = *reinterpret_cast<const u32x2*>(t.codes + s * kWave * 8);
         }
     }
@@ -125,19 +132,15 @@ __device__ __forceinline__ void stage_rows(uint8_t* dst, Src src, int e0, int K)
         __builtin_amdgcn_global_load_lds(src(c) + e, (lds_void*)(dst + c * kBRowBytes), 16, 0, 0);
 }
 
-// Wave-private LDS area for the Q2 scale pairs of one 16-row tile step.
-struct Q2Lds {
-    float2 sm[4][16];     // [group in step][row]: (4*scale, min - 4*scale)
-};
-
-// acc[m] += W_m(16 rows, steps [0, nsteps) of the chunk) x B(chunk, 16
-// columns), for NM matrices that share the token operand.  `brow` is this
-// lane's staged token row (column lane % 16).
+// acc[m] += B(chunk, 16 token columns)^T x W_m(steps [0, nsteps) of the
+// chunk, 16 rows), for NM matrices that share the token operand: lane l
+// accumulates weight row l%16 for tokens 4(l/16)+i.  `brow` is this lane's
+// staged token row (column lane % 16).
 template <int FMT, int NM>
 __device__ __forceinline__ void mma_chunk(f32x4 (&acc)[NM], const WChunk<FMT> (&w)[NM], const uint8_t* brow,
-                                          int nsteps, Q2Lds* q2 /* [NM], Q2 only */) {
+                                          int nsteps) {
     const int lane = threadIdx.x & 63;
-    const int row = lane & 15, g = lane >> 4;
+    const int g = lane >> 4;
 #pragma unroll
     for (int u = 0; u < kCap; ++u) {
         if (u >= nsteps) break;
@@ -151,43 +154,40 @@ __device__ __forceinline__ void mma_chunk(f32x4 (&acc)[NM], const WChunk<FMT> (&
                 const bf16x8 bb = *reinterpret_cast<const bf16x8*>(brow + 256 * u + 64 * g + 16 * j);
 #pragma unroll
                 for (int m = 0; m < NM; ++m)
-                    acc[m] = mfma16x16x32(mxfp4x8_to_bf16(w[m].c[u][j], scl[m]), bb, acc[m]);
+                    acc[m] = mfma16x16x32(bb, mxfp4x8_to_bf16(w[m].c[u][j], scl[m]), acc[m]);
             }
         } else {
-#pragma unroll
-            for (int m = 0; m < NM; ++m) {
-                const float sf = fp16_to_f32(w[m].sm[u]);
-                const float mf = fp16_to_f32(w[m].sm[u] >> 16);
-                q2[m].sm[g][row] = make_float2(4.f * sf, fmaf(-4.f, sf, mf));
-            }
-            __builtin_amdgcn_wave_barrier();
             const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
+            // the code mask in a register: (x & mask) | 0x3f803f80 is then one
+            // v_and_or_b32 (gfx950 VOP3 takes no second literal)
+            uint32_t qmask = 0x00600060u;
+            asm volatile("" : "+v"(qmask));
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 // elements 128u + 32j + 8g .. +7 of the row (group 4s+j)
                 const bf16x8 bb = *reinterpret_cast<const bf16x8*>(brow + 256 * u + 64 * j + 16 * g);
-                const f32x4 xs = mfma16x16x32(ones, bb, f32x4{0.f, 0.f, 0.f, 0.f});
+                const f32x4 xs = mfma16x16x32(bb, ones, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
                 for (int m = 0; m < NM; ++m) {
-                    const uint32_t c16 = ((j & 2) ? w[m].c[u][1] : w[m].c[u][0]) >> (16 * (j & 1));
-                    u32x4 av;   // eight 2-bit codes -> eight bf16(1 + q/4), two per dword
+                    // even elements of group j in byte (j&1), odd ones in byte 2 + (j&1)
+                    const uint32_t cw = w[m].c[u][j >> 1];
+                    u32x4 av;   // pair h = elements 2h, 2h+1 -> bf16(1 + q/4) in the low, high half
 #pragma unroll
                     for (int h = 0; h < 4; ++h) {
-                        const uint32_t c4 = c16 >> (4 * h);
-                        av[h] = ((c4 & 3u) << 5) | ((c4 & 0xcu) << 19) | 0x3f803f80u;
+                        const int sh = 8 * (j & 1) + 2 * h - 5;
+                        const uint32_t x = sh >= 0 ? cw >> sh : cw << -sh;
+                        av[h] = (x & qmask) | 0x3f803f80u;
                     }
-                    const f32x4 cq = mfma16x16x32(bf16x8_from_u32x4(av), bb, f32x4{0.f, 0.f, 0.f, 0.f});
-                    const float4* smp = reinterpret_cast<const float4*>(&q2[m].sm[j][4 * g]);
-                    const float4 s01 = smp[0], s23 = smp[1];
+                    const f32x4 cq = mfma16x16x32(bb, bf16x8_from_u32x4(av), f32x4{0.f, 0.f, 0.f, 0.f});
+                    const uint32_t smw = w[m].sm[u][j];
+                    const float fs = 4.f * fp16_to_f32(smw);                 // 4 * scale
+                    const float fm = fmaf(-4.f, fp16_to_f32(smw), fp16_to_f32(smw >> 16));  // min - 4 * scale
                     f32x4 ac = acc[m];
-                    ac[0] = fmaf(s01.x, cq[0], fmaf(s01.y, xs[0], ac[0]));
-                    ac[1] = fmaf(s01.z, cq[1], fmaf(s01.w, xs[1], ac[1]));
-                    ac[2] = fmaf(s23.x, cq[2], fmaf(s23.y, xs[2], ac[2]));
-                    ac[3] = fmaf(s23.z, cq[3], fmaf(s23.w, xs[3], ac[3]));
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) ac[i] = fmaf(fs, cq[i], fmaf(fm, xs[i], ac[i]));
                     acc[m] = ac;
                 }
             }
-            __builtin_amdgcn_wave_barrier();
         }
     }
 }

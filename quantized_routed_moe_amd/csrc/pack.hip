@@ -40,19 +40,31 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ s
             *reinterpret_cast<u32x4*>(dst_codes + p * 16) = c;
             dst_scales[p] = sc;
         } else {
-            // bytes 2g, 2g+1 of each of the step's four groups
+            // elements 8g..8g+7 of each of the step's four groups (bytes 2g,
+            // 2g+1 of the group's eight), even and odd elements apart
             const uint16_t* row16 = reinterpret_cast<const uint16_t*>(src_codes + grow * (K / 4));
-            uint32_t h[4];
+            uint32_t ev[4], od[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int gj = 4 * s + j;
-                h[j] = gj < G ? row16[gj * 4 + g] : 0u;
+                const uint32_t h = gj < G ? row16[gj * 4 + g] : 0u;   // element 8g+e at bits 2e
+                ev[j] = od[j] = 0u;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    ev[j] |= ((h >> (4 * i)) & 3u) << (2 * i);
+                    od[j] |= ((h >> (4 * i + 2)) & 3u) << (2 * i);
+                }
             }
-            *reinterpret_cast<u32x2*>(dst_codes + p * 8) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+            *reinterpret_cast<u32x2*>(dst_codes + p * 8) =
+                u32x2{ev[0] | (ev[1] << 8) | (od[0] << 16) | (od[1] << 24),
+                      ev[2] | (ev[3] << 8) | (od[2] << 16) | (od[3] << 24)};
+            // the block's scale words are row-major: word L = (row L/4, group 4s + L%4)
+            const int srow = static_cast<int>(ti % NT) * 16 + (L >> 2), sg = 4 * s + (L & 3);
             uint32_t sm = 0u;
-            if (gi < G) {
+            if (sg < G) {
+                const size_t srow_g = slot * n + srow;
                 const uint16_t* sc16 = reinterpret_cast<const uint16_t*>(src_scales);
-                sm = static_cast<uint32_t>(sc16[grow * G + gi]) | (static_cast<uint32_t>(src_mins[grow * G + gi]) << 16);
+                sm = static_cast<uint32_t>(sc16[srow_g * G + sg]) | (static_cast<uint32_t>(src_mins[srow_g * G + sg]) << 16);
             }
             reinterpret_cast<uint32_t*>(dst_scales)[p] = sm;
         }

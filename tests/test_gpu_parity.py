@@ -290,18 +290,28 @@ def _tiles_mxfp4(codes, scales):
 
 
 def _tiles_q2(codes, scales, mins):
-    """Q2: piece L = 16 g + r holds, for j = 0..3, bytes 2g, 2g+1 of group
-    4 step + j of row 16 tile + r; its scale word is (scale | min << 16) of
-    group 4 step + g (zero for padding)."""
+    """Q2: piece L = 16 g + r holds elements 8g..8g+7 of each group 4 step + j
+    of row 16 tile + r as two words; word t: even elements of groups 2t and
+    2t+1 in bytes 0 and 1, odd elements in bytes 2 and 3 (2 bits each,
+    ascending).  The step's scale words are row-major: (row r, group j) at
+    4 r + j, each (scale | min << 16) (zero for padding)."""
     slots, n, quarter = codes.shape
     G, S, NT = quarter // 8, -(-quarter // 32), n // 16
     cg = np.zeros((slots, n, 4 * S, 8), np.uint8)
     cg[:, :, :G] = codes.reshape(slots, n, G, 8)
-    c = cg.reshape(slots, NT, 16, S, 4, 4, 2).transpose(0, 1, 3, 5, 2, 4, 6)
+    # [slot, tile, step, g, r, j, byte] -> 16-bit chunk of elements 8g..8g+7
+    b = cg.reshape(slots, NT, 16, S, 4, 4, 2).transpose(0, 1, 3, 5, 2, 4, 6).astype(np.uint32)
+    h = b[..., 0] | (b[..., 1] << 8)
+    q = [(h >> (2 * e)) & 3 for e in range(8)]                    # element 8g+e
+    ev = q[0] | (q[2] << 2) | (q[4] << 4) | (q[6] << 6)
+    od = q[1] | (q[3] << 2) | (q[5] << 4) | (q[7] << 6)
+    w = [ev[..., 2 * t] | (ev[..., 2 * t + 1] << 8) | (od[..., 2 * t] << 16) | (od[..., 2 * t + 1] << 24)
+         for t in range(2)]
+    c = np.stack(w, axis=-1).astype("<u4")
     sm = np.zeros((slots, n, 4 * S), np.uint32)
     sm[:, :, :G] = scales.astype(np.uint32) | (mins.astype(np.uint32) << 16)
-    s = sm.reshape(slots, NT, 16, S, 4).transpose(0, 1, 3, 4, 2)
-    return c.reshape(-1), np.ascontiguousarray(s.reshape(-1)).view(np.uint8)
+    s = sm.reshape(slots, NT, 16, S, 4).transpose(0, 1, 3, 2, 4)
+    return np.ascontiguousarray(c).reshape(-1).view(np.uint8), np.ascontiguousarray(s.reshape(-1)).view(np.uint8)
 
 
 @pytest.mark.parametrize("fmt", ["mxfp4", "q2"])
