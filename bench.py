@@ -7,10 +7,12 @@ pools ("layers") and different token batches, cycling through enough pools
 that a layer's experts are evicted from the 256 MB Infinity Cache before the
 layer comes round again (as in a real decode pass over a deep MoE model).
 
-Two timed regions over the same K steps: (1) the one-call layer,
-moe_layer -- its throughput is `value` (tokens/s) and ms_per_step; (2) the
-four entry points with HIP events around moe_expert_ffn on the launch
-stream -- the average FFN duration gives the roofline figure.
+Timed regions over the same K steps: (1) the one-call layer, moe_layer,
+enqueued call by call from Python (eager_ms_per_step); (1g) the same K
+calls captured once into a HIP graph and replayed -- its throughput is
+`value` (tokens/s) and ms_per_step; (2) the four entry points with HIP
+events around moe_expert_ffn on the launch stream -- the average FFN
+duration gives the roofline figure.
 
 Prints ONE JSON line.  Default workload: decode, T=1, d=4096, E=64, k=2,
 f=2048, MXFP4 experts.
@@ -188,6 +190,10 @@ def main():
     import ctypes
     L = qm.lib()
     hip = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+    # a created stream (default priority): the legacy null stream cannot be
+    # captured; what was enqueued so far is finished first
+    torch.cuda.synchronize()
+    torch.cuda.set_stream(torch.cuda.Stream())
     stream = torch.cuda.current_stream().cuda_stream
     sc = shape.c()
     sh = ctypes.byref(sc)
@@ -235,13 +241,44 @@ def main():
     torch.cuda.synchronize()
     K = args.steps
 
-    # Timed region 1 (value): K steps of the one-call layer, moe_layer.
+    # Timed region 1 (eager): K steps of the one-call layer, moe_layer, each
+    # call enqueued from Python.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
         layer_step(args.warmup + i)
     torch.cuda.synchronize()
+    eager_elapsed = time.perf_counter() - t0
+
+    # Timed region 1g (value): the same K steps captured once into a HIP
+    # graph and replayed.  Every kernel of every step runs; the graph only
+    # removes the per-launch work of the command processor between the
+    # dependent launches (decode steps are a few launches of a few us each).
+    for fn in ("hipStreamBeginCapture", "hipStreamEndCapture", "hipGraphInstantiate", "hipGraphLaunch",
+               "hipGraphExecDestroy", "hipGraphDestroy"):
+        getattr(hip, fn).restype = ctypes.c_int
+    graph, gexec = ctypes.c_void_p(), ctypes.c_void_p()
+    sp = ctypes.c_void_p(stream)
+
+    def hip_ok(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} returned hipError {rc}")
+
+    hip_ok(hip.hipStreamBeginCapture(sp, 1), "hipStreamBeginCapture")       # thread-local capture
+    try:
+        for i in range(K):
+            layer_step(args.warmup + i)
+    finally:
+        hip_ok(hip.hipStreamEndCapture(sp, ctypes.byref(graph)), "hipStreamEndCapture")
+    hip_ok(hip.hipGraphInstantiate(ctypes.byref(gexec), graph, None, None, ctypes.c_size_t(0)), "hipGraphInstantiate")
+    hip_ok(hip.hipGraphLaunch(gexec, sp), "hipGraphLaunch")                  # warm replay
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    hip_ok(hip.hipGraphLaunch(gexec, sp), "hipGraphLaunch")
+    torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    hip.hipGraphExecDestroy(gexec)
+    hip.hipGraphDestroy(graph)
 
     # Timed region 2 (roofline): the same K steps through the four entry
     # points, with HIP events around moe_expert_ffn on the same stream.
@@ -318,6 +355,8 @@ def main():
         "weight_stream_GBps": round(gbps, 1),
         "expert_TFLOPs": round(tflops, 3),
         "active_experts_mean": U_mean,
+        "launch": "HIP graph of the K steps, replayed once",
+        "eager_ms_per_step": round(eager_elapsed / K * 1e3, 5),
         "four_call_ms_per_step": round(steps_elapsed / K * 1e3, 5),
         "roofline": roof,
     }

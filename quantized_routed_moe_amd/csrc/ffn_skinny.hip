@@ -126,7 +126,7 @@ __device__ __forceinline__ void skinny_body(const FfnArgs& a, const Item& it, in
         wt[m] = wtile<FMT>(a.codes[mat], a.scales[mat], static_cast<size_t>(it.slot) * NT + n0 / 16, S, lane);
     }
     WChunk<FMT> w[NM];
-    f32x4 acc[NM];
+    f32x4 acc[kChains<FMT>][NM];
     int pr = 0;             // MODE 0: pair of this lane's column in the current pass
     int tokc[RB];           // fused combine: token and routing weight of each column
     float wc[RB];
@@ -198,7 +198,12 @@ __device__ __forceinline__ void skinny_body(const FfnArgs& a, const Item& it, in
         // each wave's own multiplies are done: its staged rows are free
         f32x4* red = reinterpret_cast<f32x4*>(mine);
 #pragma unroll
-        for (int m = 0; m < NM; ++m) red[m * kWave + lane] = acc[m];
+        for (int m = 0; m < NM; ++m) {
+            f32x4 v = acc[0][m];
+#pragma unroll
+            for (int c = 1; c < kChains<FMT>; ++c) v += acc[c][m];
+            red[m * kWave + lane] = v;
+        }
         if (fused && wave == 0 && lane == 0) {
 #pragma unroll
             for (int c = 0; c < RB; ++c) {
@@ -232,11 +237,14 @@ __device__ __forceinline__ void skinny_body(const FfnArgs& a, const Item& it, in
                 a.y[rr * a.d + n] = v[0];
             }
         }
-        __syncthreads();
+        // the next pass overwrites the partial tiles
+        if (c0 + RB < it.r1) __syncthreads();
     };
     auto zero_acc = [&] {
 #pragma unroll
-        for (int m = 0; m < NM; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < kChains<FMT>; ++c)
+#pragma unroll
+            for (int m = 0; m < NM; ++m) acc[c][m] = f32x4{0.f, 0.f, 0.f, 0.f};
     };
 
     // First pass, first chunk: straight-line loads and multiplies, so the

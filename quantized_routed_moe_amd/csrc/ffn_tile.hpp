@@ -132,13 +132,19 @@ __device__ __forceinline__ void stage_rows(uint8_t* dst, Src src, int e0, int K)
         __builtin_amdgcn_global_load_lds(src(c) + e, (lds_void*)(dst + c * kBRowBytes), 16, 0, 0);
 }
 
-// acc[m] += B(chunk, 16 token columns)^T x W_m(steps [0, nsteps) of the
+// Independent accumulator chains per matrix: MXFP4 alternates two over the
+// MFMAs of a step (their sum is taken at the end), so consecutive dependent
+// MFMAs of a wave are two apart; Q2 adds scaled partial sums with VALU
+// instructions and keeps one.
+template <int FMT> constexpr int kChains = FMT == MOE_FMT_MXFP4 ? 2 : 1;
+
+// acc[.][m] += B(chunk, 16 token columns)^T x W_m(steps [0, nsteps) of the
 // chunk, 16 rows), for NM matrices that share the token operand: lane l
 // accumulates weight row l%16 for tokens 4(l/16)+i.  `brow` is this lane's
 // staged token row (column lane % 16).
 template <int FMT, int NM>
-__device__ __forceinline__ void mma_chunk(f32x4 (&acc)[NM], const WChunk<FMT> (&w)[NM], const uint8_t* brow,
-                                          int nsteps) {
+__device__ __forceinline__ void mma_chunk(f32x4 (&acc)[kChains<FMT>][NM], const WChunk<FMT> (&w)[NM],
+                                          const uint8_t* brow, int nsteps) {
     const int lane = threadIdx.x & 63;
     const int g = lane >> 4;
 #pragma unroll
@@ -154,7 +160,7 @@ __device__ __forceinline__ void mma_chunk(f32x4 (&acc)[NM], const WChunk<FMT> (&
                 const bf16x8 bb = *reinterpret_cast<const bf16x8*>(brow + 256 * u + 64 * g + 16 * j);
 #pragma unroll
                 for (int m = 0; m < NM; ++m)
-                    acc[m] = mfma16x16x32(bb, mxfp4x8_to_bf16(w[m].c[u][j], scl[m]), acc[m]);
+                    acc[j & 1][m] = mfma16x16x32(bb, mxfp4x8_to_bf16(w[m].c[u][j], scl[m]), acc[j & 1][m]);
             }
         } else {
             const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
@@ -182,10 +188,10 @@ __device__ __forceinline__ void mma_chunk(f32x4 (&acc)[NM], const WChunk<FMT> (&
                     const uint32_t smw = w[m].sm[u][j];
                     const float fs = 4.f * fp16_to_f32(smw);                 // 4 * scale
                     const float fm = fmaf(-4.f, fp16_to_f32(smw), fp16_to_f32(smw >> 16));  // min - 4 * scale
-                    f32x4 ac = acc[m];
+                    f32x4 ac = acc[0][m];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) ac[i] = fmaf(fs, cq[i], fmaf(fm, xs[i], ac[i]));
-                    acc[m] = ac;
+                    acc[0][m] = ac;
                 }
             }
         }

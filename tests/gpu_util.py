@@ -170,3 +170,45 @@ def check_against_oracle(case: dict, g: dict, *, rows=None, check_logits=True, s
     info["active_experts"] = int(np.sum(np.diff(offsets) > 0))
     info["act_flips"] = int(np.sum(g["act"][rows if rows is not None else slice(None)] != act))
     return info
+
+
+class HipGraph:
+    """Stream capture into a HIP graph through the HIP runtime (no torch
+    graph machinery): capture(fn, stream) records what fn enqueues on
+    `stream`, launch(stream) replays it."""
+
+    def __init__(self):
+        import ctypes
+        import os
+        self._c = ctypes
+        self.hip = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+        for name in ("hipStreamBeginCapture", "hipStreamEndCapture", "hipGraphInstantiate", "hipGraphLaunch",
+                     "hipGraphExecDestroy", "hipGraphDestroy"):
+            getattr(self.hip, name).restype = ctypes.c_int
+        self.graph = ctypes.c_void_p()
+        self.exe = ctypes.c_void_p()
+
+    def _ok(self, rc, what):
+        assert rc == 0, f"{what} returned hipError {rc}"
+
+    def capture(self, fn, stream) -> None:
+        c = self._c
+        s = c.c_void_p(stream.cuda_stream)
+        self._ok(self.hip.hipStreamBeginCapture(s, 1), "hipStreamBeginCapture")   # thread-local mode
+        try:
+            fn()
+        finally:
+            self._ok(self.hip.hipStreamEndCapture(s, c.byref(self.graph)), "hipStreamEndCapture")
+        self._ok(self.hip.hipGraphInstantiate(c.byref(self.exe), self.graph, None, None, c.c_size_t(0)),
+                 "hipGraphInstantiate")
+
+    def launch(self, stream) -> None:
+        self._ok(self.hip.hipGraphLaunch(self.exe, self._c.c_void_p(stream.cuda_stream)), "hipGraphLaunch")
+
+    def close(self) -> None:
+        if self.exe:
+            self.hip.hipGraphExecDestroy(self.exe)
+        if self.graph:
+            self.hip.hipGraphDestroy(self.graph)
+        self.exe = self._c.c_void_p()
+        self.graph = self._c.c_void_p()
