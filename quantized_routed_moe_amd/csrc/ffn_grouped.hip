@@ -17,15 +17,15 @@
 // row (1..4), so a partial tile costs MFMA work in proportion to its rows and
 // the inner loop has no branches.
 //
-// Operands in LDS, four stages deep, filled by direct global -> LDS loads
+// Operands in LDS, in a ring of stages filled by direct global -> LDS loads
 // (gfx950 global_load_lds, 16 bytes per lane: lane i of an instruction lands
 // at the instruction's LDS base + 16 i, from an address of its own choice):
 //  * weights: the raw MXFP4 pieces of the tile layout (include/moe.h): a
 //    64-element step of a 16-row tile is half of one layout block, 32 pieces
 //    of 16 code bytes, contiguous in HBM and copied as is; the 32 scale bytes
-//    with it (16 bytes per lane from lanes 0..7 of each wave: with 1-, 2- or
-//    4-byte lanes the LDS destination advances 4 bytes per lane, so a
-//    2-byte copy would not be contiguous);
+//    of each of the 32 tiles with them, all in one 1 KB copy by wave 0 (two
+//    16-byte lanes per tile: with 1-, 2- or 4-byte lanes the LDS destination
+//    advances 4 bytes per lane, so narrower copies would not be contiguous);
 //  * tokens: bf16 rows of 128 B (64 elements) whose 16-byte chunks are stored
 //    XOR-swizzled by (row / 2) mod 8 -- each lane fetches the global chunk
 //    that belongs at its LDS position.  gfx950's LDS serves 256 B per cycle
@@ -37,10 +37,14 @@
 // then reads one whole 32-element group (one piece: 16 code bytes, one scale)
 // of the weight row and 64 contiguous bytes of the token row per step.
 //
-// Pipeline: every wave issues the same five LDS-bound loads per stage, three
-// stages ahead; before computing stage s it waits (vmcnt) until only the two
-// younger stages are in flight, and one barrier per stage makes every wave's
-// copy visible and frees the buffer of stage s-1 for stage s+3.  No register
+// Pipeline: a ring of NST stages (4 to 7: a stage holds only the token rows
+// of the unit's live column tiles, so units with few rows keep more weight
+// bytes in flight); every wave issues its LDS-bound loads of a stage (two
+// weight, up to two token, wave 0 the scales too) NST - 1 stages ahead;
+// before computing stage s it waits (vmcnt, counting its own loads) until
+// only the younger stages are in flight, and one barrier per stage makes
+// every wave's copy visible and frees the buffer of stage s-1 for stage
+// s+NST-1.  No register
 // ring and no LDS store pass: the registers go to the accumulators and to the
 // B fragments, which are all read at the start of a stage so that their LDS
 // latency overlaps the multiplies.  Padding token rows (past the expert's
@@ -66,13 +70,31 @@ constexpr int kGN = 512;        // weight rows per tile
 constexpr int kGK = 64;         // K per step
 constexpr int kGWaves = 8;
 constexpr int kGThreads = kGWaves * 64;
-constexpr int kStages = 4;
 constexpr int kStageW = kGN * 32;            // 32 tiles x 32 pieces x 16 B
 constexpr int kStageS = kGN * 2;             // 32 tiles x 32 scale bytes
-constexpr int kStageX = kGM * 128;           // 128 token rows x 64 bf16
-constexpr int kStageBytes = kStageW + kStageS + kStageX;
-constexpr int kLoadsPerStage = 5;            // per wave: 2 weight, 1 scale, 2 token
-constexpr int kLoadsPerStageNoX = 3;         // a wave whose token rows no column tile reads
+constexpr int kLdsBytes = 153600;            // the stage ring (of 160 KB per CU)
+
+// Stage ring of a unit whose valid token rows fill NTT 32-row column tiles:
+// a stage holds the weights, their scales and only the 32*NTT token rows the
+// multiplies read, so units with few rows keep more stages (and bytes) in
+// flight: 7 stages for NTT = 1, 6, 5 and 4 for NTT = 4.
+template <int NTT> struct Ring {
+    static constexpr int x_bytes = 32 * NTT * 128;              // token rows x 64 bf16
+    static constexpr int stage = kStageW + kStageS + x_bytes;
+    static constexpr int count = kLdsBytes / stage;
+    static_assert(count >= 4 && count <= 8, "ring depth");
+};
+
+// Waits until at most r (<= R) stages of L loads each are still in flight.
+template <int L, int R>
+__device__ __forceinline__ void wait_stages(int r) {
+    if constexpr (R == 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (r >= R) wait_vmcnt<R * L>();
+        else wait_stages<L, R - 1>(r);
+    }
+}
 
 // Byte offset of 16-byte chunk `chunk` (0..7) of token row `row` (128 B) in
 // the token tile (see the swizzle above).
@@ -80,9 +102,10 @@ __device__ __forceinline__ int xswz(int row, int chunk) { return row * 128 + ((c
 
 template <int MODE>
 __global__ __launch_bounds__(kGThreads) void ffn_grouped_kernel(FfnArgs a) {
-    __shared__ __align__(16) uint8_t lds[kStages][kStageBytes];
+    __shared__ __align__(16) uint8_t lds[kLdsBytes];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int N = MODE == 0 ? a.f : a.d;
     const int K = MODE == 0 ? a.d : a.f;
     const int NT = MODE == 0 ? a.f / (kGN / 2) : a.d / kGN;
@@ -140,8 +163,8 @@ __global__ __launch_bounds__(kGThreads) void ffn_grouped_kernel(FfnArgs a) {
         return;
     }
 
-    // ---- load roles of this lane (per stage: 2 weight, 1 scale, 2 token
-    // instructions per wave)
+    // ---- load roles of this lane (per stage: 2 weight and 2 token
+    // instructions per wave, and one scale instruction by wave 0)
     auto tile_base = [&](int tt, int& mat) {     // layout tile index of workgroup tile tt (0..31)
         mat = 2;
         int tile = nt * (kGN / 16) + tt;
@@ -158,10 +181,10 @@ __global__ __launch_bounds__(kGThreads) void ffn_grouped_kernel(FfnArgs a) {
         const size_t blk = tile_base(4 * wave + 2 * i + (lane >> 5), mat);
         wsrc[i] = a.codes[mat] + blk * 64 * 16 + (lane & 31) * 16;
     }
-    const uint8_t* ssrc;         // lanes 0..7: scale bytes 16 (lane & 1) .. +16 of tile 4w + (lane >> 1)
+    const uint8_t* ssrc;         // wave 0: scale bytes 16 (lane & 1) .. +16 of tile lane >> 1
     {
         int mat;
-        const size_t blk = tile_base(4 * wave + ((lane >> 1) & 3), mat);
+        const size_t blk = tile_base(lane >> 1, mat);
         ssrc = a.scales[mat] + blk * 64 + 16 * (lane & 1);
     }
     const uint16_t* xsrc[2];     // token row 16w + 8i + (lane >> 3), global chunk for LDS chunk lane & 7
@@ -177,15 +200,17 @@ __global__ __launch_bounds__(kGThreads) void ffn_grouped_kernel(FfnArgs a) {
     // that own them (rows 16w .. 16w+15) copy no token rows at all.
     const int ntt = __builtin_amdgcn_readfirstlane(ceil_div(nvalid, 32));
     const bool x_live = 16 * wave < 32 * ntt;
-    auto issue = [&](int s) {    // stage s -> LDS buffer s % kStages
-        uint8_t* base = lds[s % kStages];
+    // stage s of a ring of NST stages of SB bytes -> LDS buffer s % NST
+    auto issue = [&](int s, auto nst_c, auto sb_c) {
+        constexpr int NST = decltype(nst_c)::value, SB = decltype(sb_c)::value;
+        uint8_t* base = lds + (s % NST) * SB;
         const size_t half = static_cast<size_t>(s >> 1) * 1024 + (s & 1) * 512;
 #pragma unroll
         for (int i = 0; i < 2; ++i)
             __builtin_amdgcn_global_load_lds(wsrc[i] + half, (lds_void*)(base + (4 * wave + 2 * i) * 512), 16, 0, 0);
-        if (lane < 8)
+        if (wave == 0)     // all 32 tiles' scale bytes of the stage: one 1 KB copy
             __builtin_amdgcn_global_load_lds(ssrc + (s >> 1) * 64 + (s & 1) * 32,
-                                             (lds_void*)(base + kStageW + 4 * wave * 32), 16, 0, 0);
+                                             (lds_void*)(base + kStageW), 16, 0, 0);
         if (x_live) {
 #pragma unroll
             for (int i = 0; i < 2; ++i)
@@ -210,21 +235,26 @@ __global__ __launch_bounds__(kGThreads) void ffn_grouped_kernel(FfnArgs a) {
 
     auto kloop = [&](auto ntt_c) {
         constexpr int NTT = decltype(ntt_c)::value;
+        constexpr int NST = Ring<NTT>::count, SB = Ring<NTT>::stage;
+        const auto nst_c = std::integral_constant<int, NST>{};
+        const auto sb_c = std::integral_constant<int, SB>{};
+        for (int s = 0; s < NST - 1 && s < S; ++s) issue(s, nst_c, sb_c);
         for (int s = 0; s < S; ++s) {
-            // stage s is in LDS once at most the two younger stages are in
-            // flight (each wave counts its own loads per stage)
-            if (x_live) {
-                if (s + 2 < S) wait_vmcnt<2 * kLoadsPerStage>();
-                else if (s + 1 < S) wait_vmcnt<kLoadsPerStage>();
-                else wait_vmcnt<0>();
+            // stage s is in LDS once at most the younger stages issued so far
+            // (up to NST - 2) are in flight; each wave counts its own loads
+            const int younger = min(NST - 2, S - 1 - s);
+            if (wave == 0) {
+                if (x_live) wait_stages<5, NST - 2>(younger);
+                else wait_stages<3, NST - 2>(younger);
             } else {
-                if (s + 2 < S) wait_vmcnt<2 * kLoadsPerStageNoX>();
-                else if (s + 1 < S) wait_vmcnt<kLoadsPerStageNoX>();
-                else wait_vmcnt<0>();
+                if (x_live) wait_stages<4, NST - 2>(younger);
+                else wait_stages<2, NST - 2>(younger);
             }
+            // one barrier: every wave's copy of stage s is visible, and every
+            // wave is done with stage s - 1, whose buffer stage s + NST - 1 takes
             __builtin_amdgcn_s_barrier();
-            if (s + 3 < S) issue(s + 3);
-            const uint8_t* wb = lds[s % kStages];
+            if (s + NST - 1 < S) issue(s + NST - 1, nst_c, sb_c);
+            const uint8_t* wb = lds + (s % NST) * SB;
             const uint8_t* sb = wb + kStageW;
             const uint8_t* xb = sb + kStageS;
             // weight operand first, then the token fragments one sub-step
@@ -262,9 +292,6 @@ __global__ __launch_bounds__(kGThreads) void ffn_grouped_kernel(FfnArgs a) {
         }
     };
 
-    issue(0);
-    issue(1);
-    issue(2);
     switch (ntt) {
         case 1: kloop(std::integral_constant<int, 1>{}); break;
         case 2: kloop(std::integral_constant<int, 2>{}); break;
