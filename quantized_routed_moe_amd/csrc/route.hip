@@ -8,7 +8,7 @@
 // Kernels:
 //   router_rows_kernel  small T: one workgroup per expert streams W_r[e] once
 //                       and dots it with every token (T <= kRowsMaxT).
-//   router_mfma_kernel  large T: fp32 MFMA tiles, 16 tokens x 16 experts per
+//   router_mfma_kernel  large T: fp32 MFMA tiles, 32 tokens x 16 experts per
 //                       workgroup, eight waves splitting K.
 //   topk_kernel         one wave64 per token, lane = expert.
 #include "common.hpp"
@@ -81,62 +81,90 @@ __global__ __launch_bounds__(kRowsThreads) void router_rows_kernel(
     router_rows_block(x, wr, bias, logits, blockIdx.x, blockIdx.y * kRowsMaxT, T, d, E);
 }
 
-// Large-T router.  Workgroup = 8 waves = 16 tokens x 16 experts; the waves
-// split K and their partial tiles are summed in LDS in wave order.  fp32 MFMA
-// 16x16x4: in MFMA s of a 16-wide K step, lane group g (= lane / 16) supplies
-// element k0 + 4g + s, so each lane reads 4 consecutive floats of W_r and 4
-// consecutive bf16 of x per step.  A wave issues the loads of kRouterUnroll
-// steps before their MFMAs; the loads are unconditional (addresses clamped,
-// values masked), which keeps every load of a batch in flight at once.
+// Large-T router.  Workgroup = 8 waves = 32 tokens x 16 experts, one
+// workgroup per CU at T = 2048, E = 64; the waves split K eight ways and their
+// partial tiles are summed in LDS in wave order.  fp32 MFMA 16x16x4 (the
+// router stays in float32): in MFMA s of a 16-wide K step, lane group g (=
+// lane / 16) supplies element k0 + 4g + s, so a lane reads 4 consecutive
+// floats of W_r and 4 consecutive bf16 of each of its two token rows per
+// step; both token sub-tiles share the W_r operand.  Loads run one batch of
+// kRouterUnroll steps ahead of the multiplies (two register sets); they are
+// unconditional (addresses clamped, values masked), so each batch's loads
+// are in flight together.
 constexpr int kRouterWaves = 8;
-constexpr int kRouterUnroll = 16;
+constexpr int kRouterUnroll = 8;
+constexpr int kRouterTokens = 32;
 
 __global__ __launch_bounds__(kRouterWaves * 64) void router_mfma_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ bias,
     float* __restrict__ logits, int T, int d, int E) {
-    __shared__ __align__(16) f32x4 red[kRouterWaves][kWave];
+    __shared__ __align__(16) f32x4 red[kRouterWaves][2][kWave];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int t0 = blockIdx.x * 16, e0 = blockIdx.y * 16;
+    const int t0 = blockIdx.x * kRouterTokens, e0 = blockIdx.y * 16;
     const int row = lane & 15, g = lane >> 4;
-    const int tok = t0 + row, ex = e0 + row;
-    const bool tok_ok = tok < T, ex_ok = ex < E;
-    const uint16_t* xr = x + static_cast<size_t>(tok_ok ? tok : 0) * d + 4 * g;
+    const int ex = e0 + row;
+    const bool ex_ok = ex < E;
+    const uint16_t* xr[2];
+    bool tok_ok[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int tok = t0 + 16 * h + row;
+        tok_ok[h] = tok < T;
+        xr[h] = x + static_cast<size_t>(tok_ok[h] ? tok : 0) * d + 4 * g;
+    }
     const float* wrow = wr + static_cast<size_t>(ex_ok ? ex : 0) * d + 4 * g;
     const int S = d / 16;
     const int s_beg = (S * wave) / kRouterWaves, s_end = (S * (wave + 1)) / kRouterWaves;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int sb = s_beg; sb < s_end; sb += kRouterUnroll) {
-        float4 wv[kRouterUnroll];
-        u32x2 xv[kRouterUnroll];
+    f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    float4 wv[2][kRouterUnroll];
+    u32x2 xv[2][kRouterUnroll][2];
+    auto load = [&](int buf, int sb) {
 #pragma unroll
         for (int u = 0; u < kRouterUnroll; ++u) {
-            const int s = min(sb + u, s_end - 1);
-            wv[u] = *reinterpret_cast<const float4*>(wrow + 16 * s);
-            xv[u] = *reinterpret_cast<const u32x2*>(xr + 16 * s);
+            const int s = max(min(sb + u, s_end - 1), 0);
+            wv[buf][u] = *reinterpret_cast<const float4*>(wrow + 16 * s);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) xv[buf][u][h] = *reinterpret_cast<const u32x2*>(xr[h] + 16 * s);
         }
+    };
+    auto mul = [&](int buf, int sb) {
 #pragma unroll
         for (int u = 0; u < kRouterUnroll; ++u) {
             // the lane's A value (its token row) and B value (its expert
             // column) are masked separately
             const bool ok = sb + u < s_end;
-            const float4 w = ok && ex_ok ? wv[u] : make_float4(0.f, 0.f, 0.f, 0.f);
-            const u32x2 xx = ok && tok_ok ? xv[u] : u32x2{0u, 0u};
-            // A = x (16 tokens x 4), B = W_r^T (4 x 16 experts)
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16lo(xx[0]), w.x, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16hi(xx[0]), w.y, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16lo(xx[1]), w.z, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16hi(xx[1]), w.w, acc, 0, 0, 0);
-        }
-    }
-    red[wave][lane] = acc;
-    __syncthreads();
-    // acc[i] of lane l = C[token 4(l/16) + i][expert l%16]
-    for (int idx = threadIdx.x; idx < 256; idx += kRouterWaves * 64) {
-        const int l = idx >> 2, i = idx & 3;
-        float v = red[0][l][i];
+            const float4 w = ok && ex_ok ? wv[buf][u] : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-        for (int w = 1; w < kRouterWaves; ++w) v += red[w][l][i];
-        const int t = t0 + 4 * (l >> 4) + i, e = e0 + (l & 15);
+            for (int h = 0; h < 2; ++h) {
+                const u32x2 xx = ok && tok_ok[h] ? xv[buf][u][h] : u32x2{0u, 0u};
+                // A = x (16 tokens x 4), B = W_r^T (4 x 16 experts)
+                acc[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16lo(xx[0]), w.x, acc[h], 0, 0, 0);
+                acc[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16hi(xx[0]), w.y, acc[h], 0, 0, 0);
+                acc[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16lo(xx[1]), w.z, acc[h], 0, 0, 0);
+                acc[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16hi(xx[1]), w.w, acc[h], 0, 0, 0);
+            }
+        }
+    };
+    // two register sets: batch b + 1 loads while batch b multiplies (the
+    // loop is unrolled by two so that every set index is a constant)
+    load(0, s_beg);
+    for (int sb = s_beg; sb < s_end; sb += 2 * kRouterUnroll) {
+        if (sb + kRouterUnroll < s_end) load(1, sb + kRouterUnroll);
+        mul(0, sb);
+        if (sb + kRouterUnroll >= s_end) break;
+        if (sb + 2 * kRouterUnroll < s_end) load(0, sb + 2 * kRouterUnroll);
+        mul(1, sb + kRouterUnroll);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) red[wave][h][lane] = acc[h];
+    __syncthreads();
+    // acc[h][i] of lane l = C[token 16h + 4(l/16) + i][expert l%16]
+    for (int idx = threadIdx.x; idx < 2 * 256; idx += kRouterWaves * 64) {
+        const int h = idx >> 8, l = (idx >> 2) & 63, i = idx & 3;
+        float v = red[0][h][l][i];
+#pragma unroll
+        for (int w = 1; w < kRouterWaves; ++w) v += red[w][h][l][i];
+        const int t = t0 + 16 * h + 4 * (l >> 4) + i, e = e0 + (l & 15);
         if (t < T && e < E) logits[static_cast<size_t>(t) * E + e] = v + (bias ? bias[e] : 0.f);
     }
 }
@@ -164,7 +192,7 @@ hipError_t launch_route(const moe_shape& s, const uint16_t* x, const float* wr, 
             const hipError_t err = launch_router_logits(s, x, wr, bias, logits, st);
             if (err != hipSuccess) return err;
         } else {
-            router_mfma_kernel<<<dim3(ceil_div(s.T, 16), ceil_div(s.E, 16)), kRouterWaves * 64, 0, st>>>(
+            router_mfma_kernel<<<dim3(ceil_div(s.T, kRouterTokens), ceil_div(s.E, 16)), kRouterWaves * 64, 0, st>>>(
                 x, wr, bias, logits, s.T, s.d, s.E);
         }
         hipError_t err = hipGetLastError();
