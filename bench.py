@@ -43,7 +43,9 @@ METRIC = "MoE layer tokens/s; decode weight-stream GB/s; prefill expert TFLOP/s"
 # different number of experts each step: theirs is the average of the counted
 # steps.  Must be re-measured (or removed) whenever an FFN kernel changes.
 MEASURED_FFN_TRAFFIC = {
-    3: (2 * (284239.3 + 166545.8 + 12.0) + (16419.0 + 65622.5)) * 1024,
+    1: (2 * (8794.0 + 4438.7) + (8.0 + 32.0)) * 1024,
+    3: (2 * (284086.7 + 166739.9 + 12.0) + (16410.0 + 65572.7)) * 1024,
+    4: (2 * (27874.1 + 14211.8) + (128.0 + 512.0)) * 1024,
 }
 
 MX_BYTES_PER_EXPERT = lambda d, f: 3 * d * f // 2 + 3 * d * f // 32      # codes + e8m0 scales
