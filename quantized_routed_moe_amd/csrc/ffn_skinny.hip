@@ -117,7 +117,7 @@ __device__ __forceinline__ void skinny_body(const FfnArgs& a, const Item& it, in
     const bool fused = MODE == 1 && a.fuse_combine;
     uint8_t* mine = region[wave];
     const uint8_t* brow = mine + (col < RB ? col : RB - 1) * kBRowBytes;
-    constexpr bool b_first = MODE == 1 || PERM_LDS;
+    constexpr bool b_first = MODE == 1;
 
     WTile wt[NM];
 #pragma unroll
@@ -337,8 +337,9 @@ __device__ __forceinline__ void wave_dispatch(SmallRouting& r, int n, int E) {
 // whole batch from the logits itself (top-k by one wave per token, then the
 // one-wave counting sort: a few hundred instructions), so no routing launch
 // and no read of routing results from HBM precede its weight loads.
-// Workgroup 0 also writes ids, w, offsets, perm and inv and zeroes `out` for
-// the down launch's scatter-add, after its own item.  Arithmetic as topk_kernel and the dispatch
+// Workgroup 0 also writes ids, w, offsets, perm and inv after its own item,
+// and every workgroup zeroes its share of `out` for the down launch's
+// scatter-add.  Arithmetic as topk_kernel and the dispatch
 // kernel, so every output is identical.
 template <int FMT, int RB>
 __global__ __launch_bounds__(kGateUpWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void ffn_gate_up_routed_kernel(FfnArgs a) {
@@ -356,6 +357,8 @@ __global__ __launch_bounds__(kGateUpWaves * 64) __attribute__((amdgpu_waves_per_
         lo = r.offsets[lane];
         hi = r.offsets[lane + 1];
     }
+    // items blockIdx.x, + gridDim.x, ... (a grid of resident workgroups, so
+    // the routing above is done once per workgroup, not once per item)
     const int NT = a.f / 16;
     run_item<FMT, 0, kGateUpWaves, RB, true>(a, pick_item(lo, hi, sl, blockIdx.x / NT), (blockIdx.x % NT) * 16, r.perm);
     // after the item: no stores ahead of its loads (the down launch is the
@@ -368,10 +371,14 @@ __global__ __launch_bounds__(kGateUpWaves * 64) __attribute__((amdgpu_waves_per_
             a.inv_out[i] = r.inv[i];
         }
         for (int i = tid; i <= E; i += blockDim.x) a.offsets_out[i] = r.offsets[i];
-        if (a.fuse_combine) {
-            float4* o4 = reinterpret_cast<float4*>(a.out);
-            for (int i = tid; i < T * a.d / 4; i += blockDim.x) o4[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
+    }
+    if (a.fuse_combine) {       // every workgroup zeroes its share of out
+        const int total = T * a.d / 4;
+        const int chunk = ceil_div(total, static_cast<int>(gridDim.x));
+        const int end = min(total, (static_cast<int>(blockIdx.x) + 1) * chunk);
+        float4* o4 = reinterpret_cast<float4*>(a.out);
+        for (int i = static_cast<int>(blockIdx.x) * chunk + tid; i < end; i += blockDim.x)
+            o4[i] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
 }
 
@@ -416,6 +423,9 @@ bool ffn_uses_grouped(const moe_shape& s, int fmt) {
 }
 
 bool routed_ffn_supported(const moe_shape& s, int fmt) {
+    // one workgroup per (expert, tile) item, each routing the whole batch:
+    // past a few tokens the items of inactive experts (which still route
+    // before they find out) cost more than the separate routing launches
     return s.T <= kGateUpWaves && s.T * s.k <= kRoutedMaxPairs && !ffn_uses_grouped(s, fmt);
 }
 

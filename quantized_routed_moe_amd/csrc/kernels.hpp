@@ -44,7 +44,7 @@ hipError_t launch_dispatch(const moe_shape& s, const int32_t* ids, int32_t* offs
 hipError_t launch_ffn(const moe_shape& s, int fmt, const FfnArgs& a, hipStream_t st);
 bool grouped_supported(const moe_shape& s, int fmt);
 bool ffn_uses_grouped(const moe_shape& s, int fmt);
-// Router logits only (no top-k), T <= 32.
+// Router logits only (no top-k), by the per-expert row kernel (small T).
 hipError_t launch_router_logits(const moe_shape& s, const uint16_t* x, const float* wr, const float* bias,
                                 float* logits, hipStream_t st);
 // moe_layer for small batches: the skinny FFN whose gate/up launch routes the

@@ -236,13 +236,14 @@ def test_power_of_two_scaling(c):
 
 @pytest.mark.parametrize("shape", [(1, 256, 8, 1, 128), (3, 512, 16, 2, 256), (8, 256, 64, 3, 128),
                                    (5, 384, 8, 8, 160), (7, 1024, 32, 2, 512), (1, 256, 64, 64, 128),
-                                   (8, 256, 64, 16, 128)])
+                                   (16, 256, 64, 2, 128), (32, 256, 16, 2, 128), (12, 384, 8, 1, 160),
+                                   (20, 256, 32, 3, 128), (8, 256, 64, 16, 128), (33, 256, 16, 2, 128)])
 @pytest.mark.parametrize("fmt", ["mxfp4", "q2"])
 def test_layer_small_T_fused_path_equals_steps(shape, fmt):
     """moe_layer's small-batch path (T <= 8, T*k <= 64: logits-only router
     launch, routing inside every gate/up workgroup, scatter-add combine for
-    k <= 2) gives exactly what the four entry points give; the last shape
-    (T*k = 128) takes the general path."""
+    k <= 2) gives exactly what the four entry points give; the shapes with
+    T > 8 or T*k > 64 take the general path."""
     T, d, E, k, f = shape
     case = synthetic.make_case(T, d, E, k, f, fmt, seed=zlib.crc32(repr(shape).encode()) % 997, zipf=1.1)
     dc = device_case(case)
