@@ -306,8 +306,24 @@ int moe_layer(const moe_shape* shape, const uint16_t* x, const float* w_router, 
         if ((rc = hip_rc(qrmoe::launch_ffn_routed(s, experts->gate.fmt, a, stream))) != MOE_OK) return rc;
         return fuse_combine ? MOE_OK : do_combine(s, y, inv, topk_w, out, stream);
     }
-    if ((rc = do_route(s, x, w_router, bias, logits, topk_ids, topk_w, stream)) != MOE_OK) return rc;
-    if ((rc = do_dispatch(s, topk_ids, offsets, perm, inv, ws, stream)) != MOE_OK) return rc;
+    // Other batches: routing (top-k and dispatch in one workgroup for up to
+    // 16 tokens), the FFN, and the combine -- on the skinny path with k <= 2
+    // a scatter-add inside the down launch (out zeroed by the gate/up launch).
+    if (qrmoe::small_route_supported(s)) {
+        if ((rc = hip_rc(qrmoe::launch_small_route(s, x, w_router, bias, logits, topk_ids, topk_w, offsets, perm,
+                                                   inv, stream))) != MOE_OK)
+            return rc;
+    } else {
+        if ((rc = do_route(s, x, w_router, bias, logits, topk_ids, topk_w, stream)) != MOE_OK) return rc;
+        if ((rc = do_dispatch(s, topk_ids, offsets, perm, inv, ws, stream)) != MOE_OK) return rc;
+    }
+    if (s.k <= 2 && !qrmoe::ffn_uses_grouped(s, experts->gate.fmt)) {
+        FfnArgs a = ffn_args(s, x, experts, offsets, perm, y, ws);
+        a.topk_w = topk_w;
+        a.out = out;
+        a.fuse_combine = 1;
+        return hip_rc(qrmoe::launch_ffn(s, experts->gate.fmt, a, stream));
+    }
     if ((rc = do_ffn(s, x, experts, offsets, perm, y, ws, stream)) != MOE_OK) return rc;
     return do_combine(s, y, inv, topk_w, out, stream);
 }

@@ -288,7 +288,20 @@ __device__ __forceinline__ void run_item(const FfnArgs& a, const Item& it, int n
     skinny_body<FMT, MODE, KW, RB, PERM_LDS>(a, it, n0, perm);
 }
 
-// The last workgroup of the down launch zeroes the y rows past offsets[E].
+// Every workgroup zeroes its share of out (the fused combine's scatter-add
+// target), after its item.
+__device__ __forceinline__ void zero_out_share(const FfnArgs& a) {
+    const int total = a.T * a.d / 4;
+    const int chunk = ceil_div(total, static_cast<int>(gridDim.x));
+    const int end = min(total, (static_cast<int>(blockIdx.x) + 1) * chunk);
+    float4* o4 = reinterpret_cast<float4*>(a.out);
+    for (int i = static_cast<int>(blockIdx.x) * chunk + static_cast<int>(threadIdx.x); i < end;
+         i += static_cast<int>(blockDim.x))
+        o4[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+// The last workgroup of the down launch zeroes the y rows past offsets[E];
+// with the fused combine the gate/up launch zeroes out.
 template <int FMT, int MODE, int KW, int RB>
 __global__ __launch_bounds__(KW * 64) __attribute__((amdgpu_waves_per_eu(4))) void ffn_skinny_kernel(FfnArgs a) {
     if (MODE == 1 && blockIdx.x == gridDim.x - 1) {
@@ -297,41 +310,10 @@ __global__ __launch_bounds__(KW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
     }
     const int NT = (MODE == 0 ? a.f : a.d) / 16;
     run_item<FMT, MODE, KW, RB>(a, find_item(a, blockIdx.x / NT), (blockIdx.x % NT) * 16, a.perm);
+    if (MODE == 0 && a.fuse_combine) zero_out_share(a);
 }
 
 // ------------------------------------------------------------ routed gate/up
-
-// Routing of a batch of at most kRoutedMaxPairs pairs, held in LDS.
-constexpr int kRoutedMaxPairs = 64;
-struct SmallRouting {
-    int32_t ids[kRoutedMaxPairs];
-    float w[kRoutedMaxPairs];
-    int32_t perm[kRoutedMaxPairs];
-    int32_t inv[kRoutedMaxPairs];
-    int32_t offsets[kMaxExperts + 1];
-};
-
-// Stable counting sort of n <= 64 pairs by expert id, by one wave: pair p
-// (lane p) goes to row (pairs with a smaller id) + (pairs with its id and a
-// smaller index); offsets[x] = pairs with an id below x.  The same
-// permutation as the dispatch kernel's for valid ids.
-__device__ __forceinline__ void wave_dispatch(SmallRouting& r, int n, int E) {
-    const int lane = threadIdx.x & 63;
-    const int e = lane < n ? r.ids[lane] : 0x7fffffff;
-    int before = 0, tie = 0, below_lane = 0;
-    for (int q = 0; q < n; ++q) {
-        const int eq = lane_value(e, q);
-        before += eq < e;
-        tie += (eq == e) & (q < lane);
-        below_lane += eq < lane;
-    }
-    if (lane < n) {
-        r.perm[before + tie] = lane;
-        r.inv[lane] = before + tie;
-    }
-    if (lane < E) r.offsets[lane] = below_lane;
-    if (lane == 0) r.offsets[E] = n;
-}
 
 // Gate/up launch of moe_layer for small batches: every workgroup routes the
 // whole batch from the logits itself (top-k by one wave per token, then the
@@ -372,14 +354,7 @@ __global__ __launch_bounds__(kGateUpWaves * 64) __attribute__((amdgpu_waves_per_
         }
         for (int i = tid; i <= E; i += blockDim.x) a.offsets_out[i] = r.offsets[i];
     }
-    if (a.fuse_combine) {       // every workgroup zeroes its share of out
-        const int total = T * a.d / 4;
-        const int chunk = ceil_div(total, static_cast<int>(gridDim.x));
-        const int end = min(total, (static_cast<int>(blockIdx.x) + 1) * chunk);
-        float4* o4 = reinterpret_cast<float4*>(a.out);
-        for (int i = static_cast<int>(blockIdx.x) * chunk + tid; i < end; i += blockDim.x)
-            o4[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
+    if (a.fuse_combine) zero_out_share(a);
 }
 
 // ------------------------------------------------------------ launch

@@ -21,8 +21,9 @@ struct FfnArgs {
     uint16_t* act;                // bf16 [T*k][f] (workspace)
     float* y;                     // fp32 [T*k][d]
     uint32_t* status;             // workspace header
-    // moe_layer with k <= 2 only: the down projection also scatter-adds
-    // w[p] * y[r] into out (zeroed beforehand), replacing the combine kernel
+    // moe_layer with k <= 2 on the skinny path only: the gate/up launch
+    // zeroes out and the down projection scatter-adds w[p] * y[r] into it
+    // instead of writing y, replacing the combine kernel
     const float* topk_w;          // [T*k]
     float* out;                   // [T][d]
     int fuse_combine;
@@ -47,6 +48,12 @@ bool ffn_uses_grouped(const moe_shape& s, int fmt);
 // Router logits only (no top-k), by the per-expert row kernel (small T).
 hipError_t launch_router_logits(const moe_shape& s, const uint16_t* x, const float* wr, const float* bias,
                                 float* logits, hipStream_t st);
+// Router logits + top-k + dispatch of a small batch, the last two in one
+// workgroup (T <= 16, T*k <= 64).
+bool small_route_supported(const moe_shape& s);
+hipError_t launch_small_route(const moe_shape& s, const uint16_t* x, const float* wr, const float* bias,
+                              float* logits, int32_t* ids, float* w, int32_t* offsets, int32_t* perm,
+                              int32_t* inv, hipStream_t st);
 // moe_layer for small batches: the skinny FFN whose gate/up launch routes the
 // batch from a.logits (see FfnArgs).
 bool routed_ffn_supported(const moe_shape& s, int fmt);

@@ -178,6 +178,46 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
               w + static_cast<size_t>(t) * k, E, k);
 }
 
+// Top-k and dispatch of a small batch (T <= kSmallRouteT tokens, T*k <=
+// kRoutedMaxPairs pairs) in one workgroup: one wave per token for the top-k,
+// then the one-wave stable counting sort in LDS.  The arithmetic of
+// topk_kernel and of the dispatch kernel (whose permutation the counting sort
+// reproduces for valid ids, and top-k ids are always valid), so every output
+// is identical; one launch instead of two.
+constexpr int kSmallRouteT = 16;
+
+__global__ __launch_bounds__(kSmallRouteT * 64) void small_route_kernel(
+    const float* __restrict__ logits, int32_t* __restrict__ ids, float* __restrict__ w,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv, int T, int E, int k) {
+    __shared__ SmallRouting r;
+    const int tid = threadIdx.x, wave = tid >> 6;
+    const int n = T * k;
+    if (wave < T) topk_wave(logits + static_cast<size_t>(wave) * E, r.ids + wave * k, r.w + wave * k, E, k);
+    __syncthreads();
+    if (wave == 0) wave_dispatch(r, n, E);
+    __syncthreads();
+    for (int i = tid; i < n; i += blockDim.x) {
+        ids[i] = r.ids[i];
+        w[i] = r.w[i];
+        perm[i] = r.perm[i];
+        inv[i] = r.inv[i];
+    }
+    for (int i = tid; i <= E; i += blockDim.x) offsets[i] = r.offsets[i];
+}
+
+bool small_route_supported(const moe_shape& s) { return s.T <= kSmallRouteT && s.T * s.k <= kRoutedMaxPairs; }
+
+hipError_t launch_small_route(const moe_shape& s, const uint16_t* x, const float* wr, const float* bias,
+                              float* logits, int32_t* ids, float* w, int32_t* offsets, int32_t* perm,
+                              int32_t* inv, hipStream_t st) {
+    if (wr) {
+        const hipError_t err = launch_router_logits(s, x, wr, bias, logits, st);
+        if (err != hipSuccess) return err;
+    }
+    small_route_kernel<<<1, kSmallRouteT * 64, 0, st>>>(logits, ids, w, offsets, perm, inv, s.T, s.E, s.k);
+    return hipGetLastError();
+}
+
 hipError_t launch_router_logits(const moe_shape& s, const uint16_t* x, const float* wr, const float* bias,
                                 float* logits, hipStream_t st) {
     dim3 grid(s.E, ceil_div(s.T, kRowsMaxT));

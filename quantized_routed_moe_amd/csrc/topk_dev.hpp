@@ -1,5 +1,6 @@
-// Top-k of one token by one wave, shared by the top-k kernel and the
-// skinny FFN's in-workgroup routing (moe_layer, small batches).
+// Top-k of one token by one wave, and the routing of a small batch in LDS
+// (top-k + stable counting sort), shared by the top-k kernel, the fused
+// small-batch routing kernel and the skinny FFN's in-workgroup routing.
 #pragma once
 
 #include "common.hpp"
@@ -41,6 +42,38 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ lrow, int32_
         ids[lane] = my_sel;
         w[lane] = ex / sum;
     }
+}
+
+// Routing of a batch of at most kRoutedMaxPairs pairs, held in LDS.
+constexpr int kRoutedMaxPairs = 64;
+struct SmallRouting {
+    int32_t ids[kRoutedMaxPairs];
+    float w[kRoutedMaxPairs];
+    int32_t perm[kRoutedMaxPairs];
+    int32_t inv[kRoutedMaxPairs];
+    int32_t offsets[kMaxExperts + 1];
+};
+
+// Stable counting sort of n <= 64 pairs by expert id, by one wave: pair p
+// (lane p) goes to row (pairs with a smaller id) + (pairs with its id and a
+// smaller index); offsets[x] = pairs with an id below x.  The same
+// permutation as the dispatch kernel's for valid ids.
+__device__ __forceinline__ void wave_dispatch(SmallRouting& r, int n, int E) {
+    const int lane = threadIdx.x & 63;
+    const int e = lane < n ? r.ids[lane] : 0x7fffffff;
+    int before = 0, tie = 0, below_lane = 0;
+    for (int q = 0; q < n; ++q) {
+        const int eq = lane_value(e, q);
+        before += eq < e;
+        tie += (eq == e) & (q < lane);
+        below_lane += eq < lane;
+    }
+    if (lane < n) {
+        r.perm[before + tie] = lane;
+        r.inv[lane] = before + tie;
+    }
+    if (lane < E) r.offsets[lane] = below_lane;
+    if (lane == 0) r.offsets[E] = n;
 }
 
 }  // namespace qrmoe
