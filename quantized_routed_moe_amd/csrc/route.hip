@@ -8,8 +8,9 @@
 // Kernels:
 //   router_rows_kernel  small T: one workgroup per expert streams W_r[e] once
 //                       and dots it with every token (T <= kRowsMaxT).
-//   router_mfma_kernel  large T: fp32 MFMA tiles, 32 tokens x 16 experts per
-//                       workgroup, eight waves splitting K.
+//   router_mfma_kernel  large T: 32 tokens x 16 experts per workgroup, eight
+//                       waves splitting K; float32 scores from three bf16
+//                       parts of W_r on the bf16 matrix cores.
 //   topk_kernel         one wave64 per token, lane = expert.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -83,17 +84,50 @@ __global__ __launch_bounds__(kRowsThreads) void router_rows_kernel(
 
 // Large-T router.  Workgroup = 8 waves = 32 tokens x 16 experts, one
 // workgroup per CU at T = 2048, E = 64; the waves split K eight ways and their
-// partial tiles are summed in LDS in wave order.  fp32 MFMA 16x16x4 (the
-// router stays in float32): in MFMA s of a 16-wide K step, lane group g (=
-// lane / 16) supplies element k0 + 4g + s, so a lane reads 4 consecutive
-// floats of W_r and 4 consecutive bf16 of each of its two token rows per
-// step; both token sub-tiles share the W_r operand.  Loads run one batch of
-// kRouterUnroll steps ahead of the multiplies (two register sets); they are
+// partial tiles are summed in LDS in wave order.
+//
+// The scores stay float32 but run on the bf16 matrix cores: x is bf16
+// already, and each W_r element is split in registers into three bf16 parts
+// hi + mid + lo (hi = bf16(w), mid = bf16(w - hi), lo = bf16(w - hi - mid);
+// each subtraction is exact in fp32 and each part takes the next 8
+// significant bits, so the parts sum to w within 2^-24 relative).  A bf16 x
+// bf16 product is exact in fp32, so x * w is formed exactly as three
+// products and only the fp32 accumulation of the 16x16x32 MFMAs rounds --
+// the accuracy of a float32 dot product at three bf16 MFMAs per K step of 32
+// instead of eight fp32 16x16x4 ones (a sixteenth of the bf16 rate each).
+//
+// In a K step of 32, lane group g (= lane / 16) supplies elements 8g .. 8g+7
+// of its token row (one 16-byte load) and of its expert row (two), so the
+// MFMA operands come straight from the loads.  Loads run one batch of
+// kRouterBatch steps ahead of the multiplies (two register sets); they are
 // unconditional (addresses clamped, values masked), so each batch's loads
 // are in flight together.
 constexpr int kRouterWaves = 8;
-constexpr int kRouterUnroll = 8;
+constexpr int kRouterBatch = 4;
 constexpr int kRouterTokens = 32;
+constexpr int kRouterStep = 32;
+
+// Splits eight floats into three bf16x8 parts whose sum is the floats to
+// within 2^-24 relative (see above), two elements per packed conversion
+// (round to nearest even).
+__device__ __forceinline__ void split3_bf16(const float4& a, const float4& b, bf16x8& hi, bf16x8& mid, bf16x8& lo) {
+    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    u32x4 ph, pm, pl;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const f32x2 w{v[2 * p], v[2 * p + 1]};
+        const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(w, bf16x2));
+        const f32x2 r1{w[0] - __uint_as_float(h << 16), w[1] - __uint_as_float(h & 0xffff0000u)};
+        const uint32_t m = __builtin_bit_cast(uint32_t, __builtin_convertvector(r1, bf16x2));
+        const f32x2 r2{r1[0] - __uint_as_float(m << 16), r1[1] - __uint_as_float(m & 0xffff0000u)};
+        ph[p] = h;
+        pm[p] = m;
+        pl[p] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r2, bf16x2));
+    }
+    hi = bf16x8_from_u32x4(ph);
+    mid = bf16x8_from_u32x4(pm);
+    lo = bf16x8_from_u32x4(pl);
+}
 
 __global__ __launch_bounds__(kRouterWaves * 64) void router_mfma_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ bias,
@@ -110,50 +144,53 @@ __global__ __launch_bounds__(kRouterWaves * 64) void router_mfma_kernel(
     for (int h = 0; h < 2; ++h) {
         const int tok = t0 + 16 * h + row;
         tok_ok[h] = tok < T;
-        xr[h] = x + static_cast<size_t>(tok_ok[h] ? tok : 0) * d + 4 * g;
+        xr[h] = x + static_cast<size_t>(tok_ok[h] ? tok : 0) * d + 8 * g;
     }
-    const float* wrow = wr + static_cast<size_t>(ex_ok ? ex : 0) * d + 4 * g;
-    const int S = d / 16;
+    const float* wrow = wr + static_cast<size_t>(ex_ok ? ex : 0) * d + 8 * g;
+    const int S = d / kRouterStep;
     const int s_beg = (S * wave) / kRouterWaves, s_end = (S * (wave + 1)) / kRouterWaves;
     f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    float4 wv[2][kRouterUnroll];
-    u32x2 xv[2][kRouterUnroll][2];
+    float4 wv[2][kRouterBatch][2];
+    u32x4 xv[2][kRouterBatch][2];
     auto load = [&](int buf, int sb) {
 #pragma unroll
-        for (int u = 0; u < kRouterUnroll; ++u) {
+        for (int u = 0; u < kRouterBatch; ++u) {
             const int s = max(min(sb + u, s_end - 1), 0);
-            wv[buf][u] = *reinterpret_cast<const float4*>(wrow + 16 * s);
+            wv[buf][u][0] = *reinterpret_cast<const float4*>(wrow + kRouterStep * s);
+            wv[buf][u][1] = *reinterpret_cast<const float4*>(wrow + kRouterStep * s + 4);
 #pragma unroll
-            for (int h = 0; h < 2; ++h) xv[buf][u][h] = *reinterpret_cast<const u32x2*>(xr[h] + 16 * s);
+            for (int h = 0; h < 2; ++h) xv[buf][u][h] = *reinterpret_cast<const u32x4*>(xr[h] + kRouterStep * s);
         }
     };
     auto mul = [&](int buf, int sb) {
 #pragma unroll
-        for (int u = 0; u < kRouterUnroll; ++u) {
-            // the lane's A value (its token row) and B value (its expert
-            // column) are masked separately
+        for (int u = 0; u < kRouterBatch; ++u) {
+            // Only the token operand is masked, on steps past the slice: a
+            // reloaded step then adds x = 0 times a finite weight.  Lanes
+            // of tokens >= T or experts >= E read clamped rows; their
+            // output rows and columns are never stored.
             const bool ok = sb + u < s_end;
-            const float4 w = ok && ex_ok ? wv[buf][u] : make_float4(0.f, 0.f, 0.f, 0.f);
+            bf16x8 hi, mid, lo;
+            split3_bf16(wv[buf][u][0], wv[buf][u][1], hi, mid, lo);
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const u32x2 xx = ok && tok_ok[h] ? xv[buf][u][h] : u32x2{0u, 0u};
-                // A = x (16 tokens x 4), B = W_r^T (4 x 16 experts)
-                acc[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16lo(xx[0]), w.x, acc[h], 0, 0, 0);
-                acc[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16hi(xx[0]), w.y, acc[h], 0, 0, 0);
-                acc[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16lo(xx[1]), w.z, acc[h], 0, 0, 0);
-                acc[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16hi(xx[1]), w.w, acc[h], 0, 0, 0);
+                const bf16x8 xx = ok ? bf16x8_from_u32x4(xv[buf][u][h]) : bf16x8_zero();
+                // A = x (16 tokens x 32), B = W_r^T (32 x 16 experts)
+                acc[h] = mfma16x16x32(xx, hi, acc[h]);
+                acc[h] = mfma16x16x32(xx, mid, acc[h]);
+                acc[h] = mfma16x16x32(xx, lo, acc[h]);
             }
         }
     };
     // two register sets: batch b + 1 loads while batch b multiplies (the
     // loop is unrolled by two so that every set index is a constant)
     load(0, s_beg);
-    for (int sb = s_beg; sb < s_end; sb += 2 * kRouterUnroll) {
-        if (sb + kRouterUnroll < s_end) load(1, sb + kRouterUnroll);
+    for (int sb = s_beg; sb < s_end; sb += 2 * kRouterBatch) {
+        if (sb + kRouterBatch < s_end) load(1, sb + kRouterBatch);
         mul(0, sb);
-        if (sb + kRouterUnroll >= s_end) break;
-        if (sb + 2 * kRouterUnroll < s_end) load(0, sb + 2 * kRouterUnroll);
-        mul(1, sb + kRouterUnroll);
+        if (sb + kRouterBatch >= s_end) break;
+        if (sb + 2 * kRouterBatch < s_end) load(0, sb + 2 * kRouterBatch);
+        mul(1, sb + kRouterBatch);
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) red[wave][h][lane] = acc[h];
