@@ -73,7 +73,8 @@ enum moe_status {
 /* Device status bits, OR-ed into the workspace header by the kernels. */
 enum moe_device_status_bits {
     MOE_DEV_BAD_EXPERT_ID = 1, /* a topk id outside [0, E) reached moe_dispatch */
-    MOE_DEV_BAD_SLOT = 2       /* slot_of_expert[e] outside [0, num_slots) for a routed e */
+    MOE_DEV_BAD_SLOT = 2,      /* slot_of_expert[e] outside [0, num_slots) for a routed e */
+    MOE_DEV_CHAIN_TIMEOUT = 4  /* prefill FFN: a down tile gave up waiting for its gate/up tiles */
 };
 
 typedef struct moe_shape {
@@ -179,8 +180,13 @@ typedef struct moe_experts {
 
 /* Workspace bytes moe_dispatch / moe_expert_ffn / moe_layer need for `shape`
    (a 256-byte header holding the device status word, then the bf16 SwiGLU
-   intermediate act[T*k][f]).  Returns 0 for an invalid shape.  The header
-   must be zeroed once before first use (moe_workspace_init does it). */
+   intermediate act[T*k][f], then, when f % 256 == 0, the ready flags of the
+   single-launch prefill FFN: 8 bytes per 128-row m-tile and 256 rows of f,
+   for the (T*k)/128 + min(E, T*k) m-tiles there can be, rounded up; every
+   launch writes a value of its own into them, so they never need clearing).
+   Returns 0 for an invalid shape.  The header must be zeroed once before
+   first use (moe_workspace_init does it).  A workspace serves one call at a
+   time: calls that overlap on one workspace race. */
 size_t moe_workspace_bytes(const moe_shape* shape);
 
 /* Clears the workspace header (device status word) on `stream`. */

@@ -33,6 +33,7 @@ MOE_ERR_DEVICE = -8
 
 MOE_DEV_BAD_EXPERT_ID = 1
 MOE_DEV_BAD_SLOT = 2
+MOE_DEV_CHAIN_TIMEOUT = 4
 
 MOE_FMT_MXFP4 = 1
 MOE_FMT_Q2G32 = 2

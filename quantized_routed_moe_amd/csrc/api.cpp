@@ -29,9 +29,11 @@ int check_shape(const moe_shape* s) {
     return MOE_OK;
 }
 
-size_t ffn_ws_bytes(const moe_shape& s) {
-    return kHeader + align256(static_cast<size_t>(s.T) * s.k * s.f * 2);
-}
+size_t act_bytes(const moe_shape& s) { return align256(static_cast<size_t>(s.T) * s.k * s.f * 2); }
+
+size_t flag_bytes(const moe_shape& s) { return align256(static_cast<size_t>(qrmoe::grouped_flag_count(s)) * 8); }
+
+size_t ffn_ws_bytes(const moe_shape& s) { return kHeader + act_bytes(s) + flag_bytes(s); }
 
 struct LayerCarve {
     size_t offsets, perm, inv, y, total;
@@ -120,6 +122,8 @@ FfnArgs ffn_args(const moe_shape& s, const uint16_t* x, const moe_experts* ex, c
         a.scales[i] = static_cast<const uint8_t*>(mats[i]->scales);
     }
     a.act = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + kHeader);
+    a.flags = flag_bytes(s) ? reinterpret_cast<unsigned long long*>(static_cast<char*>(ws) + kHeader + act_bytes(s))
+                            : nullptr;
     a.y = y;
     a.status = static_cast<uint32_t*>(ws);
     return a;

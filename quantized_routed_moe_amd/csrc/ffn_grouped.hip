@@ -60,6 +60,7 @@
 // measured ~1.5x slower).  Units are derived from offsets on the device.
 #include <type_traits>
 
+#include "chain.hpp"
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -100,10 +101,13 @@ __device__ __forceinline__ void wait_stages(int r) {
 // the token tile (see the swizzle above).
 __device__ __forceinline__ int xswz(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
 
-template <int MODE>
-__global__ __launch_bounds__(kGThreads) void ffn_grouped_kernel(FfnArgs a) {
-    __shared__ __align__(16) uint8_t lds[kLdsBytes];
-
+// One work unit (see Schedule above) on the workgroup's LDS ring `lds`.
+// CHAIN (both projections in one launch): a gate/up unit stores act with
+// device-scope stores and then raises flag `unit`; a down unit first waits
+// for the flags of every gate/up unit of its m-tile, then reads act with
+// device-scope loads (chain.hpp).
+template <int MODE, bool CHAIN>
+__device__ __forceinline__ void grouped_unit(const FfnArgs& a, int unit, unsigned long long tag, uint8_t* lds) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int N = MODE == 0 ? a.f : a.d;
@@ -129,7 +133,6 @@ __global__ __launch_bounds__(kGThreads) void ffn_grouped_kernel(FfnArgs a) {
     const int n_full = lane_value(incl, 63);
     const uint64_t has_part = __ballot(rem > 0);
     const int total_units = (n_full + __popcll(has_part)) * NT;
-    const int unit = blockIdx.x;
     if (unit >= total_units) return;
     int e, mti, nt;
     if (unit < n_full * NT) {
@@ -160,7 +163,16 @@ __global__ __launch_bounds__(kGThreads) void ffn_grouped_kernel(FfnArgs a) {
             for (int i = tid; i < nvalid * kGN; i += kGThreads)
                 a.y[static_cast<size_t>(r_base + i / kGN) * a.d + nt * kGN + i % kGN] = 0.f;
         }
+        if (CHAIN && MODE == 0) raise_flag(a.flags + unit, tag);   // its act is never read
         return;
+    }
+    if constexpr (CHAIN && MODE == 1) {
+        // units are numbered m-tile-major in both projections, so the gate/up
+        // units of this m-tile are flags [m-tile * NT0, + NT0)
+        const int NT0 = a.f / (kGN / 2);
+        if (wave == 0 && !wait_flags(a.flags + static_cast<size_t>(unit / NT) * NT0, NT0, tag) && lane == 0)
+            raise_status(a.status, MOE_DEV_CHAIN_TIMEOUT);
+        __syncthreads();
     }
 
     // ---- load roles of this lane (per stage: 2 weight and 2 token
@@ -215,7 +227,8 @@ __global__ __launch_bounds__(kGThreads) void ffn_grouped_kernel(FfnArgs a) {
 #pragma unroll
             for (int i = 0; i < 2; ++i)
                 __builtin_amdgcn_global_load_lds(xsrc[i] + s * kGK,
-                                                 (lds_void*)(base + kStageW + kStageS + (16 * wave + 8 * i) * 128), 16, 0, 0);
+                                                 (lds_void*)(base + kStageW + kStageS + (16 * wave + 8 * i) * 128), 16, 0,
+                                                 CHAIN && MODE == 1 ? kAuxDevice : 0);
         }
     };
 
@@ -318,7 +331,13 @@ __global__ __launch_bounds__(kGThreads) void ffn_grouped_kernel(FfnArgs a) {
                     pk[hh] = static_cast<uint32_t>(lo) | (static_cast<uint32_t>(hi) << 16);
                 }
                 const int n = nt * (kGN / 2) + 32 * wave + nl;
-                *reinterpret_cast<u32x2*>(a.act + r * a.f + n) = u32x2{pk[0], pk[1]};
+                if constexpr (CHAIN) {
+                    __hip_atomic_store(reinterpret_cast<unsigned long long*>(a.act + r * a.f + n),
+                                       static_cast<unsigned long long>(pk[0]) | (static_cast<unsigned long long>(pk[1]) << 32),
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                } else {
+                    *reinterpret_cast<u32x2*>(a.act + r * a.f + n) = u32x2{pk[0], pk[1]};
+                }
             } else {
 #pragma unroll
                 for (int m = 0; m < 2; ++m) {
@@ -329,27 +348,63 @@ __global__ __launch_bounds__(kGThreads) void ffn_grouped_kernel(FfnArgs a) {
             }
         }
     }
+    if constexpr (CHAIN && MODE == 0) raise_flag(a.flags + unit, tag);
 }
 
-__global__ void zero_tail_rows_kernel(FfnArgs a) {
+// Zeroes the y rows past offsets[E] (pairs with an invalid expert id); block
+// `blk` of `nblk` takes every nblk-th float4.
+__device__ __forceinline__ void zero_tail_rows(const FfnArgs& a, int blk, int nblk) {
     const int r_lo = a.offsets[a.E], r_hi = a.T * a.k;
     const int n4 = a.d / 4;
     float4* base = reinterpret_cast<float4*>(a.y + static_cast<size_t>(r_lo) * a.d);
     const long long total = static_cast<long long>(r_hi - r_lo) * n4;
-    for (long long i = blockIdx.x * static_cast<long long>(blockDim.x) + threadIdx.x; i < total;
-         i += static_cast<long long>(gridDim.x) * blockDim.x)
+    for (long long i = blk * static_cast<long long>(blockDim.x) + threadIdx.x; i < total;
+         i += static_cast<long long>(nblk) * blockDim.x)
         base[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kGThreads) void ffn_grouped_kernel(FfnArgs a) {
+    __shared__ __align__(16) uint8_t lds[kLdsBytes];
+    grouped_unit<MODE, false>(a, blockIdx.x, 0, lds);
+}
+
+__global__ void zero_tail_rows_kernel(FfnArgs a) { zero_tail_rows(a, blockIdx.x, gridDim.x); }
+
+// Both projections in one launch: workgroups [0, ub0) are the gate/up units,
+// [ub0, ub0 + ub1) the down units (each waits for its m-tile's gate/up
+// units, chain.hpp), the last one zeroes the y rows past offsets[E].  The
+// down units thus fill the CUs that the gate/up launch's last, uneven units
+// leave idle, instead of waiting for all of them behind a kernel boundary.
+__global__ __launch_bounds__(kGThreads) void ffn_grouped_chained_kernel(FfnArgs a, int ub0, int ub1) {
+    __shared__ __align__(16) uint8_t lds[kLdsBytes];
+    const unsigned long long tag = chain_tag();
+    const int b = blockIdx.x;
+    if (b < ub0) grouped_unit<0, true>(a, b, tag, lds);
+    else if (b < ub0 + ub1) grouped_unit<1, true>(a, b - ub0, tag, lds);
+    else zero_tail_rows(a, 0, 1);
 }
 
 bool grouped_supported(const moe_shape& s, int fmt) {
     return fmt == MOE_FMT_MXFP4 && s.f % (kGN / 2) == 0 && s.d % kGN == 0;
 }
 
-hipError_t launch_ffn_grouped(const moe_shape& s, const FfnArgs& a, hipStream_t st) {
+static int max_mtiles(const moe_shape& s) {
     const int pairs = s.T * s.k;
-    const int max_mtiles = ceil_div(pairs, kGM) + (s.E < pairs ? s.E : pairs);
-    const int units0 = max_mtiles * (s.f / (kGN / 2));
-    const int units1 = max_mtiles * (s.d / kGN);
+    return ceil_div(pairs, kGM) + (s.E < pairs ? s.E : pairs);
+}
+
+int grouped_flag_count(const moe_shape& s) {
+    return s.f % (kGN / 2) == 0 ? max_mtiles(s) * (s.f / (kGN / 2)) : 0;
+}
+
+hipError_t launch_ffn_grouped(const moe_shape& s, const FfnArgs& a, hipStream_t st) {
+    const int units0 = max_mtiles(s) * (s.f / (kGN / 2));
+    const int units1 = max_mtiles(s) * (s.d / kGN);
+    if (a.flags) {
+        ffn_grouped_chained_kernel<<<units0 + units1 + 1, kGThreads, 0, st>>>(a, units0, units1);
+        return hipGetLastError();
+    }
     ffn_grouped_kernel<0><<<units0, kGThreads, 0, st>>>(a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;

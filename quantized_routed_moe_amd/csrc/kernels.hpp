@@ -36,6 +36,9 @@ struct FfnArgs {
     int32_t* offsets_out;
     int32_t* perm_out;
     int32_t* inv_out;
+    // Ready flags of the single-launch grouped FFN (workspace), one per
+    // gate/up unit (grouped_flag_count); null: two launches.
+    unsigned long long* flags;
 };
 
 hipError_t launch_route(const moe_shape& s, const uint16_t* x, const float* wr, const float* bias,
@@ -59,6 +62,8 @@ hipError_t launch_small_route(const moe_shape& s, const uint16_t* x, const float
 bool routed_ffn_supported(const moe_shape& s, int fmt);
 hipError_t launch_ffn_routed(const moe_shape& s, int fmt, const FfnArgs& a, hipStream_t st);
 hipError_t launch_ffn_grouped(const moe_shape& s, const FfnArgs& a, hipStream_t st);
+// Ready flags the grouped FFN needs in the workspace (0: none).
+int grouped_flag_count(const moe_shape& s);
 hipError_t launch_combine(const moe_shape& s, const float* y, const int32_t* inv, const float* w,
                           float* out, hipStream_t st);
 hipError_t launch_clear_header(uint32_t* header, hipStream_t st);

@@ -57,11 +57,18 @@ def test_shape_validation(bad):
 
 def test_workspace_sizes():
     s = _shape(T=5, d=4096, E=64, k=2, f=2048)
-    # 256-byte header + bf16 act[T*k][f] rounded up to 256
-    assert qm.lib().moe_workspace_bytes(ctypes.byref(s)) == 256 + 5 * 2 * 2048 * 2
-    lw = qm.lib().moe_layer_workspace_bytes(ctypes.byref(s))
     al = lambda v: (v + 255) // 256 * 256
-    assert lw == 256 + al(5 * 2 * 2048 * 2) + al(65 * 4) + 2 * al(10 * 4) + al(10 * 4096 * 4)
+    # 256-byte header + bf16 act[T*k][f] + 8-byte ready flags, one per
+    # (m-tile, 256 rows of f) for ceil(T*k / 128) + min(E, T*k) m-tiles,
+    # each part rounded up to 256
+    mtiles = -(-10 // 128) + min(64, 10)
+    ffn = 256 + al(5 * 2 * 2048 * 2) + al(mtiles * (2048 // 256) * 8)
+    assert qm.lib().moe_workspace_bytes(ctypes.byref(s)) == ffn
+    lw = qm.lib().moe_layer_workspace_bytes(ctypes.byref(s))
+    assert lw == ffn + al(65 * 4) + 2 * al(10 * 4) + al(10 * 4096 * 4)
+    # no flags when f is not a multiple of 256 (no single-launch grouped FFN)
+    s2 = _shape(T=5, d=4096, E=64, k=2, f=224)
+    assert qm.lib().moe_workspace_bytes(ctypes.byref(s2)) == 256 + al(5 * 2 * 224 * 2)
 
 
 def test_null_shape_and_zero_tokens():
