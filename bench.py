@@ -44,7 +44,7 @@ METRIC = "MoE layer tokens/s; decode weight-stream GB/s; prefill expert TFLOP/s"
 # steps.  Must be re-measured (or removed) whenever an FFN kernel changes.
 MEASURED_FFN_TRAFFIC = {
     1: (2 * (8794.0 + 4438.7) + (8.0 + 32.0)) * 1024,
-    3: (2 * (284086.7 + 166739.9 + 12.0) + (16410.0 + 65572.7)) * 1024,
+    3: (2 * 453305.0 + 98375.6) * 1024,
     4: (2 * (27874.1 + 14211.8) + (128.0 + 512.0)) * 1024,
 }
 
@@ -333,7 +333,8 @@ def main():
         roof = dict(bound="hbm", achieved=round(gbps, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
                     frac=round(gbps / HBM_PEAK_GBPS, 4), traffic=traffic)
     roof["traffic_unit"] = "HBM bytes per call (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
-    roof["kernel"] = "moe_expert_ffn (gate/up + SwiGLU kernel, down kernel)"
+    roof["kernel"] = ("moe_expert_ffn (one launch: gate/up + SwiGLU tiles, then down tiles)" if T * k >= 256 and w["fmt"] == "mxfp4"
+                      else "moe_expert_ffn (gate/up + SwiGLU kernel, down kernel)")
     roof["algorithmic_bytes_per_launch"] = round(ffn_bytes)
     roof["avg_launch_ms"] = round(ffn_avg_s * 1e3, 5)
 
