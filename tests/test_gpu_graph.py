@@ -87,3 +87,60 @@ def test_layer_graph_replays_equal_eager(shape, fmt):
             g.close()
         assert qm.moe_read_device_status(ba["ws"], stream) == 0
         assert qm.moe_read_device_status(bb["ws"], stream) == 0
+
+
+def test_single_launch_ffn_replays_with_new_inputs():
+    """The prefill FFN runs as one launch whose down tiles wait on ready
+    flags raised by the gate/up tiles.  Each replay of a captured call must
+    wait for its own gate/up tiles, not trust flags left by the previous
+    replay: between replays the token rows change and act is poisoned with
+    NaN (the flags are left alone), so a down tile that read act early would
+    show up in y."""
+    shape, fmt = (300, 512, 8, 2, 256), "mxfp4"
+    T, d, E, k, f = shape
+    seed = zlib.crc32(repr((shape, fmt, "chain")).encode()) % 1000
+    print(f"single-launch FFN replays: shape {shape} {fmt} seed {seed}", flush=True)
+    dc = device_case(synthetic.make_case(T, d, E, k, f, fmt, seed=seed, zipf=1.1))
+    s = dc["shape"]
+    dev = dc["x"].device
+    stream = torch.cuda.Stream()
+    gen = torch.Generator(device="cpu").manual_seed(seed)
+    xs = [dc["x"]] + [(torch.randn((T, d), generator=gen) * (1 + r)).to(torch.bfloat16).view(torch.int16).to(dev)
+                      for r in range(3)]
+    with torch.cuda.stream(stream):
+        logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+        ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+        w = torch.empty((T, k), dtype=torch.float32, device=dev)
+        offsets = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+        perm = torch.empty((T * k,), dtype=torch.int32, device=dev)
+        inv = torch.empty((T * k,), dtype=torch.int32, device=dev)
+        ws_ref = qm.alloc_workspace(s, device=dev, stream=stream)
+        qm.moe_route_topk(s, dc["x"], dc["w_router"], dc["bias"], logits, ids, w, stream)
+        qm.moe_dispatch(s, ids, offsets, perm, inv, ws_ref, stream)
+        want = []
+        for x in xs:                          # eager results, own workspace
+            y = torch.empty((T * k, d), dtype=torch.float32, device=dev)
+            qm.moe_expert_ffn(s, x, dc["experts"], offsets, perm, y, ws_ref, stream)
+            stream.synchronize()
+            want.append(y.cpu().numpy().copy())
+        assert not np.array_equal(want[0], want[1])
+        x_buf = xs[0].clone()
+        y = torch.empty((T * k, d), dtype=torch.float32, device=dev)
+        ws = qm.alloc_workspace(s, device=dev, stream=stream)
+        act = ws[256:256 + T * k * f * 2]
+        g = HipGraph()
+        try:
+            g.capture(lambda: qm.moe_expert_ffn(s, x_buf, dc["experts"], offsets, perm, y, ws, stream), stream)
+            for rep in range(2 * len(xs)):
+                r = rep % len(xs)
+                x_buf.copy_(xs[r])
+                act.view(torch.int16).fill_(0x7fc0)          # bf16 NaN
+                y.fill_(float("nan"))
+                stream.synchronize()
+                g.launch(stream)
+                stream.synchronize()
+                assert np.array_equal(y.cpu().numpy(), want[r]), f"replay {rep} (inputs {r}) differs"
+        finally:
+            g.close()
+        assert qm.moe_read_device_status(ws, stream) == 0
+        assert qm.moe_read_device_status(ws_ref, stream) == 0
