@@ -44,7 +44,7 @@ METRIC = "MoE layer tokens/s; decode weight-stream GB/s; prefill expert TFLOP/s"
 # steps.  Must be re-measured (or removed) whenever an FFN kernel changes.
 MEASURED_FFN_TRAFFIC = {
     1: (2 * (8794.0 + 4438.7) + (8.0 + 32.0)) * 1024,
-    3: (2 * 453305.0 + 98375.6) * 1024,
+    3: (2 * 469754.6 + 98485.0) * 1024,
     4: (2 * (27874.1 + 14211.8) + (128.0 + 512.0)) * 1024,
 }
 
