@@ -43,7 +43,7 @@ METRIC = "MoE layer tokens/s; decode weight-stream GB/s; prefill expert TFLOP/s"
 # different number of experts each step: theirs is the average of the counted
 # steps.  Must be re-measured (or removed) whenever an FFN kernel changes.
 MEASURED_FFN_TRAFFIC = {
-    1: (2 * (8794.0 + 4438.7) + (8.0 + 32.0)) * 1024,
+    1: (2 * (13158.5 + 4436.2) + (8.0 + 32.0)) * 1024,
     3: (2 * 469754.6 + 98485.0) * 1024,
     4: (2 * (27874.1 + 14211.8) + (128.0 + 512.0)) * 1024,
 }
