@@ -109,6 +109,14 @@ def dequant_row(mat: dict, slot: int, row: int, K: int) -> list:
         for i in range(K):
             q = (int(codes[i // 4]) >> (2 * (i % 4))) & 3
             out.append(fp16_value(int(sc[i // 32])) * q + fp16_value(int(mn[i // 32])))
+    elif mat["fmt"] == "q4":
+        codes = mat["codes"][slot][row]
+        sc = mat["scales"][slot][row]
+        mn = mat["mins"][slot][row]
+        for i in range(K):
+            byte = int(codes[i // 2])
+            q = (byte & 0xF) if i % 2 == 0 else (byte >> 4)
+            out.append(fp16_value(int(sc[i // 32])) * q + fp16_value(int(mn[i // 32])))
     else:
         raise ValueError(mat["fmt"])
     return out

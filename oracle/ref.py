@@ -129,6 +129,30 @@ def dequant_q2(codes, scale_bits, min_bits) -> np.ndarray:
     return s * q + m
 
 
+def dequant_q4(codes, scale_bits, min_bits) -> np.ndarray:
+    """Decode a 4-bit group-asymmetric matrix pack to float64.
+
+    The pages name 4-bit "GPTQ-style" quantisation with dequantisation at
+    inference time ("antirez ds4: DeepSeek Metal inference", section
+    技术深度解析) and a q4 model build ("DwarfStar 4 ... 完整指南", section
+    性能实测参考), nothing more.  Reading taken (the group-wise affine form of
+    the 2-bit pack, with a zero point folded into the min):
+      w = scale * q + min, q in {0, ..., 15}, one IEEE fp16 scale and one fp16
+      min per group of 32 consecutive elements along K.
+    codes uint8 [..., n, K/2]: element 2i of a row is the low nibble of byte
+      i, element 2i+1 the high nibble (the order of the MXFP4 pack).
+    scale_bits, min_bits uint16 [..., n, K/32] (fp16 bit patterns).
+    """
+    codes = np.asarray(codes, dtype=np.uint8)
+    q = np.stack([codes & 0x0F, codes >> 4], axis=-1)
+    q = q.reshape(*codes.shape[:-1], codes.shape[-1] * 2).astype(np.float64)
+    s = np.repeat(fp16_bits_to_f64(scale_bits), 32, axis=-1)
+    m = np.repeat(fp16_bits_to_f64(min_bits), 32, axis=-1)
+    if s.shape != q.shape or m.shape != q.shape:
+        raise ValueError("scale/min shape does not match codes")
+    return s * q + m
+
+
 def dequant(mat: dict, slot: int) -> np.ndarray:
     """Dequantise one expert slot of a matrix pack (dict with 'fmt' and arrays)."""
     fmt = mat["fmt"]
@@ -136,6 +160,8 @@ def dequant(mat: dict, slot: int) -> np.ndarray:
         return dequant_mxfp4(mat["codes"][slot], mat["scales"][slot])
     if fmt == "q2":
         return dequant_q2(mat["codes"][slot], mat["scales"][slot], mat["mins"][slot])
+    if fmt == "q4":
+        return dequant_q4(mat["codes"][slot], mat["scales"][slot], mat["mins"][slot])
     raise ValueError(f"unknown format {fmt!r}")
 
 

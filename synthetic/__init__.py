@@ -23,6 +23,8 @@ Value recipe:
   MXFP4    codes uniform over all 16 e2m1 codes (each nibble), e8m0 scale bytes
            uniform over {119..123} (scales 2**-8 .. 2**-4)
   Q2       codes uniform over {0..3}, fp16 scale U[0.005, 0.02], fp16 min U[-0.04, 0]
+  Q4       codes uniform over {0..15}, fp16 scale U[0.001, 0.004], fp16 min U[-0.04, 0]
+           (the same weight range as Q2: 15 steps of a quarter of Q2's scale)
 """
 
 from __future__ import annotations
@@ -76,6 +78,11 @@ def make_matrix(fmt: str, slots: int, n: int, K: int, rng: np.random.Generator) 
         scales = _fp16_bits(rng.uniform(0.005, 0.02, size=(slots, n, K // 32)))
         mins = _fp16_bits(rng.uniform(-0.04, 0.0, size=(slots, n, K // 32)))
         return dict(fmt="q2", codes=codes, scales=scales, mins=mins)
+    if fmt == "q4":
+        codes = rng.integers(0, 256, size=(slots, n, K // 2), dtype=np.uint8)
+        scales = _fp16_bits(rng.uniform(0.001, 0.004, size=(slots, n, K // 32)))
+        mins = _fp16_bits(rng.uniform(-0.04, 0.0, size=(slots, n, K // 32)))
+        return dict(fmt="q4", codes=codes, scales=scales, mins=mins)
     raise ValueError(fmt)
 
 

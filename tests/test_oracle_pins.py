@@ -82,6 +82,19 @@ def test_q2_hand_decoded_row():
     assert brute.dequant_row(mat, 0, 0, 64) == list(want)
 
 
+def test_q4_hand_decoded_row():
+    fx = _read_fixture("q4_row.txt")
+    codes = np.array([int(v, 16) for v in fx["bytes"]], np.uint8)[None, :]
+    sc = np.array([int(v, 16) for v in fx["scales"]], np.uint16)[None, :]
+    mn = np.array([int(v, 16) for v in fx["mins"]], np.uint16)[None, :]
+    want = np.array([float(v) for v in fx["values"]])
+    got = ref.dequant_q4(codes, sc, mn)[0]
+    assert got.shape == want.shape == (64,)
+    assert np.array_equal(got, want)
+    mat = dict(fmt="q4", codes=codes[None], scales=sc[None], mins=mn[None])
+    assert brute.dequant_row(mat, 0, 0, 64) == list(want)
+
+
 def test_mxfp4_values_exact_in_bf16():
     """Every e2m1 code times a scale 2**-8..2**-4 is a bf16 value, so MXFP4
     weights can be widened to bf16 for matrix cores with no rounding."""
@@ -100,6 +113,28 @@ def test_q2_values_exact_in_fp32():
     for q in range(4):
         w = sc * q + mn
         assert np.array_equal(w.astype(np.float32).astype(np.float64), w)
+
+
+def test_q4_values_exact_in_fp32():
+    """scale*q + min of fp16 scale/min is exact in float32 for q = 0..15 and
+    the generator's ranges (an fp16 significand times a 4-bit integer needs
+    15 bits), so the device's float32 group sums lose nothing to the format."""
+    rng = np.random.default_rng(8)
+    sc = rng.uniform(0.001, 0.004, 20000).astype(np.float16).astype(np.float64)
+    mn = rng.uniform(-0.04, 0.0, 20000).astype(np.float16).astype(np.float64)
+    for q in range(16):
+        w = sc * q + mn
+        assert np.array_equal(w.astype(np.float32).astype(np.float64), w)
+
+
+def test_q4_one_plus_q_over_16_exact_in_bf16():
+    """1 + q/16 (q = 0..15) is a bf16 value with the bit pattern 0x3F80 | q << 3:
+    the device multiplies bf16(1 + q/16) operands and applies scale and min
+    per group, so this pins that the operand carries q exactly."""
+    for q in range(16):
+        v = 1.0 + q / 16.0
+        assert brute.round_bf16(v) == v
+        assert brute.bf16_value(0x3F80 | (q << 3)) == v
 
 
 # ------------------------------------------------------------ bf16 rounding
@@ -212,7 +247,7 @@ def _dense_weights_brute(mat, slot, n, K):
     return np.array([brute.dequant_row(mat, slot, r, K) for r in range(n)])
 
 
-@pytest.mark.parametrize("fmt", ["mxfp4", "q2"])
+@pytest.mark.parametrize("fmt", ["mxfp4", "q2", "q4"])
 def test_single_expert_is_dense_swiglu(fmt):
     """E = 1, k = 1: the layer is a dense SwiGLU MLP (torch float64)."""
     c = _small_case(fmt, T=5, d=64, E=1, k=1, f=32, seed=4)
@@ -255,7 +290,7 @@ def test_identity_experts_closed_form():
             assert r["out"][t, n] == want
 
 
-@pytest.mark.parametrize("fmt", ["mxfp4", "q2"])
+@pytest.mark.parametrize("fmt", ["mxfp4", "q2", "q4"])
 def test_ref_matches_brute_small(fmt):
     for seed, (T, d, E, k, f) in enumerate([(3, 64, 4, 2, 32), (6, 32, 8, 3, 64), (2, 96, 3, 3, 32)]):
         c = _small_case(fmt, T=T, d=d, E=E, k=k, f=f, seed=seed, zipf=1.1 if seed == 1 else None)
