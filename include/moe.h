@@ -96,7 +96,13 @@ enum moe_format {
     /* 2-bit group-asymmetric: w = scale * q + min, q in {0,1,2,3}; element 4i+j
        of a row is bits (2j, 2j+1) of byte i; one fp16 scale and one fp16 min per
        32 consecutive elements along K. */
-    MOE_FMT_Q2G32 = 2
+    MOE_FMT_Q2G32 = 2,
+    /* 4-bit group-asymmetric: w = scale * q + min, q in {0..15}; element 2i
+       of a row is the LOW nibble of byte i, element 2i+1 the HIGH nibble; one
+       fp16 scale and one fp16 min per 32 consecutive elements along K (the
+       4-bit "GPTQ-style" pack of "antirez ds4: DeepSeek Metal inference",
+       section 技术深度解析, read as the affine form of the 2-bit pack). */
+    MOE_FMT_Q4G32 = 3
 };
 
 /* Memory layouts of a quantised matrix of n rows x K elements per slot
@@ -105,6 +111,8 @@ enum moe_format {
    MOE_LAYOUT_ROWS -- the interchange layout (input of moe_pack_qmat only):
      MXFP4: codes uint8 [slots][n][K/2], scales uint8 [slots][n][G], mins NULL.
      Q2:    codes uint8 [slots][n][K/4], scales and mins fp16 bits
+            uint16 [slots][n][G].
+     Q4:    codes uint8 [slots][n][K/2], scales and mins fp16 bits
             uint16 [slots][n][G].
 
    MOE_LAYOUT_TILES -- the layout the expert FFN reads (moe_pack_qmat writes
@@ -134,6 +142,16 @@ enum moe_format {
                                                 fp16 scale | fp16 min << 16 of
                                                 row 16*tile + r, group
                                                 4*step + j (padding 0)
+            mins   NULL (the mins live in scales)
+     Q4:    codes  [slots][n/16][S][64][16 B]  elements 8g..8g+7 (g = L/16)
+                                                of each of the step's four
+                                                groups (padding: 0), as four
+                                                little-endian uint32; word j
+                                                holds group 4*step+j: bits
+                                                4h..4h+3 element 8g+2h and
+                                                bits 16+4h..19+4h element
+                                                8g+2h+1 (h = 0..3)
+            scales as Q2
             mins   NULL (the mins live in scales)
    Sizes: moe_qmat_bytes. */
 enum moe_layout {

@@ -37,7 +37,8 @@ MOE_DEV_CHAIN_TIMEOUT = 4
 
 MOE_FMT_MXFP4 = 1
 MOE_FMT_Q2G32 = 2
-FORMATS = {"mxfp4": MOE_FMT_MXFP4, "q2": MOE_FMT_Q2G32}
+MOE_FMT_Q4G32 = 3
+FORMATS = {"mxfp4": MOE_FMT_MXFP4, "q2": MOE_FMT_Q2G32, "q4": MOE_FMT_Q4G32}
 
 MOE_LAYOUT_ROWS = 0
 MOE_LAYOUT_TILES = 1

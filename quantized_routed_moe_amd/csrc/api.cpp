@@ -53,18 +53,18 @@ LayerCarve layer_carve(const moe_shape& s) {
 // Array sizes of one (fmt, layout) matrix; false when the request is invalid.
 bool qmat_sizes(int fmt, int layout, int slots, int n, int K, size_t* codes, size_t* scales, size_t* mins) {
     *codes = *scales = *mins = 0;
-    if (fmt != MOE_FMT_MXFP4 && fmt != MOE_FMT_Q2G32) return false;
+    if (fmt != MOE_FMT_MXFP4 && fmt != MOE_FMT_Q2G32 && fmt != MOE_FMT_Q4G32) return false;
     if (layout != MOE_LAYOUT_ROWS && layout != MOE_LAYOUT_TILES) return false;
     if (slots < 1 || n < 16 || n % 16 || K < 32 || K % 32) return false;
     const size_t rows = static_cast<size_t>(slots) * n;
     const size_t groups = rows * (K / 32);
     if (layout == MOE_LAYOUT_ROWS) {
-        *codes = fmt == MOE_FMT_MXFP4 ? rows * (K / 2) : rows * (K / 4);
+        *codes = fmt == MOE_FMT_Q2G32 ? rows * (K / 4) : rows * (K / 2);
         *scales = fmt == MOE_FMT_MXFP4 ? groups : groups * 2;
         *mins = fmt == MOE_FMT_MXFP4 ? 0 : groups * 2;
     } else {
         const size_t pieces = static_cast<size_t>(slots) * (n / 16) * ((K + 127) / 128) * 64;
-        *codes = pieces * (fmt == MOE_FMT_MXFP4 ? 16 : 8);
+        *codes = pieces * (fmt == MOE_FMT_Q2G32 ? 8 : 16);
         *scales = pieces * (fmt == MOE_FMT_MXFP4 ? 1 : 4);
     }
     return true;
@@ -82,7 +82,7 @@ int check_qmat(const moe_qmat& m, int fmt) {
 int check_experts(const moe_shape& s, const moe_experts* ex) {
     if (!ex) return MOE_ERR_NULL;
     const int fmt = ex->gate.fmt;
-    if (fmt != MOE_FMT_MXFP4 && fmt != MOE_FMT_Q2G32) return MOE_ERR_FORMAT;
+    if (fmt != MOE_FMT_MXFP4 && fmt != MOE_FMT_Q2G32 && fmt != MOE_FMT_Q4G32) return MOE_ERR_FORMAT;
     int rc;
     if ((rc = check_qmat(ex->gate, fmt)) != MOE_OK) return rc;
     if ((rc = check_qmat(ex->up, fmt)) != MOE_OK) return rc;
@@ -208,13 +208,14 @@ int moe_pack_qmat(const moe_qmat* src, const moe_qmat* dst, int32_t slots, int32
         return MOE_ERR_FORMAT;
     size_t c, s, m;
     if (!qmat_sizes(src->fmt, MOE_LAYOUT_ROWS, slots, n, K, &c, &s, &m)) {
-        return src->fmt != MOE_FMT_MXFP4 && src->fmt != MOE_FMT_Q2G32 ? MOE_ERR_FORMAT : MOE_ERR_SHAPE;
+        return src->fmt != MOE_FMT_MXFP4 && src->fmt != MOE_FMT_Q2G32 && src->fmt != MOE_FMT_Q4G32 ? MOE_ERR_FORMAT
+                                                                                                : MOE_ERR_SHAPE;
     }
-    const bool q2 = src->fmt == MOE_FMT_Q2G32;
-    if (!src->codes || !src->scales || !dst->codes || !dst->scales || (q2 && !src->mins)) return MOE_ERR_NULL;
-    if (dst->mins || (!q2 && src->mins)) return MOE_ERR_FORMAT;
+    const bool with_mins = src->fmt == MOE_FMT_Q2G32 || src->fmt == MOE_FMT_Q4G32;
+    if (!src->codes || !src->scales || !dst->codes || !dst->scales || (with_mins && !src->mins)) return MOE_ERR_NULL;
+    if (dst->mins || (!with_mins && src->mins)) return MOE_ERR_FORMAT;
     if (!aligned(src->codes, 16) || !aligned(dst->codes, 16) || !aligned(src->scales, 4) ||
-        !aligned(dst->scales, 4) || (q2 && !aligned(src->mins, 4)))
+        !aligned(dst->scales, 4) || (with_mins && !aligned(src->mins, 4)))
         return MOE_ERR_ALIGN;
     return hip_rc(qrmoe::launch_pack(src->fmt, src->codes, src->scales, src->mins, const_cast<void*>(dst->codes),
                                      const_cast<void*>(dst->scales), slots, n, K, stream));

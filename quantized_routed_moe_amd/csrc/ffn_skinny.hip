@@ -467,13 +467,21 @@ bool routed_ffn_supported(const moe_shape& s, int fmt) {
     return s.T <= kGateUpWaves && s.T * s.k <= kRoutedMaxPairs && !ffn_uses_grouped(s, fmt);
 }
 
+static hipError_t launch_two_fmt(const moe_shape& s, int fmt, const FfnArgs& a, hipStream_t st, bool routed) {
+    switch (fmt) {
+        case MOE_FMT_MXFP4: return launch_two<MOE_FMT_MXFP4>(s, a, st, routed);
+        case MOE_FMT_Q2G32: return launch_two<MOE_FMT_Q2G32>(s, a, st, routed);
+        default: return launch_two<MOE_FMT_Q4G32>(s, a, st, routed);
+    }
+}
+
 hipError_t launch_ffn_routed(const moe_shape& s, int fmt, const FfnArgs& a, hipStream_t st) {
-    return fmt == MOE_FMT_MXFP4 ? launch_two<MOE_FMT_MXFP4>(s, a, st, true) : launch_two<MOE_FMT_Q2G32>(s, a, st, true);
+    return launch_two_fmt(s, fmt, a, st, true);
 }
 
 hipError_t launch_ffn(const moe_shape& s, int fmt, const FfnArgs& a, hipStream_t st) {
     if (ffn_uses_grouped(s, fmt)) return launch_ffn_grouped(s, a, st);
-    return fmt == MOE_FMT_MXFP4 ? launch_two<MOE_FMT_MXFP4>(s, a, st, false) : launch_two<MOE_FMT_Q2G32>(s, a, st, false);
+    return launch_two_fmt(s, fmt, a, st, false);
 }
 
 }  // namespace qrmoe

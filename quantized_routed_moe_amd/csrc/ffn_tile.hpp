@@ -30,6 +30,10 @@
 //    The offset 1 keeps the cancellation between C and xs small.  A lane
 //    loads the four (scale, min) words of its own row for the step (16
 //    contiguous bytes of the row-major scale block).
+//  * Q4: as Q2 with 4-bit codes: one word per group, the even elements'
+//    nibbles in its low half and the odd ones' in its high half, so one
+//    shift and one and-or give bf16(1 + q/16) pairs (0x3F80 | q<<3, exact),
+//    and the group contributes (16*scale)*C + (min - 16*scale)*xs.
 //
 // Token operand: the wave copies the K slice of each real token row of the
 // column pass (kCap steps = 512 bf16 = 1 KB per row) straight from global
@@ -54,6 +58,7 @@ constexpr int kBRowBytes = kCap * kStepK * 2 + 16;
 template <int FMT> struct PieceBytes;
 template <> struct PieceBytes<MOE_FMT_MXFP4> { static constexpr int codes = 16, scales = 1; };
 template <> struct PieceBytes<MOE_FMT_Q2G32> { static constexpr int codes = 8, scales = 4; };
+template <> struct PieceBytes<MOE_FMT_Q4G32> { static constexpr int codes = 16, scales = 4; };
 
 template <int FMT> struct WChunk;
 template <> struct WChunk<MOE_FMT_MXFP4> {
@@ -63,6 +68,10 @@ template <> struct WChunk<MOE_FMT_MXFP4> {
 template <> struct WChunk<MOE_FMT_Q2G32> {
     u32x2 c[kCap];        // elements 8g..8g+7 of groups 4s..4s+3 (dword t: groups 4s+2t, 4s+2t+1)
     u32x4 sm[kCap];       // fp16 scale | fp16 min << 16 of (row, group 4s+j), j = 0..3
+};
+template <> struct WChunk<MOE_FMT_Q4G32> {
+    u32x4 c[kCap];        // elements 8g..8g+7 of groups 4s..4s+3 (dword j: group 4s+j)
+    u32x4 sm[kCap];       // as Q2
 };
 
 // Weight loads per chunk and matrix (code blocks + scale loads).
@@ -104,7 +113,8 @@ __device__ __forceinline__ void load_w(WChunk<FMT>& w, const WTile& t, int s0, i
         } else {
             // row-major scale block: the four words of row L%16
             w.sm[u] = *reinterpret_cast<const u32x4*>(t.scales + s * kWave * 4 + 16 * (lane & 15));
-            w.c[u] = *reinterpret_cast<const u32x2*>(t.codes + s * kWave * 8);
+            if constexpr (FMT == MOE_FMT_Q4G32) w.c[u] = *reinterpret_cast<const u32x4*>(t.codes + s * kWave * 16);
+            else w.c[u] = *reinterpret_cast<const u32x2*>(t.codes + s * kWave * 8);
         }
     }
 }
@@ -163,10 +173,13 @@ __device__ __forceinline__ void mma_chunk(f32x4 (&acc)[kChains<FMT>][NM], const 
                     acc[j & 1][m] = mfma16x16x32(bb, mxfp4x8_to_bf16(w[m].c[u][j], scl[m]), acc[j & 1][m]);
             }
         } else {
+            // Q2: codes q/4 steps at bits 5-6 of each bf16 half; Q4: q/16 steps at bits 3-6
+            constexpr bool q4 = FMT == MOE_FMT_Q4G32;
+            constexpr float kStep = q4 ? 16.f : 4.f;      // 1/step of the operand 1 + q/kStep
             const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
             // the code mask in a register: (x & mask) | 0x3f803f80 is then one
             // v_and_or_b32 (gfx950 VOP3 takes no second literal)
-            uint32_t qmask = 0x00600060u;
+            uint32_t qmask = q4 ? 0x00780078u : 0x00600060u;
             asm volatile("" : "+v"(qmask));
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -175,19 +188,23 @@ __device__ __forceinline__ void mma_chunk(f32x4 (&acc)[kChains<FMT>][NM], const 
                 const f32x4 xs = mfma16x16x32(bb, ones, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
                 for (int m = 0; m < NM; ++m) {
-                    // even elements of group j in byte (j&1), odd ones in byte 2 + (j&1)
-                    const uint32_t cw = w[m].c[u][j >> 1];
-                    u32x4 av;   // pair h = elements 2h, 2h+1 -> bf16(1 + q/4) in the low, high half
+                    // Q2: even elements of group j in byte (j&1), odd ones in
+                    // byte 2 + (j&1).  Q4: group j is word j, even elements
+                    // in its low half, odd ones in its high half.
+                    uint32_t cw;
+                    if constexpr (q4) cw = w[m].c[u][j];
+                    else cw = w[m].c[u][j >> 1];
+                    u32x4 av;   // pair h = elements 2h, 2h+1 -> bf16(1 + q/kStep) in the low, high half
 #pragma unroll
                     for (int h = 0; h < 4; ++h) {
-                        const int sh = 8 * (j & 1) + 2 * h - 5;
+                        const int sh = q4 ? 4 * h - 3 : 8 * (j & 1) + 2 * h - 5;
                         const uint32_t x = sh >= 0 ? cw >> sh : cw << -sh;
                         av[h] = (x & qmask) | 0x3f803f80u;
                     }
                     const f32x4 cq = mfma16x16x32(bb, bf16x8_from_u32x4(av), f32x4{0.f, 0.f, 0.f, 0.f});
                     const uint32_t smw = w[m].sm[u][j];
-                    const float fs = 4.f * fp16_to_f32(smw);                 // 4 * scale
-                    const float fm = fmaf(-4.f, fp16_to_f32(smw), fp16_to_f32(smw >> 16));  // min - 4 * scale
+                    const float fs = kStep * fp16_to_f32(smw);                 // kStep * scale
+                    const float fm = fmaf(-kStep, fp16_to_f32(smw), fp16_to_f32(smw >> 16));  // min - kStep * scale
                     f32x4 ac = acc[0][m];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) ac[i] = fmaf(fs, cq[i], fmaf(fm, xs[i], ac[i]));

@@ -154,7 +154,7 @@ def test_layer_validation():
     assert L.moe_layer(*args(out=None)) == qm.MOE_ERR_NULL
     assert L.moe_layer(*args(wsb=need - 1)) == qm.MOE_ERR_WORKSPACE
     assert L.moe_layer(*args(x=None)) == qm.MOE_ERR_NULL
-    assert L.moe_layer(*args(ex=_experts(fmt=3))) == qm.MOE_ERR_FORMAT
+    assert L.moe_layer(*args(ex=_experts(fmt=7))) == qm.MOE_ERR_FORMAT
     assert L.moe_layer(*args(wr=None, bias=A16)) == qm.MOE_ERR_UNSUPPORTED
 
 
@@ -173,6 +173,10 @@ def test_qmat_bytes():
     assert _qbytes(MX, TILES, 64, 2048, 4096)[1:] == (64 * 2048 * 2048, 64 * 2048 * 128, 0)
     assert _qbytes(MX, TILES, 2, 32, 160)[1:] == (2 * 2 * 2 * 64 * 16, 2 * 2 * 2 * 64, 0)
     assert _qbytes(Q2, TILES, 3, 16, 96)[1:] == (3 * 1 * 1 * 64 * 8, 3 * 1 * 1 * 64 * 4, 0)
+    Q4 = qm.MOE_FMT_Q4G32
+    assert _qbytes(Q4, ROWS, 3, 16, 96)[1:] == (3 * 16 * 48, 3 * 16 * 3 * 2, 3 * 16 * 3 * 2)
+    assert _qbytes(Q4, TILES, 3, 16, 96)[1:] == (3 * 1 * 1 * 64 * 16, 3 * 1 * 1 * 64 * 4, 0)
+    assert _qbytes(Q4, TILES, 64, 2048, 4096)[1:] == (64 * 2048 * 2048, 64 * 2048 * 128 * 4, 0)
     for bad in [(5, TILES, 1, 16, 32), (MX, 2, 1, 16, 32), (MX, TILES, 0, 16, 32), (MX, TILES, 1, 24, 32),
                 (MX, TILES, 1, 16, 48), (MX, ROWS, 1, 0, 32), (Q2, TILES, 1, 16, 0)]:
         assert _qbytes(*bad) == (0, 0, 0, 0), bad
@@ -200,3 +204,8 @@ def test_pack_validation():
     assert pk(rows(c=A16 + 4), tiles()) == qm.MOE_ERR_ALIGN
     assert pk(rows(), tiles(sc=A16 + 2)) == qm.MOE_ERR_ALIGN
     assert pk(rows(Q2, mn=A16 + 2), tiles(Q2)) == qm.MOE_ERR_ALIGN
+    Q4 = qm.MOE_FMT_Q4G32
+    assert pk(rows(Q4), tiles(Q4)) == qm.MOE_ERR_NULL           # Q4 rows need mins
+    assert pk(rows(Q4, mn=A16), tiles(Q2)) == qm.MOE_ERR_FORMAT
+    assert pk(rows(Q4, mn=A16), tiles(Q4, mn=A16)) == qm.MOE_ERR_FORMAT
+    assert pk(rows(Q4, mn=A16 + 2), tiles(Q4)) == qm.MOE_ERR_ALIGN

@@ -20,9 +20,11 @@ pytestmark = pytest.mark.gpu
 
 CASES = [
     # (T, d, E, k, f), format: the small-batch routed path (T <= 8, k <= 2,
-    # MXFP4 and Q2), the skinny four-kernel path and the grouped path
+    # MXFP4, Q2 and Q4), the skinny four-kernel path and the grouped path
     ((1, 256, 8, 2, 128), "mxfp4"),
     ((1, 256, 8, 2, 128), "q2"),
+    ((1, 256, 8, 2, 128), "q4"),
+    ((16, 256, 16, 2, 128), "q4"),
     ((5, 512, 16, 2, 256), "mxfp4"),
     ((16, 256, 16, 2, 128), "q2"),
     ((12, 256, 8, 3, 128), "mxfp4"),

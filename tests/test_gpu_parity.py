@@ -66,14 +66,14 @@ SHAPES = [
     (1, 32, 1, 1, 32),
     (64, 1024, 32, 2, 512),
     # T*k >= 256 with d % 512 == 0 and f % 256 == 0: the LDS-tiled grouped path
-    # (MXFP4); Q2 takes the skinny path at these sizes
+    # (MXFP4); Q2 and Q4 take the skinny path at these sizes
     (300, 512, 8, 2, 256),
     (700, 1024, 16, 2, 512),
     (257, 512, 64, 4, 768),
 ]
 
 
-@pytest.mark.parametrize("fmt", ["mxfp4", "q2"])
+@pytest.mark.parametrize("fmt", ["mxfp4", "q2", "q4"])
 @pytest.mark.parametrize("shape", SHAPES)
 def test_ragged_shapes(fmt, shape):
     T, d, E, k, f = shape
@@ -128,7 +128,7 @@ def test_exact_ties_and_signed_zero():
     assert g["ids"][3].tolist() == [6, 0, 2]
 
 
-@pytest.mark.parametrize("fmt", ["mxfp4", "q2"])
+@pytest.mark.parametrize("fmt", ["mxfp4", "q2", "q4"])
 def test_single_expert_and_full_fanout(fmt):
     c1 = synthetic.make_case(9, 128, 1, 1, 64, fmt, seed=5)
     check_against_oracle(c1, run_steps(device_case(c1)))
@@ -238,7 +238,7 @@ def test_power_of_two_scaling(c):
                                    (5, 384, 8, 8, 160), (7, 1024, 32, 2, 512), (1, 256, 64, 64, 128),
                                    (16, 256, 64, 2, 128), (32, 256, 16, 2, 128), (12, 384, 8, 1, 160),
                                    (20, 256, 32, 3, 128), (8, 256, 64, 16, 128), (33, 256, 16, 2, 128)])
-@pytest.mark.parametrize("fmt", ["mxfp4", "q2"])
+@pytest.mark.parametrize("fmt", ["mxfp4", "q2", "q4"])
 def test_layer_small_T_fused_path_equals_steps(shape, fmt):
     """moe_layer's small-batch path (T <= 8, T*k <= 64: logits-only router
     launch, routing inside every gate/up workgroup, scatter-add combine for
@@ -315,7 +315,29 @@ def _tiles_q2(codes, scales, mins):
     return np.ascontiguousarray(c).reshape(-1).view(np.uint8), np.ascontiguousarray(s.reshape(-1)).view(np.uint8)
 
 
-@pytest.mark.parametrize("fmt", ["mxfp4", "q2"])
+def _tiles_q4(codes, scales, mins):
+    """Q4: piece L = 16 g + r holds elements 8g..8g+7 of each group 4 step + j
+    of row 16 tile + r as four words; word j: the nibble of element 8g+2h at
+    bits 4h..4h+3 and that of element 8g+2h+1 at bits 16+4h..19+4h.  Scale
+    words as Q2."""
+    slots, n, half = codes.shape
+    G, S, NT = half // 16, -(-half // 64), n // 16
+    cg = np.zeros((slots, n, 4 * S, 16), np.uint8)
+    cg[:, :, :G] = codes.reshape(slots, n, G, 16)
+    # [slot, tile, step, g, r, j, h]: byte 4g + h of group 4 step + j of row 16 tile + r
+    b = cg.reshape(slots, NT, 16, S, 4, 4, 4).transpose(0, 1, 3, 5, 2, 4, 6).astype(np.uint32)
+    w = np.zeros(b.shape[:-1], np.uint32)
+    for h in range(4):
+        w |= (b[..., h] & 0xF) << (4 * h)
+        w |= (b[..., h] >> 4) << (16 + 4 * h)
+    c = w.astype("<u4")
+    sm = np.zeros((slots, n, 4 * S), np.uint32)
+    sm[:, :, :G] = scales.astype(np.uint32) | (mins.astype(np.uint32) << 16)
+    s = sm.reshape(slots, NT, 16, S, 4).transpose(0, 1, 3, 2, 4)
+    return np.ascontiguousarray(c).reshape(-1).view(np.uint8), np.ascontiguousarray(s.reshape(-1)).view(np.uint8)
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "q2", "q4"])
 @pytest.mark.parametrize("n,K", [(48, 224), (16, 32), (32, 512)])
 def test_pack_layout(fmt, n, K):
     rng = np.random.default_rng(n * 7 + K)
@@ -324,13 +346,15 @@ def test_pack_layout(fmt, n, K):
     got_c, got_s = q.codes.cpu().numpy(), q.scales.cpu().numpy()
     if fmt == "mxfp4":
         want_c, want_s = _tiles_mxfp4(m["codes"], m["scales"])
-    else:
+    elif fmt == "q2":
         want_c, want_s = _tiles_q2(m["codes"], m["scales"], m["mins"])
+    else:
+        want_c, want_s = _tiles_q4(m["codes"], m["scales"], m["mins"])
     assert np.array_equal(got_c, want_c)
     assert np.array_equal(got_s, want_s)
 
 
-@pytest.mark.parametrize("fmt", ["mxfp4", "q2"])
+@pytest.mark.parametrize("fmt", ["mxfp4", "q2", "q4"])
 def test_repeated_ids_within_a_token(fmt):
     """moe_dispatch takes ids from any source: tokens that name expert 3 twice
     give it 20 rows of 12 tokens (two 16-row column tiles, the second ragged)."""
