@@ -17,7 +17,10 @@ duration gives the roofline figure.
 Prints ONE JSON line.  Default workload: decode, T=1, d=4096, E=64, k=2,
 f=2048, MXFP4 experts.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 0..4]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 0..6]
+
+Workloads 0-4 are the configurations the targets are quoted on; 5 and 6
+run the 4-bit group-asymmetric pack at 16 tokens and at 1 token.
 """
 
 from __future__ import annotations
@@ -46,10 +49,14 @@ MEASURED_FFN_TRAFFIC = {
     1: (2 * (13158.5 + 4436.2) + (8.0 + 32.0)) * 1024,
     3: (2 * 469754.6 + 98485.0) * 1024,
     4: (2 * (27874.1 + 14211.8) + (128.0 + 512.0)) * 1024,
+    5: (2 * (43130.4 + 19618.4) + (310.9 + 512.0)) * 1024,
+    6: (2 * (15475.2 + 5207.2) + (8.0 + 32.0)) * 1024,
 }
 
 MX_BYTES_PER_EXPERT = lambda d, f: 3 * d * f // 2 + 3 * d * f // 32      # codes + e8m0 scales
 Q2_BYTES_PER_EXPERT = lambda d, f: 3 * d * f // 4 + 3 * d * f // 32 * 4  # codes + fp16 scale + min
+Q4_BYTES_PER_EXPERT = lambda d, f: 3 * d * f // 2 + 3 * d * f // 32 * 4  # codes + fp16 scale + min
+BYTES_PER_EXPERT = {"mxfp4": MX_BYTES_PER_EXPERT, "q2": Q2_BYTES_PER_EXPERT, "q4": Q4_BYTES_PER_EXPERT}
 
 
 def parse():
@@ -57,7 +64,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", type=int, default=1, choices=[0, 1, 2, 3, 4])
+    import synthetic
+    p.add_argument("--workload", type=int, default=1, choices=sorted(synthetic.WORKLOADS))
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-steps", type=int, default=0,
                    help="oracle steps timed on the host (0 = automatic)")
@@ -82,7 +90,8 @@ def copy_calibration(mib: int) -> None:
 
 def make_pool(torch, w, gen, dev):
     """One layer's experts on the device: uniform codes, scales as in the
-    synthetic recipe (e8m0 bytes 119..123; Q2 fp16 scale U[.005,.02], min U[-.04,0])."""
+    synthetic recipe (e8m0 bytes 119..123; Q2 fp16 scale U[.005,.02], min
+    U[-.04,0]; Q4 fp16 scale U[.001,.004], min U[-.04,0])."""
     import quantized_routed_moe_amd as qm
 
     E, d, f = w["E"], w["d"], w["f"]
@@ -95,8 +104,10 @@ def make_pool(torch, w, gen, dev):
             scales = torch.randint(119, 124, (E, n, K // 32), dtype=torch.uint8, device=dev, generator=gen)
             rows = qm.QMat(codes, scales, None, qm.MOE_LAYOUT_ROWS)
         else:
-            codes = torch.randint(0, 256, (E, n, K // 4), dtype=torch.uint8, device=dev, generator=gen)
-            sc = (torch.rand((E, n, K // 32), device=dev, generator=gen) * 0.015 + 0.005).half().view(torch.int16)
+            q2 = w["fmt"] == "q2"
+            codes = torch.randint(0, 256, (E, n, K // 4 if q2 else K // 2), dtype=torch.uint8, device=dev, generator=gen)
+            lo, span = (0.005, 0.015) if q2 else (0.001, 0.003)
+            sc = (torch.rand((E, n, K // 32), device=dev, generator=gen) * span + lo).half().view(torch.int16)
             mn = (torch.rand((E, n, K // 32), device=dev, generator=gen) * -0.04).half().view(torch.int16)
             rows = qm.QMat(codes, sc.contiguous(), mn.contiguous(), qm.MOE_LAYOUT_ROWS)
         return qm.pack_qmat(w["fmt"], rows, E, n, K)
@@ -155,7 +166,7 @@ def main():
     gen = torch.Generator(device=dev)
     gen.manual_seed(1000 * c + 123)
 
-    per_expert = (MX_BYTES_PER_EXPERT if w["fmt"] == "mxfp4" else Q2_BYTES_PER_EXPERT)(d, f)
+    per_expert = BYTES_PER_EXPERT[w["fmt"]](d, f)
     touched_guess = min(E, max(2, T * k)) * per_expert
     n_pools = 1 + math.ceil(512 * 2 ** 20 / touched_guess)
     n_pools = max(2, min(n_pools, 24))
@@ -364,7 +375,7 @@ def main():
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        n = args.cpu_sample_steps or {0: 200, 1: 6, 2: 4, 3: 1, 4: 3}[c]
+        n = args.cpu_sample_steps or {0: 200, 1: 6, 2: 4, 3: 1, 4: 3, 5: 3, 6: 6}[c]
         res["cpu_baseline"] = cpu_baseline(c, n)
     print(json.dumps(res), flush=True)
 

@@ -113,7 +113,7 @@ __device__ __forceinline__ void skinny_body(const FfnArgs& a, const Item& it, in
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: K-slice branches stay scalar
     const int col = lane & 15;
     const int s_beg = (S * wave) / KW, s_end = (S * (wave + 1)) / KW;
-    const int nk = ceil_div(s_end - s_beg, kCap);
+    const int nk = ceil_div(s_end - s_beg, kCapOf<FMT>);
     const bool fused = MODE == 1 && a.fuse_combine;
     uint8_t* mine = region[wave];
     const uint8_t* brow = mine + (col < RB ? col : RB - 1) * kBRowBytes;
@@ -159,7 +159,7 @@ __device__ __forceinline__ void skinny_body(const FfnArgs& a, const Item& it, in
     // `weights`) and waits until the staged token rows have landed.
     auto issue = [&](int c0, int kc, bool weights) {
         const int nreal = min(RB, it.r1 - c0);
-        const int s0 = s_beg + kc * kCap;
+        const int s0 = s_beg + kc * kCapOf<FMT>;
         // staged row c: sorted row min(c0 + c, r1 - 1) (pr is clamped alike)
         auto src_row = [&](int c) -> const uint16_t* {
             if constexpr (MODE == 0) return a.x + static_cast<size_t>(lane_value(pr, c) / a.k) * a.d;
@@ -189,7 +189,7 @@ __device__ __forceinline__ void skinny_body(const FfnArgs& a, const Item& it, in
         }
     };
     auto multiply = [&](int kc) {
-        mma_chunk<FMT, NM>(acc, w, brow, min(kCap, s_end - (s_beg + kc * kCap)));
+        mma_chunk<FMT, NM>(acc, w, brow, min(kCapOf<FMT>, s_end - (s_beg + kc * kCapOf<FMT>)));
     };
     // Sums the waves' partial tiles of the pass at c0 in wave order and
     // stores its columns.

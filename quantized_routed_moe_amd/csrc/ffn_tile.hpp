@@ -55,6 +55,11 @@ constexpr int kStepK = 128;    // K elements per step of the tile layout
 // 16-byte bank groups (row stride 1040 B = 260 banks = 4 mod 64).
 constexpr int kBRowBytes = kCap * kStepK * 2 + 16;
 
+// K steps per register chunk of a format: Q4 holds two (its 16 code bytes
+// and 16 scale bytes per step would not fit 128 VGPRs at four); a staged
+// token row still spans kCap steps, of which the chunk reads the first.
+template <int FMT> constexpr int kCapOf = FMT == MOE_FMT_Q4G32 ? 2 : kCap;
+
 template <int FMT> struct PieceBytes;
 template <> struct PieceBytes<MOE_FMT_MXFP4> { static constexpr int codes = 16, scales = 1; };
 template <> struct PieceBytes<MOE_FMT_Q2G32> { static constexpr int codes = 8, scales = 4; };
@@ -70,12 +75,12 @@ template <> struct WChunk<MOE_FMT_Q2G32> {
     u32x4 sm[kCap];       // fp16 scale | fp16 min << 16 of (row, group 4s+j), j = 0..3
 };
 template <> struct WChunk<MOE_FMT_Q4G32> {
-    u32x4 c[kCap];        // elements 8g..8g+7 of groups 4s..4s+3 (dword j: group 4s+j)
-    u32x4 sm[kCap];       // as Q2
+    u32x4 c[kCapOf<MOE_FMT_Q4G32>];     // elements 8g..8g+7 of groups 4s..4s+3 (dword j: group 4s+j)
+    u32x4 sm[kCapOf<MOE_FMT_Q4G32>];    // as Q2
 };
 
 // Weight loads per chunk and matrix (code blocks + scale loads).
-template <int FMT> constexpr int kWLoads = FMT == MOE_FMT_MXFP4 ? kCap + 1 : 2 * kCap;
+template <int FMT> constexpr int kWLoads = FMT == MOE_FMT_MXFP4 ? kCap + 1 : 2 * kCapOf<FMT>;
 
 // One 16-row tile of one matrix: this lane's code piece of step 0 and the
 // tile's scale block of step 0.
@@ -106,7 +111,7 @@ __device__ __forceinline__ void load_w(WChunk<FMT>& w, const WTile& t, int s0, i
         w.sraw = *reinterpret_cast<const uint32_t*>(t.scales + s * kWave + 4 * (lane & 15));
     }
 #pragma unroll
-    for (int u = 0; u < kCap; ++u) {
+    for (int u = 0; u < kCapOf<FMT>; ++u) {
         const size_t s = static_cast<size_t>(max(min(s0 + u, s1 - 1), 0));
         if constexpr (FMT == MOE_FMT_MXFP4) {
             w.c[u] = *reinterpret_cast<const u32x4*>(t.codes + s * kWave * 16);
@@ -158,7 +163,7 @@ __device__ __forceinline__ void mma_chunk(f32x4 (&acc)[kChains<FMT>][NM], const 
     const int lane = threadIdx.x & 63;
     const int g = lane >> 4;
 #pragma unroll
-    for (int u = 0; u < kCap; ++u) {
+    for (int u = 0; u < kCapOf<FMT>; ++u) {
         if (u >= nsteps) break;
         if constexpr (FMT == MOE_FMT_MXFP4) {
             float scl[NM];

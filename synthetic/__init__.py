@@ -42,6 +42,10 @@ WORKLOADS = {
             zipf=1.1),
     4: dict(name="two-bit", T=16, d=4096, E=64, k=2, f=2048, fmt="q2", router="device",
             zipf=1.1),
+    # the 4-bit group-asymmetric pack (not among the quoted configurations)
+    5: dict(name="four-bit", T=16, d=4096, E=64, k=2, f=2048, fmt="q4", router="device",
+            zipf=1.1),
+    6: dict(name="four-bit decode", T=1, d=4096, E=64, k=2, f=2048, fmt="q4", router="device"),
 }
 
 # stream ids within a workload
