@@ -34,6 +34,21 @@ def test_workload_full(c):
     _assert_layer_equals_steps(lay, g)
 
 
+@pytest.mark.parametrize("T,fmt", [(16, "mxfp4"), (1, "mxfp4"), (16, "q4")])
+def test_fanout_k4_full_shape(T, fmt):
+    """Top-4 fanout at the full expert shape (d=4096, f=2048, E=64): twice the
+    rows per token of the quoted workloads, and the combine over four slots
+    (not fused into the down projection)."""
+    case = synthetic.make_case(T, 4096, 64, 4, 2048, fmt, seed=7100 + T, zipf=1.1)
+    _say(f"k=4 fanout: T={T} d=4096 E=64 k=4 f=2048 {fmt}")
+    dc = device_case(case)
+    g = run_steps(dc)
+    assert g["status"] == 0
+    info = check_against_oracle(case, g, strict=True)
+    _say(f"  parity ok {info}")
+    _assert_layer_equals_steps(run_layer(dc), g)
+
+
 def _assert_layer_equals_steps(lay, g):
     bad = [n for n in ("ids", "w", "logits", "out") if not np.array_equal(lay[n], g[n])]
     if bad:
