@@ -20,7 +20,9 @@ f=2048, MXFP4 experts.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 0..6]
 
 Workloads 0-4 are the configurations the targets are quoted on; 5 and 6
-run the 4-bit group-asymmetric pack at 16 tokens and at 1 token.
+run the 4-bit group-asymmetric pack at 16 tokens and at 1 token.  --bank N
+runs the workload through an N-slot expert bank paged from pinned host
+memory instead (its own JSON line: paging included, PCIe roofline).
 """
 
 from __future__ import annotations
@@ -67,6 +69,8 @@ def parse():
     import synthetic
     p.add_argument("--workload", type=int, default=1, choices=sorted(synthetic.WORKLOADS))
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--bank", type=int, default=0, metavar="N",
+                   help="run the workload through an N-slot expert bank paged from pinned host memory")
     p.add_argument("--cpu-sample-steps", type=int, default=0,
                    help="oracle steps timed on the host (0 = automatic)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -141,6 +145,110 @@ def cpu_baseline(c, steps):
                        f"{total:.1f} s of host time; input generation not timed")
 
 
+def bank_main(args):
+    """--bank N: K layer calls of the workload through an N-slot expert bank
+    whose misses are copied from a pinned host pool of all E experts (one
+    layer).  Each call synchronises once (the host learns which experts have
+    rows), so the calls run eagerly.  `value` includes the paging; the
+    roofline figure is the host -> device copy rate of moe_bank_fetch against
+    PCIe 5.0 x16 (63 GB/s per direction)."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    import quantized_routed_moe_amd as qm
+    import synthetic
+
+    c, N = args.workload, args.bank
+    w = synthetic.WORKLOADS[c]
+    T, d, E, k, f = w["T"], w["d"], w["E"], w["k"], w["f"]
+    if not 1 <= N <= E:
+        raise SystemExit(f"--bank must be in 1..{E}")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1000 * c + 321)
+    pool = make_pool(torch, w, gen, dev)
+    bank = qm.SlotBank(pool, N, dev)
+    del pool
+    torch.cuda.empty_cache()
+    wr = (torch.randn((E, d), device=dev, generator=gen) / math.sqrt(d)).contiguous()
+    b = torch.from_numpy(synthetic.zipf_bias(E, w["zipf"])).to(dev) if w.get("zipf") else None
+    n_x = 4 if T >= 1024 else 61
+    xs = torch.randn((n_x, T, d), device=dev, generator=gen).to(torch.bfloat16).view(torch.int16).contiguous()
+    shape = qm.Shape(T, d, E, k, f)
+    ws = qm.alloc_workspace(shape, layer=True, device=dev)
+    for i in range(args.warmup):
+        bank.layer(xs[i % n_x], k, w_router=wr, bias=b, ws=ws)
+    torch.cuda.synchronize()
+    K = args.steps
+    tot = dict(active=0, hits=0, misses=0, passes=0, bytes_paged=0)
+    t0 = time.perf_counter()
+    for i in range(K):
+        bank.layer(xs[(args.warmup + i) % n_x], k, w_router=wr, bias=b, ws=ws)
+        for n in tot:
+            tot[n] += bank.last_stats[n]
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    assert qm.moe_read_device_status(ws) == 0
+
+    # the copy engine alone: moe_bank_fetch of min(N, 8) experts, HIP events
+    L = qm.lib()
+    hip = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+    stream = torch.cuda.current_stream().cuda_stream
+    n_f = min(N, 8)
+    le = (ctypes.c_int32 * n_f)(*range(n_f))
+    ls = (ctypes.c_int32 * n_f)(*range(n_f))
+    sl = bank.slots.c()
+    per_expert = BYTES_PER_EXPERT[w["fmt"]](d, f)
+    ev = [ctypes.c_void_p(), ctypes.c_void_p()]
+    for e_ in ev:
+        hip.hipEventCreate(ctypes.byref(e_))
+    rates = []
+    for _ in range(5):
+        hip.hipEventRecord(ev[0], ctypes.c_void_p(stream))
+        if L.moe_bank_fetch(ctypes.byref(bank.pool_c), ctypes.byref(sl), d, f, le, ls, n_f, ctypes.c_void_p(stream)):
+            raise RuntimeError("moe_bank_fetch failed")
+        hip.hipEventRecord(ev[1], ctypes.c_void_p(stream))
+        hip.hipEventSynchronize(ev[1])
+        ms = ctypes.c_float()
+        hip.hipEventElapsedTime(ctypes.byref(ms), ev[0], ev[1])
+        rates.append(n_f * per_expert / (ms.value / 1e3) / 1e9)
+    for e_ in ev:
+        hip.hipEventDestroy(e_)
+    # the fetched slots now hold experts 0..n_f-1: the bank's books are stale
+    bank.state = qm.BankState(E, N)
+    pcie = float(np.median(rates))
+    peak = 63.0
+    res = {
+        "metric": "MoE layer tokens/s through an expert slot bank (paging included)",
+        "value": round(T * K / elapsed, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / K * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w['name']} through a {N}-slot bank: T={T} d={d} E={E} k={k} f={f} {w['fmt']}",
+                   "T": T, "d": d, "E": E, "k": k, "f": f, "format": w["fmt"], "bank_slots": N,
+                   "parallelism": "none (1 GPU)"},
+        "launch": "eager; one host synchronisation per call",
+        "bank": {"hit_rate": round(tot["hits"] / max(tot["active"], 1), 4),
+                 "misses_per_call": round(tot["misses"] / K, 3), "passes_per_call": round(tot["passes"] / K, 3),
+                 "bytes_paged_per_call": round(tot["bytes_paged"] / K),
+                 "device_bytes": N * per_expert, "pool_host_bytes": E * per_expert},
+        "roofline": {"bound": "pcie", "achieved": round(pcie, 2), "peak": peak, "unit": "GB/s",
+                     "frac": round(pcie / peak, 4), "traffic": None,
+                     "kernel": f"moe_bank_fetch of {n_f} experts (host -> device DMA)"},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -150,6 +258,9 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
                                    "(expert-parallel sharding is designed, not built)"}))
         sys.exit(2)
+    if args.bank:
+        bank_main(args)
+        return
 
     import numpy as np
     import torch

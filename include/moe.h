@@ -187,9 +187,12 @@ int moe_pack_qmat(const moe_qmat* src, const moe_qmat* dst, int32_t slots, int32
 /* The experts of one layer.  gate and up are n=f rows of K=d; down is n=d
    rows of K=f.  All three use the same format and MOE_LAYOUT_TILES.  Expert e lives in pack slot
    slot_of_expert[e] (device int32 [E]) or, when slot_of_expert is NULL, in
-   slot e (then num_slots >= E is required).  A routed expert whose slot is
-   outside [0, num_slots) is not computed: its y rows are written as zeros and
-   MOE_DEV_BAD_SLOT is raised. */
+   slot e (then num_slots >= E is required).  slot_of_expert[e] ==
+   MOE_SLOT_SKIP leaves expert e out of this call: its y rows are not written
+   and no status is raised (a slot-bank pass that computes other experts).
+   A routed expert whose slot is otherwise outside [0, num_slots) is not
+   computed: its y rows are written as zeros and MOE_DEV_BAD_SLOT is raised. */
+enum { MOE_SLOT_SKIP = -2 };
 typedef struct moe_experts {
     moe_qmat gate, up, down;
     const int32_t* slot_of_expert;
@@ -251,6 +254,87 @@ int moe_layer(const moe_shape* shape, const uint16_t* x, const float* w_router,
               const float* bias, float* logits, const moe_experts* experts,
               int32_t* topk_ids, float* topk_w, float* out, void* ws, size_t ws_bytes,
               hipStream_t stream);
+
+/* ---- Slot bank: N < E resident expert slots in HBM, paged from a host pool.
+
+   The pages' SSD sidecar keeps the routed experts outside the dense model
+   and pages them through a bounded cache of expert slots, whose size trades
+   memory for fewer reads (Anemll/ds4-ssd README, sections "Run SSD Sidecar
+   Mode": --moe-slot-bank caps the resident routed-expert slots, --ssd-cache
+   sizes the bank in bytes; the 10100.com article on ds4-ssd, section 核心功能:
+   routed experts paged through a slot-bank cache).  Here the pool of all E
+   experts sits in pinned host memory (standing in for the sidecar files) and
+   the bank is a moe_experts pack of num_slots slots in HBM; misses are copied
+   host -> device by the DMA engines.  The pages name no replacement policy;
+   this library evicts the least recently used slot.
+
+   moe_bank is host-side bookkeeping; the caller allocates its arrays. */
+typedef struct moe_bank {
+    int32_t E;                /* experts in the pool, 1..64 */
+    int32_t num_slots;        /* N, 1..E: slots of the device bank */
+    int32_t* slot_of_expert;  /* HOST int32 [E]: slot holding expert e, or -1 */
+    int32_t* expert_of_slot;  /* HOST int32 [N]: expert held by slot s, or -1 (empty) */
+    uint64_t* last_use;       /* HOST uint64 [N]: request stamp of the slot's last use */
+    uint64_t clock;           /* request stamps handed out so far */
+} moe_bank;
+
+/* Empties the bank (every slot -1, stamps and clock 0).  Errors:
+   MOE_ERR_NULL, MOE_ERR_SHAPE (E outside 1..64, N outside 1..E). */
+int moe_bank_reset(moe_bank* bank);
+
+/* Plans one pass over the distinct experts want[0..n_want) (HOST int32,
+   ids in [0, E), no repeats, n_want <= num_slots):
+     - a wanted expert already resident is a hit;
+     - each miss, in `want` order, takes the lowest-numbered empty slot, else
+       the least recently used slot whose expert is not wanted in this pass
+       (the evicted expert's slot_of_expert becomes -1);
+     - then every wanted expert's slot is stamped ++clock, in `want` order.
+   Out (HOST): load_expert / load_slot int32 [n_want], the misses in order,
+   and *n_load, their count.  The bank state is updated; the copies are the
+   caller's (moe_bank_fetch).  Errors (bank unchanged): MOE_ERR_NULL,
+   MOE_ERR_SHAPE (n_want outside 0..num_slots, an id outside [0, E) or
+   repeated). */
+int moe_bank_plan(moe_bank* bank, const int32_t* want, int32_t n_want, int32_t* load_expert,
+                  int32_t* load_slot, int32_t* n_load);
+
+/* Enqueues on `stream` the host -> device copies of the planned loads:
+   expert load_expert[i] of `pool` into slot load_slot[i] of `slots`, for
+   i < n_load (HOST arrays), every array of gate, up and down.  pool: the
+   packs of all E experts in HOST memory (pinned, e.g. hipHostMalloc, for
+   asynchronous DMA; num_slots = E, slot_of_expert NULL); slots: the device
+   bank (num_slots = N); same fmt, MOE_LAYOUT_TILES, hidden size d and
+   expert size f.  Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_FORMAT,
+   MOE_ERR_HIP. */
+int moe_bank_fetch(const moe_experts* pool, const moe_experts* slots, int32_t d, int32_t f,
+                   const int32_t* load_expert, const int32_t* load_slot, int32_t n_load,
+                   hipStream_t stream);
+
+/* Counters of one moe_layer_banked call (HOST). */
+typedef struct moe_bank_stats {
+    int32_t active;           /* distinct routed experts */
+    int32_t hits;             /* of them already resident */
+    int32_t misses;           /* paged in */
+    int32_t passes;           /* FFN passes (ceil(active / N), at least 1) */
+    int64_t bytes_paged;      /* host -> device bytes enqueued */
+} moe_bank_stats;
+
+/* moe_layer over a slot bank.  Routes and dispatches on the device, then
+   SYNCHRONISES `stream` to read the per-expert row counts.  The active
+   experts, resident ones first, then in id order, are split into passes of
+   at most N; each pass plans (moe_bank_plan), pages its misses in
+   (moe_bank_fetch), writes `slot_map` (DEVICE int32 [E]: the pass's slots,
+   MOE_SLOT_SKIP elsewhere) with a one-workgroup kernel and runs
+   moe_expert_ffn on the bank; one combine follows.  Everything after the
+   synchronisation is enqueued on `stream` in that order, so a pass's loads
+   never overwrite a slot an earlier pass reads.  `slots` is the device bank
+   (its slot_of_expert is ignored); `ws` as for moe_layer.  Results equal
+   moe_layer's bit for bit (an expert's rows do not depend on its slot or
+   pass).  stats may be NULL.  Errors: those of the calls above. */
+int moe_layer_banked(const moe_shape* shape, const uint16_t* x, const float* w_router,
+                     const float* bias, float* logits, const moe_experts* pool, moe_bank* bank,
+                     const moe_experts* slots, int32_t* slot_map, int32_t* topk_ids, float* topk_w,
+                     float* out, void* ws, size_t ws_bytes, hipStream_t stream,
+                     moe_bank_stats* stats);
 
 /* Human-readable name of a status code (static storage). */
 const char* moe_status_str(int status);

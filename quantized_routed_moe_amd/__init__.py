@@ -43,11 +43,14 @@ FORMATS = {"mxfp4": MOE_FMT_MXFP4, "q2": MOE_FMT_Q2G32, "q4": MOE_FMT_Q4G32}
 MOE_LAYOUT_ROWS = 0
 MOE_LAYOUT_TILES = 1
 
+MOE_SLOT_SKIP = -2
+
 # Every symbol include/moe.h declares.
 EXPORTS = (
     "moe_workspace_bytes", "moe_workspace_init", "moe_route_topk", "moe_dispatch",
     "moe_expert_ffn", "moe_combine", "moe_layer_workspace_bytes", "moe_layer",
     "moe_status_str", "moe_read_device_status", "moe_qmat_bytes", "moe_pack_qmat",
+    "moe_bank_reset", "moe_bank_plan", "moe_bank_fetch", "moe_layer_banked",
 )
 
 
@@ -70,6 +73,16 @@ class moe_qmat(ctypes.Structure):
 class moe_experts(ctypes.Structure):
     _fields_ = [("gate", moe_qmat), ("up", moe_qmat), ("down", moe_qmat),
                 ("slot_of_expert", ctypes.c_void_p), ("num_slots", ctypes.c_int32)]
+
+
+class moe_bank(ctypes.Structure):
+    _fields_ = [("E", ctypes.c_int32), ("num_slots", ctypes.c_int32), ("slot_of_expert", ctypes.c_void_p),
+                ("expert_of_slot", ctypes.c_void_p), ("last_use", ctypes.c_void_p), ("clock", ctypes.c_uint64)]
+
+
+class moe_bank_stats(ctypes.Structure):
+    _fields_ = [("active", ctypes.c_int32), ("hits", ctypes.c_int32), ("misses", ctypes.c_int32),
+                ("passes", ctypes.c_int32), ("bytes_paged", ctypes.c_int64)]
 
 
 _LIB = None
@@ -103,6 +116,10 @@ def lib() -> ctypes.CDLL:
             "moe_read_device_status": (_I, [_P, _P, _P]),
             "moe_qmat_bytes": (_SZ, [_I, _I, _I, _I, _I, _P, _P, _P]),
             "moe_pack_qmat": (_I, [_P, _P, _I, _I, _I, _P]),
+            "moe_bank_reset": (_I, [_P]),
+            "moe_bank_plan": (_I, [_P, _P, _I, _P, _P, _P]),
+            "moe_bank_fetch": (_I, [_P, _P, _I, _I, _P, _P, _I, _P]),
+            "moe_layer_banked": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -368,3 +385,99 @@ def layer(x, experts: Experts, k: int, *, w_router=None, bias=None, logits=None,
         ws = alloc_workspace(shape, layer=True, device=dev, stream=stream)
     moe_layer(shape, x, w_router, bias, logits, experts, ids, w, out, ws, stream)
     return out, ids, w, logits
+
+
+# ------------------------------------------------------------------ slot bank
+
+class BankState:
+    """Host bookkeeping of an N-slot bank over E experts (moe_bank; the
+    arrays are numpy, owned here)."""
+
+    def __init__(self, E: int, num_slots: int):
+        self.slot_of_expert = np.full(E, -1, dtype=np.int32)
+        self.expert_of_slot = np.full(num_slots, -1, dtype=np.int32)
+        self.last_use = np.zeros(num_slots, dtype=np.uint64)
+        self.c = moe_bank(E, num_slots, self.slot_of_expert.ctypes.data, self.expert_of_slot.ctypes.data,
+                          self.last_use.ctypes.data, 0)
+        _check(lib().moe_bank_reset(ctypes.byref(self.c)), "moe_bank_reset")
+
+    def plan(self, want) -> list:
+        """moe_bank_plan over the distinct expert ids `want`; returns the
+        loads [(expert, slot), ...]."""
+        w = np.ascontiguousarray(want, dtype=np.int32)
+        n = len(w)
+        le = np.zeros(max(n, 1), dtype=np.int32)
+        ls = np.zeros(max(n, 1), dtype=np.int32)
+        nl = ctypes.c_int32(0)
+        _check(lib().moe_bank_plan(ctypes.byref(self.c), w.ctypes.data if n else None, n, le.ctypes.data,
+                                   ls.ctypes.data, ctypes.byref(nl)), "moe_bank_plan")
+        return [(int(le[i]), int(ls[i])) for i in range(nl.value)]
+
+
+def _host_qmat(m: QMat, fmt: int) -> moe_qmat:
+    for t in (m.codes, m.scales):
+        if t.is_cuda or not t.is_contiguous():
+            raise ValueError("a host pool holds contiguous CPU tensors")
+    return moe_qmat(fmt, MOE_LAYOUT_TILES, m.codes.data_ptr(), m.scales.data_ptr(), None)
+
+
+class SlotBank:
+    """Experts paged through `num_slots` device slots from a pool of all E
+    experts in pinned host memory (moe_layer_banked).  `experts` is a device
+    pack of the E experts (tile layout); its bytes are copied once into the
+    pinned pool, after which the device pack may be dropped."""
+
+    def __init__(self, experts: Experts, num_slots: int, device="cuda"):
+        torch = _torch()
+        E = experts.num_slots
+        self.fmt, self.E, self.num_slots, self.d, self.f = experts.fmt, E, num_slots, experts.d, experts.f
+        fmtc = FORMATS[self.fmt]
+
+        def host_copy(t):
+            h = torch.empty(t.numel(), dtype=torch.uint8, pin_memory=True)
+            h.copy_(t.view(torch.uint8).reshape(-1))
+            return h
+
+        def bank_mat(n, K):
+            cb, sb, _ = moe_qmat_bytes(self.fmt, MOE_LAYOUT_TILES, num_slots, n, K)
+            return QMat(torch.zeros(cb, dtype=torch.uint8, device=device),
+                        torch.zeros(sb, dtype=torch.uint8, device=device), None, MOE_LAYOUT_TILES)
+
+        self.pool = {m: QMat(host_copy(getattr(experts, m).codes), host_copy(getattr(experts, m).scales), None,
+                             MOE_LAYOUT_TILES) for m in ("gate", "up", "down")}
+        self.pool_c = moe_experts(_host_qmat(self.pool["gate"], fmtc), _host_qmat(self.pool["up"], fmtc),
+                                  _host_qmat(self.pool["down"], fmtc), None, E)
+        self.slots = Experts(self.fmt, bank_mat(self.f, self.d), bank_mat(self.f, self.d), bank_mat(self.d, self.f),
+                             None, num_slots, self.d, self.f)
+        self.slot_map = torch.full((E,), MOE_SLOT_SKIP, dtype=torch.int32, device=device)
+        self.state = BankState(E, num_slots)
+        self.last_stats = None
+
+    def layer(self, x, k: int, *, w_router=None, bias=None, logits=None, ws=None, stream=None):
+        """One layer call through the bank (synchronises the stream once);
+        returns (out, topk_ids, topk_w, logits) and sets last_stats."""
+        torch = _torch()
+        T, d = x.shape
+        shape = Shape(T, d, self.E, k, self.f)
+        dev = x.device
+        if logits is None:
+            logits = torch.empty((T, self.E), dtype=torch.float32, device=dev)
+        ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+        w = torch.empty((T, k), dtype=torch.float32, device=dev)
+        out = torch.empty((T, d), dtype=torch.float32, device=dev)
+        if ws is None:
+            ws = alloc_workspace(shape, layer=True, device=dev, stream=stream)
+        st = moe_bank_stats()
+        sl = self.slots.c()
+        rc = lib().moe_layer_banked(
+            ctypes.byref(shape.c()), _ptr(x, (torch.int16, torch.bfloat16, torch.uint16), "x"),
+            _ptr(w_router, torch.float32, "w_router", allow_none=True),
+            _ptr(bias, torch.float32, "bias", allow_none=True), _ptr(logits, torch.float32, "logits"),
+            ctypes.byref(self.pool_c), ctypes.byref(self.state.c), ctypes.byref(sl),
+            _ptr(self.slot_map, torch.int32, "slot_map"), _ptr(ids, torch.int32, "topk_ids"),
+            _ptr(w, torch.float32, "topk_w"), _ptr(out, torch.float32, "out"), _ptr(ws, name="ws"),
+            ws.numel() * ws.element_size(), _stream(stream), ctypes.byref(st))
+        _check(rc, "moe_layer_banked")
+        self.last_stats = dict(active=st.active, hits=st.hits, misses=st.misses, passes=st.passes,
+                               bytes_paged=int(st.bytes_paged))
+        return out, ids, w, logits

@@ -8,14 +8,19 @@
 
 #include "../../include/moe.h"
 #include "kernels.hpp"
+#include "workspace.hpp"
 
 namespace {
 
 using qrmoe::FfnArgs;
 
-constexpr size_t kHeader = 256;
-
-size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+using qrmoe::act_bytes;
+using qrmoe::align256;
+using qrmoe::flag_bytes;
+using qrmoe::kHeader;
+using qrmoe::ffn_ws_bytes;
+using qrmoe::LayerCarve;
+using qrmoe::layer_carve;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -29,26 +34,6 @@ int check_shape(const moe_shape* s) {
     return MOE_OK;
 }
 
-size_t act_bytes(const moe_shape& s) { return align256(static_cast<size_t>(s.T) * s.k * s.f * 2); }
-
-size_t flag_bytes(const moe_shape& s) { return align256(static_cast<size_t>(qrmoe::grouped_flag_count(s)) * 8); }
-
-size_t ffn_ws_bytes(const moe_shape& s) { return kHeader + act_bytes(s) + flag_bytes(s); }
-
-struct LayerCarve {
-    size_t offsets, perm, inv, y, total;
-};
-
-LayerCarve layer_carve(const moe_shape& s) {
-    LayerCarve c;
-    const size_t pairs = static_cast<size_t>(s.T) * s.k;
-    c.offsets = ffn_ws_bytes(s);
-    c.perm = c.offsets + align256(static_cast<size_t>(s.E + 1) * 4);
-    c.inv = c.perm + align256(pairs * 4);
-    c.y = c.inv + align256(pairs * 4);
-    c.total = c.y + align256(pairs * s.d * 4);
-    return c;
-}
 
 // Array sizes of one (fmt, layout) matrix; false when the request is invalid.
 bool qmat_sizes(int fmt, int layout, int slots, int n, int K, size_t* codes, size_t* scales, size_t* mins) {

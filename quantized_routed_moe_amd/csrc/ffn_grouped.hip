@@ -178,7 +178,12 @@ __device__ __forceinline__ void grouped_unit(const FfnArgs& a, int unit, unsigne
     const int r_base = a.offsets[e] + mti * kGM;
     const int nvalid = min(kGM, a.offsets[e + 1] - r_base);
     const int slot = a.slot_of_expert ? a.slot_of_expert[e] : e;
-    if (slot < 0 || slot >= a.num_slots) {
+    if (slot < 0 || slot >= a.num_slots) {      // MOE_SLOT_SKIP: left out of this call, rows untouched
+        const bool skip = slot == MOE_SLOT_SKIP;
+        if (skip) {
+            if (CHAIN && MODE == 0) raise_flag(a.flags + unit, tag);
+            return;
+        }
         if (tid == 0 && nt == 0 && mti == 0) raise_status(a.status, MOE_DEV_BAD_SLOT);
         if (MODE == 1) {
             for (int i = tid; i < nvalid * kGN; i += kGThreads)

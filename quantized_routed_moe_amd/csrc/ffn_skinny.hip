@@ -275,11 +275,12 @@ __device__ __forceinline__ void skinny_body(const FfnArgs& a, const Item& it, in
     }
 }
 
-// An item whose expert has no valid slot is skipped: its y rows read as zero
-// and MOE_DEV_BAD_SLOT is raised.
+// An item whose expert is left out of the call (MOE_SLOT_SKIP) writes
+// nothing; one whose slot is otherwise invalid is skipped too, but its y rows
+// read as zero and MOE_DEV_BAD_SLOT is raised.
 template <int FMT, int MODE, int KW, int RB, bool PERM_LDS = false>
 __device__ __forceinline__ void run_item(const FfnArgs& a, const Item& it, int n0, const int32_t* perm) {
-    if (it.e < 0) return;
+    if (it.e < 0 || it.slot == MOE_SLOT_SKIP) return;
     if (it.slot < 0 || it.slot >= a.num_slots) {
         if (threadIdx.x == 0 && n0 == 0) raise_status(a.status, MOE_DEV_BAD_SLOT);
         if (MODE == 1) zero_y_tile(a, n0, it.r0, it.r1);

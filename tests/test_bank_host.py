@@ -1,0 +1,212 @@
+"""The expert slot bank on the host (no GPU needed).
+
+The oracle (oracle/bank.py) is pinned to least-recently-used replacement by
+a textbook reference string, by the LRU stack-distance property and by a
+multi-expert case worked out by hand; the library's moe_bank_plan must then
+equal it exactly (integer work) on random pass sequences, and reject every
+invalid request with the documented status."""
+
+import ctypes
+
+import numpy as np
+import pytest
+
+import quantized_routed_moe_amd as qm
+from oracle import bank as ob
+
+A16 = 0x10000          # fake, aligned "device" addresses (never dereferenced)
+
+
+# ---------------------------------------------------------------- oracle pins
+
+def test_oracle_textbook_reference_string():
+    # The classic 20-reference string of the operating-systems textbooks
+    # (Silberschatz, Galvin, Gagne, "Operating System Concepts", page
+    # replacement): with 3 frames LRU takes 12 faults (FIFO 15, OPT 9).
+    refs = [7, 0, 1, 2, 0, 3, 0, 4, 2, 3, 0, 3, 2, 1, 2, 0, 1, 7, 0, 1]
+    b = ob.SlotBank(8, 3)
+    faults = sum(len(b.plan([e])) for e in refs)
+    assert faults == 12
+    assert sorted(e for e in b.holder) == [0, 1, 7]
+
+
+def test_oracle_lru_stack_distance():
+    # A reference hits an LRU cache of N slots iff fewer than N distinct
+    # other keys were referenced since its previous reference.
+    rng = np.random.default_rng(5)
+    for N in (1, 2, 3, 5, 8):
+        refs = [int(v) for v in rng.integers(0, 12, size=400)]
+        b = ob.SlotBank(12, N)
+        for i, e in enumerate(refs):
+            hit = len(b.plan([e])) == 0
+            prev = [j for j in range(i) if refs[j] == e]
+            expect = bool(prev) and len(set(refs[prev[-1] + 1:i])) < N
+            assert hit == expect, (N, i)
+
+
+def test_oracle_hand_worked_passes():
+    # E = 6, N = 3; loads derived by hand from the rules in oracle/bank.py.
+    calls = [[0, 1], [2], [3, 0], [4, 5], [0, 1, 2, 3]]
+    got = ob.run_layer_calls(6, 3, calls)
+    assert [c["loads"] for c in got] == [
+        [[(0, 0), (1, 1)]],
+        [[(2, 2)]],
+        [[(3, 1)]],
+        [[(4, 2), (5, 0)]],
+        [[(0, 2), (1, 0)], [(2, 1)]],     # 3 resident first: passes [3, 0, 1] and [2]
+    ]
+    assert [c["hits"] for c in got] == [0, 0, 1, 0, 1]
+    assert got[-1]["holder"] == [1, 2, 0]
+
+
+def test_oracle_invariants():
+    rng = np.random.default_rng(9)
+    E = 16
+    seen = set()
+    big = ob.SlotBank(E, E)
+    misses = 0
+    for _ in range(200):
+        want = [int(v) for v in rng.choice(E, size=int(rng.integers(1, 5)), replace=False)]
+        seen |= set(want)
+        misses += len(big.plan(want))
+    assert misses == len(seen)            # N >= E: compulsory misses only
+    for N in (2, 4, 7):
+        b = ob.SlotBank(E, N)
+        for _ in range(300):
+            want = [int(v) for v in rng.choice(E, size=int(rng.integers(0, N + 1)), replace=False)]
+            before = list(b.holder)
+            loads = b.plan(want)
+            held = [e for e in b.holder if e is not None]
+            assert len(held) == len(set(held))
+            assert set(want) <= set(held)
+            for e, s in loads:
+                assert before[s] not in want
+            assert len(loads) == len([e for e in want if e not in before])
+
+
+# ------------------------------------------------- library against the oracle
+
+@pytest.mark.parametrize("E,N", [(8, 1), (8, 3), (16, 5), (64, 8), (64, 64), (33, 32)])
+def test_plan_equals_oracle(E, N):
+    rng = np.random.default_rng(1000 * E + N)
+    lib_b = qm.BankState(E, N)
+    ora = ob.SlotBank(E, N)
+    for step in range(400):
+        n = int(rng.integers(0, N + 1))
+        want = [int(v) for v in rng.choice(E, size=n, replace=False)]
+        assert lib_b.plan(want) == ora.plan(want), step
+        holder = [-1 if h is None else h for h in ora.holder]
+        assert lib_b.expert_of_slot.tolist() == holder
+        for e in range(E):
+            s = ora.slot_of(e)
+            assert lib_b.slot_of_expert[e] == (-1 if s is None else s)
+
+
+def test_layer_pass_order_is_the_oracles():
+    # moe_layer_banked plans its passes with moe_bank_plan over the active
+    # experts, resident first, then the rest, in id order (the oracle's
+    # layer_passes); replay that on the host with the library's planner.
+    rng = np.random.default_rng(3)
+    E, N = 64, 8
+    lib_b = qm.BankState(E, N)
+    calls = [sorted(set(int(v) for v in rng.integers(0, E, size=int(rng.integers(1, 40))))) for _ in range(60)]
+    expect = ob.run_layer_calls(E, N, calls)
+    for c, ex in zip(calls, expect):
+        res = [e for e in c if lib_b.slot_of_expert[e] >= 0]
+        order = res + [e for e in c if lib_b.slot_of_expert[e] < 0]
+        passes = [order[i:i + N] for i in range(0, len(order), N)]
+        assert [lib_b.plan(p) for p in passes] == ex["loads"]
+
+
+# ----------------------------------------------------------------- validation
+
+def _bank(E=8, N=3):
+    return qm.BankState(E, N)
+
+
+def test_plan_rejects_bad_requests():
+    b = _bank()
+    L = qm.lib()
+    le = (ctypes.c_int32 * 8)()
+    ls = (ctypes.c_int32 * 8)()
+    n = ctypes.c_int32(-5)
+
+    def plan(ids, count=None):
+        arr = (ctypes.c_int32 * max(len(ids), 1))(*ids)
+        return L.moe_bank_plan(ctypes.byref(b.c), arr, len(ids) if count is None else count, le, ls,
+                               ctypes.byref(n))
+
+    before = (b.slot_of_expert.copy(), b.expert_of_slot.copy(), b.last_use.copy(), b.c.clock)
+    assert plan([1, 1]) == qm.MOE_ERR_SHAPE          # repeated id
+    assert plan([8]) == qm.MOE_ERR_SHAPE             # id >= E
+    assert plan([-1]) == qm.MOE_ERR_SHAPE
+    assert plan([0, 1, 2, 3]) == qm.MOE_ERR_SHAPE    # more than N
+    assert plan([0], count=-1) == qm.MOE_ERR_SHAPE
+    assert L.moe_bank_plan(ctypes.byref(b.c), None, 1, le, ls, ctypes.byref(n)) == qm.MOE_ERR_NULL
+    assert L.moe_bank_plan(ctypes.byref(b.c), None, 0, None, None, None) == qm.MOE_ERR_NULL
+    assert L.moe_bank_plan(None, None, 0, None, None, ctypes.byref(n)) == qm.MOE_ERR_NULL
+    after = (b.slot_of_expert, b.expert_of_slot, b.last_use, b.c.clock)
+    assert all(np.array_equal(x, y) for x, y in zip(before[:3], after[:3])) and before[3] == after[3]
+    assert plan([], count=0) == qm.MOE_OK and n.value == 0
+
+
+@pytest.mark.parametrize("E,N", [(0, 1), (65, 8), (8, 0), (8, 9)])
+def test_bank_shape_limits(E, N):
+    st = qm.moe_bank(E, N, A16, A16, A16, 0)
+    assert qm.lib().moe_bank_reset(ctypes.byref(st)) == qm.MOE_ERR_SHAPE
+
+
+def test_bank_null_arrays():
+    st = qm.moe_bank(8, 2, None, A16, A16, 0)
+    assert qm.lib().moe_bank_reset(ctypes.byref(st)) == qm.MOE_ERR_NULL
+    assert qm.lib().moe_bank_reset(None) == qm.MOE_ERR_NULL
+
+
+def _qm(fmt=qm.MOE_FMT_MXFP4, layout=qm.MOE_LAYOUT_TILES, codes=A16, scales=A16, mins=None):
+    return qm.moe_qmat(fmt, layout, codes, scales, mins)
+
+
+def _ex(num_slots, **kw):
+    return qm.moe_experts(_qm(**kw), _qm(**kw), _qm(**kw), None, num_slots)
+
+
+def test_fetch_validation():
+    L = qm.lib()
+    pool, slots = _ex(8), _ex(3)
+    le = (ctypes.c_int32 * 1)(0)
+    ls = (ctypes.c_int32 * 1)(0)
+    assert L.moe_bank_fetch(None, ctypes.byref(slots), 256, 128, le, ls, 1, None) == qm.MOE_ERR_NULL
+    assert L.moe_bank_fetch(ctypes.byref(_ex(8, fmt=qm.MOE_FMT_Q2G32)), ctypes.byref(slots), 256, 128, le, ls, 1,
+                            None) == qm.MOE_ERR_FORMAT
+    assert L.moe_bank_fetch(ctypes.byref(_ex(8, layout=qm.MOE_LAYOUT_ROWS)), ctypes.byref(slots), 256, 128, le, ls,
+                            1, None) == qm.MOE_ERR_FORMAT
+    assert L.moe_bank_fetch(ctypes.byref(pool), ctypes.byref(slots), 256, 100, le, ls, 1, None) == qm.MOE_ERR_SHAPE
+    bad_e = (ctypes.c_int32 * 1)(8)
+    bad_s = (ctypes.c_int32 * 1)(3)
+    assert L.moe_bank_fetch(ctypes.byref(pool), ctypes.byref(slots), 256, 128, bad_e, ls, 1, None) == qm.MOE_ERR_SHAPE
+    assert L.moe_bank_fetch(ctypes.byref(pool), ctypes.byref(slots), 256, 128, le, bad_s, 1, None) == qm.MOE_ERR_SHAPE
+    assert L.moe_bank_fetch(ctypes.byref(pool), ctypes.byref(slots), 256, 128, None, ls, 1, None) == qm.MOE_ERR_NULL
+    assert L.moe_bank_fetch(ctypes.byref(pool), ctypes.byref(slots), 256, 128, le, ls, 0, None) == qm.MOE_OK
+
+
+def test_layer_banked_validation():
+    L = qm.lib()
+    b = _bank(8, 3)
+    shape = qm.moe_shape(4, 256, 8, 2, 128)
+    pool, slots = _ex(8), _ex(3)
+    st = qm.moe_bank_stats()
+
+    def call(shape=shape, pool=pool, slots=slots, bank=b.c, slot_map=A16, ws_bytes=1 << 30, ws=A16):
+        return L.moe_layer_banked(ctypes.byref(shape), A16, A16, None, A16, ctypes.byref(pool), ctypes.byref(bank),
+                                  ctypes.byref(slots), slot_map, A16, A16, A16, ws, ws_bytes, None, ctypes.byref(st))
+
+    assert call(slot_map=None) == qm.MOE_ERR_NULL
+    assert call(ws=None) == qm.MOE_ERR_NULL
+    assert call(slot_map=A16 + 2) == qm.MOE_ERR_ALIGN
+    assert call(shape=qm.moe_shape(4, 256, 16, 2, 128)) == qm.MOE_ERR_SHAPE       # bank E != shape E
+    assert call(shape=qm.moe_shape(4, 250, 8, 2, 128)) == qm.MOE_ERR_SHAPE        # invalid shape
+    assert call(slots=_ex(4)) == qm.MOE_ERR_SHAPE                                  # bank N != slots
+    assert call(pool=_ex(7)) == qm.MOE_ERR_SHAPE                                   # pool smaller than E
+    assert call(ws_bytes=1024) == qm.MOE_ERR_WORKSPACE
+    assert call(shape=qm.moe_shape(0, 256, 8, 2, 128)) == qm.MOE_OK               # T = 0: nothing
+    assert (st.active, st.hits, st.misses, st.passes, st.bytes_paged) == (0, 0, 0, 0, 0)
