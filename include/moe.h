@@ -255,6 +255,28 @@ int moe_layer(const moe_shape* shape, const uint16_t* x, const float* w_router,
               int32_t* topk_ids, float* topk_w, float* out, void* ws, size_t ws_bytes,
               hipStream_t stream);
 
+/* ---- Shared expert: one always-on SwiGLU expert beside the routed ones.
+
+   DeepSeek blocks add a shared expert that every token passes through; the
+   pages name it only through a decode knob that prefetches its down
+   projection (Anemll/ds4-ssd README, section "Experimental Pro Support",
+   shared-down decode prefetch).  Reading taken: weight 1, same SwiGLU and
+   rounding points as a routed expert, added after the routed terms:
+     out[t][m] = sum_{j<k} topk_w[t][j] * y[inv[t*k+j]][m] + ys[t][m]
+     ys[t] = Wd_s . bf16_rne( silu(Wg_s . x[t]) * (Wu_s . x[t]) )
+   `shared` is a pack of the same format and layout as `experts` (slot 0 is
+   used; its slot_of_expert is ignored).  Its rows are computed in the same
+   launches as the routed experts' (its T rows follow the T*k routed rows in
+   act and y, and its down weights are prefetched with theirs at decode).
+   The workspace is moe_layer_shared_workspace_bytes(shape) (offsets, perm,
+   inv and y carved from it).  Errors: as moe_layer, plus MOE_ERR_FORMAT /
+   MOE_ERR_NULL / MOE_ERR_ALIGN for the shared pack. */
+size_t moe_layer_shared_workspace_bytes(const moe_shape* shape);
+int moe_layer_shared(const moe_shape* shape, const uint16_t* x, const float* w_router,
+                     const float* bias, float* logits, const moe_experts* experts,
+                     const moe_experts* shared, int32_t* topk_ids, float* topk_w, float* out,
+                     void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* ---- Slot bank: N < E resident expert slots in HBM, paged from a host pool.
 
    The pages' SSD sidecar keeps the routed experts outside the dense model

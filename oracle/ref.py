@@ -248,8 +248,8 @@ def expert_ffn(x_bits, k: int, offsets, perm, gate: dict, up: dict, down: dict,
       g = W_g[e] x_t,  u = W_u[e] x_t           (float64 over exact weights)
       act_r = bf16_RNE(silu(g) * u)             (the SwiGLU rounding point)
       y_r = W_d[e] act_r                        (float64)
-    Only experts with at least one row are dequantised ("loads only the
-    activated experts' weights").  slot_of_expert maps expert -> pack slot
+    Only experts with at least one row are dequantised: the block-sparse
+    kernel reads no inactive expert's weights.  slot_of_expert maps expert -> pack slot
     (identity when None).
 
     Returns act float64 [T*k, f] (bf16 values) and y float64 [T*k, d].
@@ -356,3 +356,30 @@ def layer(x_bits, k: int, gate: dict, up: dict, down: dict, *, logits=None,
     out = combine(y, inv, w, k)
     return dict(logits=logits, ids=ids, w=w, offsets=offsets, perm=perm, inv=inv,
                 act=act, y=y, out=out)
+
+
+# ---------------------------------------------------------------------------
+# Shared expert
+# ---------------------------------------------------------------------------
+
+def shared_expert(x_bits, gate: dict, up: dict, down: dict):
+    """The always-on shared expert of a DeepSeek block (the pages name it only
+    through a knob that prefetches its down projection at decode: Anemll/
+    ds4-ssd README, section "Experimental Pro Support").  Every token goes
+    through slot 0 of the given packs with the routed experts' SwiGLU and
+    rounding point:  ys_t = W_d bf16_RNE(silu(W_g x_t) * (W_u x_t)).
+    Returns ys float64 [T, d]."""
+    x = bf16_bits_to_f64(x_bits)
+    wg, wu, wd = dequant(gate, 0), dequant(up, 0), dequant(down, 0)
+    act = round_bf16(silu(x @ wg.T) * (x @ wu.T))
+    return act @ wd.T
+
+
+def layer_shared(x_bits, k: int, gate: dict, up: dict, down: dict, shared: dict, **kw):
+    """The layer with a shared expert, weight 1, added after the routed
+    terms: out[t] = sum_j w[t, j] y[inv[t*k + j]] + ys[t].  `shared` holds
+    the shared expert's gate/up/down packs; other arguments as ``layer``."""
+    r = layer(x_bits, k, gate, up, down, **kw)
+    r["ys"] = shared_expert(x_bits, shared["gate"], shared["up"], shared["down"])
+    r["out"] = r["out"] + r["ys"]
+    return r

@@ -51,6 +51,7 @@ EXPORTS = (
     "moe_expert_ffn", "moe_combine", "moe_layer_workspace_bytes", "moe_layer",
     "moe_status_str", "moe_read_device_status", "moe_qmat_bytes", "moe_pack_qmat",
     "moe_bank_reset", "moe_bank_plan", "moe_bank_fetch", "moe_layer_banked",
+    "moe_layer_shared_workspace_bytes", "moe_layer_shared",
 )
 
 
@@ -116,6 +117,8 @@ def lib() -> ctypes.CDLL:
             "moe_read_device_status": (_I, [_P, _P, _P]),
             "moe_qmat_bytes": (_SZ, [_I, _I, _I, _I, _I, _P, _P, _P]),
             "moe_pack_qmat": (_I, [_P, _P, _I, _I, _I, _P]),
+            "moe_layer_shared_workspace_bytes": (_SZ, [_P]),
+            "moe_layer_shared": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
             "moe_bank_reset": (_I, [_P]),
             "moe_bank_plan": (_I, [_P, _P, _I, _P, _P, _P]),
             "moe_bank_fetch": (_I, [_P, _P, _I, _I, _P, _P, _I, _P]),
@@ -384,6 +387,39 @@ def layer(x, experts: Experts, k: int, *, w_router=None, bias=None, logits=None,
     if ws is None:
         ws = alloc_workspace(shape, layer=True, device=dev, stream=stream)
     moe_layer(shape, x, w_router, bias, logits, experts, ids, w, out, ws, stream)
+    return out, ids, w, logits
+
+
+# -------------------------------------------------------------- shared expert
+
+def layer_shared(x, experts: Experts, shared: Experts, k: int, *, w_router=None, bias=None, logits=None,
+                 ws=None, stream=None):
+    """moe_layer_shared: the layer plus an always-on shared expert (weight 1,
+    slot 0 of `shared`); returns (out, topk_ids, topk_w, logits)."""
+    torch = _torch()
+    T, d = x.shape
+    E = int(w_router.shape[0]) if w_router is not None else int(logits.shape[1])
+    shape = Shape(T, d, E, k, experts.f)
+    dev = x.device
+    if logits is None:
+        logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    out = torch.empty((T, d), dtype=torch.float32, device=dev)
+    if ws is None:
+        n = int(lib().moe_layer_shared_workspace_bytes(ctypes.byref(shape.c())))
+        if n == 0:
+            raise MoeError(MOE_ERR_SHAPE, "layer_shared")
+        ws = torch.empty(n, dtype=torch.uint8, device=dev)
+        moe_workspace_init(ws, stream)
+    ex, sh = experts.c(), shared.c()
+    rc = lib().moe_layer_shared(
+        ctypes.byref(shape.c()), _ptr(x, (torch.int16, torch.bfloat16, torch.uint16), "x"),
+        _ptr(w_router, torch.float32, "w_router", allow_none=True),
+        _ptr(bias, torch.float32, "bias", allow_none=True), _ptr(logits, torch.float32, "logits"),
+        ctypes.byref(ex), ctypes.byref(sh), _ptr(ids, torch.int32, "topk_ids"), _ptr(w, torch.float32, "topk_w"),
+        _ptr(out, torch.float32, "out"), _ptr(ws, name="ws"), ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc, "moe_layer_shared")
     return out, ids, w, logits
 
 

@@ -318,6 +318,58 @@ int moe_layer(const moe_shape* shape, const uint16_t* x, const float* w_router, 
     return do_combine(s, y, inv, topk_w, out, stream);
 }
 
+size_t moe_layer_shared_workspace_bytes(const moe_shape* shape) {
+    if (check_shape(shape) != MOE_OK) return 0;
+    return layer_carve(*shape, true).total;
+}
+
+int moe_layer_shared(const moe_shape* shape, const uint16_t* x, const float* w_router, const float* bias,
+                     float* logits, const moe_experts* experts, const moe_experts* shared, int32_t* topk_ids,
+                     float* topk_w, float* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+    int rc = check_shape(shape);
+    if (rc != MOE_OK) return rc;
+    if (shape->T == 0) return MOE_OK;
+    const moe_shape& s = *shape;
+    if (!ws || !out || !x || !shared || !experts) return MOE_ERR_NULL;
+    if (!aligned(ws, 16) || !aligned(out, 16)) return MOE_ERR_ALIGN;
+    const LayerCarve c = layer_carve(s, true);
+    if (ws_bytes < c.total) return MOE_ERR_WORKSPACE;
+    char* base = static_cast<char*>(ws);
+    int32_t* offsets = reinterpret_cast<int32_t*>(base + c.offsets);
+    int32_t* perm = reinterpret_cast<int32_t*>(base + c.perm);
+    int32_t* inv = reinterpret_cast<int32_t*>(base + c.inv);
+    float* y = reinterpret_cast<float*>(base + c.y);
+    if ((rc = check_route_args(s, x, w_router, bias, logits, topk_ids, topk_w)) != MOE_OK) return rc;
+    if ((rc = check_ffn_args(s, x, experts, offsets, perm, y, ws, ws_bytes)) != MOE_OK) return rc;
+    const int fmt = experts->gate.fmt;
+    const moe_qmat* sm[3] = {&shared->gate, &shared->up, &shared->down};
+    for (const moe_qmat* m : sm)
+        if ((rc = check_qmat(*m, fmt)) != MOE_OK) return rc;
+    if (shared->num_slots < 1) return MOE_ERR_SHAPE;
+    // routing: the dispatch also writes perm[T*k + t] = t*k, the rows of the
+    // shared expert
+    if (qrmoe::small_route_supported(s)) {
+        if ((rc = hip_rc(qrmoe::launch_small_route(s, x, w_router, bias, logits, topk_ids, topk_w, offsets, perm,
+                                                   inv, stream, true))) != MOE_OK)
+            return rc;
+    } else {
+        if ((rc = do_route(s, x, w_router, bias, logits, topk_ids, topk_w, stream)) != MOE_OK) return rc;
+        if ((rc = hip_rc(qrmoe::launch_dispatch(s, topk_ids, offsets, perm, inv, static_cast<uint32_t*>(ws),
+                                                stream, true))) != MOE_OK)
+            return rc;
+    }
+    FfnArgs a = ffn_args(s, x, experts, offsets, perm, y, ws);
+    a.flags = flag_bytes(s, true) ? reinterpret_cast<unsigned long long*>(base + kHeader + act_bytes(s, true))
+                                  : nullptr;
+    a.has_shared = 1;
+    for (int i = 0; i < 3; ++i) {
+        a.sh_codes[i] = static_cast<const uint8_t*>(sm[i]->codes);
+        a.sh_scales[i] = static_cast<const uint8_t*>(sm[i]->scales);
+    }
+    if ((rc = hip_rc(qrmoe::launch_ffn(s, fmt, a, stream))) != MOE_OK) return rc;
+    return hip_rc(qrmoe::launch_combine(s, y, inv, topk_w, out, stream, true));
+}
+
 const char* moe_status_str(int status) {
     switch (status) {
         case MOE_OK: return "MOE_OK";

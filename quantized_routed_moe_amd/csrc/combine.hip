@@ -11,7 +11,8 @@ namespace qrmoe {
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
                                                        const int32_t* __restrict__ inv,
                                                        const float* __restrict__ w,
-                                                       float* __restrict__ out, int d, int k) {
+                                                       float* __restrict__ out, int d, int k,
+                                                       const float* __restrict__ y_shared) {
     const int t = blockIdx.x;
     const int d4 = d / 4;
     for (int i = threadIdx.x; i < d4; i += blockDim.x) {
@@ -25,6 +26,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
             acc.z = __fadd_rn(acc.z, __fmul_rn(wj, v.z));
             acc.w = __fadd_rn(acc.w, __fmul_rn(wj, v.w));
         }
+        if (y_shared) {     // the shared expert, weight 1, after the routed terms
+            const float4 v = reinterpret_cast<const float4*>(y_shared + static_cast<size_t>(t) * d)[i];
+            acc.x = __fadd_rn(acc.x, v.x);
+            acc.y = __fadd_rn(acc.y, v.y);
+            acc.z = __fadd_rn(acc.z, v.z);
+            acc.w = __fadd_rn(acc.w, v.w);
+        }
         reinterpret_cast<float4*>(out + static_cast<size_t>(t) * d)[i] = acc;
     }
 }
@@ -34,8 +42,9 @@ __global__ void clear_header_kernel(uint32_t* header) {
 }
 
 hipError_t launch_combine(const moe_shape& s, const float* y, const int32_t* inv, const float* w,
-                          float* out, hipStream_t st) {
-    combine_kernel<<<s.T, 256, 0, st>>>(y, inv, w, out, s.d, s.k);
+                          float* out, hipStream_t st, bool shared) {
+    const float* ys = shared ? y + static_cast<size_t>(s.T) * s.k * s.d : nullptr;
+    combine_kernel<<<s.T, 256, 0, st>>>(y, inv, w, out, s.d, s.k, ys);
     return hipGetLastError();
 }
 

@@ -22,13 +22,15 @@ constexpr int kDispThreads = 1024;
 
 __global__ __launch_bounds__(kDispThreads) void dispatch_kernel(
     const int32_t* __restrict__ ids, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
-    int32_t* __restrict__ inv, uint32_t* __restrict__ status, int n_pairs, int E) {
+    int32_t* __restrict__ inv, uint32_t* __restrict__ status, int n_pairs, int E, int shared_rows, int k) {
     dispatch_block<kDispThreads>(ids, offsets, perm, inv, status, n_pairs, E);
+    for (int t = threadIdx.x; t < shared_rows; t += kDispThreads) perm[n_pairs + t] = t * k;
 }
 
 hipError_t launch_dispatch(const moe_shape& s, const int32_t* ids, int32_t* offsets, int32_t* perm,
-                           int32_t* inv, uint32_t* status, hipStream_t st) {
-    dispatch_kernel<<<1, kDispThreads, 0, st>>>(ids, offsets, perm, inv, status, s.T * s.k, s.E);
+                           int32_t* inv, uint32_t* status, hipStream_t st, bool shared) {
+    dispatch_kernel<<<1, kDispThreads, 0, st>>>(ids, offsets, perm, inv, status, s.T * s.k, s.E,
+                                                shared ? s.T : 0, s.k);
     return hipGetLastError();
 }
 

@@ -139,17 +139,24 @@ __device__ __forceinline__ void grouped_unit(const FfnArgs& a, int unit, unsigne
     }
     const int n_full = lane_value(incl, 63);
     const uint64_t has_part = __ballot(rem > 0);
-    const int total_units = (n_full + __popcll(has_part)) * NT;
+    // the shared expert's m-tiles (rows [T*k, T*k + T)) come first
+    const int n_sh = a.has_shared ? ceil_div(a.T, kGM) : 0;
+    const int total_units = (n_sh + n_full + __popcll(has_part)) * NT;
     if (unit >= total_units) return;
     int e, mti, nt;
-    // m-tile position p -> full m-tile qi or partial m-tile qi
+    // m-tile position p -> shared m-tile, full m-tile qi or partial m-tile qi
     const int n_part = __popcll(has_part);
-    const int p = unit / NT;
+    const int p = unit / NT - n_sh;
     nt = unit % NT;
     const int groups = min(n_full / kFullPerPart, n_part);
     bool is_full;
     int qi;
-    if (p < groups * (kFullPerPart + 1)) {
+    if (p < 0) {
+        e = a.E;
+        mti = p + n_sh;
+        is_full = true;
+        qi = 0;
+    } else if (p < groups * (kFullPerPart + 1)) {
         const int gg = p / (kFullPerPart + 1), rr = p % (kFullPerPart + 1);
         is_full = rr < kFullPerPart;
         qi = is_full ? gg * kFullPerPart + rr : gg;
@@ -158,7 +165,9 @@ __device__ __forceinline__ void grouped_unit(const FfnArgs& a, int unit, unsigne
         is_full = p2 < rf;
         qi = is_full ? groups * kFullPerPart + p2 : groups + (p2 - rf);
     }
-    if (is_full) {
+    if (p < 0) {
+        // shared m-tile: e and mti set above
+    } else if (is_full) {
         const int q = qi;
         const int excl = incl - full;
         const uint64_t below = __ballot(full > 0 && excl <= q);
@@ -175,10 +184,13 @@ __device__ __forceinline__ void grouped_unit(const FfnArgs& a, int unit, unsigne
         e = __ffsll(static_cast<unsigned long long>(hit)) - 1;
         mti = lane_value(full, e);
     }
-    const int r_base = a.offsets[e] + mti * kGM;
-    const int nvalid = min(kGM, a.offsets[e + 1] - r_base);
-    const int slot = a.slot_of_expert ? a.slot_of_expert[e] : e;
-    if (slot < 0 || slot >= a.num_slots) {      // MOE_SLOT_SKIP: left out of this call, rows untouched
+    const bool sh = e == a.E;
+    const int r_base = (sh ? a.T * a.k : a.offsets[e]) + mti * kGM;
+    const int nvalid = min(kGM, (sh ? a.T * a.k + a.T : a.offsets[e + 1]) - r_base);
+    const int slot = sh ? 0 : a.slot_of_expert ? a.slot_of_expert[e] : e;
+    const uint8_t* const* wcodes = sh ? a.sh_codes : a.codes;
+    const uint8_t* const* wscales = sh ? a.sh_scales : a.scales;
+    if (!sh && (slot < 0 || slot >= a.num_slots)) {      // MOE_SLOT_SKIP: left out of this call, rows untouched
         const bool skip = slot == MOE_SLOT_SKIP;
         if (skip) {
             if (CHAIN && MODE == 0) raise_flag(a.flags + unit, tag);
@@ -217,13 +229,13 @@ __device__ __forceinline__ void grouped_unit(const FfnArgs& a, int unit, unsigne
     for (int i = 0; i < 2; ++i) {
         int mat;
         const size_t blk = tile_base(4 * wave + 2 * i + (lane >> 5), mat);
-        wsrc[i] = a.codes[mat] + blk * 64 * 16 + (lane & 31) * 16;
+        wsrc[i] = wcodes[mat] + blk * 64 * 16 + (lane & 31) * 16;
     }
     const uint8_t* ssrc;         // wave 0: scale bytes 16 (lane & 1) .. +16 of tile lane >> 1
     {
         int mat;
         const size_t blk = tile_base(lane >> 1, mat);
-        ssrc = a.scales[mat] + blk * 64 + 16 * (lane & 1);
+        ssrc = wscales[mat] + blk * 64 + 16 * (lane & 1);
     }
     const uint16_t* xsrc[2];     // token row 16w + 8i + (lane >> 3), global chunk for LDS chunk lane & 7
 #pragma unroll
@@ -415,18 +427,18 @@ bool grouped_supported(const moe_shape& s, int fmt) {
     return fmt == MOE_FMT_MXFP4 && s.f % (kGN / 2) == 0 && s.d % kGN == 0;
 }
 
-static int max_mtiles(const moe_shape& s) {
+static int max_mtiles(const moe_shape& s, bool shared) {
     const int pairs = s.T * s.k;
-    return ceil_div(pairs, kGM) + (s.E < pairs ? s.E : pairs);
+    return ceil_div(pairs, kGM) + (s.E < pairs ? s.E : pairs) + (shared ? ceil_div(s.T, kGM) : 0);
 }
 
-int grouped_flag_count(const moe_shape& s) {
-    return s.f % (kGN / 2) == 0 ? max_mtiles(s) * (s.f / (kGN / 2)) : 0;
+int grouped_flag_count(const moe_shape& s, bool shared) {
+    return s.f % (kGN / 2) == 0 ? max_mtiles(s, shared) * (s.f / (kGN / 2)) : 0;
 }
 
 hipError_t launch_ffn_grouped(const moe_shape& s, const FfnArgs& a, hipStream_t st) {
-    const int units0 = max_mtiles(s) * (s.f / (kGN / 2));
-    const int units1 = max_mtiles(s) * (s.d / kGN);
+    const int units0 = max_mtiles(s, a.has_shared) * (s.f / (kGN / 2));
+    const int units1 = max_mtiles(s, a.has_shared) * (s.d / kGN);
     if (a.flags) {
         ffn_grouped_chained_kernel<<<units0 + units1 + 1, kGThreads, 0, st>>>(a, units0, units1);
         return hipGetLastError();

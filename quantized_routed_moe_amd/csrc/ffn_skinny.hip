@@ -61,6 +61,25 @@ __device__ __forceinline__ Item find_item(const FfnArgs& a, int ai) {
     return pick_item(lo, hi, sl, ai);
 }
 
+// Item ai of the launch: with a shared expert, item 0 is the shared expert
+// (e = E, rows [T*k, T*k + T), slot 0 of its own pack) and item ai > 0 the
+// (ai-1)-th active routed expert.
+__device__ __forceinline__ Item item_at(const FfnArgs& a, int ai) {
+    if (a.has_shared) {
+        if (ai == 0) return Item{a.E, a.T * a.k, a.T * a.k + a.T, 0};
+        --ai;
+    }
+    return find_item(a, ai);
+}
+
+// Pack of an item: the shared expert's own, or the routed experts'.
+__device__ __forceinline__ const uint8_t* item_codes(const FfnArgs& a, const Item& it, int mat) {
+    return it.e == a.E ? a.sh_codes[mat] : a.codes[mat];
+}
+__device__ __forceinline__ const uint8_t* item_scales(const FfnArgs& a, const Item& it, int mat) {
+    return it.e == a.E ? a.sh_scales[mat] : a.scales[mat];
+}
+
 // Zero y rows [r0, r1) x [n0, n0+16) (down tiles of an expert whose slot is invalid).
 __device__ __forceinline__ void zero_y_tile(const FfnArgs& a, int n0, int r0, int r1) {
     for (int i = threadIdx.x; i < (r1 - r0) * 16; i += blockDim.x)
@@ -123,7 +142,8 @@ __device__ __forceinline__ void skinny_body(const FfnArgs& a, const Item& it, in
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
         const int mat = MODE == 0 ? m : 2;
-        wt[m] = wtile<FMT>(a.codes[mat], a.scales[mat], static_cast<size_t>(it.slot) * NT + n0 / 16, S, lane);
+        wt[m] = wtile<FMT>(item_codes(a, it, mat), item_scales(a, it, mat), static_cast<size_t>(it.slot) * NT + n0 / 16,
+                           S, lane);
     }
     WChunk<FMT> w[NM];
     f32x4 acc[kChains<FMT>][NM];
@@ -281,7 +301,7 @@ __device__ __forceinline__ void skinny_body(const FfnArgs& a, const Item& it, in
 template <int FMT, int MODE, int KW, int RB, bool PERM_LDS = false>
 __device__ __forceinline__ void run_item(const FfnArgs& a, const Item& it, int n0, const int32_t* perm) {
     if (it.e < 0 || it.slot == MOE_SLOT_SKIP) return;
-    if (it.slot < 0 || it.slot >= a.num_slots) {
+    if (it.e < a.E && (it.slot < 0 || it.slot >= a.num_slots)) {
         if (threadIdx.x == 0 && n0 == 0) raise_status(a.status, MOE_DEV_BAD_SLOT);
         if (MODE == 1) zero_y_tile(a, n0, it.r0, it.r1);
         return;
@@ -332,10 +352,10 @@ __device__ __forceinline__ void prefetch_down(const FfnArgs& a, int j, int n_pf,
         const int ai = i / NTd, t = i % NTd;
         const Item it = item_of(ai);
         if (it.e < 0) break;                  // past the active experts (ai grows with q)
-        if (it.slot < 0 || it.slot >= a.num_slots) continue;
+        if (it.e < a.E && (it.slot < 0 || it.slot >= a.num_slots)) continue;
         const size_t blk = (static_cast<size_t>(it.slot) * NTd + t) * S;
-        const uint8_t* c = a.codes[2] + blk * kWave * PieceBytes<FMT>::codes;
-        const uint8_t* sc = a.scales[2] + blk * kWave * PieceBytes<FMT>::scales;
+        const uint8_t* c = item_codes(a, it, 2) + blk * kWave * PieceBytes<FMT>::codes;
+        const uint8_t* sc = item_scales(a, it, 2) + blk * kWave * PieceBytes<FMT>::scales;
         // 1 KB per instruction, lanes past the end re-read the last 16 bytes
         for (int o = 0; o < code_bytes; o += 1024)
             __builtin_amdgcn_global_load_lds(c + min(o + 16 * lane, code_bytes - 16), (lds_void*)scratch, 16, 0, 0);
@@ -356,16 +376,16 @@ __global__ __launch_bounds__(KW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
     }
     const int NT = (MODE == 0 ? a.f : a.d) / 16;
     if (MODE == 0) {
-        const int g_items = min(a.E, a.T * a.k) * NT;
+        const int g_items = (min(a.E, a.T * a.k) + a.has_shared) * NT;
         if (static_cast<int>(blockIdx.x) >= g_items) {
             __shared__ __align__(16) uint8_t pf[KW][1024];
             prefetch_down<FMT>(a, blockIdx.x - g_items, gridDim.x - g_items,
-                               [&](int ai) { return find_item(a, ai); }, pf[threadIdx.x >> 6]);
+                               [&](int ai) { return item_at(a, ai); }, pf[threadIdx.x >> 6]);
             if (a.fuse_combine) zero_out_share(a);
             return;
         }
     }
-    run_item<FMT, MODE, KW, RB>(a, find_item(a, blockIdx.x / NT), (blockIdx.x % NT) * 16, a.perm);
+    run_item<FMT, MODE, KW, RB>(a, item_at(a, blockIdx.x / NT), (blockIdx.x % NT) * 16, a.perm);
     if (MODE == 0 && a.fuse_combine) zero_out_share(a);
 }
 
@@ -428,7 +448,7 @@ static int staged_rows(int T) { return T <= 1 ? 1 : T <= 2 ? 2 : T <= 4 ? 4 : T 
 
 template <int FMT, int RB>
 static hipError_t launch_two_rb(const moe_shape& s, const FfnArgs& a, hipStream_t st, bool routed) {
-    const int umax = s.E < s.T * s.k ? s.E : s.T * s.k;
+    const int umax = (s.E < s.T * s.k ? s.E : s.T * s.k) + a.has_shared;
     const int g_items = umax * (s.f / 16);
     const int g_up = g_items + (g_items + kDownPrefetchWGs <= kResidentGateUpWGs ? kDownPrefetchWGs : 0);
     if (routed) {

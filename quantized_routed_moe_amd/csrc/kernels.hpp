@@ -39,12 +39,20 @@ struct FfnArgs {
     // Ready flags of the single-launch grouped FFN (workspace), one per
     // gate/up unit (grouped_flag_count); null: two launches.
     unsigned long long* flags;
+    // Shared expert (moe_layer_shared): one more item whose rows are the T
+    // rows after the routed ones, [T*k, T*k + T) in act and y (row T*k + t is
+    // token t: the dispatch writes perm[T*k + t] = t*k), with its own pack
+    // (one slot) -- computed in the same launches as the routed experts.
+    int has_shared;
+    const uint8_t* sh_codes[3];
+    const uint8_t* sh_scales[3];
 };
 
 hipError_t launch_route(const moe_shape& s, const uint16_t* x, const float* wr, const float* bias,
                         float* logits, int32_t* ids, float* w, hipStream_t st);
+// shared: also perm[T*k + t] = t*k for t < T (the shared expert's rows).
 hipError_t launch_dispatch(const moe_shape& s, const int32_t* ids, int32_t* offsets, int32_t* perm,
-                           int32_t* inv, uint32_t* status, hipStream_t st);
+                           int32_t* inv, uint32_t* status, hipStream_t st, bool shared = false);
 hipError_t launch_ffn(const moe_shape& s, int fmt, const FfnArgs& a, hipStream_t st);
 bool grouped_supported(const moe_shape& s, int fmt);
 bool ffn_uses_grouped(const moe_shape& s, int fmt);
@@ -56,16 +64,17 @@ hipError_t launch_router_logits(const moe_shape& s, const uint16_t* x, const flo
 bool small_route_supported(const moe_shape& s);
 hipError_t launch_small_route(const moe_shape& s, const uint16_t* x, const float* wr, const float* bias,
                               float* logits, int32_t* ids, float* w, int32_t* offsets, int32_t* perm,
-                              int32_t* inv, hipStream_t st);
+                              int32_t* inv, hipStream_t st, bool shared = false);
 // moe_layer for small batches: the skinny FFN whose gate/up launch routes the
 // batch from a.logits (see FfnArgs).
 bool routed_ffn_supported(const moe_shape& s, int fmt);
 hipError_t launch_ffn_routed(const moe_shape& s, int fmt, const FfnArgs& a, hipStream_t st);
 hipError_t launch_ffn_grouped(const moe_shape& s, const FfnArgs& a, hipStream_t st);
 // Ready flags the grouped FFN needs in the workspace (0: none).
-int grouped_flag_count(const moe_shape& s);
+int grouped_flag_count(const moe_shape& s, bool shared = false);
+// shared: out[t] also adds y[T*k + t] (weight 1) after the routed terms.
 hipError_t launch_combine(const moe_shape& s, const float* y, const int32_t* inv, const float* w,
-                          float* out, hipStream_t st);
+                          float* out, hipStream_t st, bool shared = false);
 hipError_t launch_clear_header(uint32_t* header, hipStream_t st);
 hipError_t launch_pack(int fmt, const void* src_codes, const void* src_scales, const void* src_mins, void* dst_codes,
                        void* dst_scales, int slots, int n, int K, hipStream_t st);

@@ -225,7 +225,8 @@ constexpr int kSmallRouteT = 16;
 
 __global__ __launch_bounds__(kSmallRouteT * 64) void small_route_kernel(
     const float* __restrict__ logits, int32_t* __restrict__ ids, float* __restrict__ w,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv, int T, int E, int k) {
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv, int T, int E, int k,
+    int shared) {
     __shared__ SmallRouting r;
     const int tid = threadIdx.x, wave = tid >> 6;
     const int n = T * k;
@@ -240,18 +241,20 @@ __global__ __launch_bounds__(kSmallRouteT * 64) void small_route_kernel(
         inv[i] = r.inv[i];
     }
     for (int i = tid; i <= E; i += blockDim.x) offsets[i] = r.offsets[i];
+    if (shared && tid < T) perm[n + tid] = tid * k;       // the shared expert's rows
 }
 
 bool small_route_supported(const moe_shape& s) { return s.T <= kSmallRouteT && s.T * s.k <= kRoutedMaxPairs; }
 
 hipError_t launch_small_route(const moe_shape& s, const uint16_t* x, const float* wr, const float* bias,
                               float* logits, int32_t* ids, float* w, int32_t* offsets, int32_t* perm,
-                              int32_t* inv, hipStream_t st) {
+                              int32_t* inv, hipStream_t st, bool shared) {
     if (wr) {
         const hipError_t err = launch_router_logits(s, x, wr, bias, logits, st);
         if (err != hipSuccess) return err;
     }
-    small_route_kernel<<<1, kSmallRouteT * 64, 0, st>>>(logits, ids, w, offsets, perm, inv, s.T, s.E, s.k);
+    small_route_kernel<<<1, kSmallRouteT * 64, 0, st>>>(logits, ids, w, offsets, perm, inv, s.T, s.E, s.k,
+                                                        shared ? 1 : 0);
     return hipGetLastError();
 }
 

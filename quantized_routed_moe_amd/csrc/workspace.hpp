@@ -1,7 +1,8 @@
 // Workspace sizes and carving, shared by the entry points of api.cpp and the
 // slot-bank layer (bank.hip).  Layout: a 256-byte header (device status
-// word), act bf16 [T*k][f], the ready flags of the single-launch prefill FFN;
-// moe_layer then carves offsets, perm, inv and y fp32 [T*k][d].
+// word), act bf16 [rows][f], the ready flags of the single-launch prefill FFN;
+// moe_layer then carves offsets, perm [rows], inv [T*k] and y fp32 [rows][d];
+// rows = T*k, plus T with a shared expert.
 #pragma once
 
 #include <cstddef>
@@ -16,24 +17,34 @@ constexpr size_t kHeader = 256;
 
 inline size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
-inline size_t act_bytes(const moe_shape& s) { return align256(static_cast<size_t>(s.T) * s.k * s.f * 2); }
+// Rows of act, y and perm: the T*k routed pairs, plus T rows of the shared
+// expert when there is one.
+inline size_t ffn_rows(const moe_shape& s, bool shared) {
+    return static_cast<size_t>(s.T) * s.k + (shared ? static_cast<size_t>(s.T) : 0);
+}
 
-inline size_t flag_bytes(const moe_shape& s) { return align256(static_cast<size_t>(grouped_flag_count(s)) * 8); }
+inline size_t act_bytes(const moe_shape& s, bool shared = false) { return align256(ffn_rows(s, shared) * s.f * 2); }
 
-inline size_t ffn_ws_bytes(const moe_shape& s) { return kHeader + act_bytes(s) + flag_bytes(s); }
+inline size_t flag_bytes(const moe_shape& s, bool shared = false) {
+    return align256(static_cast<size_t>(grouped_flag_count(s, shared)) * 8);
+}
+
+inline size_t ffn_ws_bytes(const moe_shape& s, bool shared = false) {
+    return kHeader + act_bytes(s, shared) + flag_bytes(s, shared);
+}
 
 struct LayerCarve {
     size_t offsets, perm, inv, y, total;
 };
 
-inline LayerCarve layer_carve(const moe_shape& s) {
+inline LayerCarve layer_carve(const moe_shape& s, bool shared = false) {
     LayerCarve c;
-    const size_t pairs = static_cast<size_t>(s.T) * s.k;
-    c.offsets = ffn_ws_bytes(s);
+    const size_t pairs = static_cast<size_t>(s.T) * s.k, rows = ffn_rows(s, shared);
+    c.offsets = ffn_ws_bytes(s, shared);
     c.perm = c.offsets + align256(static_cast<size_t>(s.E + 1) * 4);
-    c.inv = c.perm + align256(pairs * 4);
+    c.inv = c.perm + align256(rows * 4);
     c.y = c.inv + align256(pairs * 4);
-    c.total = c.y + align256(pairs * s.d * 4);
+    c.total = c.y + align256(rows * s.d * 4);
     return c;
 }
 

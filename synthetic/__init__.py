@@ -51,6 +51,7 @@ WORKLOADS = {
 # stream ids within a workload
 _S_X, _S_X2, _S_WR, _S_LOGITS = 0, 1, 2, 3
 _S_MAT = {"gate": 10, "up": 20, "down": 30}
+_S_SHARED = {"gate": 40, "up": 50, "down": 60}
 
 
 def _rng(stream: int, seed: int) -> np.random.Generator:
@@ -127,3 +128,12 @@ def workload(c: int, seed_offset: int = 0) -> dict:
     return make_case(w["T"], w["d"], w["E"], w["k"], w["f"], w["fmt"], router=w["router"],
                      seed=1000 * c + seed_offset, zipf=w.get("zipf"),
                      correlated=w.get("correlated", False))
+
+
+def make_shared(case: dict, seed: int = 0) -> dict:
+    """A shared expert for `case`: one slot of gate/up/down packs in the
+    case's format, drawn like the routed experts from streams of their own."""
+    fmt, d, f = case["fmt"], case["d"], case["f"]
+    return {"gate": make_matrix(fmt, 1, f, d, _rng(_S_SHARED["gate"], seed)),
+            "up": make_matrix(fmt, 1, f, d, _rng(_S_SHARED["up"], seed)),
+            "down": make_matrix(fmt, 1, d, f, _rng(_S_SHARED["down"], seed))}

@@ -22,7 +22,7 @@ def _declared_symbols():
 
 def test_library_exports_every_declared_symbol():
     syms = _declared_symbols()
-    assert len(syms) == 16
+    assert len(syms) == 18
     assert sorted(qm.EXPORTS) == syms
     L = ctypes.CDLL(qm.LIB_PATH)
     for s in syms:
@@ -209,3 +209,29 @@ def test_pack_validation():
     assert pk(rows(Q4, mn=A16), tiles(Q2)) == qm.MOE_ERR_FORMAT
     assert pk(rows(Q4, mn=A16), tiles(Q4, mn=A16)) == qm.MOE_ERR_FORMAT
     assert pk(rows(Q4, mn=A16 + 2), tiles(Q4)) == qm.MOE_ERR_ALIGN
+
+
+def test_layer_shared_validation():
+    """moe_layer_shared rejects bad shared packs and workspaces on the host."""
+    L = qm.lib()
+    s = _shape(T=4, d=256, E=8, k=2, f=128)
+    need = L.moe_layer_shared_workspace_bytes(ctypes.byref(s))
+    assert need > L.moe_layer_workspace_bytes(ctypes.byref(s))        # T more rows of act, perm and y
+    assert L.moe_layer_shared_workspace_bytes(ctypes.byref(_shape(k=0))) == 0
+
+    def mat(fmt=qm.MOE_FMT_MXFP4, layout=qm.MOE_LAYOUT_TILES, mins=None):
+        return qm.moe_qmat(fmt, layout, A16, A16, mins)
+
+    ex = qm.moe_experts(mat(), mat(), mat(), None, 8)
+
+    def call(shared, ws_bytes=need, ws=A16):
+        return L.moe_layer_shared(ctypes.byref(s), A16, A16, None, A16, ctypes.byref(ex),
+                                  None if shared is None else ctypes.byref(shared), A16, A16, A16, ws, ws_bytes,
+                                  None)
+
+    assert call(None) == qm.MOE_ERR_NULL
+    assert call(qm.moe_experts(mat(qm.MOE_FMT_Q2G32), mat(), mat(), None, 1)) == qm.MOE_ERR_FORMAT
+    assert call(qm.moe_experts(mat(), mat(layout=qm.MOE_LAYOUT_ROWS), mat(), None, 1)) == qm.MOE_ERR_FORMAT
+    assert call(qm.moe_experts(mat(), mat(), mat(), None, 0)) == qm.MOE_ERR_SHAPE
+    assert call(qm.moe_experts(mat(), mat(), mat(), None, 1), ws_bytes=need - 256) == qm.MOE_ERR_WORKSPACE
+    assert call(qm.moe_experts(mat(), mat(), mat(), None, 1), ws=A16 + 8) == qm.MOE_ERR_ALIGN

@@ -364,3 +364,49 @@ def test_combine_order_and_weights():
     out = ref.combine(y, inv, w, 2)
     want = np.array([0.25 * y[5] + 0.75 * y[0], 0.5 * y[1] + 0.5 * y[4], y[2]])
     assert np.array_equal(out, want)
+
+
+# ---------------------------------------------------------------- shared expert
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "q2", "q4"])
+def test_shared_expert_is_dense_swiglu(fmt):
+    """The shared expert is a dense SwiGLU MLP over every token (torch
+    float64 on the scalar twin's dequantised rows and bf16 rounding)."""
+    c = _small_case(fmt, T=6, d=64, E=4, k=2, f=32, seed=12)
+    sh = synthetic.make_shared(c, seed=3)
+    ys = ref.shared_expert(c["x"], sh["gate"], sh["up"], sh["down"])
+    x = torch.tensor([[brute.bf16_value(int(b)) for b in row] for row in c["x"]], dtype=torch.float64)
+    wg = torch.from_numpy(_dense_weights_brute(sh["gate"], 0, 32, 64))
+    wu = torch.from_numpy(_dense_weights_brute(sh["up"], 0, 32, 64))
+    wd = torch.from_numpy(_dense_weights_brute(sh["down"], 0, 64, 32))
+    h = torch.nn.functional.silu(x @ wg.T) * (x @ wu.T)
+    act = torch.tensor([[brute.round_bf16(float(v)) for v in row] for row in h], dtype=torch.float64)
+    assert np.allclose(ys, (act @ wd.T).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_shared_expert_with_zero_down_adds_nothing():
+    """All-zero MXFP4 down codes make the shared expert's output exactly 0,
+    so the layer with it equals the layer without it."""
+    c = _small_case("mxfp4", T=5, d=64, E=4, k=2, f=32, seed=13)
+    sh = synthetic.make_shared(c, seed=4)
+    sh["down"] = dict(sh["down"], codes=np.zeros_like(sh["down"]["codes"]))
+    a = ref.layer(c["x"], 2, c["gate"], c["up"], c["down"], w_router=c["w_router"])
+    b = ref.layer_shared(c["x"], 2, c["gate"], c["up"], c["down"], sh, w_router=c["w_router"])
+    assert np.array_equal(a["out"], b["out"]) and not np.any(b["ys"])
+
+
+def test_shared_expert_is_one_more_routed_slot():
+    """With weight 1 the shared expert is the same as routing every token to
+    one extra expert: the oracle layer over E + 1 experts with k + 1 slots
+    whose last slot is that expert with weight 1 (built by hand here)."""
+    c = _small_case("q4", T=4, d=64, E=3, k=1, f=32, seed=14)
+    sh = synthetic.make_shared(c, seed=5)
+    r = ref.layer_shared(c["x"], 1, c["gate"], c["up"], c["down"], sh, w_router=c["w_router"])
+    ids = np.concatenate([r["ids"], np.full((4, 1), 3)], axis=1)
+    w = np.concatenate([r["w"], np.ones((4, 1))], axis=1)
+    packs = {m: {n: np.concatenate([c[m][n], sh[m][n]]) if n != "fmt" else "q4" for n in c[m]}
+             for m in ("gate", "up", "down")}
+    offsets, perm, inv = ref.dispatch(ids, 4)
+    _, y = ref.expert_ffn(c["x"], 2, offsets, perm, packs["gate"], packs["up"], packs["down"])
+    out = ref.combine(y, inv, w, 2)
+    assert np.allclose(r["out"], out, rtol=1e-13, atol=1e-13)
