@@ -22,7 +22,8 @@ f=2048, MXFP4 experts.
 Workloads 0-4 are the configurations the targets are quoted on; 5 and 6
 run the 4-bit group-asymmetric pack at 16 tokens and at 1 token.  --bank N
 runs the workload through an N-slot expert bank paged from pinned host
-memory instead (its own JSON line: paging included, PCIe roofline).
+memory instead (its own JSON line: paging included, PCIe roofline);
+--shared adds an always-on shared expert (moe_layer_shared; its own JSON line).
 """
 
 from __future__ import annotations
@@ -69,6 +70,8 @@ def parse():
     import synthetic
     p.add_argument("--workload", type=int, default=1, choices=sorted(synthetic.WORKLOADS))
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--shared", action="store_true",
+                   help="run the workload with a shared expert (moe_layer_shared)")
     p.add_argument("--bank", type=int, default=0, metavar="N",
                    help="run the workload through an N-slot expert bank paged from pinned host memory")
     p.add_argument("--cpu-sample-steps", type=int, default=0,
@@ -249,6 +252,142 @@ def bank_main(args):
     print(json.dumps(res), flush=True)
 
 
+def shared_main(args):
+    """--shared: K layer steps of moe_layer_shared (the routed experts plus an
+    always-on shared expert of the same format and size), captured into a HIP
+    graph and replayed, as `value` in main().  The roofline divides the
+    algorithmic bytes (or flops) of all experts the step runs, shared expert
+    included, by the whole layer step: a lower bound for the FFN's own rate."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    import quantized_routed_moe_amd as qm
+    import synthetic
+
+    c = args.workload
+    w = synthetic.WORKLOADS[c]
+    T, d, E, k, f = w["T"], w["d"], w["E"], w["k"], w["f"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1000 * c + 555)
+    per_expert = BYTES_PER_EXPERT[w["fmt"]](d, f)
+    n_pools = max(2, min(24, 1 + math.ceil(512 * 2 ** 20 / ((min(E, max(2, T * k)) + 1) * per_expert))))
+    pools = [make_pool(torch, w, gen, dev) for _ in range(n_pools)]
+    shareds = [make_pool(torch, dict(w, E=1), gen, dev) for _ in range(n_pools)]
+    routers = []
+    for _ in range(n_pools):
+        wr = torch.randn((E, d), device=dev, generator=gen) / math.sqrt(d)
+        b = torch.from_numpy(synthetic.zipf_bias(E, w["zipf"])).to(dev) if w.get("zipf") else None
+        routers.append((wr.contiguous(), b))
+    n_x = 4 if T >= 1024 else 61
+    xs = torch.randn((n_x, T, d), device=dev, generator=gen).to(torch.bfloat16).view(torch.int16).contiguous()
+    shape = qm.Shape(T, d, E, k, f)
+    L = qm.lib()
+    sc = shape.c()
+    ws = torch.empty(int(L.moe_layer_shared_workspace_bytes(ctypes.byref(sc))), dtype=torch.uint8, device=dev)
+    qm.moe_workspace_init(ws)
+    logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    tw = torch.empty((T, k), dtype=torch.float32, device=dev)
+    out = torch.empty((T, d), dtype=torch.float32, device=dev)
+    hip = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+    torch.cuda.synchronize()
+    torch.cuda.set_stream(torch.cuda.Stream())
+    stream = torch.cuda.current_stream().cuda_stream
+    ex_c = [p_.c() for p_ in pools]
+    sh_c = [p_.c() for p_ in shareds]
+
+    def layer_step(j):
+        p = j % n_pools
+        wr, b = routers[p]
+        if L.moe_layer_shared(ctypes.byref(sc), xs.data_ptr() + (j % n_x) * T * d * 2, wr.data_ptr(),
+                              None if b is None else b.data_ptr(), logits.data_ptr(), ctypes.byref(ex_c[p]),
+                              ctypes.byref(sh_c[p]), ids.data_ptr(), tw.data_ptr(), out.data_ptr(), ws.data_ptr(),
+                              ws.numel(), stream):
+            raise RuntimeError("moe_layer_shared failed")
+
+    for i in range(args.warmup):
+        layer_step(i)
+    torch.cuda.synchronize()
+    K = args.steps
+    t0 = time.perf_counter()
+    for i in range(K):
+        layer_step(args.warmup + i)
+    torch.cuda.synchronize()
+    eager = time.perf_counter() - t0
+    for fn in ("hipStreamBeginCapture", "hipStreamEndCapture", "hipGraphInstantiate", "hipGraphLaunch"):
+        getattr(hip, fn).restype = ctypes.c_int
+    graph, gexec = ctypes.c_void_p(), ctypes.c_void_p()
+    sp = ctypes.c_void_p(stream)
+    if hip.hipStreamBeginCapture(sp, 1):
+        raise RuntimeError("hipStreamBeginCapture failed")
+    try:
+        for i in range(K):
+            layer_step(args.warmup + i)
+    finally:
+        if hip.hipStreamEndCapture(sp, ctypes.byref(graph)):
+            raise RuntimeError("hipStreamEndCapture failed")
+    if hip.hipGraphInstantiate(ctypes.byref(gexec), graph, None, None, ctypes.c_size_t(0)):
+        raise RuntimeError("hipGraphInstantiate failed")
+    hip.hipGraphLaunch(gexec, sp)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    hip.hipGraphLaunch(gexec, sp)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    hip.hipGraphExecDestroy(gexec)
+    hip.hipGraphDestroy(graph)
+    assert qm.moe_read_device_status(ws) == 0
+    # activated routed experts per step (routing replayed untimed)
+    U = []
+    wsr = qm.alloc_workspace(shape, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(T * k, dtype=torch.int32, device=dev)
+    inv = torch.empty(T * k, dtype=torch.int32, device=dev)
+    for i in range(K):
+        j = args.warmup + i
+        wr, b = routers[j % n_pools]
+        qm.moe_route_topk(shape, xs[j % n_x], wr, b, logits, ids, tw)
+        qm.moe_dispatch(shape, ids, offsets, perm, inv, wsr)
+        U.append(int((offsets[1:] - offsets[:-1] > 0).sum().item()))
+    U_mean = float(np.mean(U))
+    step_s = elapsed / K
+    rows = T * k + T
+    layer_bytes = (U_mean + 1) * per_expert + T * d * 2 + rows * f * 4 + rows * d * 8 + T * d * 4
+    flops = 2.0 * rows * 3 * d * f
+    if T * k >= 1024:
+        ach, peak, unit, bound = flops / step_s / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", "mfma"
+    else:
+        ach, peak, unit, bound = layer_bytes / step_s / 1e9, HBM_PEAK_GBPS, "GB/s", "hbm"
+    res = {
+        "metric": "MoE layer tokens/s with a shared expert",
+        "value": round(T * K / elapsed, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w['name']} + shared expert: T={T} d={d} E={E} k={k} f={f} {w['fmt']}",
+                   "T": T, "d": d, "E": E, "k": k, "f": f, "format": w["fmt"], "shared_experts": 1,
+                   "weight_pools": n_pools, "parallelism": "none (1 GPU)"},
+        "launch": "HIP graph of the K steps, replayed once",
+        "eager_ms_per_step": round(eager / K * 1e3, 5),
+        "active_experts_mean": U_mean,
+        "roofline": {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
+                     "frac": round(ach / peak, 4), "traffic": None,
+                     "kernel": "moe_layer_shared, whole layer step (routed + shared experts' work / step time)"},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -260,6 +399,9 @@ def main():
         sys.exit(2)
     if args.bank:
         bank_main(args)
+        return
+    if args.shared:
+        shared_main(args)
         return
 
     import numpy as np

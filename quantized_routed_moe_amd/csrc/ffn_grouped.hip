@@ -188,8 +188,10 @@ __device__ __forceinline__ void grouped_unit(const FfnArgs& a, int unit, unsigne
     const int r_base = (sh ? a.T * a.k : a.offsets[e]) + mti * kGM;
     const int nvalid = min(kGM, (sh ? a.T * a.k + a.T : a.offsets[e + 1]) - r_base);
     const int slot = sh ? 0 : a.slot_of_expert ? a.slot_of_expert[e] : e;
-    const uint8_t* const* wcodes = sh ? a.sh_codes : a.codes;
-    const uint8_t* const* wscales = sh ? a.sh_scales : a.scales;
+    // element-wise selects: choosing between the two pointer arrays would
+    // put the kernel argument block in scratch memory
+    auto wcodes = [&](int mat) { return sh ? a.sh_codes[mat] : a.codes[mat]; };
+    auto wscales = [&](int mat) { return sh ? a.sh_scales[mat] : a.scales[mat]; };
     if (!sh && (slot < 0 || slot >= a.num_slots)) {      // MOE_SLOT_SKIP: left out of this call, rows untouched
         const bool skip = slot == MOE_SLOT_SKIP;
         if (skip) {
@@ -229,13 +231,13 @@ __device__ __forceinline__ void grouped_unit(const FfnArgs& a, int unit, unsigne
     for (int i = 0; i < 2; ++i) {
         int mat;
         const size_t blk = tile_base(4 * wave + 2 * i + (lane >> 5), mat);
-        wsrc[i] = wcodes[mat] + blk * 64 * 16 + (lane & 31) * 16;
+        wsrc[i] = wcodes(mat) + blk * 64 * 16 + (lane & 31) * 16;
     }
     const uint8_t* ssrc;         // wave 0: scale bytes 16 (lane & 1) .. +16 of tile lane >> 1
     {
         int mat;
         const size_t blk = tile_base(lane >> 1, mat);
-        ssrc = wscales[mat] + blk * 64 + 16 * (lane & 1);
+        ssrc = wscales(mat) + blk * 64 + 16 * (lane & 1);
     }
     const uint16_t* xsrc[2];     // token row 16w + 8i + (lane >> 3), global chunk for LDS chunk lane & 7
 #pragma unroll

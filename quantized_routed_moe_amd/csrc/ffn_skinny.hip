@@ -61,11 +61,13 @@ __device__ __forceinline__ Item find_item(const FfnArgs& a, int ai) {
     return pick_item(lo, hi, sl, ai);
 }
 
-// Item ai of the launch: with a shared expert, item 0 is the shared expert
-// (e = E, rows [T*k, T*k + T), slot 0 of its own pack) and item ai > 0 the
-// (ai-1)-th active routed expert.
+// Item ai of the launch.  SH (a shared expert; separate instantiations, so
+// the kernels without one are unchanged): item 0 is the shared expert (e = E,
+// rows [T*k, T*k + T), slot 0 of its own pack) and item ai > 0 the (ai-1)-th
+// active routed expert.
+template <bool SH>
 __device__ __forceinline__ Item item_at(const FfnArgs& a, int ai) {
-    if (a.has_shared) {
+    if constexpr (SH) {
         if (ai == 0) return Item{a.E, a.T * a.k, a.T * a.k + a.T, 0};
         --ai;
     }
@@ -73,11 +75,15 @@ __device__ __forceinline__ Item item_at(const FfnArgs& a, int ai) {
 }
 
 // Pack of an item: the shared expert's own, or the routed experts'.
+template <bool SH>
 __device__ __forceinline__ const uint8_t* item_codes(const FfnArgs& a, const Item& it, int mat) {
-    return it.e == a.E ? a.sh_codes[mat] : a.codes[mat];
+    if constexpr (SH) return it.e == a.E ? a.sh_codes[mat] : a.codes[mat];
+    return a.codes[mat];
 }
+template <bool SH>
 __device__ __forceinline__ const uint8_t* item_scales(const FfnArgs& a, const Item& it, int mat) {
-    return it.e == a.E ? a.sh_scales[mat] : a.scales[mat];
+    if constexpr (SH) return it.e == a.E ? a.sh_scales[mat] : a.scales[mat];
+    return a.scales[mat];
 }
 
 // Zero y rows [r0, r1) x [n0, n0+16) (down tiles of an expert whose slot is invalid).
@@ -116,7 +122,7 @@ __device__ __forceinline__ void zero_y_tail(const FfnArgs& a) {
 // `it` is the item's expert, rows and slot, `n0` its first weight row; `perm`
 // is the sorted-row -> pair map (global, or with PERM_LDS the workgroup's own
 // LDS copy).
-template <int FMT, int MODE, int KW, int RB, bool PERM_LDS>
+template <int FMT, int MODE, int KW, int RB, bool PERM_LDS, bool SH>
 __device__ __forceinline__ void skinny_body(const FfnArgs& a, const Item& it, int n0, const int32_t* perm) {
     constexpr int NM = MODE == 0 ? 2 : 1;
     // Per wave: RB staged token rows; after the pass's multiplies the same
@@ -142,7 +148,7 @@ __device__ __forceinline__ void skinny_body(const FfnArgs& a, const Item& it, in
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
         const int mat = MODE == 0 ? m : 2;
-        wt[m] = wtile<FMT>(item_codes(a, it, mat), item_scales(a, it, mat), static_cast<size_t>(it.slot) * NT + n0 / 16,
+        wt[m] = wtile<FMT>(item_codes<SH>(a, it, mat), item_scales<SH>(a, it, mat), static_cast<size_t>(it.slot) * NT + n0 / 16,
                            S, lane);
     }
     WChunk<FMT> w[NM];
@@ -298,15 +304,15 @@ __device__ __forceinline__ void skinny_body(const FfnArgs& a, const Item& it, in
 // An item whose expert is left out of the call (MOE_SLOT_SKIP) writes
 // nothing; one whose slot is otherwise invalid is skipped too, but its y rows
 // read as zero and MOE_DEV_BAD_SLOT is raised.
-template <int FMT, int MODE, int KW, int RB, bool PERM_LDS = false>
+template <int FMT, int MODE, int KW, int RB, bool PERM_LDS = false, bool SH = false>
 __device__ __forceinline__ void run_item(const FfnArgs& a, const Item& it, int n0, const int32_t* perm) {
     if (it.e < 0 || it.slot == MOE_SLOT_SKIP) return;
-    if (it.e < a.E && (it.slot < 0 || it.slot >= a.num_slots)) {
+    if ((!SH || it.e < a.E) && (it.slot < 0 || it.slot >= a.num_slots)) {
         if (threadIdx.x == 0 && n0 == 0) raise_status(a.status, MOE_DEV_BAD_SLOT);
         if (MODE == 1) zero_y_tile(a, n0, it.r0, it.r1);
         return;
     }
-    skinny_body<FMT, MODE, KW, RB, PERM_LDS>(a, it, n0, perm);
+    skinny_body<FMT, MODE, KW, RB, PERM_LDS, SH>(a, it, n0, perm);
 }
 
 // Every workgroup zeroes its share of out (the fused combine's scatter-add
@@ -340,7 +346,7 @@ constexpr int kDownPrefetchWGs = 128;
 // VGPRs, 256 CUs.
 constexpr int kResidentGateUpWGs = 512;
 
-template <int FMT, typename ItemOf>
+template <int FMT, bool SH, typename ItemOf>
 __device__ __forceinline__ void prefetch_down(const FfnArgs& a, int j, int n_pf, ItemOf item_of, uint8_t* scratch) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -352,10 +358,10 @@ __device__ __forceinline__ void prefetch_down(const FfnArgs& a, int j, int n_pf,
         const int ai = i / NTd, t = i % NTd;
         const Item it = item_of(ai);
         if (it.e < 0) break;                  // past the active experts (ai grows with q)
-        if (it.e < a.E && (it.slot < 0 || it.slot >= a.num_slots)) continue;
+        if ((!SH || it.e < a.E) && (it.slot < 0 || it.slot >= a.num_slots)) continue;
         const size_t blk = (static_cast<size_t>(it.slot) * NTd + t) * S;
-        const uint8_t* c = item_codes(a, it, 2) + blk * kWave * PieceBytes<FMT>::codes;
-        const uint8_t* sc = item_scales(a, it, 2) + blk * kWave * PieceBytes<FMT>::scales;
+        const uint8_t* c = item_codes<SH>(a, it, 2) + blk * kWave * PieceBytes<FMT>::codes;
+        const uint8_t* sc = item_scales<SH>(a, it, 2) + blk * kWave * PieceBytes<FMT>::scales;
         // 1 KB per instruction, lanes past the end re-read the last 16 bytes
         for (int o = 0; o < code_bytes; o += 1024)
             __builtin_amdgcn_global_load_lds(c + min(o + 16 * lane, code_bytes - 16), (lds_void*)scratch, 16, 0, 0);
@@ -368,7 +374,7 @@ __device__ __forceinline__ void prefetch_down(const FfnArgs& a, int j, int n_pf,
 // The last workgroup of the down launch zeroes the y rows past offsets[E];
 // with the fused combine the gate/up launch zeroes out.  Gate/up workgroups
 // past the items prefetch down weights.
-template <int FMT, int MODE, int KW, int RB>
+template <int FMT, int MODE, int KW, int RB, bool SH>
 __global__ __launch_bounds__(KW * 64) __attribute__((amdgpu_waves_per_eu(4))) void ffn_skinny_kernel(FfnArgs a) {
     if (MODE == 1 && blockIdx.x == gridDim.x - 1) {
         zero_y_tail(a);
@@ -376,16 +382,16 @@ __global__ __launch_bounds__(KW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
     }
     const int NT = (MODE == 0 ? a.f : a.d) / 16;
     if (MODE == 0) {
-        const int g_items = (min(a.E, a.T * a.k) + a.has_shared) * NT;
+        const int g_items = (min(a.E, a.T * a.k) + (SH ? 1 : 0)) * NT;
         if (static_cast<int>(blockIdx.x) >= g_items) {
             __shared__ __align__(16) uint8_t pf[KW][1024];
-            prefetch_down<FMT>(a, blockIdx.x - g_items, gridDim.x - g_items,
-                               [&](int ai) { return item_at(a, ai); }, pf[threadIdx.x >> 6]);
+            prefetch_down<FMT, SH>(a, blockIdx.x - g_items, gridDim.x - g_items,
+                                   [&](int ai) { return item_at<SH>(a, ai); }, pf[threadIdx.x >> 6]);
             if (a.fuse_combine) zero_out_share(a);
             return;
         }
     }
-    run_item<FMT, MODE, KW, RB>(a, item_at(a, blockIdx.x / NT), (blockIdx.x % NT) * 16, a.perm);
+    run_item<FMT, MODE, KW, RB, false, SH>(a, item_at<SH>(a, blockIdx.x / NT), (blockIdx.x % NT) * 16, a.perm);
     if (MODE == 0 && a.fuse_combine) zero_out_share(a);
 }
 
@@ -419,8 +425,8 @@ __global__ __launch_bounds__(kGateUpWaves * 64) __attribute__((amdgpu_waves_per_
     const int g_items = min(E, n) * NT;
     if (static_cast<int>(blockIdx.x) >= g_items) {
         __shared__ __align__(16) uint8_t pf[kGateUpWaves][1024];
-        prefetch_down<FMT>(a, blockIdx.x - g_items, gridDim.x - g_items,
-                           [&](int ai) { return pick_item(lo, hi, sl, ai); }, pf[wave]);
+        prefetch_down<FMT, false>(a, blockIdx.x - g_items, gridDim.x - g_items,
+                                  [&](int ai) { return pick_item(lo, hi, sl, ai); }, pf[wave]);
     } else {
         run_item<FMT, 0, kGateUpWaves, RB, true>(a, pick_item(lo, hi, sl, blockIdx.x / NT), (blockIdx.x % NT) * 16,
                                                  r.perm);
@@ -446,21 +452,26 @@ __global__ __launch_bounds__(kGateUpWaves * 64) __attribute__((amdgpu_waves_per_
 // passes), so RB follows T; 16 rows of 1 KB per wave fill most of the LDS.
 static int staged_rows(int T) { return T <= 1 ? 1 : T <= 2 ? 2 : T <= 4 ? 4 : T <= 16 ? 8 : 16; }
 
-template <int FMT, int RB>
-static hipError_t launch_two_rb(const moe_shape& s, const FfnArgs& a, hipStream_t st, bool routed) {
-    const int umax = (s.E < s.T * s.k ? s.E : s.T * s.k) + a.has_shared;
+template <int FMT, int RB, bool SH>
+static hipError_t launch_two_sh(const moe_shape& s, const FfnArgs& a, hipStream_t st, bool routed) {
+    const int umax = (s.E < s.T * s.k ? s.E : s.T * s.k) + (SH ? 1 : 0);
     const int g_items = umax * (s.f / 16);
     const int g_up = g_items + (g_items + kDownPrefetchWGs <= kResidentGateUpWGs ? kDownPrefetchWGs : 0);
     if (routed) {
-        if constexpr (RB <= kGateUpWaves)
+        if constexpr (RB <= kGateUpWaves && !SH)
             ffn_gate_up_routed_kernel<FMT, RB><<<g_up, kGateUpWaves * 64, 0, st>>>(a);
     } else {
-        ffn_skinny_kernel<FMT, 0, kGateUpWaves, RB><<<g_up, kGateUpWaves * 64, 0, st>>>(a);
+        ffn_skinny_kernel<FMT, 0, kGateUpWaves, RB, SH><<<g_up, kGateUpWaves * 64, 0, st>>>(a);
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    ffn_skinny_kernel<FMT, 1, kDownWaves, RB><<<umax * (s.d / 16) + 1, kDownWaves * 64, 0, st>>>(a);
+    ffn_skinny_kernel<FMT, 1, kDownWaves, RB, SH><<<umax * (s.d / 16) + 1, kDownWaves * 64, 0, st>>>(a);
     return hipGetLastError();
+}
+
+template <int FMT, int RB>
+static hipError_t launch_two_rb(const moe_shape& s, const FfnArgs& a, hipStream_t st, bool routed) {
+    return a.has_shared ? launch_two_sh<FMT, RB, true>(s, a, st, routed) : launch_two_sh<FMT, RB, false>(s, a, st, routed);
 }
 
 template <int FMT>
