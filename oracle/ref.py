@@ -383,3 +383,126 @@ def layer_shared(x_bits, k: int, gate: dict, up: dict, down: dict, shared: dict,
     r["ys"] = shared_expert(x_bits, shared["gate"], shared["up"], shared["down"])
     r["out"] = r["out"] + r["ys"]
     return r
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 activations (the matrix cores' scaled fp4 x fp8 path)
+# ---------------------------------------------------------------------------
+
+# OCP Microscaling Formats (MX) v1.0, FP8 E4M3: sign, 4 exponent bits (bias 7),
+# 3 mantissa bits; exponent field 0 is subnormal (m/8 * 2**-6); S.1111.111 is
+# NaN and there is no infinity, so the largest finite magnitude is
+# 1.75 * 2**8 = 448.  A block of 32 elements shares one E8M0 scale.
+E4M3_MAX = 448.0
+E4M3_EMAX = 8            # exponent of the largest normal
+
+
+def e4m3_to_f64(codes) -> np.ndarray:
+    """Decode E4M3 codes (uint8) to float64; NaN codes decode to NaN."""
+    c = np.asarray(codes).astype(np.int64)
+    s, e, m = c >> 7, (c >> 3) & 15, c & 7
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * 2.0 ** (e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return np.where(s == 1, -mag, mag)
+
+
+def _e4m3_table() -> np.ndarray:
+    return e4m3_to_f64(np.arange(256))
+
+
+def round_e4m3(q) -> np.ndarray:
+    """Round float64 values to the nearest E4M3 value (ties to even
+    mantissa), saturating magnitudes above 448 to 448."""
+    q = np.asarray(q, dtype=np.float64)
+    a = np.abs(q)
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, -6.0)                      # below 2**-6 the step is the subnormal 2**-9
+    step = 2.0 ** (e - 3.0)
+    r = np.round(a / step) * step                # numpy rounds half to even
+    r = np.minimum(r, E4M3_MAX)
+    return np.where(q < 0, -r, r)
+
+
+def encode_e4m3(v) -> np.ndarray:
+    """E4M3 code of values that are exactly representable (and not NaN);
+    +0 for zero, the sign bit kept for negative values."""
+    v = np.asarray(v, dtype=np.float64)
+    table = _e4m3_table()
+    pos = table[:127]                            # codes 0..126: the non-negative finite values, increasing
+    idx = np.searchsorted(pos, np.abs(v))
+    if not np.array_equal(pos[np.minimum(idx, 126)], np.abs(v)):
+        raise ValueError("value not representable in E4M3")
+    return (idx + np.where(v < 0, 128, 0)).astype(np.uint8)
+
+
+def quantize_mxfp8(v):
+    """Quantise float64 values [..., K] (K a multiple of 32) to MXFP8 along
+    the last axis (OCP MX v1.0 conversion): per block of 32, the shared
+    scale is 2**(floor(log2(amax)) - 8) (8 = E4M3's largest exponent; E8M0
+    byte = that exponent + 127, clamped to 0..254; an all-zero block gets
+    byte 0), and each element is v / scale rounded to E4M3 as round_e4m3.
+    Returns (codes uint8 [..., K], scale bytes uint8 [..., K/32])."""
+    v = np.asarray(v, dtype=np.float64)
+    blocks = v.reshape(v.shape[:-1] + (v.shape[-1] // 32, 32))
+    amax = np.abs(blocks).max(axis=-1)
+    with np.errstate(divide="ignore"):
+        ex = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - E4M3_EMAX, -127.0)
+    sbyte = np.clip(ex + 127.0, 0, 254)
+    scale = 2.0 ** (sbyte - 127.0)
+    q = round_e4m3(blocks / scale[..., None])
+    return encode_e4m3(q).reshape(v.shape), sbyte.astype(np.uint8)
+
+
+def mxfp8_to_f64(codes, scale_bytes) -> np.ndarray:
+    """Values of MXFP8 data [..., K] with scale bytes [..., K/32]."""
+    c = np.asarray(codes)
+    vals = e4m3_to_f64(c).reshape(c.shape[:-1] + (c.shape[-1] // 32, 32))
+    return (vals * 2.0 ** (np.asarray(scale_bytes, dtype=np.float64) - 127.0)[..., None]).reshape(c.shape)
+
+
+def expert_ffn_mx8(x_bits, k: int, offsets, perm, gate: dict, up: dict, down: dict, slot_of_expert=None):
+    """Steps 4 and 5 with MXFP8 activations (the matrix cores' native scaled
+    fp4 x fp8 products): the token rows x_t and the SwiGLU output are each
+    quantised to MXFP8 along their contraction axis (quantize_mxfp8) in
+    place of the bf16 rounding point; products and sums are float64.
+    Returns act float64 [T*k, f] (the MXFP8 values), its codes and scale
+    bytes, and y float64 [T*k, d]."""
+    xq, xs = quantize_mxfp8(bf16_bits_to_f64(x_bits))
+    xv = mxfp8_to_f64(xq, xs)
+    offsets = np.asarray(offsets, dtype=np.int64)
+    perm = np.asarray(perm, dtype=np.int64)
+    E = offsets.size - 1
+    R = perm.size
+    f, d = gate["codes"].shape[1], down["codes"].shape[1]
+    h = np.zeros((R, f))
+    y = np.zeros((R, d))
+    wd = {}
+    for e in range(E):
+        r0, r1 = offsets[e], offsets[e + 1]
+        if r1 <= r0:
+            continue
+        slot = e if slot_of_expert is None else int(slot_of_expert[e])
+        xt = xv[perm[r0:r1] // k]
+        h[r0:r1] = silu(xt @ dequant(gate, slot).T) * (xt @ dequant(up, slot).T)
+        wd[e] = dequant(down, slot)
+    aq, asc = quantize_mxfp8(h)
+    act = mxfp8_to_f64(aq, asc)
+    for e, w in wd.items():
+        r0, r1 = offsets[e], offsets[e + 1]
+        y[r0:r1] = act[r0:r1] @ w.T
+    return act, aq, asc, y
+
+
+def layer_mx8(x_bits, k: int, gate: dict, up: dict, down: dict, *, logits=None, w_router=None, bias=None):
+    """The layer with MXFP8 activations in the expert FFN (routing and
+    combine as ``layer``)."""
+    if logits is None:
+        logits = router_logits(x_bits, w_router, bias)
+    logits = np.asarray(logits, dtype=np.float64)
+    ids, w = route_topk(logits, k)
+    offsets, perm, inv = dispatch(ids, logits.shape[1])
+    act, aq, asc, y = expert_ffn_mx8(x_bits, k, offsets, perm, gate, up, down)
+    out = combine(y, inv, w, k)
+    return dict(logits=logits, ids=ids, w=w, offsets=offsets, perm=perm, inv=inv, act=act, act_codes=aq,
+                act_scales=asc, y=y, out=out)

@@ -410,3 +410,90 @@ def test_shared_expert_is_one_more_routed_slot():
     _, y = ref.expert_ffn(c["x"], 2, offsets, perm, packs["gate"], packs["up"], packs["down"])
     out = ref.combine(y, inv, w, 2)
     assert np.allclose(r["out"], out, rtol=1e-13, atol=1e-13)
+
+
+# ------------------------------------------------------------- MXFP8 activations
+
+def test_e4m3_decode_against_spec_and_torch():
+    """E4M3 (OCP MX v1.0 FP8): largest normal 448 (0x7E), smallest normal
+    2**-6 (0x08), smallest subnormal 2**-9 (0x01), 1.0 = 0x38, NaN at
+    S.1111.111; every finite code equals torch's float8_e4m3fn decoding."""
+    t = ref.e4m3_to_f64(np.arange(256))
+    assert t[0x7E] == 448.0 and t[0x08] == 2.0 ** -6 and t[0x01] == 2.0 ** -9 and t[0x38] == 1.0
+    assert t[0xFE] == -448.0 and np.isnan(t[0x7F]) and np.isnan(t[0xFF])
+    tt = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    fin = ~np.isnan(t)
+    assert np.array_equal(np.isnan(tt), ~fin)
+    assert np.array_equal(t[fin], tt[fin])
+
+
+def test_e4m3_rounding_against_torch():
+    """round_e4m3 is round-to-nearest-even with saturation: equal to torch's
+    float8_e4m3fn cast of the value clamped to [-448, 448], on random values
+    over the whole range and on every midpoint between neighbours."""
+    rng = np.random.default_rng(21)
+    v = (rng.standard_normal(20000) * 2.0 ** rng.integers(-12, 10, 20000)).astype(np.float32).astype(np.float64)
+    pos = np.unique(np.abs(ref.e4m3_to_f64(np.arange(127))))
+    mids = (pos[1:] + pos[:-1]) / 2
+    v = np.concatenate([v, mids, -mids, [500.0, -1e6, 0.0]])
+    want = torch.from_numpy(np.clip(v, -448.0, 448.0)).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(ref.round_e4m3(v), want)
+
+
+def test_mxfp8_quantizer_rules():
+    rng = np.random.default_rng(22)
+    v = rng.standard_normal((5, 128)) * 2.0 ** rng.integers(-20, 20, (5, 1))
+    v[2, 32:64] = 0.0
+    codes, sb = ref.quantize_mxfp8(v)
+    vals = ref.mxfp8_to_f64(codes, sb)
+    blocks = np.abs(v).reshape(5, 4, 32).max(axis=-1)
+    scale = 2.0 ** (sb.astype(np.float64) - 127)
+    nz = blocks > 0
+    # the block maximum lands in [2**8, 2**9) before rounding
+    assert np.all((blocks[nz] / scale[nz] >= 256) & (blocks[nz] / scale[nz] < 512))
+    assert sb[2, 1] == 0 and not np.any(vals[2, 32:64])
+    # within half an E4M3 step (relative 2**-4) of the input where no
+    # saturation applies (scaled magnitude <= 448); above it, exactly 448
+    err = np.abs(vals - v) / np.maximum(np.abs(v), 1e-300)
+    scaled = np.abs(v) / scale.repeat(32, axis=1)
+    normal = (scaled >= 2.0 ** -6) & (scaled <= 448)
+    assert np.all(err[normal] <= 2.0 ** -4 + 1e-15)
+    assert np.all(np.abs(vals[scaled > 464]) == 448 * scale.repeat(32, axis=1)[scaled > 464])
+    c2, s2 = ref.quantize_mxfp8(vals)
+    assert np.array_equal(c2, codes) and np.array_equal(s2, sb)
+
+
+def test_mx8_single_expert_is_dense_swiglu_with_fp8_casts():
+    """E = 1, k = 1 with MXFP8 activations: a dense SwiGLU MLP in torch
+    float64 where both activations go through torch's float8_e4m3fn cast
+    with the block scale of the largest magnitude (an independent route to
+    the same quantisation)."""
+    c = _small_case("mxfp4", T=5, d=64, E=1, k=1, f=32, seed=23)
+    r = ref.layer_mx8(c["x"], 1, c["gate"], c["up"], c["down"], w_router=c["w_router"])
+
+    def mx8(t):
+        b = t.reshape(t.shape[0], -1, 32)
+        amax = b.abs().amax(dim=-1, keepdim=True)
+        sc = torch.exp2(torch.floor(torch.log2(amax)) - 8)
+        q = torch.clamp(b / sc, -448, 448).to(torch.float8_e4m3fn).to(torch.float64)
+        return (q * sc).reshape(t.shape)
+
+    x = torch.tensor([[brute.bf16_value(int(b)) for b in row] for row in c["x"]], dtype=torch.float64)
+    wg = torch.from_numpy(_dense_weights_brute(c["gate"], 0, 32, 64))
+    wu = torch.from_numpy(_dense_weights_brute(c["up"], 0, 32, 64))
+    wd = torch.from_numpy(_dense_weights_brute(c["down"], 0, 64, 32))
+    xq = mx8(x)
+    act = mx8(torch.nn.functional.silu(xq @ wg.T) * (xq @ wu.T))
+    assert np.allclose(r["out"], (act @ wd.T).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_mx8_layer_close_to_bf16_layer():
+    """MXFP8 activations move out by about their rounding (relative 2**-5
+    per element on average), no more: a dropped scale or transposed
+    operand would not stay within a few per cent of the bf16 layer."""
+    c = _small_case("mxfp4", T=12, d=256, E=8, k=2, f=128, seed=24)
+    a = ref.layer(c["x"], 2, c["gate"], c["up"], c["down"], w_router=c["w_router"])
+    b = ref.layer_mx8(c["x"], 2, c["gate"], c["up"], c["down"], w_router=c["w_router"])
+    assert np.array_equal(a["ids"], b["ids"])
+    rel = np.linalg.norm(b["out"] - a["out"]) / np.linalg.norm(a["out"])
+    assert 1e-3 < rel < 0.05, rel
