@@ -255,6 +255,35 @@ int moe_layer(const moe_shape* shape, const uint16_t* x, const float* w_router,
               int32_t* topk_ids, float* topk_w, float* out, void* ws, size_t ws_bytes,
               hipStream_t stream);
 
+/* ---- MXFP8 activations: the block-scaled fp4 x fp8 matrix cores.
+
+   A faster mode that changes the rounding points, as the pages' engine
+   keeps fast reduced-precision accelerator paths beside a switch that
+   turns them off for quality (Anemll/ds4-ssd README, section "Experimental
+   Pro Support": --no-int8 / --quality).  The token rows and the SwiGLU
+   output are quantised to MXFP8 (OCP Microscaling Formats v1.0: E4M3
+   elements, one E8M0 scale per 32 along the contraction axis, the scale
+   2^(floor(log2 amax) - 8), elements rounded to nearest even and saturated
+   at 448) instead of being kept in / rounded to bf16; MXFP4 weights and
+   MXFP8 activations then meet in the gfx950 32x32x64 block-scaled matrix
+   instruction with fp32 accumulation.  Steps 4-5 become
+     xq[r] = MXFP8(x[perm[r] / k]),  act_q[r] = MXFP8(silu(Wg xq[r]) * (Wu xq[r])),
+     y[r]  = Wd act_q[r]                                              (fp32)
+   MXFP4 weights only, and shapes the grouped FFN takes (d % 512 == 0,
+   f % 256 == 0); otherwise MOE_ERR_UNSUPPORTED.  Arguments as
+   moe_expert_ffn / moe_layer; the workspace also holds the quantised rows
+   (moe_workspace_bytes_mx8, moe_layer_mx8_workspace_bytes): after a call,
+   act_q codes u8 [T*k][f] start at byte 256 of ws. */
+size_t moe_workspace_bytes_mx8(const moe_shape* shape);
+int moe_expert_ffn_mx8(const moe_shape* shape, const uint16_t* x, const moe_experts* experts,
+                       const int32_t* offsets, const int32_t* perm, float* y, void* ws,
+                       size_t ws_bytes, hipStream_t stream);
+size_t moe_layer_mx8_workspace_bytes(const moe_shape* shape);
+int moe_layer_mx8(const moe_shape* shape, const uint16_t* x, const float* w_router,
+                  const float* bias, float* logits, const moe_experts* experts,
+                  int32_t* topk_ids, float* topk_w, float* out, void* ws, size_t ws_bytes,
+                  hipStream_t stream);
+
 /* ---- Shared expert: one always-on SwiGLU expert beside the routed ones.
 
    DeepSeek blocks add a shared expert that every token passes through; the

@@ -52,6 +52,7 @@ EXPORTS = (
     "moe_status_str", "moe_read_device_status", "moe_qmat_bytes", "moe_pack_qmat",
     "moe_bank_reset", "moe_bank_plan", "moe_bank_fetch", "moe_layer_banked",
     "moe_layer_shared_workspace_bytes", "moe_layer_shared",
+    "moe_workspace_bytes_mx8", "moe_expert_ffn_mx8", "moe_layer_mx8_workspace_bytes", "moe_layer_mx8",
 )
 
 
@@ -119,6 +120,10 @@ def lib() -> ctypes.CDLL:
             "moe_pack_qmat": (_I, [_P, _P, _I, _I, _I, _P]),
             "moe_layer_shared_workspace_bytes": (_SZ, [_P]),
             "moe_layer_shared": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+            "moe_workspace_bytes_mx8": (_SZ, [_P]),
+            "moe_expert_ffn_mx8": (_I, [_P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+            "moe_layer_mx8_workspace_bytes": (_SZ, [_P]),
+            "moe_layer_mx8": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
             "moe_bank_reset": (_I, [_P]),
             "moe_bank_plan": (_I, [_P, _P, _I, _P, _P, _P]),
             "moe_bank_fetch": (_I, [_P, _P, _I, _I, _P, _P, _I, _P]),
@@ -387,6 +392,55 @@ def layer(x, experts: Experts, k: int, *, w_router=None, bias=None, logits=None,
     if ws is None:
         ws = alloc_workspace(shape, layer=True, device=dev, stream=stream)
     moe_layer(shape, x, w_router, bias, logits, experts, ids, w, out, ws, stream)
+    return out, ids, w, logits
+
+
+# ------------------------------------------------------------ MXFP8 activations
+
+def moe_expert_ffn_mx8(shape: Shape, x, experts: Experts, offsets, perm, y, ws, stream=None) -> None:
+    torch = _torch()
+    ex = experts.c()
+    rc = lib().moe_expert_ffn_mx8(
+        ctypes.byref(shape.c()), _ptr(x, (torch.int16, torch.bfloat16, torch.uint16), "x"),
+        ctypes.byref(ex), _ptr(offsets, torch.int32, "offsets"), _ptr(perm, torch.int32, "perm"),
+        _ptr(y, torch.float32, "y"), _ptr(ws, name="ws"), ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc, "moe_expert_ffn_mx8")
+
+
+def alloc_workspace_mx8(shape: Shape, layer: bool = False, device="cuda", stream=None):
+    torch = _torch()
+    fn = lib().moe_layer_mx8_workspace_bytes if layer else lib().moe_workspace_bytes_mx8
+    n = int(fn(ctypes.byref(shape.c())))
+    if n == 0:
+        raise MoeError(MOE_ERR_SHAPE, "alloc_workspace_mx8")
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    moe_workspace_init(ws, stream)
+    return ws
+
+
+def layer_mx8(x, experts: Experts, k: int, *, w_router=None, bias=None, logits=None, ws=None, stream=None):
+    """moe_layer_mx8: the layer with MXFP8 activations in the expert FFN;
+    returns (out, topk_ids, topk_w, logits)."""
+    torch = _torch()
+    T, d = x.shape
+    E = int(w_router.shape[0]) if w_router is not None else int(logits.shape[1])
+    shape = Shape(T, d, E, k, experts.f)
+    dev = x.device
+    if logits is None:
+        logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    out = torch.empty((T, d), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = alloc_workspace_mx8(shape, layer=True, device=dev, stream=stream)
+    ex = experts.c()
+    rc = lib().moe_layer_mx8(
+        ctypes.byref(shape.c()), _ptr(x, (torch.int16, torch.bfloat16, torch.uint16), "x"),
+        _ptr(w_router, torch.float32, "w_router", allow_none=True),
+        _ptr(bias, torch.float32, "bias", allow_none=True), _ptr(logits, torch.float32, "logits"),
+        ctypes.byref(ex), _ptr(ids, torch.int32, "topk_ids"), _ptr(w, torch.float32, "topk_w"),
+        _ptr(out, torch.float32, "out"), _ptr(ws, name="ws"), ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc, "moe_layer_mx8")
     return out, ids, w, logits
 
 

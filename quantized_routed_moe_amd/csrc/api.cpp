@@ -370,6 +370,69 @@ int moe_layer_shared(const moe_shape* shape, const uint16_t* x, const float* w_r
     return hip_rc(qrmoe::launch_combine(s, y, inv, topk_w, out, stream, true));
 }
 
+size_t moe_workspace_bytes_mx8(const moe_shape* shape) {
+    if (check_shape(shape) != MOE_OK) return 0;
+    return qrmoe::mx8_carve(*shape).total;
+}
+
+size_t moe_layer_mx8_workspace_bytes(const moe_shape* shape) {
+    if (check_shape(shape) != MOE_OK) return 0;
+    return qrmoe::layer_carve_mx8(*shape).total;
+}
+
+int moe_expert_ffn_mx8(const moe_shape* shape, const uint16_t* x, const moe_experts* experts, const int32_t* offsets,
+                       const int32_t* perm, float* y, void* ws, size_t ws_bytes, hipStream_t stream) {
+    int rc = check_shape(shape);
+    if (rc != MOE_OK) return rc;
+    if (shape->T == 0) return MOE_OK;
+    const moe_shape& s = *shape;
+    if ((rc = check_ffn_args(s, x, experts, offsets, perm, y, ws, ws_bytes)) != MOE_OK) return rc;
+    if (experts->gate.fmt != MOE_FMT_MXFP4 || !qrmoe::grouped_supported(s, MOE_FMT_MXFP4)) return MOE_ERR_UNSUPPORTED;
+    const qrmoe::Mx8Carve c = qrmoe::mx8_carve(s);
+    if (ws_bytes < c.total) return MOE_ERR_WORKSPACE;
+    char* base = static_cast<char*>(ws);
+    FfnArgs a = ffn_args(s, x, experts, offsets, perm, y, ws);
+    a.act = nullptr;
+    a.flags = reinterpret_cast<unsigned long long*>(base + c.flags);
+    a.aq = reinterpret_cast<uint8_t*>(base + c.aq);
+    a.as = reinterpret_cast<uint8_t*>(base + c.as);
+    a.xq = reinterpret_cast<const uint8_t*>(base + c.xq);
+    a.xs = reinterpret_cast<const uint8_t*>(base + c.xs);
+    a.rpad = c.rpad;
+    return hip_rc(qrmoe::launch_ffn_mx8(s, a, stream));
+}
+
+int moe_layer_mx8(const moe_shape* shape, const uint16_t* x, const float* w_router, const float* bias, float* logits,
+                  const moe_experts* experts, int32_t* topk_ids, float* topk_w, float* out, void* ws, size_t ws_bytes,
+                  hipStream_t stream) {
+    int rc = check_shape(shape);
+    if (rc != MOE_OK) return rc;
+    if (shape->T == 0) return MOE_OK;
+    const moe_shape& s = *shape;
+    if (!ws || !out || !x || !experts) return MOE_ERR_NULL;
+    if (!aligned(ws, 16) || !aligned(out, 16)) return MOE_ERR_ALIGN;
+    const LayerCarve c = qrmoe::layer_carve_mx8(s);
+    if (ws_bytes < c.total) return MOE_ERR_WORKSPACE;
+    char* base = static_cast<char*>(ws);
+    int32_t* offsets = reinterpret_cast<int32_t*>(base + c.offsets);
+    int32_t* perm = reinterpret_cast<int32_t*>(base + c.perm);
+    int32_t* inv = reinterpret_cast<int32_t*>(base + c.inv);
+    float* y = reinterpret_cast<float*>(base + c.y);
+    if ((rc = check_route_args(s, x, w_router, bias, logits, topk_ids, topk_w)) != MOE_OK) return rc;
+    if ((rc = check_ffn_args(s, x, experts, offsets, perm, y, ws, ws_bytes)) != MOE_OK) return rc;
+    if (experts->gate.fmt != MOE_FMT_MXFP4 || !qrmoe::grouped_supported(s, MOE_FMT_MXFP4)) return MOE_ERR_UNSUPPORTED;
+    if (qrmoe::small_route_supported(s)) {
+        if ((rc = hip_rc(qrmoe::launch_small_route(s, x, w_router, bias, logits, topk_ids, topk_w, offsets, perm,
+                                                   inv, stream))) != MOE_OK)
+            return rc;
+    } else {
+        if ((rc = do_route(s, x, w_router, bias, logits, topk_ids, topk_w, stream)) != MOE_OK) return rc;
+        if ((rc = do_dispatch(s, topk_ids, offsets, perm, inv, ws, stream)) != MOE_OK) return rc;
+    }
+    if ((rc = moe_expert_ffn_mx8(shape, x, experts, offsets, perm, y, ws, ws_bytes, stream)) != MOE_OK) return rc;
+    return do_combine(s, y, inv, topk_w, out, stream);
+}
+
 const char* moe_status_str(int status) {
     switch (status) {
         case MOE_OK: return "MOE_OK";

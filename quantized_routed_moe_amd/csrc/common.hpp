@@ -97,6 +97,59 @@ __device__ __forceinline__ bf16x8 bf16x8_zero() {
 
 // ---------------------------------------------------------------- misc
 
+// ---- MXFP8 activations (OCP MX v1.0: E4M3 elements, one E8M0 scale per 32)
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// 32x32x64 block-scaled product, A = 32 E2M1 weights per lane (16 bytes of
+// a tile-layout piece, one K block of 32), B = 32 E4M3 token bytes per lane,
+// fp32 accumulation; sa / sb are the E8M0 scale bytes of the lane's A row
+// block and B column block.  Lane layout (measured on gfx950): lane l holds
+// A row l%32 and B column l%32; A's 32 elements are K block l/32, B's bytes
+// 0..15 and 16..31 are elements [16(l/32), +16) of K blocks 0 and 1, and
+// B's scale is that of K block l/32.
+__device__ __forceinline__ f32x16 mfma_scale_fp4_fp8(u32x4 a, i32x8 b, f32x16 c, int sa, int sb) {
+    const i32x8 a8 = {static_cast<int>(a[0]), static_cast<int>(a[1]), static_cast<int>(a[2]), static_cast<int>(a[3]),
+                      0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b, c, 4, 0, 0, sa, 0, sb);
+}
+
+// E8M0 scale byte of a block whose largest magnitude is amax:
+// floor(log2 amax) - 8 + 127 (8 = E4M3's largest exponent), clamped to
+// 0..254; 0 for an all-zero block.
+__device__ __forceinline__ int mx8_scale_byte(float amax) {
+    if (!(amax > 0.f)) return 0;
+    const int e = ilogbf(amax) - 8 + 127;
+    return e < 0 ? 0 : e > 254 ? 254 : e;
+}
+
+// v (already divided by the block scale, |v| < 512) to E4M3, round to
+// nearest even, magnitudes above 448 saturated to 448; zero is +0.
+__device__ __forceinline__ uint32_t e4m3_rne_sat(float v) {
+    const uint32_t bits = __float_as_uint(v);
+    const uint32_t sign = (bits >> 24) & 0x80u;
+    const uint32_t mag = bits & 0x7FFFFFFFu;
+    const float a = __uint_as_float(mag);
+    uint32_t code;
+    if (a >= 448.f) {
+        code = 0x7E;
+    } else if (a < 0.015625f) {                 // below 2^-6: subnormal steps of 2^-9 (exact scaling)
+        code = static_cast<uint32_t>(rintf(a * 512.f));
+    } else {
+        int e = static_cast<int>(mag >> 23) - 127;
+        uint32_t keep = (mag >> 20) & 7u;
+        const uint32_t rest = mag & 0xFFFFFu;
+        if (rest > 0x80000u || (rest == 0x80000u && (keep & 1u))) ++keep;
+        if (keep == 8u) {
+            keep = 0;
+            ++e;
+        }
+        code = static_cast<uint32_t>(e + 7) << 3 | keep;
+        if (code > 0x7Eu) code = 0x7E;
+    }
+    return code ? (sign | code) : 0u;
+}
+
 __device__ __forceinline__ float silu_mul(float g, float u) {
     // silu(g) * u = g / (1 + exp(-g)) * u
     return g / (1.0f + expf(-g)) * u;

@@ -83,9 +83,11 @@ constexpr int kFullPerPart = 2;
 // a stage holds the weights, their scales and only the 32*NTT token rows the
 // multiplies read, so units with few rows keep more stages (and bytes) in
 // flight: 7 stages for NTT = 1, 6, 5 and 4 for NTT = 4.
-template <int NTT> struct Ring {
-    static constexpr int x_bytes = 32 * NTT * 128;              // token rows x 64 bf16
-    static constexpr int stage = kStageW + kStageS + x_bytes;
+// XQ (MXFP8 activations): token rows of 64 E4M3 bytes plus their two
+// blocks' scale bytes for all 128 rows (256 bytes).
+template <int NTT, bool XQ = false> struct Ring {
+    static constexpr int x_bytes = 32 * NTT * (XQ ? 64 : 128);  // token rows x 64 elements
+    static constexpr int stage = kStageW + kStageS + x_bytes + (XQ ? 256 : 0);
     static constexpr int count = kLdsBytes / stage;
     static_assert(count >= 4 && count <= 8, "ring depth");
 };
@@ -104,13 +106,16 @@ __device__ __forceinline__ void wait_stages(int r) {
 // Byte offset of 16-byte chunk `chunk` (0..7) of token row `row` (128 B) in
 // the token tile (see the swizzle above).
 __device__ __forceinline__ int xswz(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
+// The same for E4M3 token rows (64 B, chunks 0..3): chunk ^ (row / 4) mod 4
+// puts 16 consecutive rows at one logical chunk in 16 distinct bank groups.
+__device__ __forceinline__ int xswz8(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4); }
 
 // One work unit (see Schedule above) on the workgroup's LDS ring `lds`.
 // CHAIN (both projections in one launch): a gate/up unit stores act with
 // device-scope stores and then raises flag `unit`; a down unit first waits
 // for the flags of every gate/up unit of its m-tile, then reads act with
 // device-scope loads (chain.hpp).
-template <int MODE, bool CHAIN>
+template <int MODE, bool CHAIN, bool XQ = false>
 __device__ __forceinline__ void grouped_unit(const FfnArgs& a, int unit, unsigned long long tag, uint8_t* lds) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -240,13 +245,23 @@ __device__ __forceinline__ void grouped_unit(const FfnArgs& a, int unit, unsigne
         ssrc = wscales(mat) + blk * 64 + 16 * (lane & 1);
     }
     const uint16_t* xsrc[2];     // token row 16w + 8i + (lane >> 3), global chunk for LDS chunk lane & 7
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int row = 16 * wave + 8 * i + (lane >> 3);
+    const uint8_t* qsrc = nullptr;   // XQ: E4M3 token row 16w + (lane >> 2), global chunk for LDS chunk lane & 3
+    const uint8_t* qssrc = nullptr;  // XQ, wave 1, lanes 0..15: scale bytes of rows r_base + 16 (lane & 7) .. +16, block lane >> 3
+    if constexpr (XQ) {
+        const int row = 16 * wave + (lane >> 2);
         const int rr = r_base + (row < nvalid ? row : 0);
-        const uint16_t* rowp = MODE == 0 ? a.x + static_cast<size_t>(a.perm[rr] / a.k) * a.d
-                                         : a.act + static_cast<size_t>(rr) * a.f;
-        xsrc[i] = rowp + (((lane & 7) ^ ((row >> 1) & 7)) << 3);
+        qsrc = (MODE == 0 ? a.xq + static_cast<size_t>(rr) * a.d : a.aq + static_cast<size_t>(rr) * a.f) +
+               (((lane & 3) ^ ((row >> 2) & 3)) << 4);
+        qssrc = (MODE == 0 ? a.xs : a.as) + static_cast<size_t>(lane >> 3 & 1) * a.rpad + r_base + 16 * (lane & 7);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int row = 16 * wave + 8 * i + (lane >> 3);
+            const int rr = r_base + (row < nvalid ? row : 0);
+            const uint16_t* rowp = MODE == 0 ? a.x + static_cast<size_t>(a.perm[rr] / a.k) * a.d
+                                             : a.act + static_cast<size_t>(rr) * a.f;
+            xsrc[i] = rowp + (((lane & 7) ^ ((row >> 1) & 7)) << 3);
+        }
     }
     // Token rows at or past 32 * (live column tiles) are never read: the waves
     // that own them (rows 16w .. 16w+15) copy no token rows at all.
@@ -263,7 +278,16 @@ __device__ __forceinline__ void grouped_unit(const FfnArgs& a, int unit, unsigne
         if (wave == 0)     // all 32 tiles' scale bytes of the stage: one 1 KB copy
             __builtin_amdgcn_global_load_lds(ssrc + (s >> 1) * 64 + (s & 1) * 32,
                                              (lds_void*)(base + kStageW), 16, 0, 0);
-        if (x_live) {
+        if constexpr (XQ) {
+            constexpr int XB = SB - kStageW - kStageS - 256;        // token rows of the stage
+            if (x_live)
+                __builtin_amdgcn_global_load_lds(qsrc + s * kGK, (lds_void*)(base + kStageW + kStageS + 16 * wave * 64), 16,
+                                                 0, CHAIN && MODE == 1 ? kAuxDevice : 0);
+            if (wave == 1 && lane < 16)   // both K blocks' scale bytes of all 128 rows
+                __builtin_amdgcn_global_load_lds(qssrc + static_cast<size_t>(2 * s) * a.rpad,
+                                                 (lds_void*)(base + kStageW + kStageS + XB), 16, 0,
+                                                 CHAIN && MODE == 1 ? kAuxDevice : 0);
+        } else if (x_live) {
 #pragma unroll
             for (int i = 0; i < 2; ++i)
                 __builtin_amdgcn_global_load_lds(xsrc[i] + s * kGK,
@@ -288,7 +312,7 @@ __device__ __forceinline__ void grouped_unit(const FfnArgs& a, int unit, unsigne
 
     auto kloop = [&](auto ntt_c) {
         constexpr int NTT = decltype(ntt_c)::value;
-        constexpr int NST = Ring<NTT>::count, SB = Ring<NTT>::stage;
+        constexpr int NST = Ring<NTT, XQ>::count, SB = Ring<NTT, XQ>::stage;
         const auto nst_c = std::integral_constant<int, NST>{};
         const auto sb_c = std::integral_constant<int, SB>{};
         for (int s = 0; s < NST - 1 && s < S; ++s) issue(s, nst_c, sb_c);
@@ -296,7 +320,11 @@ __device__ __forceinline__ void grouped_unit(const FfnArgs& a, int unit, unsigne
             // stage s is in LDS once at most the younger stages issued so far
             // (up to NST - 2) are in flight; each wave counts its own loads
             const int younger = min(NST - 2, S - 1 - s);
-            if (wave == 0) {
+            if constexpr (XQ) {          // waves 0 and 1 always hold live rows
+                if (wave <= 1) wait_stages<4, NST - 2>(younger);
+                else if (x_live) wait_stages<3, NST - 2>(younger);
+                else wait_stages<2, NST - 2>(younger);
+            } else if (wave == 0) {
                 if (x_live) wait_stages<5, NST - 2>(younger);
                 else wait_stages<3, NST - 2>(younger);
             } else {
@@ -317,6 +345,29 @@ __device__ __forceinline__ void grouped_unit(const FfnArgs& a, int unit, unsigne
             const u32x4 c0 = *reinterpret_cast<const u32x4*>(wb + pc0 * 16);
             const u32x4 c1 = *reinterpret_cast<const u32x4*>(wb + pc1 * 16);
             const uint32_t sc0 = sb[pc0], sc1 = sb[pc1];
+            if constexpr (XQ) {
+                // one block-scaled 32x32x64 product per (weight tile, column
+                // tile): the pieces and their E8M0 bytes go in as they are,
+                // the token fragment is chunks h and 2 + h of the E4M3 row
+                const uint8_t* xsb = xb + 32 * NTT * 64;
+                i32x8 b[NTT];
+                int bs[NTT];
+#pragma unroll
+                for (int t = 0; t < NTT; ++t) {
+                    const u32x4 lo = *reinterpret_cast<const u32x4*>(xb + xswz8(32 * t + r32, h));
+                    const u32x4 hi = *reinterpret_cast<const u32x4*>(xb + xswz8(32 * t + r32, 2 + h));
+                    b[t] = i32x8{static_cast<int>(lo[0]), static_cast<int>(lo[1]), static_cast<int>(lo[2]),
+                                 static_cast<int>(lo[3]), static_cast<int>(hi[0]), static_cast<int>(hi[1]),
+                                 static_cast<int>(hi[2]), static_cast<int>(hi[3])};
+                    bs[t] = xsb[128 * h + 32 * t + r32];
+                }
+#pragma unroll
+                for (int t = 0; t < NTT; ++t) {
+                    acc[0][t] = mfma_scale_fp4_fp8(c0, b[t], acc[0][t], static_cast<int>(sc0), bs[t]);
+                    acc[1][t] = mfma_scale_fp4_fp8(c1, b[t], acc[1][t], static_cast<int>(sc1), bs[t]);
+                }
+                continue;
+            }
             u32x4 bcur[NTT], bnext[NTT];
 #pragma unroll
             for (int t = 0; t < NTT; ++t) bcur[t] = *reinterpret_cast<const u32x4*>(xb + xswz(32 * t + r32, 4 * h));
@@ -354,6 +405,42 @@ __device__ __forceinline__ void grouped_unit(const FfnArgs& a, int unit, unsigne
 
     // ---- epilogue.  Lane l holds, for element i, weight row
     // 8*(i/4) + 4*(l/32) + i%4 of the 32-row tile and token row l%32.
+    if constexpr (XQ && MODE == 0) {
+        // act to MXFP8: a wave's 32 gate rows of one token are one block of
+        // 32 act columns, 16 values in lane l and 16 in lane l ^ 32
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            if (t >= ntt) continue;
+            float v[16];
+            float amax = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                v[i] = silu_mul(acc[0][t][i], acc[1][t][i]);
+                amax = fmaxf(amax, fabsf(v[i]));
+            }
+            amax = fmaxf(amax, __shfl_xor(amax, 32));
+            const int j = 32 * t + r32;
+            if (j >= nvalid) continue;
+            const int sbyte = mx8_scale_byte(amax);
+            const size_t r = static_cast<size_t>(r_base + j);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                uint32_t word = 0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) word |= e4m3_rne_sat(ldexpf(v[4 * q + i], 127 - sbyte)) << (8 * i);
+                uint32_t* dst = reinterpret_cast<uint32_t*>(a.aq + r * a.f + nt * (kGN / 2) + 32 * wave + 8 * q + 4 * h);
+                if constexpr (CHAIN) __hip_atomic_store(dst, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                else *dst = word;
+            }
+            if (h == 0) {
+                uint8_t* ds = a.as + static_cast<size_t>(nt * (kGN / 64) + wave) * a.rpad + r;
+                if constexpr (CHAIN) __hip_atomic_store(ds, static_cast<uint8_t>(sbyte), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                else *ds = static_cast<uint8_t>(sbyte);
+            }
+        }
+        if constexpr (CHAIN) raise_flag(a.flags + unit, tag);
+        return;
+    }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const int j = 32 * t + r32;
@@ -416,12 +503,13 @@ __global__ void zero_tail_rows_kernel(FfnArgs a) { zero_tail_rows(a, blockIdx.x,
 // units, chain.hpp), the last one zeroes the y rows past offsets[E].  The
 // down units thus fill the CUs that the gate/up launch's last, uneven units
 // leave idle, instead of waiting for all of them behind a kernel boundary.
+template <bool XQ>
 __global__ __launch_bounds__(kGThreads) void ffn_grouped_chained_kernel(FfnArgs a, int ub0, int ub1) {
     __shared__ __align__(16) uint8_t lds[kLdsBytes];
     const unsigned long long tag = chain_tag();
     const int b = blockIdx.x;
-    if (b < ub0) grouped_unit<0, true>(a, b, tag, lds);
-    else if (b < ub0 + ub1) grouped_unit<1, true>(a, b - ub0, tag, lds);
+    if (b < ub0) grouped_unit<0, true, XQ>(a, b, tag, lds);
+    else if (b < ub0 + ub1) grouped_unit<1, true, XQ>(a, b - ub0, tag, lds);
     else zero_tail_rows(a, 0, 1);
 }
 
@@ -442,7 +530,7 @@ hipError_t launch_ffn_grouped(const moe_shape& s, const FfnArgs& a, hipStream_t 
     const int units0 = max_mtiles(s, a.has_shared) * (s.f / (kGN / 2));
     const int units1 = max_mtiles(s, a.has_shared) * (s.d / kGN);
     if (a.flags) {
-        ffn_grouped_chained_kernel<<<units0 + units1 + 1, kGThreads, 0, st>>>(a, units0, units1);
+        ffn_grouped_chained_kernel<false><<<units0 + units1 + 1, kGThreads, 0, st>>>(a, units0, units1);
         return hipGetLastError();
     }
     ffn_grouped_kernel<0><<<units0, kGThreads, 0, st>>>(a);
@@ -452,6 +540,63 @@ hipError_t launch_ffn_grouped(const moe_shape& s, const FfnArgs& a, hipStream_t 
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     zero_tail_rows_kernel<<<64, 256, 0, st>>>(a);
+    return hipGetLastError();
+}
+
+// MXFP8 token rows in sorted-row order: row r is token perm[r] / k; one
+// thread per block of 32 elements (E8M0 scale of the block maximum, E4M3
+// elements rounded to nearest even and saturated at 448).  xs is block-major,
+// [d/32][rpad], so an m-tile's scale bytes of one block are contiguous.
+__global__ __launch_bounds__(256) void mx8_gather_quant_kernel(const uint16_t* __restrict__ x,
+                                                             const int32_t* __restrict__ perm, int k, int d, int R,
+                                                             int rpad, uint8_t* __restrict__ xq,
+                                                             uint8_t* __restrict__ xs) {
+    const int nb = d / 32;
+    const long long i = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= static_cast<long long>(R) * nb) return;
+    const int r = static_cast<int>(i / nb), b = static_cast<int>(i % nb);
+    const int t = perm[r] / k;
+    const u32x4* src = reinterpret_cast<const u32x4*>(x + static_cast<size_t>(t) * d + 32 * b);
+    float v[32];
+    float amax = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const u32x4 w = src[c];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            v[8 * c + 2 * e] = __uint_as_float(w[e] << 16);
+            v[8 * c + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(v[e]));
+    const int sbyte = mx8_scale_byte(amax);
+    u32x4 out[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) word |= e4m3_rne_sat(ldexpf(v[16 * c + 4 * e + q], 127 - sbyte)) << (8 * q);
+            out[c][e] = word;
+        }
+    u32x4* dst = reinterpret_cast<u32x4*>(xq + static_cast<size_t>(r) * d + 32 * b);
+    dst[0] = out[0];
+    dst[1] = out[1];
+    xs[static_cast<size_t>(b) * rpad + r] = static_cast<uint8_t>(sbyte);
+}
+
+hipError_t launch_ffn_mx8(const moe_shape& s, const FfnArgs& a, hipStream_t st) {
+    const int R = s.T * s.k;
+    const long long n = static_cast<long long>(R) * (s.d / 32);
+    mx8_gather_quant_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, st>>>(
+        a.x, a.perm, s.k, s.d, R, a.rpad, const_cast<uint8_t*>(a.xq), const_cast<uint8_t*>(a.xs));
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int units0 = max_mtiles(s, false) * (s.f / (kGN / 2));
+    const int units1 = max_mtiles(s, false) * (s.d / kGN);
+    ffn_grouped_chained_kernel<true><<<units0 + units1 + 1, kGThreads, 0, st>>>(a, units0, units1);
     return hipGetLastError();
 }
 

@@ -46,6 +46,15 @@ struct FfnArgs {
     int has_shared;
     const uint8_t* sh_codes[3];
     const uint8_t* sh_scales[3];
+    // MXFP8 activations (grouped path, MXFP4 weights): token rows quantised
+    // and gathered in sorted-row order, xq u8 [T*k][d] with scale bytes
+    // xs [d/32][rpad]; the SwiGLU output aq u8 [T*k][f] with as [f/32][rpad]
+    // (rpad = T*k + 128: a padded m-tile reads whole 128-row scale runs).
+    const uint8_t* xq;
+    const uint8_t* xs;
+    uint8_t* aq;
+    uint8_t* as;
+    int rpad;
 };
 
 hipError_t launch_route(const moe_shape& s, const uint16_t* x, const float* wr, const float* bias,
@@ -70,6 +79,9 @@ hipError_t launch_small_route(const moe_shape& s, const uint16_t* x, const float
 bool routed_ffn_supported(const moe_shape& s, int fmt);
 hipError_t launch_ffn_routed(const moe_shape& s, int fmt, const FfnArgs& a, hipStream_t st);
 hipError_t launch_ffn_grouped(const moe_shape& s, const FfnArgs& a, hipStream_t st);
+// MXFP8 activations: gather + quantise the token rows into a.xq / a.xs, then
+// the single-launch grouped FFN on the block-scaled fp4 x fp8 matrix cores.
+hipError_t launch_ffn_mx8(const moe_shape& s, const FfnArgs& a, hipStream_t st);
 // Ready flags the grouped FFN needs in the workspace (0: none).
 int grouped_flag_count(const moe_shape& s, bool shared = false);
 // shared: out[t] also adds y[T*k + t] (weight 1) after the routed terms.
