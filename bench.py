@@ -40,6 +40,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0         # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
+MFMA_FP8_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 matrix, published (the fp4 x fp8 products run at it)
 METRIC = "MoE layer tokens/s; decode weight-stream GB/s; prefill expert TFLOP/s"
 
 # HBM bytes per moe_expert_ffn call from rocprofv3 counter runs of the current
@@ -70,6 +71,8 @@ def parse():
     import synthetic
     p.add_argument("--workload", type=int, default=1, choices=sorted(synthetic.WORKLOADS))
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--mx8", action="store_true",
+                   help="MXFP8 activations on the block-scaled fp4 x fp8 matrix cores (moe_layer_mx8)")
     p.add_argument("--shared", action="store_true",
                    help="run the workload with a shared expert (moe_layer_shared)")
     p.add_argument("--bank", type=int, default=0, metavar="N",
@@ -449,7 +452,10 @@ def main():
     inv = torch.empty((T * k,), dtype=torch.int32, device=dev)
     y = torch.empty((T * k, d), dtype=torch.float32, device=dev)
     out = torch.empty((T, d), dtype=torch.float32, device=dev)
-    ws = qm.alloc_workspace(shape, layer=True, device=dev)
+    mx8 = args.mx8
+    if mx8 and (w["fmt"] != "mxfp4" or d % 512 or f % 256):
+        raise SystemExit("--mx8 needs MXFP4 experts with d % 512 == 0 and f % 256 == 0")
+    ws = qm.alloc_workspace_mx8(shape, layer=True, device=dev) if mx8 else qm.alloc_workspace(shape, layer=True, device=dev)
 
     # Raw C-ABI calls with precomputed arguments keep the host far ahead of
     # the GPU, so HIP event pairs measure kernels, not launch latency.
@@ -469,7 +475,9 @@ def main():
     lg_p, ids_p, tw_p = logits.data_ptr(), ids.data_ptr(), tw.data_ptr()
     off_p, perm_p, inv_p = offsets.data_ptr(), perm.data_ptr(), inv.data_ptr()
     y_p, out_p, ws_p, ws_n = y.data_ptr(), out.data_ptr(), ws.data_ptr(), ws.numel()
-    ffn_ws_n = qm.moe_workspace_bytes(shape)
+    ffn_ws_n = int(L.moe_workspace_bytes_mx8(ctypes.byref(shape.c()))) if mx8 else qm.moe_workspace_bytes(shape)
+    ffn_call = L.moe_expert_ffn_mx8 if mx8 else L.moe_expert_ffn
+    layer_call = L.moe_layer_mx8 if mx8 else L.moe_layer
     wr_p = [None if r is None else r[0].data_ptr() for r in routers]
     b_p = [None if (r is None or r[1] is None) else r[1].data_ptr() for r in routers]
     given_p = None if given is None else given.data_ptr()
@@ -487,7 +495,7 @@ def main():
         rc |= L.moe_dispatch(sh, ids_p, off_p, perm_p, inv_p, ws_p, ws_n, stream)
         if ev is not None:
             hip.hipEventRecord(ev[0], ctypes.c_void_p(stream))
-        rc |= L.moe_expert_ffn(sh, xp, ex_ref[p], off_p, perm_p, y_p, ws_p, ffn_ws_n, stream)
+        rc |= ffn_call(sh, xp, ex_ref[p], off_p, perm_p, y_p, ws_p, ffn_ws_n, stream)
         if ev is not None:
             hip.hipEventRecord(ev[1], ctypes.c_void_p(stream))
         rc |= L.moe_combine(sh, y_p, inv_p, tw_p, out_p, stream)
@@ -497,8 +505,8 @@ def main():
     def layer_step(j):
         p = j % n_pools
         set_logits(j)
-        if L.moe_layer(sh, xb + (j % n_x) * xstride, wr_p[p], b_p[p], lg_p, ex_ref[p], ids_p, tw_p, out_p,
-                       ws_p, ws_n, stream):
+        if layer_call(sh, xb + (j % n_x) * xstride, wr_p[p], b_p[p], lg_p, ex_ref[p], ids_p, tw_p, out_p,
+                      ws_p, ws_n, stream):
             raise RuntimeError("moe_layer failed")
 
     for i in range(args.warmup):
@@ -590,14 +598,18 @@ def main():
 
     traffic = MEASURED_FFN_TRAFFIC.get(c)
     traffic = None if traffic is None else round(traffic)
+    if mx8:
+        traffic = None
     if T * k >= 1024:
-        roof = dict(bound="mfma", achieved=round(tflops, 2), peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), traffic=traffic)
+        peak = MFMA_FP8_PEAK_TFLOPS if mx8 else MFMA_BF16_PEAK_TFLOPS
+        roof = dict(bound="mfma", achieved=round(tflops, 2), peak=peak, unit="TFLOP/s",
+                    frac=round(tflops / peak, 4), traffic=traffic)
     else:
         roof = dict(bound="hbm", achieved=round(gbps, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
                     frac=round(gbps / HBM_PEAK_GBPS, 4), traffic=traffic)
     roof["traffic_unit"] = "HBM bytes per call (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
-    roof["kernel"] = ("moe_expert_ffn (one launch: gate/up + SwiGLU tiles, then down tiles)" if T * k >= 256 and w["fmt"] == "mxfp4"
+    roof["kernel"] = ("moe_expert_ffn_mx8 (token quantisation, then one launch of block-scaled fp4 x fp8 tiles)" if mx8
+                      else "moe_expert_ffn (one launch: gate/up + SwiGLU tiles, then down tiles)" if T * k >= 256 and w["fmt"] == "mxfp4"
                       else "moe_expert_ffn (gate/up + SwiGLU kernel, down kernel)")
     roof["algorithmic_bytes_per_launch"] = round(ffn_bytes)
     roof["avg_launch_ms"] = round(ffn_avg_s * 1e3, 5)
@@ -614,9 +626,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "mxfp8 activations x mxfp4 weights" if mx8 else "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{w['name']}: T={T} d={d} E={E} k={k} f={f} {w['fmt']}",
+        "config": {"workload": f"{w['name']}{' (MXFP8 activations)' if mx8 else ''}: T={T} d={d} E={E} k={k} f={f} {w['fmt']}",
                    "T": T, "d": d, "E": E, "k": k, "f": f, "format": w["fmt"],
                    "weight_pools": n_pools, "parallelism": "none (1 GPU)"},
         "weight_stream_GBps": round(gbps, 1),
@@ -627,7 +639,7 @@ def main():
         "four_call_ms_per_step": round(steps_elapsed / K * 1e3, 5),
         "roofline": roof,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not mx8:
         n = args.cpu_sample_steps or {0: 200, 1: 6, 2: 4, 3: 1, 4: 3, 5: 3, 6: 6}[c]
         res["cpu_baseline"] = cpu_baseline(c, n)
     print(json.dumps(res), flush=True)
