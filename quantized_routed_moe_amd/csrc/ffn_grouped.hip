@@ -425,9 +425,9 @@ __device__ __forceinline__ void grouped_unit(const FfnArgs& a, int unit, unsigne
             const size_t r = static_cast<size_t>(r_base + j);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                uint32_t word = 0;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) word |= e4m3_rne_sat(ldexpf(v[4 * q + i], 127 - sbyte)) << (8 * i);
+                const int sh = 127 - sbyte;
+                const uint32_t word = e4m3x4_rne_sat(ldexpf(v[4 * q], sh), ldexpf(v[4 * q + 1], sh),
+                                                     ldexpf(v[4 * q + 2], sh), ldexpf(v[4 * q + 3], sh));
                 uint32_t* dst = reinterpret_cast<uint32_t*>(a.aq + r * a.f + nt * (kGN / 2) + 32 * wave + 8 * q + 4 * h);
                 if constexpr (CHAIN) __hip_atomic_store(dst, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 else *dst = word;
@@ -576,10 +576,9 @@ __global__ __launch_bounds__(256) void mx8_gather_quant_kernel(const uint16_t* _
     for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            uint32_t word = 0;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) word |= e4m3_rne_sat(ldexpf(v[16 * c + 4 * e + q], 127 - sbyte)) << (8 * q);
-            out[c][e] = word;
+            const int sh = 127 - sbyte;
+            const float* vv = v + 16 * c + 4 * e;
+            out[c][e] = e4m3x4_rne_sat(ldexpf(vv[0], sh), ldexpf(vv[1], sh), ldexpf(vv[2], sh), ldexpf(vv[3], sh));
         }
     u32x4* dst = reinterpret_cast<u32x4*>(xq + static_cast<size_t>(r) * d + 32 * b);
     dst[0] = out[0];
