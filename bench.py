@@ -146,9 +146,14 @@ def cpu_baseline(c, steps):
                   w_router=case["w_router"], bias=case["bias"])
         total += time.perf_counter() - t0
         tokens += case["T"]
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count() or 1
     return dict(value=tokens / total, unit="tokens/s", cores=int(blas), kind="oracle",
                 sample=f"{steps} seeded step(s) of the workload ({tokens} tokens), NumPy float64 oracle, "
-                       f"{total:.1f} s of host time; input generation not timed")
+                       f"{total:.1f} s of host time; input generation not timed; BLAS threads {blas} of "
+                       f"{affinity} cores in the process affinity mask")
 
 
 def bank_main(args):
@@ -613,6 +618,8 @@ def main():
                       else "moe_expert_ffn (gate/up + SwiGLU kernel, down kernel)")
     roof["algorithmic_bytes_per_launch"] = round(ffn_bytes)
     roof["avg_launch_ms"] = round(ffn_avg_s * 1e3, 5)
+    p10, p50, p90 = np.percentile(np.asarray(ffn_ms) * 1e3, [10, 50, 90])
+    roof["launch_us_p10_p50_p90"] = [round(float(p10), 2), round(float(p50), 2), round(float(p90), 2)]
 
     ms_per_step = elapsed / K * 1e3
     res = {
