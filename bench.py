@@ -50,6 +50,8 @@ METRIC = "MoE layer tokens/s; decode weight-stream GB/s; prefill expert TFLOP/s"
 # different number of experts each step: theirs is the average of the counted
 # steps.  Must be re-measured (or removed) whenever an FFN kernel changes.
 MEASURED_FFN_TRAFFIC = {
+    0: (2 * (209.0 + 112.6) + (2.0 + 8.0)) * 1024,
+    2: (2 * (18725.6 + 8930.0) + (40.0 + 160.0)) * 1024,
     1: (2 * (13158.5 + 4436.2) + (8.0 + 32.0)) * 1024,
     3: (2 * 469576.9 + 98466.6) * 1024,
     4: (2 * (27874.1 + 14211.8) + (128.0 + 512.0)) * 1024,
