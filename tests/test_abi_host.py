@@ -235,3 +235,30 @@ def test_layer_shared_validation():
     assert call(qm.moe_experts(mat(), mat(), mat(), None, 0)) == qm.MOE_ERR_SHAPE
     assert call(qm.moe_experts(mat(), mat(), mat(), None, 1), ws_bytes=need - 256) == qm.MOE_ERR_WORKSPACE
     assert call(qm.moe_experts(mat(), mat(), mat(), None, 1), ws=A16 + 8) == qm.MOE_ERR_ALIGN
+
+
+def test_mx8_validation():
+    """The MXFP8-activation entry points reject what they cannot run before
+    any HIP call: other formats or shapes the grouped FFN does not take,
+    short workspaces, invalid shapes."""
+    L = qm.lib()
+    s = _shape(T=64, d=512, E=8, k=2, f=256)
+    need = L.moe_workspace_bytes_mx8(ctypes.byref(s))
+    assert need > L.moe_workspace_bytes(ctypes.byref(s))       # plus the quantised token rows
+    assert L.moe_layer_mx8_workspace_bytes(ctypes.byref(s)) > need
+    assert L.moe_workspace_bytes_mx8(ctypes.byref(_shape(k=0))) == 0
+
+    def mat(fmt=qm.MOE_FMT_MXFP4):
+        return qm.moe_qmat(fmt, qm.MOE_LAYOUT_TILES, A16, A16, None)
+
+    def ffn(shape, fmt=qm.MOE_FMT_MXFP4, ws_bytes=need):
+        ex = qm.moe_experts(mat(fmt), mat(fmt), mat(fmt), None, 8)
+        return L.moe_expert_ffn_mx8(ctypes.byref(shape), A16, ctypes.byref(ex), A16, A16, A16, A16, ws_bytes, None)
+
+    assert ffn(s, qm.MOE_FMT_Q2G32) == qm.MOE_ERR_UNSUPPORTED
+    assert ffn(s, qm.MOE_FMT_Q4G32) == qm.MOE_ERR_UNSUPPORTED
+    s2 = _shape(T=64, d=256, E=8, k=2, f=256)                    # d not a multiple of 512
+    assert ffn(s2, ws_bytes=L.moe_workspace_bytes_mx8(ctypes.byref(s2))) == qm.MOE_ERR_UNSUPPORTED
+    assert ffn(s, ws_bytes=need - 256) == qm.MOE_ERR_WORKSPACE
+    assert ffn(_shape(T=64, d=512, E=8, k=9, f=256)) == qm.MOE_ERR_SHAPE
+    assert ffn(_shape(T=0, d=512, E=8, k=2, f=256)) == qm.MOE_OK
