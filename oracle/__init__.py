@@ -18,8 +18,8 @@ Two implementations live here:
 
 Sources for what is computed (the pages only describe the layer in prose):
 
-* the routed-expert kernel loads only the activated experts' weights and is
-  "block sparse" -- "antirez ds4: DeepSeek Metal inference" (ainews.cool),
+* the routed-expert kernel reads the weights of the activated experts only,
+  block-sparse -- "antirez ds4: DeepSeek Metal inference" (ainews.cool),
   section "技术深度解析" (technical deep dive), which also gives 64 experts
   with top-2 routing and on-the-fly dequantisation;
 * the routed-expert count is a run-time knob -- Anemll/ds4-ssd README,

@@ -132,7 +132,7 @@ def dequant_q2(codes, scale_bits, min_bits) -> np.ndarray:
 def dequant_q4(codes, scale_bits, min_bits) -> np.ndarray:
     """Decode a 4-bit group-asymmetric matrix pack to float64.
 
-    The pages name 4-bit "GPTQ-style" quantisation with dequantisation at
+    The pages name a GPTQ-like 4-bit quantisation with dequantisation at
     inference time ("antirez ds4: DeepSeek Metal inference", section
     技术深度解析) and a q4 model build ("DwarfStar 4 ... 完整指南", section
     性能实测参考), nothing more.  Reading taken (the group-wise affine form of

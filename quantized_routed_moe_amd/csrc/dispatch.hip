@@ -1,6 +1,6 @@
 // Token-by-expert dispatch: a stable counting sort of the T*k (token, slot)
 // pairs by expert id.  It is what lets every activated expert's weights be
-// streamed once for all of its rows -- the "block sparse" routed-expert
+// streamed once for all of its rows -- the block-sparse routed-expert
 // kernel of "antirez ds4: DeepSeek Metal inference" (section 技术深度解析).
 //
 // One workgroup of 1024 threads.  Pass 1 counts pairs per expert (LDS
