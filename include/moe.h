@@ -24,6 +24,14 @@
  *   5. y[r][m] = Wd[e][m,:] . act[r]                                          (fp32)
  *   6. out[t][m] = sum_{j=0..k-1} topk_w[t][j] * y[inv[t*k+j]][m]  (j order) (fp32)
  *
+ * Entry points: moe_route_topk (1-2), moe_dispatch (3), moe_expert_ffn (4-5),
+ * moe_combine (6) and moe_layer (1-6 in one call); moe_pack_qmat lays
+ * weights out for the kernels.  Beside the layer: moe_layer_shared (an
+ * always-on shared expert), moe_expert_ffn_mx8 / moe_layer_mx8 (MXFP8
+ * activations on the block-scaled matrix cores), and the slot bank
+ * (moe_bank_reset / moe_bank_plan / moe_bank_fetch / moe_layer_banked:
+ * N device expert slots paged from host memory).
+ *
  * Conventions for every entry point:
  *   - Every data pointer is a DEVICE pointer (HBM of the current HIP
  *     device) unless stated otherwise; `moe_shape` / `moe_experts` structs are
