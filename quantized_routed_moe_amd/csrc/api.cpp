@@ -346,6 +346,31 @@ int moe_layer_shared(const moe_shape* shape, const uint16_t* x, const float* w_r
     for (const moe_qmat* m : sm)
         if ((rc = check_qmat(*m, fmt)) != MOE_OK) return rc;
     if (shared->num_slots < 1) return MOE_ERR_SHAPE;
+    auto set_shared = [&](FfnArgs& a) {
+        a.has_shared = 1;
+        for (int i = 0; i < 3; ++i) {
+            a.sh_codes[i] = static_cast<const uint8_t*>(sm[i]->codes);
+            a.sh_scales[i] = static_cast<const uint8_t*>(sm[i]->scales);
+        }
+    };
+    // Small batches: the gate/up launch routes the batch itself (as in
+    // moe_layer) and writes perm[T*k + t] = t*k for the shared expert's rows.
+    if (qrmoe::routed_ffn_supported(s, fmt)) {
+        if (w_router && (rc = hip_rc(qrmoe::launch_router_logits(s, x, w_router, bias, logits, stream))) != MOE_OK)
+            return rc;
+        FfnArgs a = ffn_args(s, x, experts, offsets, perm, y, ws);
+        a.flags = nullptr;
+        a.act = reinterpret_cast<uint16_t*>(base + kHeader);
+        set_shared(a);
+        a.logits = logits;
+        a.ids_out = topk_ids;
+        a.w_out = topk_w;
+        a.offsets_out = offsets;
+        a.perm_out = perm;
+        a.inv_out = inv;
+        if ((rc = hip_rc(qrmoe::launch_ffn_routed(s, fmt, a, stream))) != MOE_OK) return rc;
+        return hip_rc(qrmoe::launch_combine(s, y, inv, topk_w, out, stream, true));
+    }
     // routing: the dispatch also writes perm[T*k + t] = t*k, the rows of the
     // shared expert
     if (qrmoe::small_route_supported(s)) {
@@ -361,11 +386,7 @@ int moe_layer_shared(const moe_shape* shape, const uint16_t* x, const float* w_r
     FfnArgs a = ffn_args(s, x, experts, offsets, perm, y, ws);
     a.flags = flag_bytes(s, true) ? reinterpret_cast<unsigned long long*>(base + kHeader + act_bytes(s, true))
                                   : nullptr;
-    a.has_shared = 1;
-    for (int i = 0; i < 3; ++i) {
-        a.sh_codes[i] = static_cast<const uint8_t*>(sm[i]->codes);
-        a.sh_scales[i] = static_cast<const uint8_t*>(sm[i]->scales);
-    }
+    set_shared(a);
     if ((rc = hip_rc(qrmoe::launch_ffn(s, fmt, a, stream))) != MOE_OK) return rc;
     return hip_rc(qrmoe::launch_combine(s, y, inv, topk_w, out, stream, true));
 }

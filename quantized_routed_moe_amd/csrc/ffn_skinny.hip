@@ -405,7 +405,7 @@ __global__ __launch_bounds__(KW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
 // and every workgroup zeroes its share of `out` for the down launch's
 // scatter-add.  Arithmetic as topk_kernel and the dispatch
 // kernel, so every output is identical.
-template <int FMT, int RB>
+template <int FMT, int RB, bool SH>
 __global__ __launch_bounds__(kGateUpWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void ffn_gate_up_routed_kernel(FfnArgs a) {
     __shared__ SmallRouting r;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -415,6 +415,10 @@ __global__ __launch_bounds__(kGateUpWaves * 64) __attribute__((amdgpu_waves_per_
     if (wave < T) topk_wave(a.logits + static_cast<size_t>(wave) * E, r.ids + wave * k, r.w + wave * k, E, k);
     __syncthreads();
     if (wave == 0) wave_dispatch(r, n, E);
+    if constexpr (SH) {                 // the shared expert's rows: row n + t is token t
+        __syncthreads();
+        if (tid < T) r.perm[n + tid] = tid * k;
+    }
     __syncthreads();
     int lo = 0, hi = 0;
     if (lane < E) {
@@ -422,14 +426,20 @@ __global__ __launch_bounds__(kGateUpWaves * 64) __attribute__((amdgpu_waves_per_
         hi = r.offsets[lane + 1];
     }
     const int NT = a.f / 16;
-    const int g_items = min(E, n) * NT;
+    const int g_items = (min(E, n) + (SH ? 1 : 0)) * NT;
+    // item ai: with a shared expert, item 0 is it (rows [n, n + T), slot 0 of its pack)
+    auto item_of = [&](int ai) {
+        if constexpr (SH) {
+            if (ai == 0) return Item{E, n, n + T, 0};
+            --ai;
+        }
+        return pick_item(lo, hi, sl, ai);
+    };
     if (static_cast<int>(blockIdx.x) >= g_items) {
         __shared__ __align__(16) uint8_t pf[kGateUpWaves][1024];
-        prefetch_down<FMT, false>(a, blockIdx.x - g_items, gridDim.x - g_items,
-                                  [&](int ai) { return pick_item(lo, hi, sl, ai); }, pf[wave]);
+        prefetch_down<FMT, SH>(a, blockIdx.x - g_items, gridDim.x - g_items, item_of, pf[wave]);
     } else {
-        run_item<FMT, 0, kGateUpWaves, RB, true>(a, pick_item(lo, hi, sl, blockIdx.x / NT), (blockIdx.x % NT) * 16,
-                                                 r.perm);
+        run_item<FMT, 0, kGateUpWaves, RB, true, SH>(a, item_of(blockIdx.x / NT), (blockIdx.x % NT) * 16, r.perm);
     }
     // after the item: no stores ahead of its loads (the down launch is the
     // first reader of these)
@@ -441,6 +451,7 @@ __global__ __launch_bounds__(kGateUpWaves * 64) __attribute__((amdgpu_waves_per_
             a.inv_out[i] = r.inv[i];
         }
         for (int i = tid; i <= E; i += blockDim.x) a.offsets_out[i] = r.offsets[i];
+        if (SH && tid < T) a.perm_out[n + tid] = r.perm[n + tid];
     }
     if (a.fuse_combine) zero_out_share(a);
 }
@@ -458,8 +469,8 @@ static hipError_t launch_two_sh(const moe_shape& s, const FfnArgs& a, hipStream_
     const int g_items = umax * (s.f / 16);
     const int g_up = g_items + (g_items + kDownPrefetchWGs <= kResidentGateUpWGs ? kDownPrefetchWGs : 0);
     if (routed) {
-        if constexpr (RB <= kGateUpWaves && !SH)
-            ffn_gate_up_routed_kernel<FMT, RB><<<g_up, kGateUpWaves * 64, 0, st>>>(a);
+        if constexpr (RB <= kGateUpWaves)
+            ffn_gate_up_routed_kernel<FMT, RB, SH><<<g_up, kGateUpWaves * 64, 0, st>>>(a);
     } else {
         ffn_skinny_kernel<FMT, 0, kGateUpWaves, RB, SH><<<g_up, kGateUpWaves * 64, 0, st>>>(a);
     }

@@ -49,7 +49,7 @@ constexpr int kRoutedMaxPairs = 64;
 struct SmallRouting {
     int32_t ids[kRoutedMaxPairs];
     float w[kRoutedMaxPairs];
-    int32_t perm[kRoutedMaxPairs];
+    int32_t perm[kRoutedMaxPairs + 16];   // + a shared expert's rows (up to 16 tokens)
     int32_t inv[kRoutedMaxPairs];
     int32_t offsets[kMaxExperts + 1];
 };
