@@ -14,8 +14,14 @@ calls captured once into a HIP graph and replayed -- its throughput is
 events around moe_expert_ffn on the launch stream -- the average FFN
 duration gives the roofline figure.
 
-Prints ONE JSON line.  Default workload: decode, T=1, d=4096, E=64, k=2,
-f=2048, MXFP4 experts.
+Prints ONE JSON line.  Headline workload: decode, T=1, d=4096, E=64, k=2,
+f=2048, MXFP4 experts; by default the same line also carries a `workloads`
+map with every quoted configuration (0-4: tiny, decode, verify, prefill,
+two-bit), each with its own value, roofline and oracle baseline, and
+`measured_peaks`: this box's cold HBM read stream, a decode-sized cold
+stream replayed from a HIP graph, and the dense bf16 and fp4 x fp8 matrix
+loops (include/moe_peak.h), against which every roofline also reports
+`frac_measured`.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 0..6]
 
@@ -71,7 +77,11 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     import synthetic
-    p.add_argument("--workload", type=int, default=1, choices=sorted(synthetic.WORKLOADS))
+    p.add_argument("--workload", type=int, default=None, choices=sorted(synthetic.WORKLOADS),
+                   help="one workload only (default: workload 1 as the headline, plus every quoted "
+                        "configuration 0-4 in a `workloads` map of the same line)")
+    p.add_argument("--no-peaks", action="store_true",
+                   help="skip the measured stream and matrix-core peaks (include/moe_peak.h)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--mx8", action="store_true",
                    help="MXFP8 activations on the block-scaled fp4 x fp8 matrix cores (moe_layer_mx8)")
@@ -398,21 +408,152 @@ def shared_main(args):
     print(json.dumps(res), flush=True)
 
 
-def main():
-    args = parse()
-    if args.copy_calibration:
-        copy_calibration(args.copy_calibration)
-        return
-    if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
-                                   "(expert-parallel sharding is designed, not built)"}))
-        sys.exit(2)
-    if args.bank:
-        bank_main(args)
-        return
-    if args.shared:
-        shared_main(args)
-        return
+def _hip(torch):
+    import ctypes
+    hip = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+    for fn in ("hipStreamBeginCapture", "hipStreamEndCapture", "hipGraphInstantiate", "hipGraphLaunch",
+               "hipGraphExecDestroy", "hipGraphDestroy", "hipEventCreate", "hipEventRecord",
+               "hipEventSynchronize", "hipEventElapsedTime", "hipEventDestroy", "hipMemcpyAsync"):
+        getattr(hip, fn).restype = ctypes.c_int
+    return hip
+
+
+class Events:
+    """HIP event pairs recorded on a raw stream (torch.cuda.Event sees only
+    torch's current stream)."""
+
+    def __init__(self, hip, n):
+        import ctypes
+        self.c, self.hip = ctypes, hip
+        self.ev = []
+        for _ in range(n):
+            a, b = ctypes.c_void_p(), ctypes.c_void_p()
+            hip.hipEventCreate(ctypes.byref(a))
+            hip.hipEventCreate(ctypes.byref(b))
+            self.ev.append((a, b))
+
+    def ms(self):
+        out = []
+        for a, b in self.ev:
+            m = self.c.c_float()
+            self.hip.hipEventElapsedTime(self.c.byref(m), a, b)
+            out.append(m.value)
+        return out
+
+    def close(self):
+        for a, b in self.ev:
+            self.hip.hipEventDestroy(a)
+            self.hip.hipEventDestroy(b)
+        self.ev = []
+
+
+def capture_replay(hip, stream, fn, K):
+    """fn(i) for i < K captured once into a HIP graph on `stream` (a created
+    stream), replayed once to warm, then timed over one replay (seconds)."""
+    import ctypes
+
+    import torch
+
+    graph, gexec = ctypes.c_void_p(), ctypes.c_void_p()
+    sp = ctypes.c_void_p(stream)
+
+    def ok(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} returned hipError {rc}")
+
+    ok(hip.hipStreamBeginCapture(sp, 1), "hipStreamBeginCapture")       # thread-local capture
+    try:
+        for i in range(K):
+            fn(i)
+    finally:
+        ok(hip.hipStreamEndCapture(sp, ctypes.byref(graph)), "hipStreamEndCapture")
+    ok(hip.hipGraphInstantiate(ctypes.byref(gexec), graph, None, None, ctypes.c_size_t(0)), "hipGraphInstantiate")
+    ok(hip.hipGraphLaunch(gexec, sp), "hipGraphLaunch")                  # warm replay
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ok(hip.hipGraphLaunch(gexec, sp), "hipGraphLaunch")
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    hip.hipGraphExecDestroy(gexec)
+    hip.hipGraphDestroy(graph)
+    return elapsed
+
+
+def measure_peaks(stream_bytes_decode):
+    """Measured roofline of this box, in this process (include/moe_peak.h):
+      * hbm_GBps: one cold 1 GiB read stream (the Infinity Cache evicted by
+        reading another 1 GiB first), median of 5, event-timed;
+      * hbm_GBps_decode_stream: K back-to-back reads of `stream_bytes_decode`
+        bytes (the decode FFN call's algorithmic bytes), each from a
+        different buffer (24 buffers, > 256 MB, so every read is cold),
+        replayed from a HIP graph -- the rate a kernel of that size can
+        reach, launch included;
+      * bf16_TFLOPs / fp8_TFLOPs: the dense matrix-core loops (bf16 32x32x16,
+        scaled fp4 x fp8 32x32x64), median of 5."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    import quantized_routed_moe_amd as qm
+
+    L = qm.lib()
+    hip = _hip(torch)
+    torch.cuda.synchronize()
+    torch.cuda.set_stream(torch.cuda.Stream())
+    stream = torch.cuda.current_stream().cuda_stream
+    sp = ctypes.c_void_p(stream)
+    big = 1 << 30
+    bufs = [torch.empty(big, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    for b in bufs:
+        b.fill_(7)
+    sink = torch.empty(1 << 16, dtype=torch.int32, device="cuda")
+    ev = Events(hip, 5)
+    for i, (a, b) in enumerate(ev.ev):
+        if L.moe_peak_stream(bufs[(i + 1) % 2].data_ptr(), big, 0, sink.data_ptr(), sp):   # evict
+            raise RuntimeError("moe_peak_stream failed")
+        hip.hipEventRecord(a, sp)
+        if L.moe_peak_stream(bufs[i % 2].data_ptr(), big, 0, sink.data_ptr(), sp):
+            raise RuntimeError("moe_peak_stream failed")
+        hip.hipEventRecord(b, sp)
+    torch.cuda.synchronize()
+    hbm = big / (float(np.median(ev.ms())) / 1e3) / 1e9
+    ev.close()
+    del bufs
+    # decode-sized cold streams replayed from a graph
+    nb = stream_bytes_decode // 16 * 16
+    small = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(24)]
+    for b in small:
+        b.fill_(3)
+    K = 48
+    secs = capture_replay(hip, stream, lambda i: L.moe_peak_stream(small[i % 24].data_ptr(), nb, 0,
+                                                                    sink.data_ptr(), sp), K)
+    dec = nb * K / secs / 1e9
+    del small
+    torch.cuda.empty_cache()
+    res = {"hbm_GBps": round(hbm, 1), "hbm_GBps_decode_stream": round(dec, 1),
+           "decode_stream_bytes": nb, "decode_stream_us": round(secs / K * 1e6, 3)}
+    fsink = torch.empty(4096, dtype=torch.float32, device="cuda")
+    for kind, name, per in ((0, "bf16_TFLOPs", 32768), (1, "fp8_TFLOPs", 131072)):
+        iters = 4000 if kind == 0 else 2000
+        ev = Events(hip, 5)
+        L.moe_peak_mfma(kind, iters, 0, fsink.data_ptr(), sp)           # warm
+        for a, b in ev.ev:
+            hip.hipEventRecord(a, sp)
+            if L.moe_peak_mfma(kind, iters, 0, fsink.data_ptr(), sp):
+                raise RuntimeError("moe_peak_mfma failed")
+            hip.hipEventRecord(b, sp)
+        torch.cuda.synchronize()
+        flop = 1024 * 4 * iters * 8 * per
+        res[name] = round(flop / (float(np.median(ev.ms())) / 1e3) / 1e12, 1)
+        ev.close()
+    return res
+
+
+def run_workload(c, args, mx8=False, peaks=None, cpu=True):
+    """Times workload c (see the module docstring): returns its result dict
+    (value, ms_per_step, roofline, cpu_baseline, ...)."""
+    import ctypes
 
     import numpy as np
     import torch
@@ -420,7 +561,6 @@ def main():
     import quantized_routed_moe_amd as qm
     import synthetic
 
-    c = args.workload
     w = synthetic.WORKLOADS[c]
     T, d, E, k, f = w["T"], w["d"], w["E"], w["k"], w["f"]
     shape = qm.Shape(T, d, E, k, f)
@@ -459,16 +599,14 @@ def main():
     inv = torch.empty((T * k,), dtype=torch.int32, device=dev)
     y = torch.empty((T * k, d), dtype=torch.float32, device=dev)
     out = torch.empty((T, d), dtype=torch.float32, device=dev)
-    mx8 = args.mx8
     if mx8 and (w["fmt"] != "mxfp4" or d % 512 or f % 256):
         raise SystemExit("--mx8 needs MXFP4 experts with d % 512 == 0 and f % 256 == 0")
     ws = qm.alloc_workspace_mx8(shape, layer=True, device=dev) if mx8 else qm.alloc_workspace(shape, layer=True, device=dev)
 
     # Raw C-ABI calls with precomputed arguments keep the host far ahead of
     # the GPU, so HIP event pairs measure kernels, not launch latency.
-    import ctypes
     L = qm.lib()
-    hip = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+    hip = _hip(torch)
     # a created stream (default priority): the legacy null stream cannot be
     # captured; what was enqueued so far is finished first
     torch.cuda.synchronize()
@@ -535,53 +673,19 @@ def main():
     # graph and replayed.  Every kernel of every step runs; the graph only
     # removes the per-launch work of the command processor between the
     # dependent launches (decode steps are a few launches of a few us each).
-    for fn in ("hipStreamBeginCapture", "hipStreamEndCapture", "hipGraphInstantiate", "hipGraphLaunch",
-               "hipGraphExecDestroy", "hipGraphDestroy"):
-        getattr(hip, fn).restype = ctypes.c_int
-    graph, gexec = ctypes.c_void_p(), ctypes.c_void_p()
-    sp = ctypes.c_void_p(stream)
-
-    def hip_ok(rc, what):
-        if rc != 0:
-            raise RuntimeError(f"{what} returned hipError {rc}")
-
-    hip_ok(hip.hipStreamBeginCapture(sp, 1), "hipStreamBeginCapture")       # thread-local capture
-    try:
-        for i in range(K):
-            layer_step(args.warmup + i)
-    finally:
-        hip_ok(hip.hipStreamEndCapture(sp, ctypes.byref(graph)), "hipStreamEndCapture")
-    hip_ok(hip.hipGraphInstantiate(ctypes.byref(gexec), graph, None, None, ctypes.c_size_t(0)), "hipGraphInstantiate")
-    hip_ok(hip.hipGraphLaunch(gexec, sp), "hipGraphLaunch")                  # warm replay
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    hip_ok(hip.hipGraphLaunch(gexec, sp), "hipGraphLaunch")
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    hip.hipGraphExecDestroy(gexec)
-    hip.hipGraphDestroy(graph)
+    elapsed = capture_replay(hip, stream, lambda i: layer_step(args.warmup + i), K)
 
     # Timed region 2 (roofline): the same K steps through the four entry
     # points, with HIP events around moe_expert_ffn on the same stream.
-    evs = []
-    for _ in range(K):
-        a_, b_ = ctypes.c_void_p(), ctypes.c_void_p()
-        hip.hipEventCreate(ctypes.byref(a_))
-        hip.hipEventCreate(ctypes.byref(b_))
-        evs.append((a_, b_))
+    evs = Events(hip, K)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     for i in range(K):
-        step(args.warmup + i, evs[i])
+        step(args.warmup + i, evs.ev[i])
     torch.cuda.synchronize()
     steps_elapsed = time.perf_counter() - t1
-    ffn_ms = []
-    for a_, b_ in evs:
-        ms = ctypes.c_float()
-        hip.hipEventElapsedTime(ctypes.byref(ms), a_, b_)
-        ffn_ms.append(ms.value)
-        hip.hipEventDestroy(a_)
-        hip.hipEventDestroy(b_)
+    ffn_ms = evs.ms()
+    evs.close()
     assert qm.moe_read_device_status(ws) == 0
 
     # activated experts per timed step (routing replayed untimed; it is deterministic)
@@ -611,32 +715,32 @@ def main():
         peak = MFMA_FP8_PEAK_TFLOPS if mx8 else MFMA_BF16_PEAK_TFLOPS
         roof = dict(bound="mfma", achieved=round(tflops, 2), peak=peak, unit="TFLOP/s",
                     frac=round(tflops / peak, 4), traffic=traffic)
+        mpeak = None if peaks is None else peaks["fp8_TFLOPs" if mx8 else "bf16_TFLOPs"]
+        if mpeak:
+            roof["measured_peak"] = mpeak
+            roof["frac_measured"] = round(tflops / mpeak, 4)
+        roof["hbm_GBps_of_call"] = round(gbps, 1)
     else:
         roof = dict(bound="hbm", achieved=round(gbps, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
                     frac=round(gbps / HBM_PEAK_GBPS, 4), traffic=traffic)
+        if peaks is not None:
+            roof["measured_peak"] = peaks["hbm_GBps"]
+            roof["frac_measured"] = round(gbps / peaks["hbm_GBps"], 4)
     roof["traffic_unit"] = "HBM bytes per call (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
     roof["kernel"] = ("moe_expert_ffn_mx8 (token quantisation, then one launch of block-scaled fp4 x fp8 tiles)" if mx8
                       else "moe_expert_ffn (one launch: gate/up + SwiGLU tiles, then down tiles)" if T * k >= 256 and w["fmt"] == "mxfp4"
                       else "moe_expert_ffn (gate/up + SwiGLU kernel, down kernel)")
     roof["algorithmic_bytes_per_launch"] = round(ffn_bytes)
+    roof["algorithmic_flop_per_launch"] = round(flops)
     roof["avg_launch_ms"] = round(ffn_avg_s * 1e3, 5)
     p10, p50, p90 = np.percentile(np.asarray(ffn_ms) * 1e3, [10, 50, 90])
     roof["launch_us_p10_p50_p90"] = [round(float(p10), 2), round(float(p50), 2), round(float(p90), 2)]
 
-    ms_per_step = elapsed / K * 1e3
     res = {
-        "metric": METRIC,
         "value": round(T * K / elapsed, 2),
         "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
+        "ms_per_step": round(elapsed / K * 1e3, 5),
         "dtype": "mxfp8 activations x mxfp4 weights" if mx8 else "bf16",
-        "data": "synthetic",
         "config": {"workload": f"{w['name']}{' (MXFP8 activations)' if mx8 else ''}: T={T} d={d} E={E} k={k} f={f} {w['fmt']}",
                    "T": T, "d": d, "E": E, "k": k, "f": f, "format": w["fmt"],
                    "weight_pools": n_pools, "parallelism": "none (1 GPU)"},
@@ -648,9 +752,64 @@ def main():
         "four_call_ms_per_step": round(steps_elapsed / K * 1e3, 5),
         "roofline": roof,
     }
-    if not args.no_cpu_baseline and not mx8:
+    del pools, routers, xs, ws, y
+    torch.cuda.empty_cache()
+    if cpu and not args.no_cpu_baseline and not mx8:
         n = args.cpu_sample_steps or {0: 200, 1: 6, 2: 4, 3: 1, 4: 3, 5: 3, 6: 6}[c]
         res["cpu_baseline"] = cpu_baseline(c, n)
+    return res
+
+
+def main():
+    args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(expert-parallel sharding is designed, not built)"}))
+        sys.exit(2)
+    if args.bank or args.shared:
+        if args.workload is None:
+            args.workload = 1
+        (bank_main if args.bank else shared_main)(args)
+        return
+
+    import synthetic
+
+    head = 1 if args.workload is None else args.workload
+    w = synthetic.WORKLOADS[head]
+    peaks = None
+    if not args.no_peaks:
+        peaks = measure_peaks(MX_BYTES_PER_EXPERT(w["d"], w["f"]) * 2 + 57344)
+    r = run_workload(head, args, mx8=args.mx8, peaks=peaks)
+    res = {
+        "metric": METRIC,
+        "value": r["value"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": r["dtype"],
+        "data": "synthetic",
+    }
+    res.update({n: v for n, v in r.items() if n not in res})
+    if peaks is not None:
+        res["measured_peaks"] = peaks
+    if args.workload is None and not args.mx8:
+        # the other configurations in the same run, each with its own
+        # roofline and oracle baseline (the headline is workload 1)
+        res["workloads"] = {}
+        for c in (0, 1, 2, 3, 4):
+            rc = r if c == head else run_workload(c, args, peaks=peaks)
+            keep = ("value", "unit", "ms_per_step", "roofline", "cpu_baseline", "active_experts_mean",
+                    "weight_stream_GBps", "expert_TFLOPs", "eager_ms_per_step")
+            res["workloads"][synthetic.WORKLOADS[c]["name"]] = dict(
+                {"config": rc["config"]["workload"]}, **{n: rc[n] for n in keep if n in rc})
     print(json.dumps(res), flush=True)
 
 

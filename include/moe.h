@@ -82,8 +82,19 @@ enum moe_status {
 enum moe_device_status_bits {
     MOE_DEV_BAD_EXPERT_ID = 1, /* a topk id outside [0, E) reached moe_dispatch */
     MOE_DEV_BAD_SLOT = 2,      /* slot_of_expert[e] outside [0, num_slots) for a routed e */
-    MOE_DEV_CHAIN_TIMEOUT = 4  /* prefill FFN: a down tile gave up waiting for its gate/up tiles */
+    MOE_DEV_CHAIN_TIMEOUT = 4  /* prefill FFN: a down tile gave up waiting for its gate/up tiles
+                                  (its y rows then hold NaN, never a product of unfinished act rows) */
 };
+
+/* The single-launch prefill FFN (T*k >= 256 with MXFP4 experts, d % 512 == 0
+   and f % 256 == 0, and the MXFP8 entry points) hands act from its gate/up
+   tiles to its down tiles through ready flags with a bounded wait (about a
+   third of a second).  A wait that gives up makes that tile's y rows NaN and
+   raises MOE_DEV_CHAIN_TIMEOUT; a caller that must not consume such a
+   result reads the status word (moe_read_device_status) after the call.
+   Workspace header word 32 (bytes 128..131; zero after moe_workspace_init),
+   when it holds w != 0, limits each wait to w - 1 polls (w = 1: give up at
+   once): a test hook that forces the timeout path from the host. */
 
 typedef struct moe_shape {
     int32_t T; /* tokens in the call */
@@ -195,17 +206,38 @@ int moe_pack_qmat(const moe_qmat* src, const moe_qmat* dst, int32_t slots, int32
 /* The experts of one layer.  gate and up are n=f rows of K=d; down is n=d
    rows of K=f.  All three use the same format and MOE_LAYOUT_TILES.  Expert e lives in pack slot
    slot_of_expert[e] (device int32 [E]) or, when slot_of_expert is NULL, in
-   slot e (then num_slots >= E is required).  slot_of_expert[e] ==
-   MOE_SLOT_SKIP leaves expert e out of this call: its y rows are not written
-   and no status is raised (a slot-bank pass that computes other experts).
+   slot e (then num_slots >= E is required).
+   slot_of_expert[e] == MOE_SLOT_SKIP leaves expert e out of the call and
+   raises no status.  moe_expert_ffn / moe_expert_ffn_mx8 then leave its y
+   rows untouched (a slot-bank pass that computes other experts, y filling
+   up over several calls); the one-call layers (moe_layer, moe_layer_shared,
+   moe_layer_mx8) treat it as contributing zero (its y rows are zeroed, or
+   with the combine fused into the down projection nothing is added).
    A routed expert whose slot is otherwise outside [0, num_slots) is not
-   computed: its y rows are written as zeros and MOE_DEV_BAD_SLOT is raised. */
+   computed: its y rows are written as zeros and MOE_DEV_BAD_SLOT is raised.
+
+   Slot placement: with slot_bytes == 0 every array holds its slots back to
+   back (slot s of an array starts s * (its moe_qmat_bytes for one slot)
+   bytes past its pointer).  With slot_bytes != 0 (a multiple of 256) slot s
+   of EVERY array starts s * slot_bytes bytes past that array's pointer: the
+   six arrays of one expert can then share one contiguous slab per slot
+   (moe_slab_layout), which the slot bank copies in one transfer. */
 enum { MOE_SLOT_SKIP = -2 };
 typedef struct moe_experts {
     moe_qmat gate, up, down;
     const int32_t* slot_of_expert;
     int32_t num_slots;
+    uint64_t slot_bytes;      /* 0, or the stride between slots of every array (slabs) */
 } moe_experts;
+
+/* Slab layout of one expert of format fmt (hidden size d, expert size f):
+   the byte offsets of its six tile-layout arrays inside one slab, in the
+   order gate codes, gate scales, up codes, up scales, down codes, down
+   scales (offsets[6], HOST; may be NULL), each a multiple of 256.  Returns
+   the slab size (a multiple of 256) -- the moe_experts.slot_bytes of a slab
+   pack whose array pointers are base + offsets[i] -- or 0 for an invalid
+   request (unknown fmt; d or f not a positive multiple of 32). */
+size_t moe_slab_layout(int32_t fmt, int32_t d, int32_t f, size_t* offsets);
 
 /* Workspace bytes moe_dispatch / moe_expert_ffn / moe_layer need for `shape`
    (a 256-byte header holding the device status word, then the bf16 SwiGLU
@@ -327,7 +359,8 @@ int moe_layer_shared(const moe_shape* shape, const uint16_t* x, const float* w_r
    host -> device by the DMA engines.  The pages name no replacement policy;
    this library evicts the least recently used slot.
 
-   moe_bank is host-side bookkeeping; the caller allocates its arrays. */
+   moe_bank is host-side bookkeeping; the caller allocates its arrays (and,
+   for copies that overlap the expert FFN, a copy stream and two events). */
 typedef struct moe_bank {
     int32_t E;                /* experts in the pool, 1..64 */
     int32_t num_slots;        /* N, 1..E: slots of the device bank */
@@ -335,7 +368,32 @@ typedef struct moe_bank {
     int32_t* expert_of_slot;  /* HOST int32 [N]: expert held by slot s, or -1 (empty) */
     uint64_t* last_use;       /* HOST uint64 [N]: request stamp of the slot's last use */
     uint64_t clock;           /* request stamps handed out so far */
+    /* moe_layer_banked only.  NULL: the copies run on the call's stream, in
+       order with its kernels.  Otherwise the copies run on copy_stream (a
+       stream of the same device, default priority), and ev_copied /
+       ev_computed (events created by the caller, e.g. hipEventCreateWithFlags
+       with hipEventDisableTiming) order them against the FFN launches:
+       the FFN of a pass's resident experts runs while its misses are
+       copied, and copies into a slot wait for the FFN that last read it. */
+    hipStream_t copy_stream;
+    hipEvent_t ev_copied;
+    hipEvent_t ev_computed;
 } moe_bank;
+
+/* Slots of a bank sized like the pages' --ssd-cache: a byte budget, or
+   `auto` (budget_bytes == 0) from the memory still free, clamped so that the
+   largest call the caller will make (prefill_shape, e.g. a prefill chunk)
+   still finds its layer workspace:
+     avail = free_bytes - reserve_bytes - moe_layer_workspace_bytes(prefill_shape)
+     bytes = budget_bytes ? min(budget_bytes, avail) : avail
+     *num_slots = min(prefill_shape->E, bytes / moe_slab_layout(fmt, d, f, NULL))
+   free_bytes is the caller's reading of free device memory (hipMemGetInfo);
+   reserve_bytes covers the caller's other buffers of that call (x, out,
+   logits ...).  HOST only, no HIP call.  Errors: MOE_ERR_NULL,
+   MOE_ERR_SHAPE / MOE_ERR_FORMAT (invalid shape or fmt), MOE_ERR_WORKSPACE
+   (not even one slot fits; *num_slots = 0). */
+int moe_bank_slots(int32_t fmt, const moe_shape* prefill_shape, uint64_t budget_bytes, uint64_t free_bytes,
+                   uint64_t reserve_bytes, int32_t* num_slots);
 
 /* Empties the bank (every slot -1, stamps and clock 0).  Errors:
    MOE_ERR_NULL, MOE_ERR_SHAPE (E outside 1..64, N outside 1..E). */
@@ -362,8 +420,11 @@ int moe_bank_plan(moe_bank* bank, const int32_t* want, int32_t n_want, int32_t* 
    packs of all E experts in HOST memory (pinned, e.g. hipHostMalloc, for
    asynchronous DMA; num_slots = E, slot_of_expert NULL); slots: the device
    bank (num_slots = N); same fmt, MOE_LAYOUT_TILES, hidden size d and
-   expert size f.  Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_FORMAT,
-   MOE_ERR_HIP. */
+   expert size f.  When both packs are slab packs of the same layout
+   (slot_bytes == moe_slab_layout(fmt, d, f, offsets) and every array at
+   gate.codes + offsets[i]), each load is ONE copy of the whole slab;
+   otherwise six (codes and scales of each matrix).  Errors: MOE_ERR_NULL,
+   MOE_ERR_SHAPE, MOE_ERR_FORMAT, MOE_ERR_HIP. */
 int moe_bank_fetch(const moe_experts* pool, const moe_experts* slots, int32_t d, int32_t f,
                    const int32_t* load_expert, const int32_t* load_slot, int32_t n_load,
                    hipStream_t stream);
@@ -377,18 +438,23 @@ typedef struct moe_bank_stats {
     int64_t bytes_paged;      /* host -> device bytes enqueued */
 } moe_bank_stats;
 
-/* moe_layer over a slot bank.  Routes and dispatches on the device, then
-   SYNCHRONISES `stream` to read the per-expert row counts.  The active
-   experts, resident ones first, then in id order, are split into passes of
-   at most N; each pass plans (moe_bank_plan), pages its misses in
-   (moe_bank_fetch), writes `slot_map` (DEVICE int32 [E]: the pass's slots,
-   MOE_SLOT_SKIP elsewhere) with a one-workgroup kernel and runs
-   moe_expert_ffn on the bank; one combine follows.  Everything after the
-   synchronisation is enqueued on `stream` in that order, so a pass's loads
-   never overwrite a slot an earlier pass reads.  `slots` is the device bank
-   (its slot_of_expert is ignored); `ws` as for moe_layer.  Results equal
-   moe_layer's bit for bit (an expert's rows do not depend on its slot or
-   pass).  stats may be NULL.  Errors: those of the calls above. */
+/* moe_layer over a slot bank.  Every argument is validated first (nothing
+   is enqueued and the bank is unchanged on an error).  Routes and
+   dispatches on the device, then SYNCHRONISES `stream` to read the
+   per-expert row counts.  The active experts, resident ones first, then in
+   id order, are split into passes of at most N; each pass plans
+   (moe_bank_plan) and pages its misses in (moe_bank_fetch).  Its resident
+   experts' FFN (moe_expert_ffn on the bank with `slot_map`, DEVICE int32
+   [E], holding only their slots) runs first, then -- once the copies have
+   landed -- its misses' FFN; one combine follows.  Without a copy stream
+   all of it is enqueued on `stream` in that order; with one (moe_bank) the
+   copies overlap the resident experts' FFN, and a pass's copies wait for
+   the previous pass's FFN (they may overwrite the slots it reads).  `slots`
+   is the device bank (its slot_of_expert is ignored); `ws` as for
+   moe_layer.  Results equal moe_layer's bit for bit (an expert's rows do
+   not depend on its slot or pass).  stats may be NULL.  If a HIP call fails
+   midway, MOE_ERR_HIP is returned and the bank is reset (moe_bank_reset):
+   its books no longer claim slots whose copies may not have run. */
 int moe_layer_banked(const moe_shape* shape, const uint16_t* x, const float* w_router,
                      const float* bias, float* logits, const moe_experts* pool, moe_bank* bank,
                      const moe_experts* slots, int32_t* slot_map, int32_t* topk_ids, float* topk_w,

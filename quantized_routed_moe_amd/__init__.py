@@ -1,4 +1,5 @@
-"""Python binding of the routed MoE layer's C ABI (``include/moe.h``).
+"""Python binding of the routed MoE layer's C ABI (``include/moe.h``, and the
+roofline measurement kernels of ``include/moe_peak.h``).
 
 Argument marshalling only: every step of the layer runs in the HIP kernels of
 ``libqrmoe.so``.  torch supplies device memory (tensors) and the stream
@@ -53,6 +54,9 @@ EXPORTS = (
     "moe_bank_reset", "moe_bank_plan", "moe_bank_fetch", "moe_layer_banked",
     "moe_layer_shared_workspace_bytes", "moe_layer_shared",
     "moe_workspace_bytes_mx8", "moe_expert_ffn_mx8", "moe_layer_mx8_workspace_bytes", "moe_layer_mx8",
+    "moe_slab_layout", "moe_bank_slots",
+    # include/moe_peak.h
+    "moe_peak_stream", "moe_peak_mfma",
 )
 
 
@@ -74,12 +78,14 @@ class moe_qmat(ctypes.Structure):
 
 class moe_experts(ctypes.Structure):
     _fields_ = [("gate", moe_qmat), ("up", moe_qmat), ("down", moe_qmat),
-                ("slot_of_expert", ctypes.c_void_p), ("num_slots", ctypes.c_int32)]
+                ("slot_of_expert", ctypes.c_void_p), ("num_slots", ctypes.c_int32),
+                ("slot_bytes", ctypes.c_uint64)]
 
 
 class moe_bank(ctypes.Structure):
     _fields_ = [("E", ctypes.c_int32), ("num_slots", ctypes.c_int32), ("slot_of_expert", ctypes.c_void_p),
-                ("expert_of_slot", ctypes.c_void_p), ("last_use", ctypes.c_void_p), ("clock", ctypes.c_uint64)]
+                ("expert_of_slot", ctypes.c_void_p), ("last_use", ctypes.c_void_p), ("clock", ctypes.c_uint64),
+                ("copy_stream", ctypes.c_void_p), ("ev_copied", ctypes.c_void_p), ("ev_computed", ctypes.c_void_p)]
 
 
 class moe_bank_stats(ctypes.Structure):
@@ -128,6 +134,10 @@ def lib() -> ctypes.CDLL:
             "moe_bank_plan": (_I, [_P, _P, _I, _P, _P, _P]),
             "moe_bank_fetch": (_I, [_P, _P, _I, _I, _P, _P, _I, _P]),
             "moe_layer_banked": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P]),
+            "moe_slab_layout": (_SZ, [_I, _I, _I, _P]),
+            "moe_bank_slots": (_I, [_I, _P, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64, _P]),
+            "moe_peak_stream": (_I, [_P, _SZ, ctypes.c_int32, _P, _P]),
+            "moe_peak_mfma": (_I, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -203,25 +213,79 @@ class QMat:
         return moe_qmat(fmt, self.layout, codes, scales, mins)
 
 
+def slab_layout(fmt: str, d: int, f: int):
+    """moe_slab_layout: (slab bytes, [offsets of gate codes, gate scales, up
+    codes, up scales, down codes, down scales]) of one expert."""
+    off = (ctypes.c_size_t * 6)()
+    n = int(lib().moe_slab_layout(FORMATS[fmt], int(d), int(f), off))
+    if n == 0:
+        raise MoeError(MOE_ERR_SHAPE, "slab_layout")
+    return n, [int(v) for v in off]
+
+
+def _slab_experts(fmt: str, base: int, num_slots: int, d: int, f: int, soe=None) -> moe_experts:
+    """moe_experts of a slab pack whose slot 0 starts at address `base`."""
+    fmtc = FORMATS[fmt]
+    slab, off = slab_layout(fmt, d, f)
+    q = [moe_qmat(fmtc, MOE_LAYOUT_TILES, base + off[2 * m], base + off[2 * m + 1], None) for m in range(3)]
+    return moe_experts(q[0], q[1], q[2], soe, num_slots, slab)
+
+
 @dataclass
 class Experts:
     """The gate/up/down packs of one layer (device tensors, tile layout);
-    d = hidden size, f = expert FFN size."""
+    d = hidden size, f = expert FFN size.  A slab pack (``slab`` set: uint8
+    [num_slots * slot_bytes], every expert's six arrays in one slab, see
+    ``to_slabs``) has no separate QMats."""
     fmt: str
-    gate: QMat
-    up: QMat
-    down: QMat
+    gate: Optional[QMat]
+    up: Optional[QMat]
+    down: Optional[QMat]
     slot_of_expert: object = None
     num_slots: int = 0
     d: int = 0
     f: int = 0
+    slab: object = None
 
     def c(self) -> moe_experts:
         torch = _torch()
         fmt = FORMATS[self.fmt]
         soe = _ptr(self.slot_of_expert, torch.int32, "slot_of_expert", allow_none=True)
+        if self.slab is not None:
+            return _slab_experts(self.fmt, _ptr(self.slab, torch.uint8, "slab"), self.num_slots, self.d, self.f, soe)
         return moe_experts(self.gate.c(fmt, "gate"), self.up.c(fmt, "up"), self.down.c(fmt, "down"), soe,
-                           self.num_slots)
+                           self.num_slots, 0)
+
+    def slot_arrays(self):
+        """[(matrix, slot bytes of codes, slot bytes of scales, codes tensor,
+        scales tensor)] of a separate-array pack."""
+        out = []
+        for name, n, K in (("gate", self.f, self.d), ("up", self.f, self.d), ("down", self.d, self.f)):
+            cb, sb, _ = moe_qmat_bytes(self.fmt, MOE_LAYOUT_TILES, 1, n, K)
+            m = getattr(self, name)
+            out.append((name, cb, sb, m.codes, m.scales))
+        return out
+
+    def to_slabs(self, pin_host: bool = False, device=None) -> "Experts":
+        """A copy as a slab pack (moe_slab_layout): on `device` (default: the
+        pack's), or with pin_host in pinned host memory (a slot-bank pool;
+        such a pack is passed to the C ABI through _slab_experts)."""
+        torch = _torch()
+        if self.slab is not None:
+            raise ValueError("already a slab pack")
+        slab, off = slab_layout(self.fmt, self.d, self.f)
+        n = self.num_slots * slab
+        if pin_host:
+            t = torch.zeros(n, dtype=torch.uint8, pin_memory=True)
+        else:
+            t = torch.zeros(n, dtype=torch.uint8, device=device or self.gate.codes.device)
+        for i, (_, cb, sb, codes, scales) in enumerate(self.slot_arrays()):
+            cs = codes.view(torch.uint8).reshape(self.num_slots, cb)
+            ss = scales.view(torch.uint8).reshape(self.num_slots, sb)
+            view = t.view(self.num_slots, slab)
+            view[:, off[2 * i]:off[2 * i] + cb].copy_(cs)
+            view[:, off[2 * i + 1]:off[2 * i + 1] + sb].copy_(ss)
+        return Experts(self.fmt, None, None, None, self.slot_of_expert, self.num_slots, self.d, self.f, slab=t)
 
     @staticmethod
     def from_arrays(fmt: str, gate: dict, up: dict, down: dict, device="cuda",
@@ -363,6 +427,17 @@ def moe_read_device_status(ws, stream=None) -> int:
     return int(bits.value)
 
 
+def check_device_status(ws, where: str, stream=None) -> None:
+    """Synchronises the stream and raises MoeError(MOE_ERR_DEVICE) if a
+    kernel flagged bad device data or a prefill hand-off timed out (whose y
+    rows are then NaN) in the calls on `ws` since its last moe_workspace_init."""
+    bits = moe_read_device_status(ws, stream)
+    if bits:
+        err = MoeError(MOE_ERR_DEVICE, f"{where}: device status {bits:#x}")
+        err.bits = bits
+        raise err
+
+
 # --------------------------------------------------------------- conveniences
 
 def alloc_workspace(shape: Shape, layer: bool = False, device="cuda", stream=None):
@@ -376,8 +451,11 @@ def alloc_workspace(shape: Shape, layer: bool = False, device="cuda", stream=Non
     return ws
 
 
-def layer(x, experts: Experts, k: int, *, w_router=None, bias=None, logits=None, ws=None, stream=None):
-    """Run the whole layer; returns (out, topk_ids, topk_w, logits)."""
+def layer(x, experts: Experts, k: int, *, w_router=None, bias=None, logits=None, ws=None, stream=None,
+          check: bool = False):
+    """Run the whole layer; returns (out, topk_ids, topk_w, logits).  With
+    check=True the stream is synchronised and a nonzero device status word
+    (e.g. MOE_DEV_CHAIN_TIMEOUT) raises MoeError."""
     torch = _torch()
     T, d = x.shape
     E = int(w_router.shape[0]) if w_router is not None else int(logits.shape[1])
@@ -392,6 +470,8 @@ def layer(x, experts: Experts, k: int, *, w_router=None, bias=None, logits=None,
     if ws is None:
         ws = alloc_workspace(shape, layer=True, device=dev, stream=stream)
     moe_layer(shape, x, w_router, bias, logits, experts, ids, w, out, ws, stream)
+    if check:
+        check_device_status(ws, "layer", stream)
     return out, ids, w, logits
 
 
@@ -418,7 +498,8 @@ def alloc_workspace_mx8(shape: Shape, layer: bool = False, device="cuda", stream
     return ws
 
 
-def layer_mx8(x, experts: Experts, k: int, *, w_router=None, bias=None, logits=None, ws=None, stream=None):
+def layer_mx8(x, experts: Experts, k: int, *, w_router=None, bias=None, logits=None, ws=None, stream=None,
+              check: bool = False):
     """moe_layer_mx8: the layer with MXFP8 activations in the expert FFN;
     returns (out, topk_ids, topk_w, logits)."""
     torch = _torch()
@@ -441,13 +522,15 @@ def layer_mx8(x, experts: Experts, k: int, *, w_router=None, bias=None, logits=N
         ctypes.byref(ex), _ptr(ids, torch.int32, "topk_ids"), _ptr(w, torch.float32, "topk_w"),
         _ptr(out, torch.float32, "out"), _ptr(ws, name="ws"), ws.numel() * ws.element_size(), _stream(stream))
     _check(rc, "moe_layer_mx8")
+    if check:
+        check_device_status(ws, "layer_mx8", stream)
     return out, ids, w, logits
 
 
 # -------------------------------------------------------------- shared expert
 
 def layer_shared(x, experts: Experts, shared: Experts, k: int, *, w_router=None, bias=None, logits=None,
-                 ws=None, stream=None):
+                 ws=None, stream=None, check: bool = False):
     """moe_layer_shared: the layer plus an always-on shared expert (weight 1,
     slot 0 of `shared`); returns (out, topk_ids, topk_w, logits)."""
     torch = _torch()
@@ -474,6 +557,8 @@ def layer_shared(x, experts: Experts, shared: Experts, k: int, *, w_router=None,
         ctypes.byref(ex), ctypes.byref(sh), _ptr(ids, torch.int32, "topk_ids"), _ptr(w, torch.float32, "topk_w"),
         _ptr(out, torch.float32, "out"), _ptr(ws, name="ws"), ws.numel() * ws.element_size(), _stream(stream))
     _check(rc, "moe_layer_shared")
+    if check:
+        check_device_status(ws, "layer_shared", stream)
     return out, ids, w, logits
 
 
@@ -504,46 +589,89 @@ class BankState:
         return [(int(le[i]), int(ls[i])) for i in range(nl.value)]
 
 
-def _host_qmat(m: QMat, fmt: int) -> moe_qmat:
-    for t in (m.codes, m.scales):
-        if t.is_cuda or not t.is_contiguous():
-            raise ValueError("a host pool holds contiguous CPU tensors")
-    return moe_qmat(fmt, MOE_LAYOUT_TILES, m.codes.data_ptr(), m.scales.data_ptr(), None)
+def _hip_runtime():
+    """The HIP runtime torch loaded (stream and event handles must come from it)."""
+    torch = _torch()
+    hip = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+    for fn in ("hipEventCreateWithFlags", "hipEventDestroy"):
+        getattr(hip, fn).restype = ctypes.c_int
+    return hip
+
+
+def bank_slots(fmt: str, prefill_shape: Shape, budget_bytes: int = 0, reserve_bytes: int = 0,
+               free_bytes: Optional[int] = None) -> int:
+    """moe_bank_slots: the slots of a bank of `budget_bytes` (0 = auto, from
+    the device's free memory), clamped so that a call of `prefill_shape`
+    still finds its layer workspace and `reserve_bytes` of other buffers."""
+    if free_bytes is None:
+        free_bytes = int(_torch().cuda.mem_get_info()[0])
+    n = ctypes.c_int32(0)
+    _check(lib().moe_bank_slots(FORMATS[fmt], ctypes.byref(prefill_shape.c()), int(budget_bytes),
+                                int(free_bytes), int(reserve_bytes), ctypes.byref(n)), "moe_bank_slots")
+    return int(n.value)
 
 
 class SlotBank:
     """Experts paged through `num_slots` device slots from a pool of all E
     experts in pinned host memory (moe_layer_banked).  `experts` is a device
     pack of the E experts (tile layout); its bytes are copied once into the
-    pinned pool, after which the device pack may be dropped."""
+    pinned pool, after which the device pack may be dropped.  Pool and bank
+    are slab packs, so a miss is one copy.  With `overlap` the copies run on
+    a stream of their own (default priority) and the resident experts' FFN
+    runs while the misses land."""
 
-    def __init__(self, experts: Experts, num_slots: int, device="cuda"):
+    def __init__(self, experts: Experts, num_slots: int, device="cuda", overlap: bool = True):
         torch = _torch()
         E = experts.num_slots
         self.fmt, self.E, self.num_slots, self.d, self.f = experts.fmt, E, num_slots, experts.d, experts.f
-        fmtc = FORMATS[self.fmt]
-
-        def host_copy(t):
-            h = torch.empty(t.numel(), dtype=torch.uint8, pin_memory=True)
-            h.copy_(t.view(torch.uint8).reshape(-1))
-            return h
-
-        def bank_mat(n, K):
-            cb, sb, _ = moe_qmat_bytes(self.fmt, MOE_LAYOUT_TILES, num_slots, n, K)
-            return QMat(torch.zeros(cb, dtype=torch.uint8, device=device),
-                        torch.zeros(sb, dtype=torch.uint8, device=device), None, MOE_LAYOUT_TILES)
-
-        self.pool = {m: QMat(host_copy(getattr(experts, m).codes), host_copy(getattr(experts, m).scales), None,
-                             MOE_LAYOUT_TILES) for m in ("gate", "up", "down")}
-        self.pool_c = moe_experts(_host_qmat(self.pool["gate"], fmtc), _host_qmat(self.pool["up"], fmtc),
-                                  _host_qmat(self.pool["down"], fmtc), None, E)
-        self.slots = Experts(self.fmt, bank_mat(self.f, self.d), bank_mat(self.f, self.d), bank_mat(self.d, self.f),
-                             None, num_slots, self.d, self.f)
+        self.pool = experts.to_slabs(pin_host=True)
+        self.pool_c = _slab_experts(self.fmt, self.pool.slab.data_ptr(), E, self.d, self.f)
+        slab, _ = slab_layout(self.fmt, self.d, self.f)
+        self.slots = Experts(self.fmt, None, None, None, None, num_slots, self.d, self.f,
+                             slab=torch.zeros(num_slots * slab, dtype=torch.uint8, device=device))
         self.slot_map = torch.full((E,), MOE_SLOT_SKIP, dtype=torch.int32, device=device)
+        self.copy_stream = None
+        self._events = []
+        if overlap:
+            self.copy_stream = torch.cuda.Stream(device=device)
+            hip = _hip_runtime()
+            for _ in range(2):
+                ev = ctypes.c_void_p()
+                if hip.hipEventCreateWithFlags(ctypes.byref(ev), 2):     # hipEventDisableTiming
+                    raise MoeError(MOE_ERR_HIP, "SlotBank: hipEventCreateWithFlags")
+                self._events.append(ev)
         self.state = BankState(E, num_slots)
         self.last_stats = None
 
-    def layer(self, x, k: int, *, w_router=None, bias=None, logits=None, ws=None, stream=None):
+    @property
+    def state(self) -> BankState:
+        return self._state
+
+    @state.setter
+    def state(self, st: BankState) -> None:
+        # the bank's books, plus this bank's copy stream and events
+        self._state = st
+        if self.copy_stream is not None:
+            st.c.copy_stream = int(self.copy_stream.cuda_stream)
+            st.c.ev_copied = self._events[0].value
+            st.c.ev_computed = self._events[1].value
+
+    def close(self) -> None:
+        """Destroys the bank's events (call when done with the bank)."""
+        if self._events:
+            torch = _torch()
+            torch.cuda.synchronize()
+            hip = _hip_runtime()
+            for ev in self._events:
+                hip.hipEventDestroy(ev)
+            self._events = []
+            self.copy_stream = None
+            self._state.c.copy_stream = None
+            self._state.c.ev_copied = None
+            self._state.c.ev_computed = None
+
+    def layer(self, x, k: int, *, w_router=None, bias=None, logits=None, ws=None, stream=None,
+              check: bool = False):
         """One layer call through the bank (synchronises the stream once);
         returns (out, topk_ids, topk_w, logits) and sets last_stats."""
         torch = _torch()
@@ -570,4 +698,6 @@ class SlotBank:
         _check(rc, "moe_layer_banked")
         self.last_stats = dict(active=st.active, hits=st.hits, misses=st.misses, passes=st.passes,
                                bytes_paged=int(st.bytes_paged))
+        if check:
+            check_device_status(ws, "SlotBank.layer", stream)
         return out, ids, w, logits

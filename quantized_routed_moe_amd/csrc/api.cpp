@@ -8,6 +8,7 @@
 
 #include "../../include/moe.h"
 #include "kernels.hpp"
+#include "validate.hpp"
 #include "workspace.hpp"
 
 namespace {
@@ -21,62 +22,7 @@ using qrmoe::kHeader;
 using qrmoe::ffn_ws_bytes;
 using qrmoe::LayerCarve;
 using qrmoe::layer_carve;
-
-bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
-
-int check_shape(const moe_shape* s) {
-    if (!s) return MOE_ERR_NULL;
-    if (s->T < 0 || s->k < 1 || s->E < 1 || s->E > 64 || s->k > s->E) return MOE_ERR_SHAPE;
-    if (s->d < 32 || s->f < 32 || s->d % 32 || s->f % 32) return MOE_ERR_SHAPE;
-    const long long rows = static_cast<long long>(s->T) * s->k;
-    const long long wide = s->d > s->f ? s->d : s->f;
-    if (rows * wide >= (1ll << 31)) return MOE_ERR_SHAPE;
-    return MOE_OK;
-}
-
-
-// Array sizes of one (fmt, layout) matrix; false when the request is invalid.
-bool qmat_sizes(int fmt, int layout, int slots, int n, int K, size_t* codes, size_t* scales, size_t* mins) {
-    *codes = *scales = *mins = 0;
-    if (fmt != MOE_FMT_MXFP4 && fmt != MOE_FMT_Q2G32 && fmt != MOE_FMT_Q4G32) return false;
-    if (layout != MOE_LAYOUT_ROWS && layout != MOE_LAYOUT_TILES) return false;
-    if (slots < 1 || n < 16 || n % 16 || K < 32 || K % 32) return false;
-    const size_t rows = static_cast<size_t>(slots) * n;
-    const size_t groups = rows * (K / 32);
-    if (layout == MOE_LAYOUT_ROWS) {
-        *codes = fmt == MOE_FMT_Q2G32 ? rows * (K / 4) : rows * (K / 2);
-        *scales = fmt == MOE_FMT_MXFP4 ? groups : groups * 2;
-        *mins = fmt == MOE_FMT_MXFP4 ? 0 : groups * 2;
-    } else {
-        const size_t pieces = static_cast<size_t>(slots) * (n / 16) * ((K + 127) / 128) * 64;
-        *codes = pieces * (fmt == MOE_FMT_Q2G32 ? 8 : 16);
-        *scales = pieces * (fmt == MOE_FMT_MXFP4 ? 1 : 4);
-    }
-    return true;
-}
-
-// A matrix the expert FFN can read: tile layout, every pointer 16-byte aligned.
-int check_qmat(const moe_qmat& m, int fmt) {
-    if (m.fmt != fmt || m.layout != MOE_LAYOUT_TILES) return MOE_ERR_FORMAT;
-    if (!m.codes || !m.scales) return MOE_ERR_NULL;
-    if (m.mins) return MOE_ERR_FORMAT;
-    if (!aligned(m.codes, 16) || !aligned(m.scales, 16)) return MOE_ERR_ALIGN;
-    return MOE_OK;
-}
-
-int check_experts(const moe_shape& s, const moe_experts* ex) {
-    if (!ex) return MOE_ERR_NULL;
-    const int fmt = ex->gate.fmt;
-    if (fmt != MOE_FMT_MXFP4 && fmt != MOE_FMT_Q2G32 && fmt != MOE_FMT_Q4G32) return MOE_ERR_FORMAT;
-    int rc;
-    if ((rc = check_qmat(ex->gate, fmt)) != MOE_OK) return rc;
-    if ((rc = check_qmat(ex->up, fmt)) != MOE_OK) return rc;
-    if ((rc = check_qmat(ex->down, fmt)) != MOE_OK) return rc;
-    if (ex->num_slots < 1) return MOE_ERR_SHAPE;
-    if (!ex->slot_of_expert && ex->num_slots < s.E) return MOE_ERR_SHAPE;
-    if (ex->slot_of_expert && !aligned(ex->slot_of_expert, 4)) return MOE_ERR_ALIGN;
-    return MOE_OK;
-}
+using namespace qrmoe::check;
 
 int hip_rc(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
@@ -92,15 +38,19 @@ int do_dispatch(const moe_shape& s, const int32_t* ids, int32_t* offsets, int32_
     return hip_rc(qrmoe::launch_dispatch(s, ids, offsets, perm, inv, static_cast<uint32_t*>(ws), st));
 }
 
+// layer: the one-call layer, in which an expert mapped to MOE_SLOT_SKIP
+// contributes zero (its y rows are zeroed); moe_expert_ffn leaves them alone.
 FfnArgs ffn_args(const moe_shape& s, const uint16_t* x, const moe_experts* ex, const int32_t* offsets,
-                 const int32_t* perm, float* y, void* ws) {
+                 const int32_t* perm, float* y, void* ws, bool layer = false) {
     FfnArgs a{};
+    a.zero_skipped = layer;
     a.T = s.T; a.d = s.d; a.E = s.E; a.k = s.k; a.f = s.f;
     a.x = x;
     a.offsets = offsets;
     a.perm = perm;
     a.slot_of_expert = ex->slot_of_expert;
     a.num_slots = ex->num_slots;
+    a.slot_bytes = static_cast<size_t>(ex->slot_bytes);
     const moe_qmat* mats[3] = {&ex->gate, &ex->up, &ex->down};
     for (int i = 0; i < 3; ++i) {
         a.codes[i] = static_cast<const uint8_t*>(mats[i]->codes);
@@ -115,8 +65,8 @@ FfnArgs ffn_args(const moe_shape& s, const uint16_t* x, const moe_experts* ex, c
 }
 
 int do_ffn(const moe_shape& s, const uint16_t* x, const moe_experts* ex, const int32_t* offsets,
-           const int32_t* perm, float* y, void* ws, hipStream_t st) {
-    return hip_rc(qrmoe::launch_ffn(s, ex->gate.fmt, ffn_args(s, x, ex, offsets, perm, y, ws), st));
+           const int32_t* perm, float* y, void* ws, hipStream_t st, bool layer = false) {
+    return hip_rc(qrmoe::launch_ffn(s, ex->gate.fmt, ffn_args(s, x, ex, offsets, perm, y, ws, layer), st));
 }
 
 int do_combine(const moe_shape& s, const float* y, const int32_t* inv, const float* w, float* out,
@@ -124,42 +74,27 @@ int do_combine(const moe_shape& s, const float* y, const int32_t* inv, const flo
     return hip_rc(qrmoe::launch_combine(s, y, inv, w, out, st));
 }
 
-int check_route_args(const moe_shape& s, const uint16_t* x, const float* wr, const float* bias,
-                     const float* logits, const int32_t* ids, const float* w) {
-    if (!logits || !ids || !w) return MOE_ERR_NULL;
-    if (wr && !x) return MOE_ERR_NULL;
-    if (!wr && bias) return MOE_ERR_UNSUPPORTED;
-    if ((x && !aligned(x, 16)) || (wr && !aligned(wr, 16)) || !aligned(logits, 16)) return MOE_ERR_ALIGN;
-    if ((bias && !aligned(bias, 4)) || !aligned(ids, 4) || !aligned(w, 4)) return MOE_ERR_ALIGN;
-    (void)s;
-    return MOE_OK;
-}
-
-int check_dispatch_args(const moe_shape& s, const int32_t* ids, const int32_t* offsets,
-                        const int32_t* perm, const int32_t* inv, const void* ws, size_t ws_bytes) {
-    if (!ids || !offsets || !perm || !inv || !ws) return MOE_ERR_NULL;
-    if (!aligned(ids, 4) || !aligned(offsets, 4) || !aligned(perm, 4) || !aligned(inv, 4) || !aligned(ws, 16))
-        return MOE_ERR_ALIGN;
-    if (ws_bytes < kHeader) return MOE_ERR_WORKSPACE;
-    (void)s;
-    return MOE_OK;
-}
-
-int check_ffn_args(const moe_shape& s, const uint16_t* x, const moe_experts* ex, const int32_t* offsets,
-                   const int32_t* perm, const float* y, const void* ws, size_t ws_bytes) {
-    if (!x || !offsets || !perm || !y || !ws) return MOE_ERR_NULL;
-    int rc = check_experts(s, ex);
+// moe_expert_ffn_mx8; layer: called by moe_layer_mx8 (skipped experts contribute zero).
+int ffn_mx8(const moe_shape* shape, const uint16_t* x, const moe_experts* experts, const int32_t* offsets,
+            const int32_t* perm, float* y, void* ws, size_t ws_bytes, hipStream_t stream, bool layer) {
+    int rc = check_shape(shape);
     if (rc != MOE_OK) return rc;
-    if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ws, 16)) return MOE_ERR_ALIGN;
-    if (!aligned(offsets, 4) || !aligned(perm, 4)) return MOE_ERR_ALIGN;
-    if (ws_bytes < ffn_ws_bytes(s)) return MOE_ERR_WORKSPACE;
-    return MOE_OK;
-}
-
-int check_combine_args(const float* y, const int32_t* inv, const float* w, const float* out) {
-    if (!y || !inv || !w || !out) return MOE_ERR_NULL;
-    if (!aligned(y, 16) || !aligned(out, 16) || !aligned(inv, 4) || !aligned(w, 4)) return MOE_ERR_ALIGN;
-    return MOE_OK;
+    if (shape->T == 0) return MOE_OK;
+    const moe_shape& s = *shape;
+    if ((rc = check_ffn_args(s, x, experts, offsets, perm, y, ws, ws_bytes)) != MOE_OK) return rc;
+    if (experts->gate.fmt != MOE_FMT_MXFP4 || !qrmoe::grouped_supported(s, MOE_FMT_MXFP4)) return MOE_ERR_UNSUPPORTED;
+    const qrmoe::Mx8Carve c = qrmoe::mx8_carve(s);
+    if (ws_bytes < c.total) return MOE_ERR_WORKSPACE;
+    char* base = static_cast<char*>(ws);
+    FfnArgs a = ffn_args(s, x, experts, offsets, perm, y, ws, layer);
+    a.act = nullptr;
+    a.flags = reinterpret_cast<unsigned long long*>(base + c.flags);
+    a.aq = reinterpret_cast<uint8_t*>(base + c.aq);
+    a.as = reinterpret_cast<uint8_t*>(base + c.as);
+    a.xq = reinterpret_cast<const uint8_t*>(base + c.xq);
+    a.xs = reinterpret_cast<const uint8_t*>(base + c.xs);
+    a.rpad = c.rpad;
+    return hip_rc(qrmoe::launch_ffn_mx8(s, a, stream));
 }
 
 }  // namespace
@@ -283,7 +218,7 @@ int moe_layer(const moe_shape* shape, const uint16_t* x, const float* w_router, 
         if (w_router && (rc = hip_rc(qrmoe::launch_router_logits(s, x, w_router, bias, logits, stream))) != MOE_OK)
             return rc;
         const bool fuse_combine = s.k <= 2;
-        FfnArgs a = ffn_args(s, x, experts, offsets, perm, y, ws);
+        FfnArgs a = ffn_args(s, x, experts, offsets, perm, y, ws, true);
         a.topk_w = topk_w;
         a.out = fuse_combine ? out : nullptr;
         a.fuse_combine = fuse_combine;
@@ -308,13 +243,13 @@ int moe_layer(const moe_shape* shape, const uint16_t* x, const float* w_router, 
         if ((rc = do_dispatch(s, topk_ids, offsets, perm, inv, ws, stream)) != MOE_OK) return rc;
     }
     if (s.k <= 2 && !qrmoe::ffn_uses_grouped(s, experts->gate.fmt)) {
-        FfnArgs a = ffn_args(s, x, experts, offsets, perm, y, ws);
+        FfnArgs a = ffn_args(s, x, experts, offsets, perm, y, ws, true);
         a.topk_w = topk_w;
         a.out = out;
         a.fuse_combine = 1;
         return hip_rc(qrmoe::launch_ffn(s, experts->gate.fmt, a, stream));
     }
-    if ((rc = do_ffn(s, x, experts, offsets, perm, y, ws, stream)) != MOE_OK) return rc;
+    if ((rc = do_ffn(s, x, experts, offsets, perm, y, ws, stream, true)) != MOE_OK) return rc;
     return do_combine(s, y, inv, topk_w, out, stream);
 }
 
@@ -358,7 +293,7 @@ int moe_layer_shared(const moe_shape* shape, const uint16_t* x, const float* w_r
     if (qrmoe::routed_ffn_supported(s, fmt)) {
         if (w_router && (rc = hip_rc(qrmoe::launch_router_logits(s, x, w_router, bias, logits, stream))) != MOE_OK)
             return rc;
-        FfnArgs a = ffn_args(s, x, experts, offsets, perm, y, ws);
+        FfnArgs a = ffn_args(s, x, experts, offsets, perm, y, ws, true);
         a.flags = nullptr;
         a.act = reinterpret_cast<uint16_t*>(base + kHeader);
         set_shared(a);
@@ -383,7 +318,7 @@ int moe_layer_shared(const moe_shape* shape, const uint16_t* x, const float* w_r
                                                 stream, true))) != MOE_OK)
             return rc;
     }
-    FfnArgs a = ffn_args(s, x, experts, offsets, perm, y, ws);
+    FfnArgs a = ffn_args(s, x, experts, offsets, perm, y, ws, true);
     a.flags = flag_bytes(s, true) ? reinterpret_cast<unsigned long long*>(base + kHeader + act_bytes(s, true))
                                   : nullptr;
     set_shared(a);
@@ -403,24 +338,7 @@ size_t moe_layer_mx8_workspace_bytes(const moe_shape* shape) {
 
 int moe_expert_ffn_mx8(const moe_shape* shape, const uint16_t* x, const moe_experts* experts, const int32_t* offsets,
                        const int32_t* perm, float* y, void* ws, size_t ws_bytes, hipStream_t stream) {
-    int rc = check_shape(shape);
-    if (rc != MOE_OK) return rc;
-    if (shape->T == 0) return MOE_OK;
-    const moe_shape& s = *shape;
-    if ((rc = check_ffn_args(s, x, experts, offsets, perm, y, ws, ws_bytes)) != MOE_OK) return rc;
-    if (experts->gate.fmt != MOE_FMT_MXFP4 || !qrmoe::grouped_supported(s, MOE_FMT_MXFP4)) return MOE_ERR_UNSUPPORTED;
-    const qrmoe::Mx8Carve c = qrmoe::mx8_carve(s);
-    if (ws_bytes < c.total) return MOE_ERR_WORKSPACE;
-    char* base = static_cast<char*>(ws);
-    FfnArgs a = ffn_args(s, x, experts, offsets, perm, y, ws);
-    a.act = nullptr;
-    a.flags = reinterpret_cast<unsigned long long*>(base + c.flags);
-    a.aq = reinterpret_cast<uint8_t*>(base + c.aq);
-    a.as = reinterpret_cast<uint8_t*>(base + c.as);
-    a.xq = reinterpret_cast<const uint8_t*>(base + c.xq);
-    a.xs = reinterpret_cast<const uint8_t*>(base + c.xs);
-    a.rpad = c.rpad;
-    return hip_rc(qrmoe::launch_ffn_mx8(s, a, stream));
+    return ffn_mx8(shape, x, experts, offsets, perm, y, ws, ws_bytes, stream, false);
 }
 
 int moe_layer_mx8(const moe_shape* shape, const uint16_t* x, const float* w_router, const float* bias, float* logits,
@@ -450,7 +368,7 @@ int moe_layer_mx8(const moe_shape* shape, const uint16_t* x, const float* w_rout
         if ((rc = do_route(s, x, w_router, bias, logits, topk_ids, topk_w, stream)) != MOE_OK) return rc;
         if ((rc = do_dispatch(s, topk_ids, offsets, perm, inv, ws, stream)) != MOE_OK) return rc;
     }
-    if ((rc = moe_expert_ffn_mx8(shape, x, experts, offsets, perm, y, ws, ws_bytes, stream)) != MOE_OK) return rc;
+    if ((rc = ffn_mx8(shape, x, experts, offsets, perm, y, ws, ws_bytes, stream, true)) != MOE_OK) return rc;
     return do_combine(s, y, inv, topk_w, out, stream);
 }
 

@@ -43,9 +43,20 @@ constexpr int kAuxDevice = 16;
 // Polls per wave before a wait gives up: about a third of a second.
 constexpr int kMaxPolls = 1 << 18;
 
+// Polls before giving up: kMaxPolls, unless workspace header word
+// kChainPollWord holds w != 0, which sets the limit to w - 1 (w = 1: give
+// up at once without reading a flag).  A test of the timeout path sets it
+// from the host; moe_workspace_init clears it.
+__device__ __forceinline__ int chain_poll_limit(const uint32_t* header) {
+    const uint32_t v = header[kChainPollWord];
+    return v != 0u && v <= static_cast<uint32_t>(kMaxPolls) ? static_cast<int>(v) - 1 : kMaxPolls;
+}
+
 // Waits until flags[0 .. n) all hold `tag` (lane i polls flags i, i + 64,
-// ...).  False if it gave up.
-__device__ __forceinline__ bool wait_flags(const unsigned long long* flags, int n, unsigned long long tag) {
+// ...), polling each at most max_polls times.  False if it gave up.
+__device__ __forceinline__ bool wait_flags(const unsigned long long* flags, int n, unsigned long long tag,
+                                           int max_polls = kMaxPolls) {
+    if (max_polls <= 0) return false;
     const int lane = threadIdx.x & 63;
     for (int base = 0; base < n; base += kWave) {
         const int i = base + lane;
@@ -53,7 +64,7 @@ __device__ __forceinline__ bool wait_flags(const unsigned long long* flags, int 
             const unsigned long long v =
                 i < n ? __hip_atomic_load(flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : tag;
             if (__all(v == tag)) break;
-            if (polls == kMaxPolls) return false;
+            if (polls >= max_polls) return false;
             __builtin_amdgcn_s_sleep(8);
         }
     }

@@ -197,52 +197,72 @@ __device__ __forceinline__ void grouped_unit(const FfnArgs& a, int unit, unsigne
     // put the kernel argument block in scratch memory
     auto wcodes = [&](int mat) { return sh ? a.sh_codes[mat] : a.codes[mat]; };
     auto wscales = [&](int mat) { return sh ? a.sh_scales[mat] : a.scales[mat]; };
-    if (!sh && (slot < 0 || slot >= a.num_slots)) {      // MOE_SLOT_SKIP: left out of this call, rows untouched
+    // y rows [r_base, r_base + nvalid) x this unit's weight rows, all set to v
+    auto fill_y = [&](float v) {
+        for (int i = tid; i < nvalid * kGN; i += kGThreads)
+            a.y[static_cast<size_t>(r_base + i / kGN) * a.d + nt * kGN + i % kGN] = v;
+    };
+    if (!sh && (slot < 0 || slot >= a.num_slots)) {
+        // MOE_SLOT_SKIP: left out of this call -- its y rows are untouched
+        // (the slot bank fills y over several calls), or zero when the
+        // one-call layer runs (a skipped expert then contributes nothing)
         const bool skip = slot == MOE_SLOT_SKIP;
-        if (skip) {
-            if (CHAIN && MODE == 0) raise_flag(a.flags + unit, tag);
-            return;
-        }
-        if (tid == 0 && nt == 0 && mti == 0) raise_status(a.status, MOE_DEV_BAD_SLOT);
-        if (MODE == 1) {
-            for (int i = tid; i < nvalid * kGN; i += kGThreads)
-                a.y[static_cast<size_t>(r_base + i / kGN) * a.d + nt * kGN + i % kGN] = 0.f;
-        }
+        if (!skip && tid == 0 && nt == 0 && mti == 0) raise_status(a.status, MOE_DEV_BAD_SLOT);
+        if (MODE == 1 && (!skip || a.zero_skipped)) fill_y(0.f);
         if (CHAIN && MODE == 0) raise_flag(a.flags + unit, tag);   // its act is never read
         return;
     }
     if constexpr (CHAIN && MODE == 1) {
         // units are numbered m-tile-major in both projections, so the gate/up
-        // units of this m-tile are flags [m-tile * NT0, + NT0)
+        // units of this m-tile are flags [m-tile * NT0, + NT0).  A wait that
+        // gives up leaves act unknown: the unit then writes NaN into its y
+        // rows instead of a product of stale act rows, and raises
+        // MOE_DEV_CHAIN_TIMEOUT.
+        __shared__ int chain_ok;
         const int NT0 = a.f / (kGN / 2);
-        if (wave == 0 && !wait_flags(a.flags + static_cast<size_t>(unit / NT) * NT0, NT0, tag) && lane == 0)
-            raise_status(a.status, MOE_DEV_CHAIN_TIMEOUT);
+        if (wave == 0) {
+            const bool ok =
+                wait_flags(a.flags + static_cast<size_t>(unit / NT) * NT0, NT0, tag, chain_poll_limit(a.status));
+            if (lane == 0) {
+                chain_ok = ok;
+                if (!ok) raise_status(a.status, MOE_DEV_CHAIN_TIMEOUT);
+            }
+        }
         __syncthreads();
+        if (!chain_ok) {
+            fill_y(__builtin_nanf(""));
+            return;
+        }
     }
 
     // ---- load roles of this lane (per stage: 2 weight and 2 token
     // instructions per wave, and one scale instruction by wave 0)
-    auto tile_base = [&](int tt, int& mat) {     // layout tile index of workgroup tile tt (0..31)
+    auto tile_base = [&](int tt, int& mat) {     // layout block of workgroup tile tt (0..31) within its slot
         mat = 2;
         int tile = nt * (kGN / 16) + tt;
         if (MODE == 0) {
             mat = tt < kGN / 32 ? 0 : 1;
             tile = nt * (kGN / 32) + (tt & (kGN / 32 - 1));
         }
-        return (static_cast<size_t>(slot) * (N / 16) + tile) * (K / 128);
+        return static_cast<size_t>(tile) * (K / 128);
     };
+    // first byte of the slot in the codes and scales arrays: slabs of
+    // slot_bytes (moe_experts.slot_bytes), else the arrays' own slot sizes
+    const size_t slot_blocks = static_cast<size_t>(N / 16) * (K / 128);
+    const size_t slot_c = static_cast<size_t>(slot) * (a.slot_bytes ? a.slot_bytes : slot_blocks * 64 * 16);
+    const size_t slot_s = static_cast<size_t>(slot) * (a.slot_bytes ? a.slot_bytes : slot_blocks * 64);
     const uint8_t* wsrc[2];      // piece (lane & 31) of tile 4w + 2i + (lane >> 5), step 0
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         int mat;
         const size_t blk = tile_base(4 * wave + 2 * i + (lane >> 5), mat);
-        wsrc[i] = wcodes(mat) + blk * 64 * 16 + (lane & 31) * 16;
+        wsrc[i] = wcodes(mat) + slot_c + blk * 64 * 16 + (lane & 31) * 16;
     }
     const uint8_t* ssrc;         // wave 0: scale bytes 16 (lane & 1) .. +16 of tile lane >> 1
     {
         int mat;
         const size_t blk = tile_base(lane >> 1, mat);
-        ssrc = wscales(mat) + blk * 64 + 16 * (lane & 1);
+        ssrc = wscales(mat) + slot_s + blk * 64 + 16 * (lane & 1);
     }
     const uint16_t* xsrc[2];     // token row 16w + 8i + (lane >> 3), global chunk for LDS chunk lane & 7
     const uint8_t* qsrc = nullptr;   // XQ: E4M3 token row 16w + (lane >> 2), global chunk for LDS chunk lane & 3

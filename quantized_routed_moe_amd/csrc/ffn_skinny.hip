@@ -148,8 +148,8 @@ __device__ __forceinline__ void skinny_body(const FfnArgs& a, const Item& it, in
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
         const int mat = MODE == 0 ? m : 2;
-        wt[m] = wtile<FMT>(item_codes<SH>(a, it, mat), item_scales<SH>(a, it, mat), static_cast<size_t>(it.slot) * NT + n0 / 16,
-                           S, lane);
+        wt[m] = wtile<FMT>(item_codes<SH>(a, it, mat), item_scales<SH>(a, it, mat), it.slot, a.slot_bytes, NT,
+                           n0 / 16, S, lane);
     }
     WChunk<FMT> w[NM];
     f32x4 acc[kChains<FMT>][NM];
@@ -302,11 +302,17 @@ __device__ __forceinline__ void skinny_body(const FfnArgs& a, const Item& it, in
 }
 
 // An item whose expert is left out of the call (MOE_SLOT_SKIP) writes
-// nothing; one whose slot is otherwise invalid is skipped too, but its y rows
-// read as zero and MOE_DEV_BAD_SLOT is raised.
+// nothing, except that in the one-call layer (zero_skipped) its y rows read
+// as zero (with the fused combine it simply adds nothing); one whose slot is
+// otherwise invalid is skipped too, but its y rows read as zero and
+// MOE_DEV_BAD_SLOT is raised.
 template <int FMT, int MODE, int KW, int RB, bool PERM_LDS = false, bool SH = false>
 __device__ __forceinline__ void run_item(const FfnArgs& a, const Item& it, int n0, const int32_t* perm) {
-    if (it.e < 0 || it.slot == MOE_SLOT_SKIP) return;
+    if (it.e < 0) return;
+    if (it.slot == MOE_SLOT_SKIP) {
+        if (MODE == 1 && a.zero_skipped && !a.fuse_combine) zero_y_tile(a, n0, it.r0, it.r1);
+        return;
+    }
     if ((!SH || it.e < a.E) && (it.slot < 0 || it.slot >= a.num_slots)) {
         if (threadIdx.x == 0 && n0 == 0) raise_status(a.status, MOE_DEV_BAD_SLOT);
         if (MODE == 1) zero_y_tile(a, n0, it.r0, it.r1);
@@ -359,9 +365,10 @@ __device__ __forceinline__ void prefetch_down(const FfnArgs& a, int j, int n_pf,
         const Item it = item_of(ai);
         if (it.e < 0) break;                  // past the active experts (ai grows with q)
         if ((!SH || it.e < a.E) && (it.slot < 0 || it.slot >= a.num_slots)) continue;
-        const size_t blk = (static_cast<size_t>(it.slot) * NTd + t) * S;
-        const uint8_t* c = item_codes<SH>(a, it, 2) + blk * kWave * PieceBytes<FMT>::codes;
-        const uint8_t* sc = item_scales<SH>(a, it, 2) + blk * kWave * PieceBytes<FMT>::scales;
+        const WTile tl = wtile<FMT>(item_codes<SH>(a, it, 2), item_scales<SH>(a, it, 2), it.slot, a.slot_bytes, NTd, t,
+                                    S, 0);
+        const uint8_t* c = tl.codes;
+        const uint8_t* sc = tl.scales;
         // 1 KB per instruction, lanes past the end re-read the last 16 bytes
         for (int o = 0; o < code_bytes; o += 1024)
             __builtin_amdgcn_global_load_lds(c + min(o + 16 * lane, code_bytes - 16), (lds_void*)scratch, 16, 0, 0);

@@ -89,12 +89,18 @@ struct WTile {
     const uint8_t* scales;
 };
 
-// tile_index = slot * (n/16) + tile; S = K steps of the matrix.
+// Tile `tile` of slot `slot` of a matrix of NT tiles and S K steps.  The
+// slots of an array lie slot_bytes apart when the pack keeps each expert's
+// six arrays in one slab (moe_experts.slot_bytes), else back to back.
 template <int FMT>
-__device__ __forceinline__ WTile wtile(const uint8_t* codes, const uint8_t* scales, size_t tile_index, int S,
-                                       int lane) {
-    const size_t block = tile_index * S * kWave;
-    return WTile{codes + (block + lane) * PieceBytes<FMT>::codes, scales + block * PieceBytes<FMT>::scales};
+__device__ __forceinline__ WTile wtile(const uint8_t* codes, const uint8_t* scales, int slot, size_t slot_bytes,
+                                       int NT, int tile, int S, int lane) {
+    const size_t per_slot = static_cast<size_t>(NT) * S * kWave;     // pieces of one slot
+    const size_t cs = slot_bytes ? slot_bytes : per_slot * PieceBytes<FMT>::codes;
+    const size_t ss = slot_bytes ? slot_bytes : per_slot * PieceBytes<FMT>::scales;
+    const size_t block = static_cast<size_t>(tile) * S * kWave;
+    return WTile{codes + slot * cs + (block + lane) * PieceBytes<FMT>::codes,
+                 scales + slot * ss + block * PieceBytes<FMT>::scales};
 }
 
 // Loads steps [s0, s0 + kCap) of the tile; steps at or past s1 reload step

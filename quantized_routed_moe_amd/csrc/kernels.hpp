@@ -16,11 +16,16 @@ struct FfnArgs {
     const int32_t* perm;          // [T*k]
     const int32_t* slot_of_expert;  // [E] or null
     int num_slots;
+    size_t slot_bytes;            // moe_experts.slot_bytes: 0, or the stride of every array's slots (slabs)
     const uint8_t* codes[3];      // gate, up, down: tile layout (MOE_LAYOUT_TILES)
     const uint8_t* scales[3];     // MXFP4: e8m0 byte per piece; Q2: fp16 scale | fp16 min << 16
     uint16_t* act;                // bf16 [T*k][f] (workspace)
     float* y;                     // fp32 [T*k][d]
     uint32_t* status;             // workspace header
+    // The one-call layer: an expert mapped to MOE_SLOT_SKIP contributes zero
+    // (its y rows are zeroed).  Off for moe_expert_ffn, whose callers (the
+    // slot bank) fill y over several calls.
+    int zero_skipped;
     // moe_layer with k <= 2 on the skinny path only: the gate/up launch
     // zeroes out and the down projection scatter-adds w[p] * y[r] into it
     // instead of writing y, replacing the combine kernel

@@ -123,7 +123,8 @@ def check_against_oracle(case: dict, g: dict, *, rows=None, check_logits=True, s
     float64 sums round to bf16 differently on ~1e-3 of the act elements,
     and one such ulp on a large activation moves a y element by more than
     5e-3*rms on some shapes.  With strict=True (the five workloads) the
-    device out must ALSO meet REL_L2 / ELEM_RMS against the pure oracle.
+    device y and out must ALSO meet REL_L2 / ELEM_RMS against the pure
+    oracle.
     With `rows`, the FFN is checked on those sorted rows only."""
     k, E = case["k"], case["E"]
     info = {}
@@ -150,6 +151,7 @@ def check_against_oracle(case: dict, g: dict, *, rows=None, check_logits=True, s
         assert_close(g["y"], y_dev_act, "y (given device act)")
         assert_close(g["out"], ref.combine(y_dev_act, inv, w, k), "out (given device act)")
         if strict:
+            assert_close(g["y"], y, "y")
             assert_close(g["out"], ref.combine(y, inv, w, k), "out")
     else:
         act, y = ref.expert_ffn_rows(case["x"], k, offsets, perm, rows, case["gate"], case["up"],

@@ -16,13 +16,17 @@ A16 = 0x10000          # fake, 16-byte aligned "device" addresses (never derefer
 
 
 def _declared_symbols():
-    text = open(os.path.join(ROOT, "include", "moe.h")).read()
-    return sorted(set(re.findall(r"^(?:size_t|int|const char\s*\*)\s+(moe_\w+)\s*\(", text, re.M)))
+    syms = set()
+    for name in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if name.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", name)).read()
+            syms |= set(re.findall(r"^(?:size_t|int|double|const char\s*\*)\s+(moe_\w+)\s*\(", text, re.M))
+    return sorted(syms)
 
 
 def test_library_exports_every_declared_symbol():
     syms = _declared_symbols()
-    assert len(syms) == 22
+    assert len(syms) >= 24
     assert sorted(qm.EXPORTS) == syms
     L = ctypes.CDLL(qm.LIB_PATH)
     for s in syms:
@@ -262,3 +266,19 @@ def test_mx8_validation():
     assert ffn(s, ws_bytes=need - 256) == qm.MOE_ERR_WORKSPACE
     assert ffn(_shape(T=64, d=512, E=8, k=9, f=256)) == qm.MOE_ERR_SHAPE
     assert ffn(_shape(T=0, d=512, E=8, k=2, f=256)) == qm.MOE_OK
+
+
+def test_peak_kernels_validation():
+    """The roofline measurement kernels (include/moe_peak.h) reject invalid
+    requests before any HIP call."""
+    L = qm.lib()
+    assert L.moe_peak_stream(None, 1024, 0, A16, None) == qm.MOE_ERR_NULL
+    assert L.moe_peak_stream(A16, 1024, 0, None, None) == qm.MOE_ERR_NULL
+    assert L.moe_peak_stream(A16, 0, 0, A16, None) == qm.MOE_ERR_SHAPE
+    assert L.moe_peak_stream(A16, 1000, 0, A16, None) == qm.MOE_ERR_SHAPE
+    assert L.moe_peak_stream(A16, 1024, -1, A16, None) == qm.MOE_ERR_SHAPE
+    assert L.moe_peak_stream(A16 + 8, 1024, 0, A16, None) == qm.MOE_ERR_ALIGN
+    assert L.moe_peak_mfma(0, 10, 0, None, None) == qm.MOE_ERR_NULL
+    assert L.moe_peak_mfma(2, 10, 0, A16, None) == qm.MOE_ERR_SHAPE
+    assert L.moe_peak_mfma(0, 0, 0, A16, None) == qm.MOE_ERR_SHAPE
+    assert L.moe_peak_mfma(1, 10, 0, A16 + 2, None) == qm.MOE_ERR_ALIGN

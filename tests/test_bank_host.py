@@ -210,3 +210,107 @@ def test_layer_banked_validation():
     assert call(ws_bytes=1024) == qm.MOE_ERR_WORKSPACE
     assert call(shape=qm.moe_shape(0, 256, 8, 2, 128)) == qm.MOE_OK               # T = 0: nothing
     assert (st.active, st.hits, st.misses, st.passes, st.bytes_paged) == (0, 0, 0, 0, 0)
+
+
+def test_layer_banked_rejects_before_touching_the_bank():
+    """Every argument is checked before the first HIP call and before any
+    planning: a rejected call leaves the bank's books exactly as they were
+    (a bank that claimed slots whose copies never ran would later compute
+    with wrong slot contents)."""
+    L = qm.lib()
+    b = _bank(8, 3)
+    b.plan([2, 5])                                   # some residents and stamps
+    before = (b.slot_of_expert.copy(), b.expert_of_slot.copy(), b.last_use.copy(), b.c.clock)
+    shape = qm.moe_shape(4, 256, 8, 2, 128)
+    st = qm.moe_bank_stats()
+
+    def call(pool=_ex(8), slots=_ex(3), x=A16, ws=A16, out=A16):
+        return L.moe_layer_banked(ctypes.byref(shape), x, A16, None, A16, ctypes.byref(pool), ctypes.byref(b.c),
+                                  ctypes.byref(slots), A16, A16, A16, out, ws, 1 << 30, None, ctypes.byref(st))
+
+    assert call(x=A16 + 2) == qm.MOE_ERR_ALIGN                                   # route arguments
+    assert call(slots=_ex(3, fmt=qm.MOE_FMT_Q2G32)) == qm.MOE_ERR_FORMAT          # bank pack vs pool
+    assert call(slots=_ex(3, codes=A16 + 8)) == qm.MOE_ERR_ALIGN                  # FFN alignment of the bank
+    assert call(out=None) == qm.MOE_ERR_NULL
+    bad = _ex(3)
+    bad.slot_bytes = 1000                                                         # not a multiple of 256
+    assert call(slots=bad) == qm.MOE_ERR_ALIGN
+    b.c.copy_stream = A16                                                         # a copy stream needs its events
+    assert call() == qm.MOE_ERR_NULL
+    b.c.copy_stream = None
+    after = (b.slot_of_expert, b.expert_of_slot, b.last_use, b.c.clock)
+    for x0, x1 in zip(before[:3], after[:3]):
+        assert np.array_equal(x0, x1)
+    assert before[3] == after[3]
+
+
+# ------------------------------------------------------------------ sizing
+
+def _slab(fmt, d, f):
+    off = (ctypes.c_size_t * 6)()
+    n = qm.lib().moe_slab_layout(fmt, d, f, off)
+    return int(n), list(off)
+
+
+@pytest.mark.parametrize("fmt,per_expert", [(qm.MOE_FMT_MXFP4, 13_369_344), (qm.MOE_FMT_Q2G32, 9_437_184),
+                                            (qm.MOE_FMT_Q4G32, 15_728_640)])
+def test_slab_layout_at_the_expert_shape(fmt, per_expert):
+    """At d = 4096, f = 2048 every array is a multiple of 256 bytes, so a
+    slab holds exactly one expert's bytes: MXFP4 3 d f (1/2 + 1/32), Q2
+    3 d f (1/4 + 4/32), Q4 3 d f (1/2 + 4/32)."""
+    n, off = _slab(fmt, 4096, 2048)
+    assert n == per_expert
+    sizes = []
+    for name, rows, K in (("gate", 2048, 4096), ("up", 2048, 4096), ("down", 4096, 2048)):
+        c, s_, _ = qm.moe_qmat_bytes(fmt, qm.MOE_LAYOUT_TILES, 1, rows, K)
+        sizes += [c, s_]
+    assert off == list(np.cumsum([0] + sizes[:-1]))
+    assert sum(sizes) == n
+
+
+def test_slab_layout_rounds_each_array_to_256():
+    n, off = _slab(qm.MOE_FMT_MXFP4, 96, 32)          # tiny: scale arrays of a few dozen bytes
+    assert all(o % 256 == 0 for o in off) and n % 256 == 0
+    assert off == sorted(off) and len(set(off)) == 6
+    assert _slab(9, 96, 32)[0] == 0 and _slab(qm.MOE_FMT_MXFP4, 100, 32)[0] == 0
+
+
+def _slots(fmt, shape, budget, free, reserve=0):
+    n = ctypes.c_int32(-1)
+    rc = qm.lib().moe_bank_slots(fmt, ctypes.byref(shape), budget, free, reserve, ctypes.byref(n))
+    return rc, n.value
+
+
+def test_bank_slots_budget_auto_and_clamp():
+    L = qm.lib()
+    pre = qm.moe_shape(2048, 4096, 64, 2, 2048)         # a prefill chunk
+    slab = 13_369_344
+    ws = L.moe_layer_workspace_bytes(ctypes.byref(pre))
+    GiB = 1 << 30
+    # explicit budget: budget / slab, whatever the free memory beyond it
+    assert _slots(qm.MOE_FMT_MXFP4, pre, 8 * slab + 5, 200 * GiB) == (qm.MOE_OK, 8)
+    # capped at E
+    assert _slots(qm.MOE_FMT_MXFP4, pre, 100 * GiB, 200 * GiB) == (qm.MOE_OK, 64)
+    # auto: what is free after the prefill workspace and the reserve
+    free = ws + 3 * GiB + 10 * slab
+    assert _slots(qm.MOE_FMT_MXFP4, pre, 0, free, 3 * GiB) == (qm.MOE_OK, 10)
+    # the clamp: a budget larger than what is free shrinks to fit
+    assert _slots(qm.MOE_FMT_MXFP4, pre, 50 * slab, free, 3 * GiB) == (qm.MOE_OK, 10)
+    # not one slot fits
+    assert _slots(qm.MOE_FMT_MXFP4, pre, 0, ws + slab - 1) == (qm.MOE_ERR_WORKSPACE, 0)
+    assert _slots(qm.MOE_FMT_MXFP4, pre, slab - 1, 200 * GiB) == (qm.MOE_ERR_WORKSPACE, 0)
+    # other formats use their own slab size
+    assert _slots(qm.MOE_FMT_Q2G32, pre, 10 * 9_437_184, 200 * GiB) == (qm.MOE_OK, 10)
+    # validation
+    assert _slots(7, pre, 0, 200 * GiB)[0] == qm.MOE_ERR_FORMAT
+    assert _slots(qm.MOE_FMT_MXFP4, qm.moe_shape(1, 100, 64, 2, 2048), 0, 200 * GiB)[0] == qm.MOE_ERR_SHAPE
+    n = ctypes.c_int32(0)
+    assert L.moe_bank_slots(qm.MOE_FMT_MXFP4, None, 0, 1, 0, ctypes.byref(n)) == qm.MOE_ERR_NULL
+    assert L.moe_bank_slots(qm.MOE_FMT_MXFP4, ctypes.byref(pre), 0, 1, 0, None) == qm.MOE_ERR_NULL
+
+
+def test_bank_slots_python_helper_uses_the_same_rule():
+    pre = qm.Shape(16, 4096, 64, 2, 2048)
+    n = qm.bank_slots("q2", pre, budget_bytes=0, reserve_bytes=0, free_bytes=1 << 40)
+    assert n == 64
+    assert qm.bank_slots("q2", pre, budget_bytes=3 * 9_437_184, free_bytes=1 << 40) == 3

@@ -22,12 +22,13 @@ def _say(msg):
     print(msg, flush=True)
 
 
-def _bank_sequence(case, N, steps, seeds):
+def _bank_sequence(case, N, steps, seeds, overlap=True):
     """Runs `steps` layer calls (one seeded x each) through a fresh N-slot
-    bank and through moe_layer; returns the per-call routing and stats."""
+    bank (copies on a stream of their own when `overlap`) and through
+    moe_layer; returns the per-call routing and stats."""
     dc = device_case(case)
     s = dc["shape"]
-    bank = qm.SlotBank(dc["experts"], N)
+    bank = qm.SlotBank(dc["experts"], N, overlap=overlap)
     ws = qm.alloc_workspace(s, layer=True)
     calls, stats = [], []
     for i in range(steps):
@@ -54,12 +55,13 @@ def _check_stats(case, N, calls, stats):
         assert got == (ex["active"], ex["hits"], misses, ex["passes"], misses * per_expert), (i, got, ex)
 
 
-def test_bank_decode_shape():
+@pytest.mark.parametrize("overlap", [True, False])
+def test_bank_decode_shape(overlap):
     """Decode (T=1, d=4096, E=64, top-2, f=2048, MXFP4) through an 8-slot bank."""
     case = synthetic.workload(1)
     N = 8
-    _say("slot bank: decode shape, N=8, 24 calls")
-    dc, bank, calls, stats = _bank_sequence(case, N, 24, 500)
+    _say(f"slot bank: decode shape, N=8, 24 calls, overlap={overlap}")
+    dc, bank, calls, stats = _bank_sequence(case, N, 24, 500, overlap=overlap)
     _check_stats(case, N, calls, stats)
     assert sum(st["misses"] for st in stats) > 0 and sum(st["hits"] for st in stats) > 0
     # one call against the oracle, routed on the device's logits
@@ -68,16 +70,21 @@ def test_bank_decode_shape():
     o = ref.layer(case["x"], 2, case["gate"], case["up"], case["down"], logits=lg.cpu().numpy())
     assert np.array_equal(ids.cpu().numpy(), o["ids"])
     assert_close(out.cpu().numpy(), o["out"], "banked out vs oracle")
+    bank.close()
 
 
+@pytest.mark.parametrize("overlap", [True, False])
 @pytest.mark.parametrize("fmt", ["mxfp4", "q2", "q4"])
-def test_bank_multi_pass_grouped(fmt):
+def test_bank_multi_pass_grouped(fmt, overlap):
     """128 tokens x top-2 over 16 experts with 3 slots: every call needs
-    several passes; MXFP4 takes the grouped (LDS-tiled) FFN path."""
+    several passes; MXFP4 takes the grouped (LDS-tiled) FFN path.  With the
+    copy stream, a pass's copies wait for the previous pass's FFN, which
+    reads the slots they overwrite."""
     case = synthetic.make_case(128, 512, 16, 2, 256, fmt, seed=61, zipf=1.1)
     N = 3
-    _say(f"slot bank: T=128 d=512 E=16 f=256 {fmt}, N=3, 6 calls")
-    _, _, calls, stats = _bank_sequence(case, N, 6, 900)
+    _say(f"slot bank: T=128 d=512 E=16 f=256 {fmt}, N=3, 6 calls, overlap={overlap}")
+    _, bank, calls, stats = _bank_sequence(case, N, 6, 900, overlap=overlap)
+    bank.close()
     _check_stats(case, N, calls, stats)
     assert max(st["passes"] for st in stats) >= 3
 

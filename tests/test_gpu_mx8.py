@@ -73,6 +73,7 @@ CASES = [
     (100, 1024, 16, 4, 512, 1.1),
     (3, 512, 8, 2, 256, None),
     (256, 4096, 16, 2, 2048, 1.1),
+    (2048, 4096, 64, 2, 2048, 1.1),     # the prefill chunk's shape and routing
 ]
 
 

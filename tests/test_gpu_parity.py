@@ -1,6 +1,6 @@
 """Parity of the HIP path (through the C ABI) with the CPU oracle: the five
-workloads at their full sizes, ragged shapes spanning several tiles, and the
-degenerate cases of routing and dispatch."""
+workloads at their full sizes (every row), ragged shapes spanning several
+tiles, and the degenerate cases of routing and dispatch."""
 
 import zlib
 
@@ -57,19 +57,35 @@ def _assert_layer_equals_steps(lay, g):
                              f"{d.size} differ, max |diff| {d.max():.3e}, max |out| {np.abs(g['out']).max():.3e}")
 
 
-def test_workload_prefill_sampled():
+def test_workload_prefill_full():
+    """The prefill chunk (T=2048, Zipf-skewed routing, the single-launch
+    grouped FFN) on every one of its 4096 rows: act within the flip bound, y
+    and out within the layer's bounds against the pure float64 oracle (and
+    against the oracle fed the device's act), and moe_layer equal to the
+    four calls bit for bit."""
     case = synthetic.workload(3)
-    _say("workload 3 (prefill chunk T=2048), sampled rows")
+    _say("workload 3 (prefill chunk T=2048), all rows")
     dc = device_case(case)
     g = run_steps(dc)
     assert g["status"] == 0
-    rng = np.random.default_rng(0)
-    toks = rng.choice(case["T"], size=40, replace=False)
-    rows = np.sort(np.array([g["inv"][t * case["k"] + j] for t in toks for j in range(case["k"])]))
-    info = check_against_oracle(case, g, rows=rows, strict=True)
+    info = check_against_oracle(case, g, strict=True)
     _say(f"  parity ok {info}")
     lay = run_layer(dc)
-    assert np.array_equal(lay["out"], g["out"])
+    _assert_layer_equals_steps(lay, g)
+
+
+@pytest.mark.parametrize("fmt", ["q2", "q4"])
+def test_prefill_chunk_other_formats(fmt):
+    """The prefill chunk's shape (T=2048, d=4096, E=64, k=2, f=2048, Zipf)
+    with the 2-bit and 4-bit packs, on every row."""
+    case = synthetic.make_case(2048, 4096, 64, 2, 2048, fmt, seed=3000 + len(fmt), zipf=1.1)
+    _say(f"prefill chunk T=2048 {fmt}, all rows")
+    dc = device_case(case)
+    g = run_steps(dc)
+    assert g["status"] == 0
+    info = check_against_oracle(case, g, strict=True)
+    _say(f"  parity ok {info}")
+    _assert_layer_equals_steps(run_layer(dc), g)
 
 
 SHAPES = [

@@ -24,6 +24,7 @@ CASES = [
     (40, 4096, 64, 4, 2048, "mxfp4", 1.1),
     (256, 4096, 16, 2, 2048, "mxfp4", 1.1),
     (300, 4096, 16, 2, 2048, "mxfp4", 1.1),
+    (2048, 4096, 64, 2, 2048, "mxfp4", 1.1),    # the prefill chunk's shape and routing
 ]
 
 

@@ -497,3 +497,65 @@ def test_mx8_layer_close_to_bf16_layer():
     assert np.array_equal(a["ids"], b["ids"])
     rel = np.linalg.norm(b["out"] - a["out"]) / np.linalg.norm(a["out"])
     assert 1e-3 < rel < 0.05, rel
+
+
+# ---------------------------------------------- helpers that judge GPU results
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "q2", "q4"])
+def test_expert_down_equals_expert_ffn_given_its_act(fmt):
+    """ref.expert_down judges the device's down projection from the device's
+    own act.  Given the oracle's act it must return the oracle's y, on every
+    row and on any subset of rows, with the slot map applied (a permuted map
+    over more slots than experts)."""
+    T, d, E, k, f = 11, 96, 6, 3, 64
+    c = synthetic.make_case(T, d, E, k, f, fmt, seed=31, slots=9, zipf=1.1)
+    soe = np.array([8, 2, 5, 0, 7, 3], np.int32)
+    r = ref.layer(c["x"], k, c["gate"], c["up"], c["down"], w_router=c["w_router"], bias=c["bias"],
+                  slot_of_expert=soe)
+    y_all = ref.expert_down(r["act"], r["offsets"], c["down"], slot_of_expert=soe)
+    assert np.allclose(y_all, r["y"], rtol=0, atol=1e-13 * np.abs(r["y"]).max())
+    rows = np.array([0, 4, 5, 17, T * k - 1])
+    y_sub = ref.expert_down(r["act"][rows], r["offsets"], c["down"], rows=rows, slot_of_expert=soe)
+    assert np.allclose(y_sub, r["y"][rows], rtol=0, atol=1e-13 * np.abs(r["y"]).max())
+    # against the scalar twin: explicit fsum dot products over its own dequantised rows
+    e_of = np.searchsorted(r["offsets"], rows, side="right") - 1
+    for i, (row, e) in enumerate(zip(rows, e_of)):
+        for m in (0, 37, d - 1):
+            wrow = brute.dequant_row(c["down"], int(soe[e]), m, f)
+            want = math.fsum(float(a) * w for a, w in zip(r["act"][row], wrow))
+            assert abs(y_sub[i, m] - want) <= 1e-13 * max(1.0, abs(want))
+
+
+def test_expert_down_uses_the_given_act_not_its_own():
+    """One flipped act element moves y by exactly that difference times the
+    weight column (a dropped or transposed operand fails this)."""
+    c = synthetic.make_case(4, 64, 3, 2, 32, "mxfp4", seed=32)
+    r = ref.layer(c["x"], 2, c["gate"], c["up"], c["down"], w_router=c["w_router"])
+    act = r["act"].copy()
+    act[3, 7] += 0.25
+    y = ref.expert_down(act, r["offsets"], c["down"])
+    e = int(np.searchsorted(r["offsets"], 3, side="right") - 1)
+    col = np.array([brute.dequant_row(c["down"], e, m, 32)[7] for m in range(64)])
+    assert np.allclose(y[3] - r["y"][3], 0.25 * col, rtol=0, atol=1e-13)
+    assert np.array_equal(np.delete(y, 3, axis=0), np.delete(r["y"], 3, axis=0))
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "q2", "q4"])
+def test_expert_ffn_rows_equals_expert_ffn(fmt):
+    """ref.expert_ffn_rows judges sampled rows of large calls: on any subset
+    of sorted rows (spanning several experts, in any order) it must equal
+    ref.expert_ffn on those rows, with a non-identity slot map."""
+    T, d, E, k, f = 13, 128, 7, 2, 64
+    c = synthetic.make_case(T, d, E, k, f, fmt, seed=33, slots=10, zipf=1.1)
+    soe = np.array([9, 0, 4, 1, 8, 2, 6], np.int32)
+    r = ref.layer(c["x"], k, c["gate"], c["up"], c["down"], w_router=c["w_router"], bias=c["bias"],
+                  slot_of_expert=soe)
+    for rows in (np.arange(T * k), np.array([1, 2, 3, 10, 20, 25]), np.array([25, 0, 14, 3]), np.array([T * k - 1])):
+        act, y = ref.expert_ffn_rows(c["x"], k, r["offsets"], r["perm"], rows, c["gate"], c["up"], c["down"],
+                                     slot_of_expert=soe)
+        assert np.array_equal(act, r["act"][rows])
+        assert np.allclose(y, r["y"][rows], rtol=0, atol=1e-13 * np.abs(r["y"]).max())
+    # the slot map matters: identity slots give different rows
+    act_id, _ = ref.expert_ffn_rows(c["x"], k, r["offsets"], r["perm"], np.arange(T * k), c["gate"], c["up"],
+                                    c["down"])
+    assert not np.array_equal(act_id, r["act"])
