@@ -74,6 +74,7 @@ constexpr int kGThreads = kGWaves * 64;
 constexpr int kStageW = kGN * 32;            // 32 tiles x 32 pieces x 16 B
 constexpr int kStageS = kGN * 2;             // 32 tiles x 32 scale bytes
 constexpr int kLdsBytes = 153600;            // the stage ring (of 160 KB per CU)
+constexpr int kLdsAlloc = kLdsBytes + 16;    // + one word past the ring (the hand-off verdict)
 // Dispatch order: full m-tiles per partial m-tile while both remain.  At the
 // prefill workload (24 full, 44 partial m-tiles) 2 measured 3-4 % faster per
 // FFN call than all full m-tiles first; 1 was 7 % slower, 3 and 4 about even.
@@ -218,18 +219,22 @@ __device__ __forceinline__ void grouped_unit(const FfnArgs& a, int unit, unsigne
         // gives up leaves act unknown: the unit then writes NaN into its y
         // rows instead of a product of stale act rows, and raises
         // MOE_DEV_CHAIN_TIMEOUT.
-        __shared__ int chain_ok;
+        // the verdict goes through a word past the stage ring of the
+        // workgroup's one LDS array: a __shared__ variable of its own made
+        // the compiler wait for every global -> LDS copy in flight (vmcnt(0))
+        // before each stage's LDS reads, which it cannot tell apart from it
+        int* chain_ok = reinterpret_cast<int*>(lds + kLdsBytes);
         const int NT0 = a.f / (kGN / 2);
         if (wave == 0) {
             const bool ok =
                 wait_flags(a.flags + static_cast<size_t>(unit / NT) * NT0, NT0, tag, chain_poll_limit(a.status));
             if (lane == 0) {
-                chain_ok = ok;
+                *chain_ok = ok;
                 if (!ok) raise_status(a.status, MOE_DEV_CHAIN_TIMEOUT);
             }
         }
         __syncthreads();
-        if (!chain_ok) {
+        if (!*chain_ok) {
             fill_y(__builtin_nanf(""));
             return;
         }
@@ -512,7 +517,7 @@ __device__ __forceinline__ void zero_tail_rows(const FfnArgs& a, int blk, int nb
 
 template <int MODE>
 __global__ __launch_bounds__(kGThreads) void ffn_grouped_kernel(FfnArgs a) {
-    __shared__ __align__(16) uint8_t lds[kLdsBytes];
+    __shared__ __align__(16) uint8_t lds[kLdsAlloc];
     grouped_unit<MODE, false>(a, blockIdx.x, 0, lds);
 }
 
@@ -525,7 +530,7 @@ __global__ void zero_tail_rows_kernel(FfnArgs a) { zero_tail_rows(a, blockIdx.x,
 // leave idle, instead of waiting for all of them behind a kernel boundary.
 template <bool XQ>
 __global__ __launch_bounds__(kGThreads) void ffn_grouped_chained_kernel(FfnArgs a, int ub0, int ub1) {
-    __shared__ __align__(16) uint8_t lds[kLdsBytes];
+    __shared__ __align__(16) uint8_t lds[kLdsAlloc];
     const unsigned long long tag = chain_tag();
     const int b = blockIdx.x;
     if (b < ub0) grouped_unit<0, true, XQ>(a, b, tag, lds);
