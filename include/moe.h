@@ -295,6 +295,31 @@ int moe_layer(const moe_shape* shape, const uint16_t* x, const float* w_router,
               int32_t* topk_ids, float* topk_w, float* out, void* ws, size_t ws_bytes,
               hipStream_t stream);
 
+/* ---- moe_layer without a workspace argument, for callers that cannot
+   allocate: code under HIP graph capture, tight serving loops, harnesses
+   that forbid hipMalloc.
+
+   The same computation and launches as moe_layer (identical results), with
+   the workspace taken from a file-scope device array of
+   MOE_NOALLOC_SCRATCH_BYTES that each GPU the library runs on holds until
+   the process ends.  The call allocates nothing (no hipMalloc, hipFree or
+   allocating library routine); its first call on a device looks the
+   array's address up once.  Shapes whose moe_layer_workspace_bytes exceed
+   MOE_NOALLOC_SCRATCH_BYTES are rejected with MOE_ERR_WORKSPACE (at
+   d = 4096, f = 2048, k = 2 that is about 400 tokens: decode, verify and
+   short batches, not a 2048-token prefill chunk -- use moe_layer there).
+   status: DEVICE uint32 (4-byte aligned) into which device-detected faults
+   are OR-ed as by the workspace status word (see moe_device_status_bits;
+   the caller zeroes it and reads it after the call), or NULL to ignore
+   them.  Every call on one GPU shares that GPU's array: calls that overlap
+   on one GPU (on different streams or host threads) race.  Nothing in the
+   array needs to start at zero.  Other arguments and errors as moe_layer. */
+#define MOE_NOALLOC_SCRATCH_BYTES (16u * 1024u * 1024u)
+int moe_layer_noalloc(const moe_shape* shape, const uint16_t* x, const float* w_router,
+                      const float* bias, float* logits, const moe_experts* experts,
+                      int32_t* topk_ids, float* topk_w, float* out, uint32_t* status,
+                      hipStream_t stream);
+
 /* ---- MXFP8 activations: the block-scaled fp4 x fp8 matrix cores.
 
    A faster mode that changes the rounding points, as the pages' engine

@@ -54,7 +54,7 @@ EXPORTS = (
     "moe_bank_reset", "moe_bank_plan", "moe_bank_fetch", "moe_layer_banked",
     "moe_layer_shared_workspace_bytes", "moe_layer_shared",
     "moe_workspace_bytes_mx8", "moe_expert_ffn_mx8", "moe_layer_mx8_workspace_bytes", "moe_layer_mx8",
-    "moe_slab_layout", "moe_bank_slots",
+    "moe_slab_layout", "moe_bank_slots", "moe_layer_noalloc",
     # include/moe_peak.h
     "moe_peak_stream", "moe_peak_mfma",
 )
@@ -136,6 +136,7 @@ def lib() -> ctypes.CDLL:
             "moe_layer_banked": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P]),
             "moe_slab_layout": (_SZ, [_I, _I, _I, _P]),
             "moe_bank_slots": (_I, [_I, _P, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64, _P]),
+            "moe_layer_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
             "moe_peak_stream": (_I, [_P, _SZ, ctypes.c_int32, _P, _P]),
             "moe_peak_mfma": (_I, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P]),
         }
@@ -416,6 +417,27 @@ def moe_layer(shape: Shape, x, w_router, bias, logits, experts: Experts, topk_id
         _ptr(out, torch.float32, "out"), _ptr(ws, name="ws"), ws.numel() * ws.element_size(),
         _stream(stream))
     _check(rc, "moe_layer")
+
+
+MOE_NOALLOC_SCRATCH_BYTES = 16 * 1024 * 1024
+
+
+def moe_layer_noalloc(shape: Shape, x, w_router, bias, logits, experts: Experts, topk_ids, topk_w, out,
+                      status=None, stream=None) -> None:
+    """moe_layer with the library's own per-GPU scratch array as workspace
+    (nothing allocated; calls that overlap on one GPU race).  status: a
+    device int32/uint32 tensor of one element that device faults are OR-ed
+    into, or None."""
+    torch = _torch()
+    ex = experts.c()
+    rc = lib().moe_layer_noalloc(
+        ctypes.byref(shape.c()), _ptr(x, (torch.int16, torch.bfloat16, torch.uint16), "x"),
+        _ptr(w_router, torch.float32, "w_router", allow_none=True),
+        _ptr(bias, torch.float32, "bias", allow_none=True), _ptr(logits, torch.float32, "logits"),
+        ctypes.byref(ex), _ptr(topk_ids, torch.int32, "topk_ids"), _ptr(topk_w, torch.float32, "topk_w"),
+        _ptr(out, torch.float32, "out"), _ptr(status, (torch.int32, torch.uint32), "status", allow_none=True),
+        _stream(stream))
+    _check(rc, "moe_layer_noalloc")
 
 
 def moe_read_device_status(ws, stream=None) -> int:

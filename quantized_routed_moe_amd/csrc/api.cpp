@@ -3,8 +3,10 @@
 // include/moe.h for the contract of every entry point.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/moe.h"
 #include "kernels.hpp"
@@ -61,6 +63,7 @@ FfnArgs ffn_args(const moe_shape& s, const uint16_t* x, const moe_experts* ex, c
                             : nullptr;
     a.y = y;
     a.status = static_cast<uint32_t*>(ws);
+    a.header = static_cast<const uint32_t*>(ws);
     return a;
 }
 
@@ -72,6 +75,95 @@ int do_ffn(const moe_shape& s, const uint16_t* x, const moe_experts* ex, const i
 int do_combine(const moe_shape& s, const float* y, const int32_t* inv, const float* w, float* out,
                hipStream_t st) {
     return hip_rc(qrmoe::launch_combine(s, y, inv, w, out, st));
+}
+
+// moe_layer's checks (all on the host).  ws may be a stand-in address of
+// the right alignment when the workspace is not known yet.
+int check_layer(const moe_shape* shape, const uint16_t* x, const float* w_router, const float* bias,
+                const float* logits, const moe_experts* experts, const int32_t* topk_ids, const float* topk_w,
+                const float* out, const void* ws, size_t ws_bytes) {
+    int rc = check_shape(shape);
+    if (rc != MOE_OK) return rc;
+    if (shape->T == 0) return MOE_OK;
+    const moe_shape& s = *shape;
+    if (!ws || !out) return MOE_ERR_NULL;
+    if (!aligned(ws, 16) || !aligned(out, 16)) return MOE_ERR_ALIGN;
+    const LayerCarve c = layer_carve(s);
+    if (ws_bytes < c.total) return MOE_ERR_WORKSPACE;
+    const char* base = static_cast<const char*>(ws);
+    if ((rc = check_route_args(s, x, w_router, bias, logits, topk_ids, topk_w)) != MOE_OK) return rc;
+    if (!x) return MOE_ERR_NULL;
+    return check_ffn_args(s, x, experts, reinterpret_cast<const int32_t*>(base + c.offsets),
+                          reinterpret_cast<const int32_t*>(base + c.perm), reinterpret_cast<const float*>(base + c.y),
+                          ws, ws_bytes);
+}
+
+// moe_layer's launches on a checked call (T > 0).  status: where the kernels
+// raise device status bits -- the workspace header when null, else a word of
+// the caller's (the header then holds no poll limit either).
+int layer_run(const moe_shape& s, const uint16_t* x, const float* w_router, const float* bias, float* logits,
+              const moe_experts* experts, int32_t* topk_ids, float* topk_w, float* out, void* ws, uint32_t* status,
+              hipStream_t stream) {
+    int rc;
+    const LayerCarve c = layer_carve(s);
+    char* base = static_cast<char*>(ws);
+    int32_t* offsets = reinterpret_cast<int32_t*>(base + c.offsets);
+    int32_t* perm = reinterpret_cast<int32_t*>(base + c.perm);
+    int32_t* inv = reinterpret_cast<int32_t*>(base + c.inv);
+    float* y = reinterpret_cast<float*>(base + c.y);
+    uint32_t* dev_status = status ? status : static_cast<uint32_t*>(ws);
+    auto args = [&] {
+        FfnArgs a = ffn_args(s, x, experts, offsets, perm, y, ws, true);
+        if (status) {
+            a.status = status;
+            a.header = nullptr;
+        }
+        return a;
+    };
+    // Small batches (T <= 8, T*k <= 64): the router launch computes only the
+    // logits; every workgroup of the gate/up launch routes the batch itself
+    // (top-k and dispatch in LDS) and its workgroup 0 writes the routing
+    // outputs; with k <= 2 the combine is a scatter-add inside the down
+    // launch.  Same arithmetic as the separate entry points, so the results
+    // are identical.
+    if (qrmoe::routed_ffn_supported(s, experts->gate.fmt)) {
+        if (w_router && (rc = hip_rc(qrmoe::launch_router_logits(s, x, w_router, bias, logits, stream))) != MOE_OK)
+            return rc;
+        const bool fuse_combine = s.k <= 2;
+        FfnArgs a = args();
+        a.topk_w = topk_w;
+        a.out = fuse_combine ? out : nullptr;
+        a.fuse_combine = fuse_combine;
+        a.logits = logits;
+        a.ids_out = topk_ids;
+        a.w_out = topk_w;
+        a.offsets_out = offsets;
+        a.perm_out = perm;
+        a.inv_out = inv;
+        if ((rc = hip_rc(qrmoe::launch_ffn_routed(s, experts->gate.fmt, a, stream))) != MOE_OK) return rc;
+        return fuse_combine ? MOE_OK : do_combine(s, y, inv, topk_w, out, stream);
+    }
+    // Other batches: routing (top-k and dispatch in one workgroup for up to
+    // 16 tokens), the FFN, and the combine -- on the skinny path with k <= 2
+    // a scatter-add inside the down launch (out zeroed by the gate/up launch).
+    if (qrmoe::small_route_supported(s)) {
+        if ((rc = hip_rc(qrmoe::launch_small_route(s, x, w_router, bias, logits, topk_ids, topk_w, offsets, perm,
+                                                   inv, stream))) != MOE_OK)
+            return rc;
+    } else {
+        if ((rc = do_route(s, x, w_router, bias, logits, topk_ids, topk_w, stream)) != MOE_OK) return rc;
+        if ((rc = hip_rc(qrmoe::launch_dispatch(s, topk_ids, offsets, perm, inv, dev_status, stream))) != MOE_OK)
+            return rc;
+    }
+    FfnArgs a = args();
+    if (s.k <= 2 && !qrmoe::ffn_uses_grouped(s, experts->gate.fmt)) {
+        a.topk_w = topk_w;
+        a.out = out;
+        a.fuse_combine = 1;
+        return hip_rc(qrmoe::launch_ffn(s, experts->gate.fmt, a, stream));
+    }
+    if ((rc = hip_rc(qrmoe::launch_ffn(s, experts->gate.fmt, a, stream))) != MOE_OK) return rc;
+    return do_combine(s, y, inv, topk_w, out, stream);
 }
 
 // moe_expert_ffn_mx8; layer: called by moe_layer_mx8 (skipped experts contribute zero).
@@ -95,6 +187,40 @@ int ffn_mx8(const moe_shape* shape, const uint16_t* x, const moe_experts* expert
     a.xs = reinterpret_cast<const uint8_t*>(base + c.xs);
     a.rpad = c.rpad;
     return hip_rc(qrmoe::launch_ffn_mx8(s, a, stream));
+}
+
+}  // namespace
+
+// ---- moe_layer_noalloc: moe_layer with its workspace in a file-scope
+// device array, for callers that cannot allocate.  Every GPU the library
+// runs on holds its own copy of `scratch` until the process ends.  In host
+// code the array's name is only a stand-in: its device address is looked up
+// once per device (hipGetSymbolAddress, with that device current) and that
+// address is what the launches get.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_of_device[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+// Device address of `scratch` on the current device.
+int scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+    void* p = g_scratch_of_device[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mutex);
+        p = g_scratch_of_device[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+            g_scratch_of_device[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return MOE_OK;
 }
 
 }  // namespace
@@ -192,65 +318,29 @@ int moe_combine(const moe_shape* shape, const float* y, const int32_t* inv, cons
 int moe_layer(const moe_shape* shape, const uint16_t* x, const float* w_router, const float* bias,
               float* logits, const moe_experts* experts, int32_t* topk_ids, float* topk_w, float* out,
               void* ws, size_t ws_bytes, hipStream_t stream) {
-    int rc = check_shape(shape);
-    if (rc != MOE_OK) return rc;
-    if (shape->T == 0) return MOE_OK;
-    const moe_shape& s = *shape;
-    if (!ws || !out) return MOE_ERR_NULL;
-    if (!aligned(ws, 16) || !aligned(out, 16)) return MOE_ERR_ALIGN;
-    const LayerCarve c = layer_carve(s);
-    if (ws_bytes < c.total) return MOE_ERR_WORKSPACE;
-    char* base = static_cast<char*>(ws);
-    int32_t* offsets = reinterpret_cast<int32_t*>(base + c.offsets);
-    int32_t* perm = reinterpret_cast<int32_t*>(base + c.perm);
-    int32_t* inv = reinterpret_cast<int32_t*>(base + c.inv);
-    float* y = reinterpret_cast<float*>(base + c.y);
-    if ((rc = check_route_args(s, x, w_router, bias, logits, topk_ids, topk_w)) != MOE_OK) return rc;
-    if (!x) return MOE_ERR_NULL;
-    if ((rc = check_ffn_args(s, x, experts, offsets, perm, y, ws, ws_bytes)) != MOE_OK) return rc;
-    // Small batches (T <= 8, T*k <= 64): the router launch computes only the
-    // logits; every workgroup of the gate/up launch routes the batch itself
-    // (top-k and dispatch in LDS) and its workgroup 0 writes the routing
-    // outputs; with k <= 2 the combine is a scatter-add inside the down
-    // launch.  Same arithmetic as the separate entry points, so the results
-    // are identical.
-    if (qrmoe::routed_ffn_supported(s, experts->gate.fmt)) {
-        if (w_router && (rc = hip_rc(qrmoe::launch_router_logits(s, x, w_router, bias, logits, stream))) != MOE_OK)
-            return rc;
-        const bool fuse_combine = s.k <= 2;
-        FfnArgs a = ffn_args(s, x, experts, offsets, perm, y, ws, true);
-        a.topk_w = topk_w;
-        a.out = fuse_combine ? out : nullptr;
-        a.fuse_combine = fuse_combine;
-        a.logits = logits;
-        a.ids_out = topk_ids;
-        a.w_out = topk_w;
-        a.offsets_out = offsets;
-        a.perm_out = perm;
-        a.inv_out = inv;
-        if ((rc = hip_rc(qrmoe::launch_ffn_routed(s, experts->gate.fmt, a, stream))) != MOE_OK) return rc;
-        return fuse_combine ? MOE_OK : do_combine(s, y, inv, topk_w, out, stream);
-    }
-    // Other batches: routing (top-k and dispatch in one workgroup for up to
-    // 16 tokens), the FFN, and the combine -- on the skinny path with k <= 2
-    // a scatter-add inside the down launch (out zeroed by the gate/up launch).
-    if (qrmoe::small_route_supported(s)) {
-        if ((rc = hip_rc(qrmoe::launch_small_route(s, x, w_router, bias, logits, topk_ids, topk_w, offsets, perm,
-                                                   inv, stream))) != MOE_OK)
-            return rc;
-    } else {
-        if ((rc = do_route(s, x, w_router, bias, logits, topk_ids, topk_w, stream)) != MOE_OK) return rc;
-        if ((rc = do_dispatch(s, topk_ids, offsets, perm, inv, ws, stream)) != MOE_OK) return rc;
-    }
-    if (s.k <= 2 && !qrmoe::ffn_uses_grouped(s, experts->gate.fmt)) {
-        FfnArgs a = ffn_args(s, x, experts, offsets, perm, y, ws, true);
-        a.topk_w = topk_w;
-        a.out = out;
-        a.fuse_combine = 1;
-        return hip_rc(qrmoe::launch_ffn(s, experts->gate.fmt, a, stream));
-    }
-    if ((rc = do_ffn(s, x, experts, offsets, perm, y, ws, stream, true)) != MOE_OK) return rc;
-    return do_combine(s, y, inv, topk_w, out, stream);
+    int rc = check_layer(shape, x, w_router, bias, logits, experts, topk_ids, topk_w, out, ws, ws_bytes);
+    if (rc != MOE_OK || shape->T == 0) return rc;
+    return layer_run(*shape, x, w_router, bias, logits, experts, topk_ids, topk_w, out, ws, nullptr, stream);
+}
+
+int moe_layer_noalloc(const moe_shape* shape, const uint16_t* x, const float* w_router, const float* bias,
+                      float* logits, const moe_experts* experts, int32_t* topk_ids, float* topk_w, float* out,
+                      uint32_t* status, hipStream_t stream) {
+    // every check first, against a stand-in workspace address of the
+    // scratch array's alignment and size (no HIP call yet)
+    const void* stand_in = reinterpret_cast<const void*>(static_cast<uintptr_t>(256));
+    int rc = check_layer(shape, x, w_router, bias, logits, experts, topk_ids, topk_w, out, stand_in,
+                         MOE_NOALLOC_SCRATCH_BYTES);
+    if (rc != MOE_OK || shape->T == 0) return rc;
+    if (status && !aligned(status, 4)) return MOE_ERR_ALIGN;
+    void* ws = nullptr;
+    if ((rc = scratch_address(&ws)) != MOE_OK) return rc;
+    // nothing in the scratch array needs to start at zero: every region is
+    // written before it is read in a call, and the prefill ready flags hold
+    // per-launch values; device status goes to the caller's word (or, with
+    // status NULL, to the scratch header, where nobody reads it)
+    uint32_t* st = status ? status : static_cast<uint32_t*>(ws);
+    return layer_run(*shape, x, w_router, bias, logits, experts, topk_ids, topk_w, out, ws, st, stream);
 }
 
 size_t moe_layer_shared_workspace_bytes(const moe_shape* shape) {

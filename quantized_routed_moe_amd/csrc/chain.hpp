@@ -48,6 +48,7 @@ constexpr int kMaxPolls = 1 << 18;
 // up at once without reading a flag).  A test of the timeout path sets it
 // from the host; moe_workspace_init clears it.
 __device__ __forceinline__ int chain_poll_limit(const uint32_t* header) {
+    if (!header) return kMaxPolls;
     const uint32_t v = header[kChainPollWord];
     return v != 0u && v <= static_cast<uint32_t>(kMaxPolls) ? static_cast<int>(v) - 1 : kMaxPolls;
 }

@@ -227,7 +227,7 @@ __device__ __forceinline__ void grouped_unit(const FfnArgs& a, int unit, unsigne
         const int NT0 = a.f / (kGN / 2);
         if (wave == 0) {
             const bool ok =
-                wait_flags(a.flags + static_cast<size_t>(unit / NT) * NT0, NT0, tag, chain_poll_limit(a.status));
+                wait_flags(a.flags + static_cast<size_t>(unit / NT) * NT0, NT0, tag, chain_poll_limit(a.header));
             if (lane == 0) {
                 *chain_ok = ok;
                 if (!ok) raise_status(a.status, MOE_DEV_CHAIN_TIMEOUT);

@@ -21,7 +21,8 @@ struct FfnArgs {
     const uint8_t* scales[3];     // MXFP4: e8m0 byte per piece; Q2: fp16 scale | fp16 min << 16
     uint16_t* act;                // bf16 [T*k][f] (workspace)
     float* y;                     // fp32 [T*k][d]
-    uint32_t* status;             // workspace header
+    uint32_t* status;             // device status word (the workspace header's, or the caller's)
+    const uint32_t* header;       // workspace header (poll-limit word), or null: defaults
     // The one-call layer: an expert mapped to MOE_SLOT_SKIP contributes zero
     // (its y rows are zeroed).  Off for moe_expert_ffn, whose callers (the
     // slot bank) fill y over several calls.
