@@ -26,7 +26,8 @@ loops (include/moe_peak.h), against which every roofline also reports
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 0..6]
 
 Workloads 0-4 are the configurations the targets are quoted on; 5 and 6
-run the 4-bit group-asymmetric pack at 16 tokens and at 1 token.  --bank N
+run the 4-bit group-asymmetric pack at 16 tokens and at 1 token, 7 and 8 the
+2-bit and 4-bit packs at the prefill chunk's size (2048 tokens).  --bank N
 runs the workload through an N-slot expert bank paged from pinned host
 memory instead (its own JSON line: paging included, PCIe roofline);
 --shared adds an always-on shared expert (moe_layer_shared; its own JSON line).
@@ -755,7 +756,7 @@ def run_workload(c, args, mx8=False, peaks=None, cpu=True):
     del pools, routers, xs, ws, y
     torch.cuda.empty_cache()
     if cpu and not args.no_cpu_baseline and not mx8:
-        n = args.cpu_sample_steps or {0: 200, 1: 6, 2: 4, 3: 1, 4: 3, 5: 3, 6: 6}[c]
+        n = args.cpu_sample_steps or {0: 200, 1: 6, 2: 4, 3: 1, 4: 3, 5: 3, 6: 6, 7: 1, 8: 1}[c]
         res["cpu_baseline"] = cpu_baseline(c, n)
     return res
 

@@ -15,6 +15,8 @@ Workloads (d = hidden size, f = expert FFN size, E experts, top-k):
   2 spec-verify    T=5,    d=4096, E=64, k=2, f=2048, MXFP4, correlated tokens
   3 prefill chunk  T=2048, d=4096, E=64, k=2, f=2048, MXFP4, Zipf(1.1) router bias
   4 two-bit        T=16,   d=4096, E=64, k=2, f=2048, Q2,    Zipf(1.1) router bias
+  (5-8: the 4-bit pack at 16 and 1 tokens, the 2-bit and 4-bit packs at the
+  prefill chunk's size; not among the quoted configurations)
 
 Value recipe:
   x        bf16(N(0,1))   (workload 2: bf16(base + 0.3 * noise_t), base/noise N(0,1))
@@ -46,6 +48,9 @@ WORKLOADS = {
     5: dict(name="four-bit", T=16, d=4096, E=64, k=2, f=2048, fmt="q4", router="device",
             zipf=1.1),
     6: dict(name="four-bit decode", T=1, d=4096, E=64, k=2, f=2048, fmt="q4", router="device"),
+    # the prefill chunk with the 2-bit and 4-bit packs (not quoted configurations)
+    7: dict(name="two-bit prefill", T=2048, d=4096, E=64, k=2, f=2048, fmt="q2", router="device", zipf=1.1),
+    8: dict(name="four-bit prefill", T=2048, d=4096, E=64, k=2, f=2048, fmt="q4", router="device", zipf=1.1),
 }
 
 # stream ids within a workload
