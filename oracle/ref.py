@@ -461,15 +461,74 @@ def mxfp8_to_f64(codes, scale_bytes) -> np.ndarray:
     return (vals * 2.0 ** (np.asarray(scale_bytes, dtype=np.float64) - 127.0)[..., None]).reshape(c.shape)
 
 
-def expert_ffn_mx8(x_bits, k: int, offsets, perm, gate: dict, up: dict, down: dict, slot_of_expert=None):
-    """Steps 4 and 5 with MXFP8 activations (the matrix cores' native scaled
-    fp4 x fp8 products): the token rows x_t and the SwiGLU output are each
-    quantised to MXFP8 along their contraction axis (quantize_mxfp8) in
-    place of the bf16 rounding point; products and sums are float64.
-    Returns act float64 [T*k, f] (the MXFP8 values), its codes and scale
-    bytes, and y float64 [T*k, d]."""
-    xq, xs = quantize_mxfp8(bf16_bits_to_f64(x_bits))
-    xv = mxfp8_to_f64(xq, xs)
+# ---------------------------------------------------------------------------
+# MXFP4 activations (OCP MX v1.0: E2M1 elements, one E8M0 scale per 32)
+# ---------------------------------------------------------------------------
+
+E2M1_MAX = 6.0
+E2M1_EMAX = 2            # exponent of the largest normal (6 = 1.5 * 2**2)
+
+
+def round_e2m1(q) -> np.ndarray:
+    """Round float64 values to the nearest E2M1 value (ties to the even
+    mantissa), saturating magnitudes above 6 to 6.  Below 1 the step is the
+    subnormal step 0.5; in [2**e, 2**(e+1)) it is 2**(e-1)."""
+    q = np.asarray(q, dtype=np.float64)
+    a = np.abs(q)
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, 0.0)
+    step = 2.0 ** (e - 1.0)
+    r = np.round(a / step) * step                # numpy rounds half to even
+    r = np.minimum(r, E2M1_MAX)
+    return np.where(q < 0, -r, r)
+
+
+def encode_e2m1(v) -> np.ndarray:
+    """E2M1 code (0..15) of values that are exactly representable; +0 for
+    zero, the sign bit (8) for negative nonzero values."""
+    v = np.asarray(v, dtype=np.float64)
+    idx = np.searchsorted(E2M1_MAGNITUDE, np.abs(v))
+    if not np.array_equal(E2M1_MAGNITUDE[np.minimum(idx, 7)], np.abs(v)):
+        raise ValueError("value not representable in E2M1")
+    return (idx + np.where(v < 0, 8, 0)).astype(np.uint8)
+
+
+def quantize_mxfp4(v):
+    """Quantise float64 values [..., K] (K a multiple of 32) to MXFP4 along
+    the last axis (OCP MX v1.0 conversion): per block of 32, the shared
+    scale is 2**(floor(log2(amax)) - 2) (2 = E2M1's largest exponent; E8M0
+    byte = that exponent + 127, clamped to 0..254; an all-zero block gets
+    byte 0), and each element is v / scale rounded to E2M1 as round_e2m1.
+    Returns (codes uint8 [..., K], one 4-bit code per element, and scale
+    bytes uint8 [..., K/32])."""
+    v = np.asarray(v, dtype=np.float64)
+    blocks = v.reshape(v.shape[:-1] + (v.shape[-1] // 32, 32))
+    amax = np.abs(blocks).max(axis=-1)
+    with np.errstate(divide="ignore"):
+        ex = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - E2M1_EMAX, -127.0)
+    sbyte = np.clip(ex + 127.0, 0, 254)
+    scale = 2.0 ** (sbyte - 127.0)
+    q = round_e2m1(blocks / scale[..., None])
+    return encode_e2m1(q).reshape(v.shape), sbyte.astype(np.uint8)
+
+
+def mxfp4_act_to_f64(codes, scale_bytes) -> np.ndarray:
+    """Values of MXFP4 data [..., K] (one code per element) with scale
+    bytes [..., K/32]."""
+    c = np.asarray(codes)
+    vals = e2m1_to_f64(c).reshape(c.shape[:-1] + (c.shape[-1] // 32, 32))
+    return (vals * 2.0 ** (np.asarray(scale_bytes, dtype=np.float64) - 127.0)[..., None]).reshape(c.shape)
+
+
+def _expert_ffn_mx(x_bits, k, offsets, perm, gate, up, down, quantize, decode, slot_of_expert):
+    """Steps 4 and 5 with the token rows and the SwiGLU output each
+    quantised along their contraction axis by `quantize` (values back by
+    `decode`) in place of the bf16 rounding point; products and sums are
+    float64.  Returns act float64 [T*k, f] (the quantised values), its codes
+    and scale bytes, and y float64 [T*k, d]."""
+    xq, xs = quantize(bf16_bits_to_f64(x_bits))
+    xv = decode(xq, xs)
     offsets = np.asarray(offsets, dtype=np.int64)
     perm = np.asarray(perm, dtype=np.int64)
     E = offsets.size - 1
@@ -486,23 +545,50 @@ def expert_ffn_mx8(x_bits, k: int, offsets, perm, gate: dict, up: dict, down: di
         xt = xv[perm[r0:r1] // k]
         h[r0:r1] = silu(xt @ dequant(gate, slot).T) * (xt @ dequant(up, slot).T)
         wd[e] = dequant(down, slot)
-    aq, asc = quantize_mxfp8(h)
-    act = mxfp8_to_f64(aq, asc)
+    aq, asc = quantize(h)
+    act = decode(aq, asc)
     for e, w in wd.items():
         r0, r1 = offsets[e], offsets[e + 1]
         y[r0:r1] = act[r0:r1] @ w.T
     return act, aq, asc, y
 
 
-def layer_mx8(x_bits, k: int, gate: dict, up: dict, down: dict, *, logits=None, w_router=None, bias=None):
-    """The layer with MXFP8 activations in the expert FFN (routing and
-    combine as ``layer``)."""
+def expert_ffn_mx8(x_bits, k: int, offsets, perm, gate: dict, up: dict, down: dict, slot_of_expert=None):
+    """Steps 4 and 5 with MXFP8 activations (the matrix cores' native scaled
+    fp4 x fp8 products): the token rows x_t and the SwiGLU output are each
+    quantised to MXFP8 (quantize_mxfp8).  Returns act, its codes, its scale
+    bytes and y, as _expert_ffn_mx."""
+    return _expert_ffn_mx(x_bits, k, offsets, perm, gate, up, down, quantize_mxfp8, mxfp8_to_f64, slot_of_expert)
+
+
+def expert_ffn_mx4(x_bits, k: int, offsets, perm, gate: dict, up: dict, down: dict, slot_of_expert=None):
+    """Steps 4 and 5 with MXFP4 activations (the matrix cores' native scaled
+    fp4 x fp4 products): the token rows x_t and the SwiGLU output are each
+    quantised to MXFP4 (quantize_mxfp4).  Returns act, its codes (one per
+    element), its scale bytes and y, as _expert_ffn_mx."""
+    return _expert_ffn_mx(x_bits, k, offsets, perm, gate, up, down, quantize_mxfp4, mxfp4_act_to_f64,
+                          slot_of_expert)
+
+
+def _layer_mx(ffn, x_bits, k, gate, up, down, logits, w_router, bias):
     if logits is None:
         logits = router_logits(x_bits, w_router, bias)
     logits = np.asarray(logits, dtype=np.float64)
     ids, w = route_topk(logits, k)
     offsets, perm, inv = dispatch(ids, logits.shape[1])
-    act, aq, asc, y = expert_ffn_mx8(x_bits, k, offsets, perm, gate, up, down)
+    act, aq, asc, y = ffn(x_bits, k, offsets, perm, gate, up, down)
     out = combine(y, inv, w, k)
     return dict(logits=logits, ids=ids, w=w, offsets=offsets, perm=perm, inv=inv, act=act, act_codes=aq,
                 act_scales=asc, y=y, out=out)
+
+
+def layer_mx8(x_bits, k: int, gate: dict, up: dict, down: dict, *, logits=None, w_router=None, bias=None):
+    """The layer with MXFP8 activations in the expert FFN (routing and
+    combine as ``layer``)."""
+    return _layer_mx(expert_ffn_mx8, x_bits, k, gate, up, down, logits, w_router, bias)
+
+
+def layer_mx4(x_bits, k: int, gate: dict, up: dict, down: dict, *, logits=None, w_router=None, bias=None):
+    """The layer with MXFP4 activations in the expert FFN (routing and
+    combine as ``layer``)."""
+    return _layer_mx(expert_ffn_mx4, x_bits, k, gate, up, down, logits, w_router, bias)

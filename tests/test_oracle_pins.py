@@ -559,3 +559,112 @@ def test_expert_ffn_rows_equals_expert_ffn(fmt):
     act_id, _ = ref.expert_ffn_rows(c["x"], k, r["offsets"], r["perm"], np.arange(T * k), c["gate"], c["up"],
                                     c["down"])
     assert not np.array_equal(act_id, r["act"])
+
+
+# ------------------------------------------------- MXFP4 activations
+
+def _e2m1_nearest_brute(v):
+    """Nearest E2M1 value by search over the 8 magnitudes, written out:
+    the closest magnitude, a tie going to the even code (even mantissa),
+    magnitudes above 6 clamped to 6; the sign kept, zero made +0."""
+    mags = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    a = min(abs(v), 6.0)
+    best = 0
+    for c in range(8):
+        dc, db = abs(mags[c] - a), abs(mags[best] - a)
+        if dc < db or (dc == db and c % 2 == 0 and best % 2 == 1):
+            best = c
+    m = mags[best]
+    return -m if (v < 0 and m > 0) else m
+
+
+def test_e2m1_rounding_against_search():
+    """round_e2m1 (step arithmetic) against a search over the E2M1 values
+    with the tie rule spelled out, on random values, every midpoint and
+    values around the clamp."""
+    rng = np.random.default_rng(41)
+    v = rng.standard_normal(20000) * 2.0 ** rng.integers(-3, 4, 20000)
+    mags = ref.E2M1_MAGNITUDE
+    mids = (mags[1:] + mags[:-1]) / 2
+    v = np.concatenate([v, mids, -mids, mids + 1e-9, mids - 1e-9, [5.99, 6.0, 6.5, 7.0, 7.01, 1e9, -1e9, 0.0]])
+    got = ref.round_e2m1(v)
+    want = np.array([_e2m1_nearest_brute(float(t)) for t in v])
+    assert np.array_equal(got, want)
+
+
+def test_mxfp4_act_hand_worked_block():
+    fx = _read_fixture("mxfp4_act_block.txt")
+    va = np.array([float(t) for t in fx["values_a"]])
+    ca = np.array([int(t) for t in fx["codes_a"]], np.uint8)
+    assert va.size == 32 and ca.size == 32
+    v = np.stack([va, va * 2.0 ** -20])
+    codes, sb = ref.quantize_mxfp4(v)
+    assert sb[0, 0] == int(fx["scale_a"][0]) and sb[1, 0] == int(fx["scale_b"][0])
+    assert np.array_equal(codes[0], ca) and np.array_equal(codes[1], ca)
+    vals = ref.mxfp4_act_to_f64(codes, sb)
+    assert np.array_equal(vals[1], vals[0] * 2.0 ** -20)
+
+
+def test_mxfp4_act_quantizer_rules():
+    rng = np.random.default_rng(42)
+    v = rng.standard_normal((5, 128)) * 2.0 ** rng.integers(-20, 20, (5, 1))
+    v[2, 32:64] = 0.0
+    codes, sb = ref.quantize_mxfp4(v)
+    vals = ref.mxfp4_act_to_f64(codes, sb)
+    blocks = np.abs(v).reshape(5, 4, 32).max(axis=-1)
+    scale = 2.0 ** (sb.astype(np.float64) - 127)
+    nz = blocks > 0
+    # the block maximum lands in [4, 8) before rounding
+    assert np.all((blocks[nz] / scale[nz] >= 4) & (blocks[nz] / scale[nz] < 8))
+    assert sb[2, 1] == 0 and not np.any(vals[2, 32:64])
+    # within half an E2M1 step of the input where no clamp applies: the step
+    # is 0.5 below 2, 1 in [2, 4), 2 in [4, 6]; above 6, exactly 6 * scale
+    sc = scale.repeat(32, axis=1)
+    scaled = np.abs(v) / sc
+    half = np.where(scaled < 2, 0.25, np.where(scaled < 4, 0.5, 1.0))
+    ok = scaled <= 6
+    assert np.all(np.abs(vals - v)[ok] <= half[ok] * sc[ok] * (1 + 1e-12))
+    assert np.all(np.abs(vals[~ok]) == 6 * sc[~ok])
+    # quantising the quantised values again changes nothing
+    c2, s2 = ref.quantize_mxfp4(vals)
+    assert np.array_equal(c2, codes) and np.array_equal(s2, sb)
+
+
+def test_mx4_single_expert_is_dense_swiglu_with_fp4_casts():
+    """E = 1, k = 1 with MXFP4 activations: a dense SwiGLU MLP in torch
+    float64 where both activations go through a nearest-value search over
+    the E2M1 grid with the block scale of the largest magnitude (an
+    independent route to the same quantisation)."""
+    c = _small_case("mxfp4", T=5, d=64, E=1, k=1, f=32, seed=43)
+    r = ref.layer_mx4(c["x"], 1, c["gate"], c["up"], c["down"], w_router=c["w_router"])
+
+    def mx4(t):
+        b = t.reshape(t.shape[0], -1, 32)
+        amax = b.abs().amax(dim=-1, keepdim=True)
+        sc = torch.exp2(torch.floor(torch.log2(amax)) - 2)
+        q = torch.tensor([_e2m1_nearest_brute(float(u)) for u in (b / sc).flatten()],
+                         dtype=torch.float64).reshape(b.shape)
+        return (q * sc).reshape(t.shape)
+
+    x = torch.tensor([[brute.bf16_value(int(b)) for b in row] for row in c["x"]], dtype=torch.float64)
+    wg = torch.from_numpy(_dense_weights_brute(c["gate"], 0, 32, 64))
+    wu = torch.from_numpy(_dense_weights_brute(c["up"], 0, 32, 64))
+    wd = torch.from_numpy(_dense_weights_brute(c["down"], 0, 64, 32))
+    xq = mx4(x)
+    act = mx4(torch.nn.functional.silu(xq @ wg.T) * (xq @ wu.T))
+    assert np.allclose(r["out"], (act @ wd.T).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_mx4_layer_close_to_bf16_layer():
+    """MXFP4 activations move out by about their rounding (E2M1 keeps one
+    mantissa bit: relative errors of several per cent per element), no
+    more: a dropped scale or transposed operand would not stay within a
+    few tens of per cent of the bf16 layer."""
+    c = _small_case("mxfp4", T=12, d=256, E=8, k=2, f=128, seed=44)
+    a = ref.layer(c["x"], 2, c["gate"], c["up"], c["down"], w_router=c["w_router"])
+    b = ref.layer_mx4(c["x"], 2, c["gate"], c["up"], c["down"], w_router=c["w_router"])
+    m = ref.layer_mx8(c["x"], 2, c["gate"], c["up"], c["down"], w_router=c["w_router"])
+    assert np.array_equal(a["ids"], b["ids"])
+    rel = np.linalg.norm(b["out"] - a["out"]) / np.linalg.norm(a["out"])
+    rel8 = np.linalg.norm(m["out"] - a["out"]) / np.linalg.norm(a["out"])
+    assert 2 * rel8 < rel < 0.3, (rel, rel8)
