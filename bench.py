@@ -48,6 +48,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0         # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
 MFMA_FP8_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 matrix, published (the fp4 x fp8 products run at it)
+MFMA_FP4_PEAK_TFLOPS = 10100.0  # MI355X dense fp4 / fp6 matrix, published (the fp4 x fp4 products)
 METRIC = "MoE layer tokens/s; decode weight-stream GB/s; prefill expert TFLOP/s"
 
 # HBM bytes per moe_expert_ffn call from rocprofv3 counter runs of the current
@@ -86,6 +87,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--mx8", action="store_true",
                    help="MXFP8 activations on the block-scaled fp4 x fp8 matrix cores (moe_layer_mx8)")
+    p.add_argument("--mx4", action="store_true",
+                   help="MXFP4 activations on the block-scaled fp4 x fp4 matrix cores (moe_layer_mx4)")
     p.add_argument("--shared", action="store_true",
                    help="run the workload with a shared expert (moe_layer_shared)")
     p.add_argument("--bank", type=int, default=0, metavar="N",
@@ -489,8 +492,8 @@ def measure_peaks(stream_bytes_decode):
         different buffer (24 buffers, > 256 MB, so every read is cold),
         replayed from a HIP graph -- the rate a kernel of that size can
         reach, launch included;
-      * bf16_TFLOPs / fp8_TFLOPs: the dense matrix-core loops (bf16 32x32x16,
-        scaled fp4 x fp8 32x32x64), median of 5."""
+      * bf16_TFLOPs / fp8_TFLOPs / fp4_TFLOPs: the dense matrix-core loops
+        (bf16 32x32x16, scaled fp4 x fp8 and fp4 x fp4 32x32x64), median of 5."""
     import ctypes
 
     import numpy as np
@@ -535,8 +538,8 @@ def measure_peaks(stream_bytes_decode):
     res = {"hbm_GBps": round(hbm, 1), "hbm_GBps_decode_stream": round(dec, 1),
            "decode_stream_bytes": nb, "decode_stream_us": round(secs / K * 1e6, 3)}
     fsink = torch.empty(4096, dtype=torch.float32, device="cuda")
-    for kind, name, per in ((0, "bf16_TFLOPs", 32768), (1, "fp8_TFLOPs", 131072)):
-        iters = 4000 if kind == 0 else 2000
+    for kind, name, per in ((0, "bf16_TFLOPs", 32768), (1, "fp8_TFLOPs", 131072), (2, "fp4_TFLOPs", 131072)):
+        iters = {0: 4000, 1: 2000, 2: 4000}[kind]
         ev = Events(hip, 5)
         L.moe_peak_mfma(kind, iters, 0, fsink.data_ptr(), sp)           # warm
         for a, b in ev.ev:
@@ -551,7 +554,7 @@ def measure_peaks(stream_bytes_decode):
     return res
 
 
-def run_workload(c, args, mx8=False, peaks=None, cpu=True):
+def run_workload(c, args, mx=0, peaks=None, cpu=True):
     """Times workload c (see the module docstring): returns its result dict
     (value, ms_per_step, roofline, cpu_baseline, ...)."""
     import ctypes
@@ -600,9 +603,11 @@ def run_workload(c, args, mx8=False, peaks=None, cpu=True):
     inv = torch.empty((T * k,), dtype=torch.int32, device=dev)
     y = torch.empty((T * k, d), dtype=torch.float32, device=dev)
     out = torch.empty((T, d), dtype=torch.float32, device=dev)
-    if mx8 and (w["fmt"] != "mxfp4" or d % 512 or f % 256):
-        raise SystemExit("--mx8 needs MXFP4 experts with d % 512 == 0 and f % 256 == 0")
-    ws = qm.alloc_workspace_mx8(shape, layer=True, device=dev) if mx8 else qm.alloc_workspace(shape, layer=True, device=dev)
+    if mx and (w["fmt"] != "mxfp4" or d % 512 or f % 256):
+        raise SystemExit(f"--mx{mx} needs MXFP4 experts with d % 512 == 0 and f % 256 == 0")
+    ws = (qm.alloc_workspace_mx8(shape, layer=True, device=dev) if mx == 8 else
+          qm.alloc_workspace_mx4(shape, layer=True, device=dev) if mx == 4 else
+          qm.alloc_workspace(shape, layer=True, device=dev))
 
     # Raw C-ABI calls with precomputed arguments keep the host far ahead of
     # the GPU, so HIP event pairs measure kernels, not launch latency.
@@ -621,9 +626,10 @@ def run_workload(c, args, mx8=False, peaks=None, cpu=True):
     lg_p, ids_p, tw_p = logits.data_ptr(), ids.data_ptr(), tw.data_ptr()
     off_p, perm_p, inv_p = offsets.data_ptr(), perm.data_ptr(), inv.data_ptr()
     y_p, out_p, ws_p, ws_n = y.data_ptr(), out.data_ptr(), ws.data_ptr(), ws.numel()
-    ffn_ws_n = int(L.moe_workspace_bytes_mx8(ctypes.byref(shape.c()))) if mx8 else qm.moe_workspace_bytes(shape)
-    ffn_call = L.moe_expert_ffn_mx8 if mx8 else L.moe_expert_ffn
-    layer_call = L.moe_layer_mx8 if mx8 else L.moe_layer
+    ffn_ws_n = (int(getattr(L, f"moe_workspace_bytes_mx{mx}")(ctypes.byref(shape.c()))) if mx else
+                qm.moe_workspace_bytes(shape))
+    ffn_call = getattr(L, f"moe_expert_ffn_mx{mx}") if mx else L.moe_expert_ffn
+    layer_call = getattr(L, f"moe_layer_mx{mx}") if mx else L.moe_layer
     wr_p = [None if r is None else r[0].data_ptr() for r in routers]
     b_p = [None if (r is None or r[1] is None) else r[1].data_ptr() for r in routers]
     given_p = None if given is None else given.data_ptr()
@@ -701,7 +707,10 @@ def run_workload(c, args, mx8=False, peaks=None, cpu=True):
     U_mean = float(np.mean(U))
 
     weight_bytes = U_mean * per_expert
-    act_bytes = T * d * 2 + T * k * f * 2 * 2 + T * k * d * 4     # x read, act write+read, y write
+    if mx:   # x read, token codes write+read, act codes write+read, y write (scale bytes left out)
+        act_bytes = T * d * 2 + (T * k * d + T * k * f) * mx // 8 * 2 + T * k * d * 4
+    else:    # x read, act write+read, y write
+        act_bytes = T * d * 2 + T * k * f * 2 * 2 + T * k * d * 4
     ffn_bytes = weight_bytes + act_bytes
     ffn_avg_s = float(np.mean(ffn_ms)) / 1e3
     flops = 2.0 * T * k * 3 * d * f
@@ -710,13 +719,13 @@ def run_workload(c, args, mx8=False, peaks=None, cpu=True):
 
     traffic = MEASURED_FFN_TRAFFIC.get(c)
     traffic = None if traffic is None else round(traffic)
-    if mx8:
+    if mx:
         traffic = None
     if T * k >= 1024:
-        peak = MFMA_FP8_PEAK_TFLOPS if mx8 else MFMA_BF16_PEAK_TFLOPS
+        peak = {8: MFMA_FP8_PEAK_TFLOPS, 4: MFMA_FP4_PEAK_TFLOPS}.get(mx, MFMA_BF16_PEAK_TFLOPS)
         roof = dict(bound="mfma", achieved=round(tflops, 2), peak=peak, unit="TFLOP/s",
                     frac=round(tflops / peak, 4), traffic=traffic)
-        mpeak = None if peaks is None else peaks["fp8_TFLOPs" if mx8 else "bf16_TFLOPs"]
+        mpeak = None if peaks is None else peaks.get({8: "fp8_TFLOPs", 4: "fp4_TFLOPs"}.get(mx, "bf16_TFLOPs"))
         if mpeak:
             roof["measured_peak"] = mpeak
             roof["frac_measured"] = round(tflops / mpeak, 4)
@@ -728,7 +737,7 @@ def run_workload(c, args, mx8=False, peaks=None, cpu=True):
             roof["measured_peak"] = peaks["hbm_GBps"]
             roof["frac_measured"] = round(gbps / peaks["hbm_GBps"], 4)
     roof["traffic_unit"] = "HBM bytes per call (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
-    roof["kernel"] = ("moe_expert_ffn_mx8 (token quantisation, then one launch of block-scaled fp4 x fp8 tiles)" if mx8
+    roof["kernel"] = (f"moe_expert_ffn_mx{mx} (token quantisation, then one launch of block-scaled fp4 x fp{mx} tiles)" if mx
                       else "moe_expert_ffn (one launch: gate/up + SwiGLU tiles, then down tiles)" if T * k >= 256 and w["fmt"] == "mxfp4"
                       else "moe_expert_ffn (gate/up + SwiGLU kernel, down kernel)")
     roof["algorithmic_bytes_per_launch"] = round(ffn_bytes)
@@ -741,8 +750,8 @@ def run_workload(c, args, mx8=False, peaks=None, cpu=True):
         "value": round(T * K / elapsed, 2),
         "unit": "tokens/s",
         "ms_per_step": round(elapsed / K * 1e3, 5),
-        "dtype": "mxfp8 activations x mxfp4 weights" if mx8 else "bf16",
-        "config": {"workload": f"{w['name']}{' (MXFP8 activations)' if mx8 else ''}: T={T} d={d} E={E} k={k} f={f} {w['fmt']}",
+        "dtype": f"mxfp{mx} activations x mxfp4 weights" if mx else "bf16",
+        "config": {"workload": f"{w['name']}{f' (MXFP{mx} activations)' if mx else ''}: T={T} d={d} E={E} k={k} f={f} {w['fmt']}",
                    "T": T, "d": d, "E": E, "k": k, "f": f, "format": w["fmt"],
                    "weight_pools": n_pools, "parallelism": "none (1 GPU)"},
         "weight_stream_GBps": round(gbps, 1),
@@ -755,7 +764,7 @@ def run_workload(c, args, mx8=False, peaks=None, cpu=True):
     }
     del pools, routers, xs, ws, y
     torch.cuda.empty_cache()
-    if cpu and not args.no_cpu_baseline and not mx8:
+    if cpu and not args.no_cpu_baseline and not mx:
         n = args.cpu_sample_steps or {0: 200, 1: 6, 2: 4, 3: 1, 4: 3, 5: 3, 6: 6, 7: 1, 8: 1}[c]
         res["cpu_baseline"] = cpu_baseline(c, n)
     return res
@@ -783,7 +792,9 @@ def main():
     peaks = None
     if not args.no_peaks:
         peaks = measure_peaks(MX_BYTES_PER_EXPERT(w["d"], w["f"]) * 2 + 57344)
-    r = run_workload(head, args, mx8=args.mx8, peaks=peaks)
+    if args.mx8 and args.mx4:
+        raise SystemExit("--mx8 and --mx4 exclude each other")
+    r = run_workload(head, args, mx=8 if args.mx8 else 4 if args.mx4 else 0, peaks=peaks)
     res = {
         "metric": METRIC,
         "value": r["value"],
@@ -801,7 +812,7 @@ def main():
     res.update({n: v for n, v in r.items() if n not in res})
     if peaks is not None:
         res["measured_peaks"] = peaks
-    if args.workload is None and not args.mx8:
+    if args.workload is None and not (args.mx8 or args.mx4):
         # the other configurations in the same run, each with its own
         # roofline and oracle baseline (the headline is workload 1)
         res["workloads"] = {}

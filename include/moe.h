@@ -27,8 +27,9 @@
  * Entry points: moe_route_topk (1-2), moe_dispatch (3), moe_expert_ffn (4-5),
  * moe_combine (6) and moe_layer (1-6 in one call); moe_pack_qmat lays
  * weights out for the kernels.  Beside the layer: moe_layer_shared (an
- * always-on shared expert), moe_expert_ffn_mx8 / moe_layer_mx8 (MXFP8
- * activations on the block-scaled matrix cores), and the slot bank
+ * always-on shared expert), moe_expert_ffn_mx8 / moe_layer_mx8 and
+ * moe_expert_ffn_mx4 / moe_layer_mx4 (MXFP8 or MXFP4 activations on the
+ * block-scaled matrix cores), and the slot bank
  * (moe_bank_reset / moe_bank_plan / moe_bank_fetch / moe_layer_banked:
  * N device expert slots paged from host memory).
  *
@@ -345,6 +346,32 @@ int moe_expert_ffn_mx8(const moe_shape* shape, const uint16_t* x, const moe_expe
                        size_t ws_bytes, hipStream_t stream);
 size_t moe_layer_mx8_workspace_bytes(const moe_shape* shape);
 int moe_layer_mx8(const moe_shape* shape, const uint16_t* x, const float* w_router,
+                  const float* bias, float* logits, const moe_experts* experts,
+                  int32_t* topk_ids, float* topk_w, float* out, void* ws, size_t ws_bytes,
+                  hipStream_t stream);
+
+/* ---- MXFP4 activations: the block-scaled fp4 x fp4 matrix cores.
+
+   The same mode as the MXFP8 calls above with E2M1 activations (the other
+   activation format the gfx950 block-scaled instruction takes beside E4M3,
+   at twice its rate): the token rows and the SwiGLU output are quantised to
+   MXFP4 (OCP Microscaling Formats v1.0: E2M1 elements, one E8M0 scale per
+   32 along the contraction axis, the scale 2^(floor(log2 amax) - 2),
+   elements rounded to nearest, ties to even, magnitudes above 6 clamped to
+   6, zero stored as +0).  Steps 4-5 become
+     xq[r] = MXFP4(x[perm[r] / k]),  act_q[r] = MXFP4(silu(Wg xq[r]) * (Wu xq[r])),
+     y[r]  = Wd act_q[r]                                              (fp32)
+   E2M1 keeps one mantissa bit: out moves by tens of per cent (relative L2)
+   from the bf16 layer; parity is against the oracle's MXFP4 layer.  Shapes,
+   formats, arguments and errors as the MXFP8 calls; after a call, act_q
+   codes u8 [T*k][f/2] (two per byte, the even column in the low nibble)
+   start at byte 256 of ws. */
+size_t moe_workspace_bytes_mx4(const moe_shape* shape);
+int moe_expert_ffn_mx4(const moe_shape* shape, const uint16_t* x, const moe_experts* experts,
+                       const int32_t* offsets, const int32_t* perm, float* y, void* ws,
+                       size_t ws_bytes, hipStream_t stream);
+size_t moe_layer_mx4_workspace_bytes(const moe_shape* shape);
+int moe_layer_mx4(const moe_shape* shape, const uint16_t* x, const float* w_router,
                   const float* bias, float* logits, const moe_experts* experts,
                   int32_t* topk_ids, float* topk_w, float* out, void* ws, size_t ws_bytes,
                   hipStream_t stream);

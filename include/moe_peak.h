@@ -44,6 +44,8 @@ int moe_peak_stream(const void* buf, size_t bytes, int32_t workgroups, uint32_t*
      kind 0: v_mfma_f32_32x32x16_bf16      (32 x 32 x 16 bf16, 32768 flop each)
      kind 1: v_mfma_scale_f32_32x32x64_f8f6f4 with fp4 A and fp8 B
              (32 x 32 x 64, 131072 flop each; the MXFP8-activation path)
+     kind 2: the same instruction with fp4 A and fp4 B (the MXFP4-activation
+             path)
    flop = workgroups * 4 * iters * 8 * (flop each); the rate is flop / the
    kernel's duration.  sink holds workgroups * 4 floats. */
 int moe_peak_mfma(int32_t kind, int32_t iters, int32_t workgroups, float* sink, hipStream_t stream);

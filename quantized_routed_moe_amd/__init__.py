@@ -54,6 +54,7 @@ EXPORTS = (
     "moe_bank_reset", "moe_bank_plan", "moe_bank_fetch", "moe_layer_banked",
     "moe_layer_shared_workspace_bytes", "moe_layer_shared",
     "moe_workspace_bytes_mx8", "moe_expert_ffn_mx8", "moe_layer_mx8_workspace_bytes", "moe_layer_mx8",
+    "moe_workspace_bytes_mx4", "moe_expert_ffn_mx4", "moe_layer_mx4_workspace_bytes", "moe_layer_mx4",
     "moe_slab_layout", "moe_bank_slots", "moe_layer_noalloc",
     # include/moe_peak.h
     "moe_peak_stream", "moe_peak_mfma",
@@ -130,6 +131,10 @@ def lib() -> ctypes.CDLL:
             "moe_expert_ffn_mx8": (_I, [_P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
             "moe_layer_mx8_workspace_bytes": (_SZ, [_P]),
             "moe_layer_mx8": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+            "moe_workspace_bytes_mx4": (_SZ, [_P]),
+            "moe_expert_ffn_mx4": (_I, [_P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+            "moe_layer_mx4_workspace_bytes": (_SZ, [_P]),
+            "moe_layer_mx4": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
             "moe_bank_reset": (_I, [_P]),
             "moe_bank_plan": (_I, [_P, _P, _I, _P, _P, _P]),
             "moe_bank_fetch": (_I, [_P, _P, _I, _I, _P, _P, _I, _P]),
@@ -497,33 +502,47 @@ def layer(x, experts: Experts, k: int, *, w_router=None, bias=None, logits=None,
     return out, ids, w, logits
 
 
-# ------------------------------------------------------------ MXFP8 activations
+# ------------------------------------------------ MXFP8 / MXFP4 activations
 
-def moe_expert_ffn_mx8(shape: Shape, x, experts: Experts, offsets, perm, y, ws, stream=None) -> None:
+def _ffn_mxq(bits, shape: Shape, x, experts: Experts, offsets, perm, y, ws, stream=None) -> None:
     torch = _torch()
     ex = experts.c()
-    rc = lib().moe_expert_ffn_mx8(
+    name = f"moe_expert_ffn_mx{bits}"
+    rc = getattr(lib(), name)(
         ctypes.byref(shape.c()), _ptr(x, (torch.int16, torch.bfloat16, torch.uint16), "x"),
         ctypes.byref(ex), _ptr(offsets, torch.int32, "offsets"), _ptr(perm, torch.int32, "perm"),
         _ptr(y, torch.float32, "y"), _ptr(ws, name="ws"), ws.numel() * ws.element_size(), _stream(stream))
-    _check(rc, "moe_expert_ffn_mx8")
+    _check(rc, name)
 
 
-def alloc_workspace_mx8(shape: Shape, layer: bool = False, device="cuda", stream=None):
+def moe_expert_ffn_mx8(shape: Shape, x, experts: Experts, offsets, perm, y, ws, stream=None) -> None:
+    _ffn_mxq(8, shape, x, experts, offsets, perm, y, ws, stream)
+
+
+def moe_expert_ffn_mx4(shape: Shape, x, experts: Experts, offsets, perm, y, ws, stream=None) -> None:
+    _ffn_mxq(4, shape, x, experts, offsets, perm, y, ws, stream)
+
+
+def _alloc_workspace_mxq(bits, shape: Shape, layer: bool, device, stream):
     torch = _torch()
-    fn = lib().moe_layer_mx8_workspace_bytes if layer else lib().moe_workspace_bytes_mx8
+    fn = getattr(lib(), f"moe_layer_mx{bits}_workspace_bytes" if layer else f"moe_workspace_bytes_mx{bits}")
     n = int(fn(ctypes.byref(shape.c())))
     if n == 0:
-        raise MoeError(MOE_ERR_SHAPE, "alloc_workspace_mx8")
+        raise MoeError(MOE_ERR_SHAPE, f"alloc_workspace_mx{bits}")
     ws = torch.empty(n, dtype=torch.uint8, device=device)
     moe_workspace_init(ws, stream)
     return ws
 
 
-def layer_mx8(x, experts: Experts, k: int, *, w_router=None, bias=None, logits=None, ws=None, stream=None,
-              check: bool = False):
-    """moe_layer_mx8: the layer with MXFP8 activations in the expert FFN;
-    returns (out, topk_ids, topk_w, logits)."""
+def alloc_workspace_mx8(shape: Shape, layer: bool = False, device="cuda", stream=None):
+    return _alloc_workspace_mxq(8, shape, layer, device, stream)
+
+
+def alloc_workspace_mx4(shape: Shape, layer: bool = False, device="cuda", stream=None):
+    return _alloc_workspace_mxq(4, shape, layer, device, stream)
+
+
+def _layer_mxq(bits, x, experts: Experts, k: int, w_router, bias, logits, ws, stream, check):
     torch = _torch()
     T, d = x.shape
     E = int(w_router.shape[0]) if w_router is not None else int(logits.shape[1])
@@ -535,18 +554,33 @@ def layer_mx8(x, experts: Experts, k: int, *, w_router=None, bias=None, logits=N
     w = torch.empty((T, k), dtype=torch.float32, device=dev)
     out = torch.empty((T, d), dtype=torch.float32, device=dev)
     if ws is None:
-        ws = alloc_workspace_mx8(shape, layer=True, device=dev, stream=stream)
+        ws = _alloc_workspace_mxq(bits, shape, True, dev, stream)
     ex = experts.c()
-    rc = lib().moe_layer_mx8(
+    name = f"moe_layer_mx{bits}"
+    rc = getattr(lib(), name)(
         ctypes.byref(shape.c()), _ptr(x, (torch.int16, torch.bfloat16, torch.uint16), "x"),
         _ptr(w_router, torch.float32, "w_router", allow_none=True),
         _ptr(bias, torch.float32, "bias", allow_none=True), _ptr(logits, torch.float32, "logits"),
         ctypes.byref(ex), _ptr(ids, torch.int32, "topk_ids"), _ptr(w, torch.float32, "topk_w"),
         _ptr(out, torch.float32, "out"), _ptr(ws, name="ws"), ws.numel() * ws.element_size(), _stream(stream))
-    _check(rc, "moe_layer_mx8")
+    _check(rc, name)
     if check:
-        check_device_status(ws, "layer_mx8", stream)
+        check_device_status(ws, f"layer_mx{bits}", stream)
     return out, ids, w, logits
+
+
+def layer_mx8(x, experts: Experts, k: int, *, w_router=None, bias=None, logits=None, ws=None, stream=None,
+              check: bool = False):
+    """moe_layer_mx8: the layer with MXFP8 activations in the expert FFN;
+    returns (out, topk_ids, topk_w, logits)."""
+    return _layer_mxq(8, x, experts, k, w_router, bias, logits, ws, stream, check)
+
+
+def layer_mx4(x, experts: Experts, k: int, *, w_router=None, bias=None, logits=None, ws=None, stream=None,
+              check: bool = False):
+    """moe_layer_mx4: the layer with MXFP4 activations in the expert FFN;
+    returns (out, topk_ids, topk_w, logits)."""
+    return _layer_mxq(4, x, experts, k, w_router, bias, logits, ws, stream, check)
 
 
 # -------------------------------------------------------------- shared expert

@@ -166,17 +166,17 @@ int layer_run(const moe_shape& s, const uint16_t* x, const float* w_router, cons
     return do_combine(s, y, inv, topk_w, out, stream);
 }
 
-// moe_expert_ffn_mx8; layer: called by moe_layer_mx8 (skipped experts contribute zero).
-int ffn_mx8(const moe_shape* shape, const uint16_t* x, const moe_experts* experts, const int32_t* offsets,
-            const int32_t* perm, float* y, void* ws, size_t ws_bytes, hipStream_t stream, bool layer) {
+// moe_expert_ffn_mx8 / _mx4 (bits = 8 / 4); layer: called by moe_layer_mx8 /
+// _mx4 (skipped experts contribute zero).
+int ffn_mxq(const moe_shape* shape, const uint16_t* x, const moe_experts* experts, const int32_t* offsets,
+            const int32_t* perm, float* y, void* ws, size_t ws_bytes, hipStream_t stream, int bits, bool layer) {
     int rc = check_shape(shape);
     if (rc != MOE_OK) return rc;
     if (shape->T == 0) return MOE_OK;
     const moe_shape& s = *shape;
-    if ((rc = check_ffn_args(s, x, experts, offsets, perm, y, ws, ws_bytes)) != MOE_OK) return rc;
+    const qrmoe::MxqCarve c = qrmoe::mxq_carve(s, bits);
+    if ((rc = check_ffn_args(s, x, experts, offsets, perm, y, ws, ws_bytes, c.total)) != MOE_OK) return rc;
     if (experts->gate.fmt != MOE_FMT_MXFP4 || !qrmoe::grouped_supported(s, MOE_FMT_MXFP4)) return MOE_ERR_UNSUPPORTED;
-    const qrmoe::Mx8Carve c = qrmoe::mx8_carve(s);
-    if (ws_bytes < c.total) return MOE_ERR_WORKSPACE;
     char* base = static_cast<char*>(ws);
     FfnArgs a = ffn_args(s, x, experts, offsets, perm, y, ws, layer);
     a.act = nullptr;
@@ -186,7 +186,40 @@ int ffn_mx8(const moe_shape* shape, const uint16_t* x, const moe_experts* expert
     a.xq = reinterpret_cast<const uint8_t*>(base + c.xq);
     a.xs = reinterpret_cast<const uint8_t*>(base + c.xs);
     a.rpad = c.rpad;
-    return hip_rc(qrmoe::launch_ffn_mx8(s, a, stream));
+    return hip_rc(qrmoe::launch_ffn_mxq(s, a, bits, stream));
+}
+
+// moe_layer_mx8 / _mx4: route, dispatch, the quantised-activation FFN, combine.
+int layer_mxq(const moe_shape* shape, const uint16_t* x, const float* w_router, const float* bias, float* logits,
+              const moe_experts* experts, int32_t* topk_ids, float* topk_w, float* out, void* ws, size_t ws_bytes,
+              hipStream_t stream, int bits) {
+    int rc = check_shape(shape);
+    if (rc != MOE_OK) return rc;
+    if (shape->T == 0) return MOE_OK;
+    const moe_shape& s = *shape;
+    if (!ws || !out || !x || !experts) return MOE_ERR_NULL;
+    if (!aligned(ws, 16) || !aligned(out, 16)) return MOE_ERR_ALIGN;
+    const LayerCarve c = qrmoe::layer_carve_mxq(s, bits);
+    if (ws_bytes < c.total) return MOE_ERR_WORKSPACE;
+    char* base = static_cast<char*>(ws);
+    int32_t* offsets = reinterpret_cast<int32_t*>(base + c.offsets);
+    int32_t* perm = reinterpret_cast<int32_t*>(base + c.perm);
+    int32_t* inv = reinterpret_cast<int32_t*>(base + c.inv);
+    float* y = reinterpret_cast<float*>(base + c.y);
+    if ((rc = check_route_args(s, x, w_router, bias, logits, topk_ids, topk_w)) != MOE_OK) return rc;
+    if ((rc = check_ffn_args(s, x, experts, offsets, perm, y, ws, ws_bytes, qrmoe::mxq_carve(s, bits).total)) != MOE_OK)
+        return rc;
+    if (experts->gate.fmt != MOE_FMT_MXFP4 || !qrmoe::grouped_supported(s, MOE_FMT_MXFP4)) return MOE_ERR_UNSUPPORTED;
+    if (qrmoe::small_route_supported(s)) {
+        if ((rc = hip_rc(qrmoe::launch_small_route(s, x, w_router, bias, logits, topk_ids, topk_w, offsets, perm,
+                                                   inv, stream))) != MOE_OK)
+            return rc;
+    } else {
+        if ((rc = do_route(s, x, w_router, bias, logits, topk_ids, topk_w, stream)) != MOE_OK) return rc;
+        if ((rc = do_dispatch(s, topk_ids, offsets, perm, inv, ws, stream)) != MOE_OK) return rc;
+    }
+    if ((rc = ffn_mxq(shape, x, experts, offsets, perm, y, ws, ws_bytes, stream, bits, true)) != MOE_OK) return rc;
+    return do_combine(s, y, inv, topk_w, out, stream);
 }
 
 }  // namespace
@@ -418,48 +451,44 @@ int moe_layer_shared(const moe_shape* shape, const uint16_t* x, const float* w_r
 
 size_t moe_workspace_bytes_mx8(const moe_shape* shape) {
     if (check_shape(shape) != MOE_OK) return 0;
-    return qrmoe::mx8_carve(*shape).total;
+    return qrmoe::mxq_carve(*shape, 8).total;
 }
 
 size_t moe_layer_mx8_workspace_bytes(const moe_shape* shape) {
     if (check_shape(shape) != MOE_OK) return 0;
-    return qrmoe::layer_carve_mx8(*shape).total;
+    return qrmoe::layer_carve_mxq(*shape, 8).total;
 }
 
 int moe_expert_ffn_mx8(const moe_shape* shape, const uint16_t* x, const moe_experts* experts, const int32_t* offsets,
                        const int32_t* perm, float* y, void* ws, size_t ws_bytes, hipStream_t stream) {
-    return ffn_mx8(shape, x, experts, offsets, perm, y, ws, ws_bytes, stream, false);
+    return ffn_mxq(shape, x, experts, offsets, perm, y, ws, ws_bytes, stream, 8, false);
 }
 
 int moe_layer_mx8(const moe_shape* shape, const uint16_t* x, const float* w_router, const float* bias, float* logits,
                   const moe_experts* experts, int32_t* topk_ids, float* topk_w, float* out, void* ws, size_t ws_bytes,
                   hipStream_t stream) {
-    int rc = check_shape(shape);
-    if (rc != MOE_OK) return rc;
-    if (shape->T == 0) return MOE_OK;
-    const moe_shape& s = *shape;
-    if (!ws || !out || !x || !experts) return MOE_ERR_NULL;
-    if (!aligned(ws, 16) || !aligned(out, 16)) return MOE_ERR_ALIGN;
-    const LayerCarve c = qrmoe::layer_carve_mx8(s);
-    if (ws_bytes < c.total) return MOE_ERR_WORKSPACE;
-    char* base = static_cast<char*>(ws);
-    int32_t* offsets = reinterpret_cast<int32_t*>(base + c.offsets);
-    int32_t* perm = reinterpret_cast<int32_t*>(base + c.perm);
-    int32_t* inv = reinterpret_cast<int32_t*>(base + c.inv);
-    float* y = reinterpret_cast<float*>(base + c.y);
-    if ((rc = check_route_args(s, x, w_router, bias, logits, topk_ids, topk_w)) != MOE_OK) return rc;
-    if ((rc = check_ffn_args(s, x, experts, offsets, perm, y, ws, ws_bytes)) != MOE_OK) return rc;
-    if (experts->gate.fmt != MOE_FMT_MXFP4 || !qrmoe::grouped_supported(s, MOE_FMT_MXFP4)) return MOE_ERR_UNSUPPORTED;
-    if (qrmoe::small_route_supported(s)) {
-        if ((rc = hip_rc(qrmoe::launch_small_route(s, x, w_router, bias, logits, topk_ids, topk_w, offsets, perm,
-                                                   inv, stream))) != MOE_OK)
-            return rc;
-    } else {
-        if ((rc = do_route(s, x, w_router, bias, logits, topk_ids, topk_w, stream)) != MOE_OK) return rc;
-        if ((rc = do_dispatch(s, topk_ids, offsets, perm, inv, ws, stream)) != MOE_OK) return rc;
-    }
-    if ((rc = ffn_mx8(shape, x, experts, offsets, perm, y, ws, ws_bytes, stream, true)) != MOE_OK) return rc;
-    return do_combine(s, y, inv, topk_w, out, stream);
+    return layer_mxq(shape, x, w_router, bias, logits, experts, topk_ids, topk_w, out, ws, ws_bytes, stream, 8);
+}
+
+size_t moe_workspace_bytes_mx4(const moe_shape* shape) {
+    if (check_shape(shape) != MOE_OK) return 0;
+    return qrmoe::mxq_carve(*shape, 4).total;
+}
+
+size_t moe_layer_mx4_workspace_bytes(const moe_shape* shape) {
+    if (check_shape(shape) != MOE_OK) return 0;
+    return qrmoe::layer_carve_mxq(*shape, 4).total;
+}
+
+int moe_expert_ffn_mx4(const moe_shape* shape, const uint16_t* x, const moe_experts* experts, const int32_t* offsets,
+                       const int32_t* perm, float* y, void* ws, size_t ws_bytes, hipStream_t stream) {
+    return ffn_mxq(shape, x, experts, offsets, perm, y, ws, ws_bytes, stream, 4, false);
+}
+
+int moe_layer_mx4(const moe_shape* shape, const uint16_t* x, const float* w_router, const float* bias, float* logits,
+                  const moe_experts* experts, int32_t* topk_ids, float* topk_w, float* out, void* ws, size_t ws_bytes,
+                  hipStream_t stream) {
+    return layer_mxq(shape, x, w_router, bias, logits, experts, topk_ids, topk_w, out, ws, ws_bytes, stream, 4);
 }
 
 const char* moe_status_str(int status) {

@@ -115,6 +115,16 @@ __device__ __forceinline__ f32x16 mfma_scale_fp4_fp8(u32x4 a, i32x8 b, f32x16 c,
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b, c, 4, 0, 0, sa, 0, sb);
 }
 
+// The same product with B = 32 E2M1 token values per lane (16 bytes, K
+// block l/32, as A) and B's scale that of K block l/32.
+__device__ __forceinline__ f32x16 mfma_scale_fp4_fp4(u32x4 a, u32x4 b, f32x16 c, int sa, int sb) {
+    const i32x8 a8 = {static_cast<int>(a[0]), static_cast<int>(a[1]), static_cast<int>(a[2]), static_cast<int>(a[3]),
+                      0, 0, 0, 0};
+    const i32x8 b8 = {static_cast<int>(b[0]), static_cast<int>(b[1]), static_cast<int>(b[2]), static_cast<int>(b[3]),
+                      0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 4, 4, 0, sa, 0, sb);
+}
+
 // E8M0 scale byte of a block whose largest magnitude is amax:
 // floor(log2 amax) - 8 + 127 (8 = E4M3's largest exponent), clamped to
 // 0..254; 0 for an all-zero block.
@@ -122,6 +132,29 @@ __device__ __forceinline__ int mx8_scale_byte(float amax) {
     if (!(amax > 0.f)) return 0;
     const int e = ilogbf(amax) - 8 + 127;
     return e < 0 ? 0 : e > 254 ? 254 : e;
+}
+
+// MXFP4 (E2M1 elements): floor(log2 amax) - 2 + 127 (2 = E2M1's largest
+// exponent), clamped to 0..254; 0 for an all-zero block.
+__device__ __forceinline__ int mx4_scale_byte(float amax) {
+    if (!(amax > 0.f)) return 0;
+    const int e = ilogbf(amax) - 2 + 127;
+    return e < 0 ? 0 : e > 254 ? 254 : e;
+}
+
+// A value (already divided by the block scale) to its E2M1 code: nearest of
+// 0, 0.5, 1, 1.5, 2, 3, 4, 6, a tie going to the even code (even mantissa),
+// magnitudes above 6 clamped to 6, the sign in bit 3, zero made +0.  The
+// magnitude code counts the decision points passed: a tie stays below the
+// point when the lower neighbour's code is even (0.25, 1.25, 2.5, 5) and
+// passes it when the upper one's is (0.75, 1.75, 3.5).
+__device__ __forceinline__ uint32_t e2m1_rne_sat(float v) {
+    const float a = fabsf(v);
+    const uint32_t c = static_cast<uint32_t>(a > 0.25f) + static_cast<uint32_t>(a >= 0.75f) +
+                       static_cast<uint32_t>(a > 1.25f) + static_cast<uint32_t>(a >= 1.75f) +
+                       static_cast<uint32_t>(a > 2.5f) + static_cast<uint32_t>(a >= 3.5f) +
+                       static_cast<uint32_t>(a > 5.f);
+    return c | (v < 0.f && c != 0 ? 8u : 0u);
 }
 
 // Four values (already divided by the block scale) to E4M3 codes, low byte

@@ -84,10 +84,11 @@ constexpr int kFullPerPart = 2;
 // a stage holds the weights, their scales and only the 32*NTT token rows the
 // multiplies read, so units with few rows keep more stages (and bytes) in
 // flight: 7 stages for NTT = 1, 6, 5 and 4 for NTT = 4.
-// XQ (MXFP8 activations): token rows of 64 E4M3 bytes plus their two
-// blocks' scale bytes for all 128 rows (256 bytes).
-template <int NTT, bool XQ = false> struct Ring {
-    static constexpr int x_bytes = 32 * NTT * (XQ ? 64 : 128);  // token rows x 64 elements
+// XQ = 8 or 4 (MXFP8 or MXFP4 activations): token rows of 64 E4M3 bytes
+// or 32 E2M1 bytes, plus their two blocks' scale bytes for all 128 rows
+// (256 bytes); XQ = 0: bf16 token rows.
+template <int NTT, int XQ = 0> struct Ring {
+    static constexpr int x_bytes = 32 * NTT * (XQ == 8 ? 64 : XQ == 4 ? 32 : 128);  // token rows x 64 elements
     static constexpr int stage = kStageW + kStageS + x_bytes + (XQ ? 256 : 0);
     static constexpr int count = kLdsBytes / stage;
     static_assert(count >= 4 && count <= 8, "ring depth");
@@ -110,13 +111,15 @@ __device__ __forceinline__ int xswz(int row, int chunk) { return row * 128 + ((c
 // The same for E4M3 token rows (64 B, chunks 0..3): chunk ^ (row / 4) mod 4
 // puts 16 consecutive rows at one logical chunk in 16 distinct bank groups.
 __device__ __forceinline__ int xswz8(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4); }
+// And for E2M1 token rows (32 B, chunks 0..1): chunk ^ (row / 8) mod 2.
+__device__ __forceinline__ int xswz4(int row, int chunk) { return row * 32 + ((chunk ^ ((row >> 3) & 1)) << 4); }
 
 // One work unit (see Schedule above) on the workgroup's LDS ring `lds`.
 // CHAIN (both projections in one launch): a gate/up unit stores act with
 // device-scope stores and then raises flag `unit`; a down unit first waits
 // for the flags of every gate/up unit of its m-tile, then reads act with
 // device-scope loads (chain.hpp).
-template <int MODE, bool CHAIN, bool XQ = false>
+template <int MODE, bool CHAIN, int XQ = 0>
 __device__ __forceinline__ void grouped_unit(const FfnArgs& a, int unit, unsigned long long tag, uint8_t* lds) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -270,13 +273,20 @@ __device__ __forceinline__ void grouped_unit(const FfnArgs& a, int unit, unsigne
         ssrc = wscales(mat) + slot_s + blk * 64 + 16 * (lane & 1);
     }
     const uint16_t* xsrc[2];     // token row 16w + 8i + (lane >> 3), global chunk for LDS chunk lane & 7
-    const uint8_t* qsrc = nullptr;   // XQ: E4M3 token row 16w + (lane >> 2), global chunk for LDS chunk lane & 3
+    const uint8_t* qsrc = nullptr;   // XQ = 8: E4M3 token row 16w + (lane >> 2), global chunk for LDS chunk lane & 3;
+                                     // XQ = 4: E2M1 token row 32w + (lane >> 1), global chunk for LDS chunk lane & 1
     const uint8_t* qssrc = nullptr;  // XQ, wave 1, lanes 0..15: scale bytes of rows r_base + 16 (lane & 7) .. +16, block lane >> 3
-    if constexpr (XQ) {
+    if constexpr (XQ == 8) {
         const int row = 16 * wave + (lane >> 2);
         const int rr = r_base + (row < nvalid ? row : 0);
         qsrc = (MODE == 0 ? a.xq + static_cast<size_t>(rr) * a.d : a.aq + static_cast<size_t>(rr) * a.f) +
                (((lane & 3) ^ ((row >> 2) & 3)) << 4);
+        qssrc = (MODE == 0 ? a.xs : a.as) + static_cast<size_t>(lane >> 3 & 1) * a.rpad + r_base + 16 * (lane & 7);
+    } else if constexpr (XQ == 4) {
+        const int row = 32 * wave + (lane >> 1);
+        const int rr = r_base + (row < nvalid ? row : 0);
+        qsrc = (MODE == 0 ? a.xq + static_cast<size_t>(rr) * (a.d / 2) : a.aq + static_cast<size_t>(rr) * (a.f / 2)) +
+               (((lane & 1) ^ ((row >> 3) & 1)) << 4);
         qssrc = (MODE == 0 ? a.xs : a.as) + static_cast<size_t>(lane >> 3 & 1) * a.rpad + r_base + 16 * (lane & 7);
     } else {
 #pragma unroll
@@ -291,7 +301,7 @@ __device__ __forceinline__ void grouped_unit(const FfnArgs& a, int unit, unsigne
     // Token rows at or past 32 * (live column tiles) are never read: the waves
     // that own them (rows 16w .. 16w+15) copy no token rows at all.
     const int ntt = __builtin_amdgcn_readfirstlane(ceil_div(nvalid, 32));
-    const bool x_live = 16 * wave < 32 * ntt;
+    const bool x_live = XQ == 4 ? wave < ntt : 16 * wave < 32 * ntt;   // E2M1: a wave copies 32 rows
     // stage s of a ring of NST stages of SB bytes -> LDS buffer s % NST
     auto issue = [&](int s, auto nst_c, auto sb_c) {
         constexpr int NST = decltype(nst_c)::value, SB = decltype(sb_c)::value;
@@ -305,9 +315,9 @@ __device__ __forceinline__ void grouped_unit(const FfnArgs& a, int unit, unsigne
                                              (lds_void*)(base + kStageW), 16, 0, 0);
         if constexpr (XQ) {
             constexpr int XB = SB - kStageW - kStageS - 256;        // token rows of the stage
-            if (x_live)
-                __builtin_amdgcn_global_load_lds(qsrc + s * kGK, (lds_void*)(base + kStageW + kStageS + 16 * wave * 64), 16,
-                                                 0, CHAIN && MODE == 1 ? kAuxDevice : 0);
+            if (x_live)         // 1 KB: 16 E4M3 rows or 32 E2M1 rows
+                __builtin_amdgcn_global_load_lds(qsrc + s * (kGK * XQ / 8), (lds_void*)(base + kStageW + kStageS + 1024 * wave),
+                                                 16, 0, CHAIN && MODE == 1 ? kAuxDevice : 0);
             if (wave == 1 && lane < 16)   // both K blocks' scale bytes of all 128 rows
                 __builtin_amdgcn_global_load_lds(qssrc + static_cast<size_t>(2 * s) * a.rpad,
                                                  (lds_void*)(base + kStageW + kStageS + XB), 16, 0,
@@ -345,9 +355,13 @@ __device__ __forceinline__ void grouped_unit(const FfnArgs& a, int unit, unsigne
             // stage s is in LDS once at most the younger stages issued so far
             // (up to NST - 2) are in flight; each wave counts its own loads
             const int younger = min(NST - 2, S - 1 - s);
-            if constexpr (XQ) {          // waves 0 and 1 always hold live rows
+            if constexpr (XQ == 8) {     // waves 0 and 1 always hold live rows
                 if (wave <= 1) wait_stages<4, NST - 2>(younger);
                 else if (x_live) wait_stages<3, NST - 2>(younger);
+                else wait_stages<2, NST - 2>(younger);
+            } else if constexpr (XQ == 4) {   // wave 0 always holds live rows
+                if (wave == 0 || (wave == 1 && x_live)) wait_stages<4, NST - 2>(younger);
+                else if (wave == 1 || x_live) wait_stages<3, NST - 2>(younger);
                 else wait_stages<2, NST - 2>(younger);
             } else if (wave == 0) {
                 if (x_live) wait_stages<5, NST - 2>(younger);
@@ -370,7 +384,24 @@ __device__ __forceinline__ void grouped_unit(const FfnArgs& a, int unit, unsigne
             const u32x4 c0 = *reinterpret_cast<const u32x4*>(wb + pc0 * 16);
             const u32x4 c1 = *reinterpret_cast<const u32x4*>(wb + pc1 * 16);
             const uint32_t sc0 = sb[pc0], sc1 = sb[pc1];
-            if constexpr (XQ) {
+            if constexpr (XQ == 4) {
+                // fp4 x fp4: the token fragment is chunk h (K block h) of
+                // the E2M1 row, with that block's scale byte
+                const uint8_t* xsb = xb + 32 * NTT * 32;
+                u32x4 b[NTT];
+                int bs[NTT];
+#pragma unroll
+                for (int t = 0; t < NTT; ++t) {
+                    b[t] = *reinterpret_cast<const u32x4*>(xb + xswz4(32 * t + r32, h));
+                    bs[t] = xsb[128 * h + 32 * t + r32];
+                }
+#pragma unroll
+                for (int t = 0; t < NTT; ++t) {
+                    acc[0][t] = mfma_scale_fp4_fp4(c0, b[t], acc[0][t], static_cast<int>(sc0), bs[t]);
+                    acc[1][t] = mfma_scale_fp4_fp4(c1, b[t], acc[1][t], static_cast<int>(sc1), bs[t]);
+                }
+                continue;
+            } else if constexpr (XQ == 8) {
                 // one block-scaled 32x32x64 product per (weight tile, column
                 // tile): the pieces and their E8M0 bytes go in as they are,
                 // the token fragment is chunks h and 2 + h of the E4M3 row
@@ -430,7 +461,53 @@ __device__ __forceinline__ void grouped_unit(const FfnArgs& a, int unit, unsigne
 
     // ---- epilogue.  Lane l holds, for element i, weight row
     // 8*(i/4) + 4*(l/32) + i%4 of the 32-row tile and token row l%32.
-    if constexpr (XQ && MODE == 0) {
+    if constexpr (XQ == 4 && MODE == 0) {
+        // act to MXFP4: a wave's 32 gate rows of one token are one block of
+        // 32 act columns, 16 values in lane l and 16 in lane l ^ 32; the
+        // block's 16 code bytes are written as two 8-byte halves, lane l
+        // (h = 0) the first, lane l ^ 32 the second, after one exchange
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            if (t >= ntt) continue;
+            float v[16];
+            float amax = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                v[i] = silu_mul(acc[0][t][i], acc[1][t][i]);
+                amax = fmaxf(amax, fabsf(v[i]));
+            }
+            amax = fmaxf(amax, __shfl_xor(amax, 32));
+            const int sbyte = mx4_scale_byte(amax);
+            // columns 8q + 4h .. +3 of the block: nibbles of bytes 4q + 2h, 4q + 2h + 1
+            uint32_t half[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int sh = 127 - sbyte;
+                half[q] = e2m1_rne_sat(ldexpf(v[4 * q], sh)) | (e2m1_rne_sat(ldexpf(v[4 * q + 1], sh)) << 4) |
+                          (e2m1_rne_sat(ldexpf(v[4 * q + 2], sh)) << 8) | (e2m1_rne_sat(ldexpf(v[4 * q + 3], sh)) << 12);
+            }
+            const uint32_t send = h ? (half[0] | (half[1] << 16)) : (half[2] | (half[3] << 16));
+            const uint32_t recv = static_cast<uint32_t>(__shfl_xor(static_cast<int>(send), 32));
+            const int j = 32 * t + r32;
+            if (j >= nvalid) continue;
+            const uint32_t w0 = h ? ((recv & 0xFFFFu) | (half[2] << 16)) : (half[0] | (recv << 16));
+            const uint32_t w1 = h ? ((recv >> 16) | (half[3] << 16)) : (half[1] | (recv & 0xFFFF0000u));
+            const size_t r = static_cast<size_t>(r_base + j);
+            unsigned long long* dst = reinterpret_cast<unsigned long long*>(
+                a.aq + r * (a.f / 2) + (nt * (kGN / 2) + 32 * wave) / 2 + 8 * h);
+            const unsigned long long word = static_cast<unsigned long long>(w0) | (static_cast<unsigned long long>(w1) << 32);
+            if constexpr (CHAIN) __hip_atomic_store(dst, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            else *dst = word;
+            if (h == 0) {
+                uint8_t* ds = a.as + static_cast<size_t>(nt * (kGN / 64) + wave) * a.rpad + r;
+                if constexpr (CHAIN) __hip_atomic_store(ds, static_cast<uint8_t>(sbyte), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                else *ds = static_cast<uint8_t>(sbyte);
+            }
+        }
+        if constexpr (CHAIN) raise_flag(a.flags + unit, tag);
+        return;
+    }
+    if constexpr (XQ == 8 && MODE == 0) {
         // act to MXFP8: a wave's 32 gate rows of one token are one block of
         // 32 act columns, 16 values in lane l and 16 in lane l ^ 32
 #pragma unroll
@@ -528,7 +605,7 @@ __global__ void zero_tail_rows_kernel(FfnArgs a) { zero_tail_rows(a, blockIdx.x,
 // units, chain.hpp), the last one zeroes the y rows past offsets[E].  The
 // down units thus fill the CUs that the gate/up launch's last, uneven units
 // leave idle, instead of waiting for all of them behind a kernel boundary.
-template <bool XQ>
+template <int XQ>
 __global__ __launch_bounds__(kGThreads) void ffn_grouped_chained_kernel(FfnArgs a, int ub0, int ub1) {
     __shared__ __align__(16) uint8_t lds[kLdsAlloc];
     const unsigned long long tag = chain_tag();
@@ -555,7 +632,7 @@ hipError_t launch_ffn_grouped(const moe_shape& s, const FfnArgs& a, hipStream_t 
     const int units0 = max_mtiles(s, a.has_shared) * (s.f / (kGN / 2));
     const int units1 = max_mtiles(s, a.has_shared) * (s.d / kGN);
     if (a.flags) {
-        ffn_grouped_chained_kernel<false><<<units0 + units1 + 1, kGThreads, 0, st>>>(a, units0, units1);
+        ffn_grouped_chained_kernel<0><<<units0 + units1 + 1, kGThreads, 0, st>>>(a, units0, units1);
         return hipGetLastError();
     }
     ffn_grouped_kernel<0><<<units0, kGThreads, 0, st>>>(a);
@@ -568,11 +645,15 @@ hipError_t launch_ffn_grouped(const moe_shape& s, const FfnArgs& a, hipStream_t 
     return hipGetLastError();
 }
 
-// MXFP8 token rows in sorted-row order: row r is token perm[r] / k; one
-// thread per block of 32 elements (E8M0 scale of the block maximum, E4M3
-// elements rounded to nearest even and saturated at 448).  xs is block-major,
-// [d/32][rpad], so an m-tile's scale bytes of one block are contiguous.
-__global__ __launch_bounds__(256) void mx8_gather_quant_kernel(const uint16_t* __restrict__ x,
+// MXFP8 (BITS = 8) or MXFP4 (BITS = 4) token rows in sorted-row order: row
+// r is token perm[r] / k; one thread per block of 32 elements (E8M0 scale
+// of the block maximum; E4M3 elements rounded to nearest even and
+// saturated at 448, or E2M1 elements rounded to nearest even and clamped
+// at 6, two per byte, the even element in the low nibble).  xs is
+// block-major, [d/32][rpad], so an m-tile's scale bytes of one block are
+// contiguous.
+template <int BITS>
+__global__ __launch_bounds__(256) void mxq_gather_quant_kernel(const uint16_t* __restrict__ x,
                                                              const int32_t* __restrict__ perm, int k, int d, int R,
                                                              int rpad, uint8_t* __restrict__ xq,
                                                              uint8_t* __restrict__ xs) {
@@ -595,32 +676,51 @@ __global__ __launch_bounds__(256) void mx8_gather_quant_kernel(const uint16_t* _
     }
 #pragma unroll
     for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(v[e]));
-    const int sbyte = mx8_scale_byte(amax);
-    u32x4 out[2];
+    if constexpr (BITS == 8) {
+        const int sbyte = mx8_scale_byte(amax);
+        u32x4 out[2];
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int sh = 127 - sbyte;
+                const float* vv = v + 16 * c + 4 * e;
+                out[c][e] = e4m3x4_rne_sat(ldexpf(vv[0], sh), ldexpf(vv[1], sh), ldexpf(vv[2], sh), ldexpf(vv[3], sh));
+            }
+        u32x4* dst = reinterpret_cast<u32x4*>(xq + static_cast<size_t>(r) * d + 32 * b);
+        dst[0] = out[0];
+        dst[1] = out[1];
+        xs[static_cast<size_t>(b) * rpad + r] = static_cast<uint8_t>(sbyte);
+    } else {
+        const int sbyte = mx4_scale_byte(amax);
+        const int sh = 127 - sbyte;
+        u32x4 out;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int sh = 127 - sbyte;
-            const float* vv = v + 16 * c + 4 * e;
-            out[c][e] = e4m3x4_rne_sat(ldexpf(vv[0], sh), ldexpf(vv[1], sh), ldexpf(vv[2], sh), ldexpf(vv[3], sh));
+            uint32_t w = 0;
+#pragma unroll
+            for (int n = 0; n < 8; ++n) w |= e2m1_rne_sat(ldexpf(v[8 * e + n], sh)) << (4 * n);
+            out[e] = w;
         }
-    u32x4* dst = reinterpret_cast<u32x4*>(xq + static_cast<size_t>(r) * d + 32 * b);
-    dst[0] = out[0];
-    dst[1] = out[1];
-    xs[static_cast<size_t>(b) * rpad + r] = static_cast<uint8_t>(sbyte);
+        *reinterpret_cast<u32x4*>(xq + static_cast<size_t>(r) * (d / 2) + 16 * b) = out;
+        xs[static_cast<size_t>(b) * rpad + r] = static_cast<uint8_t>(sbyte);
+    }
 }
 
-hipError_t launch_ffn_mx8(const moe_shape& s, const FfnArgs& a, hipStream_t st) {
+hipError_t launch_ffn_mxq(const moe_shape& s, const FfnArgs& a, int bits, hipStream_t st) {
     const int R = s.T * s.k;
     const long long n = static_cast<long long>(R) * (s.d / 32);
-    mx8_gather_quant_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, st>>>(
-        a.x, a.perm, s.k, s.d, R, a.rpad, const_cast<uint8_t*>(a.xq), const_cast<uint8_t*>(a.xs));
+    const unsigned grid = static_cast<unsigned>((n + 255) / 256);
+    uint8_t* xq = const_cast<uint8_t*>(a.xq);
+    uint8_t* xs = const_cast<uint8_t*>(a.xs);
+    if (bits == 8) mxq_gather_quant_kernel<8><<<grid, 256, 0, st>>>(a.x, a.perm, s.k, s.d, R, a.rpad, xq, xs);
+    else mxq_gather_quant_kernel<4><<<grid, 256, 0, st>>>(a.x, a.perm, s.k, s.d, R, a.rpad, xq, xs);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int units0 = max_mtiles(s, false) * (s.f / (kGN / 2));
     const int units1 = max_mtiles(s, false) * (s.d / kGN);
-    ffn_grouped_chained_kernel<true><<<units0 + units1 + 1, kGThreads, 0, st>>>(a, units0, units1);
+    if (bits == 8) ffn_grouped_chained_kernel<8><<<units0 + units1 + 1, kGThreads, 0, st>>>(a, units0, units1);
+    else ffn_grouped_chained_kernel<4><<<units0 + units1 + 1, kGThreads, 0, st>>>(a, units0, units1);
     return hipGetLastError();
 }
 

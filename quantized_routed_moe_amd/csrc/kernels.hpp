@@ -86,8 +86,9 @@ bool routed_ffn_supported(const moe_shape& s, int fmt);
 hipError_t launch_ffn_routed(const moe_shape& s, int fmt, const FfnArgs& a, hipStream_t st);
 hipError_t launch_ffn_grouped(const moe_shape& s, const FfnArgs& a, hipStream_t st);
 // MXFP8 activations: gather + quantise the token rows into a.xq / a.xs, then
-// the single-launch grouped FFN on the block-scaled fp4 x fp8 matrix cores.
-hipError_t launch_ffn_mx8(const moe_shape& s, const FfnArgs& a, hipStream_t st);
+// the single-launch grouped FFN on the block-scaled fp4 x fp8 (bits = 8) or
+// fp4 x fp4 (bits = 4) matrix cores.
+hipError_t launch_ffn_mxq(const moe_shape& s, const FfnArgs& a, int bits, hipStream_t st);
 // Ready flags the grouped FFN needs in the workspace (0: none).
 int grouped_flag_count(const moe_shape& s, bool shared = false);
 // shared: out[t] also adds y[T*k + t] (weight 1) after the routed terms.

@@ -61,7 +61,7 @@ __global__ __launch_bounds__(256) void peak_mfma_kernel(int iters, float* __rest
 #pragma unroll
             for (int c = 0; c < 8; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
         }
-    } else {
+    } else if constexpr (KIND == 1) {
         const u32x4 a = {0x22222222u ^ static_cast<uint32_t>(lane), 0x12121212u, 0x21212121u, 0x11111111u};
         i32x8 b;
 #pragma unroll
@@ -69,6 +69,13 @@ __global__ __launch_bounds__(256) void peak_mfma_kernel(int iters, float* __rest
         for (int it = 0; it < iters; ++it) {
 #pragma unroll
             for (int c = 0; c < 8; ++c) acc[c] = mfma_scale_fp4_fp8(a, b, acc[c], 127, 127);
+        }
+    } else {
+        const u32x4 a = {0x22222222u ^ static_cast<uint32_t>(lane), 0x12121212u, 0x21212121u, 0x11111111u};
+        const u32x4 b = {0x11111111u, 0x21212121u ^ static_cast<uint32_t>(lane), 0x12121212u, 0x22222222u};
+        for (int it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) acc[c] = mfma_scale_fp4_fp4(a, b, acc[c], 127, 127);
         }
     }
     float s = 0.f;
@@ -95,11 +102,12 @@ int moe_peak_stream(const void* buf, size_t bytes, int32_t workgroups, uint32_t*
 
 int moe_peak_mfma(int32_t kind, int32_t iters, int32_t workgroups, float* sink, hipStream_t stream) {
     if (!sink) return MOE_ERR_NULL;
-    if ((kind != 0 && kind != 1) || iters < 1 || workgroups < 0) return MOE_ERR_SHAPE;
+    if (kind < 0 || kind > 2 || iters < 1 || workgroups < 0) return MOE_ERR_SHAPE;
     if (reinterpret_cast<uintptr_t>(sink) % 4) return MOE_ERR_ALIGN;
     const int g = workgroups ? workgroups : 1024;
     if (kind == 0) qrmoe::peak_mfma_kernel<0><<<g, 256, 0, stream>>>(iters, sink);
-    else qrmoe::peak_mfma_kernel<1><<<g, 256, 0, stream>>>(iters, sink);
+    else if (kind == 1) qrmoe::peak_mfma_kernel<1><<<g, 256, 0, stream>>>(iters, sink);
+    else qrmoe::peak_mfma_kernel<2><<<g, 256, 0, stream>>>(iters, sink);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

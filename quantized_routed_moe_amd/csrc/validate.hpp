@@ -90,14 +90,16 @@ inline int check_dispatch_args(const moe_shape& s, const int32_t* ids, const int
     return MOE_OK;
 }
 
+// need: the FFN workspace the call uses (the bf16 FFN's by default; the
+// quantised-activation calls pass their own, smaller for MXFP4)
 inline int check_ffn_args(const moe_shape& s, const uint16_t* x, const moe_experts* ex, const int32_t* offsets,
-                          const int32_t* perm, const float* y, const void* ws, size_t ws_bytes) {
+                          const int32_t* perm, const float* y, const void* ws, size_t ws_bytes, size_t need = 0) {
     if (!x || !offsets || !perm || !y || !ws) return MOE_ERR_NULL;
     int rc = check_experts(s, ex);
     if (rc != MOE_OK) return rc;
     if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ws, 16)) return MOE_ERR_ALIGN;
     if (!aligned(offsets, 4) || !aligned(perm, 4)) return MOE_ERR_ALIGN;
-    if (ws_bytes < ffn_ws_bytes(s)) return MOE_ERR_WORKSPACE;
+    if (ws_bytes < (need ? need : ffn_ws_bytes(s))) return MOE_ERR_WORKSPACE;
     return MOE_OK;
 }
 

@@ -48,32 +48,33 @@ inline LayerCarve layer_carve(const moe_shape& s, bool shared = false) {
     return c;
 }
 
-// MXFP8 activations (moe_expert_ffn_mx8): header, act codes u8 [R][f], act
-// scales [f/32][R + 128], the ready flags, token codes u8 [R][d], token
-// scales [d/32][R + 128] (R = T*k).
-struct Mx8Carve {
+// MXFP8 or MXFP4 activations (moe_expert_ffn_mx8 / _mx4; bits = 8 or 4):
+// header, act codes [R][f * bits / 8], act scales [f/32][R + 128], the ready
+// flags, token codes [R][d * bits / 8], token scales [d/32][R + 128]
+// (R = T*k).
+struct MxqCarve {
     size_t aq, as, flags, xq, xs, total;
     int rpad;
 };
 
-inline Mx8Carve mx8_carve(const moe_shape& s) {
-    Mx8Carve c;
+inline MxqCarve mxq_carve(const moe_shape& s, int bits) {
+    MxqCarve c;
     const size_t R = static_cast<size_t>(s.T) * s.k;
     c.rpad = static_cast<int>(R) + 128;
     c.aq = kHeader;
-    c.as = c.aq + align256(R * s.f);
+    c.as = c.aq + align256(R * s.f * bits / 8);
     c.flags = c.as + align256(static_cast<size_t>(s.f / 32) * c.rpad);
     c.xq = c.flags + flag_bytes(s);
-    c.xs = c.xq + align256(R * s.d);
+    c.xs = c.xq + align256(R * s.d * bits / 8);
     c.total = c.xs + align256(static_cast<size_t>(s.d / 32) * c.rpad);
     return c;
 }
 
-// moe_layer_mx8: the MXFP8 FFN workspace, then offsets, perm, inv and y.
-inline LayerCarve layer_carve_mx8(const moe_shape& s) {
+// moe_layer_mx8 / _mx4: the FFN workspace above, then offsets, perm, inv and y.
+inline LayerCarve layer_carve_mxq(const moe_shape& s, int bits) {
     LayerCarve c;
     const size_t pairs = static_cast<size_t>(s.T) * s.k;
-    c.offsets = mx8_carve(s).total;
+    c.offsets = mxq_carve(s, bits).total;
     c.perm = c.offsets + align256(static_cast<size_t>(s.E + 1) * 4);
     c.inv = c.perm + align256(pairs * 4);
     c.y = c.inv + align256(pairs * 4);

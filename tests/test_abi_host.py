@@ -241,28 +241,34 @@ def test_layer_shared_validation():
     assert call(qm.moe_experts(mat(), mat(), mat(), None, 1), ws=A16 + 8) == qm.MOE_ERR_ALIGN
 
 
-def test_mx8_validation():
-    """The MXFP8-activation entry points reject what they cannot run before
-    any HIP call: other formats or shapes the grouped FFN does not take,
-    short workspaces, invalid shapes."""
+@pytest.mark.parametrize("bits", [8, 4])
+def test_mx_validation(bits):
+    """The MXFP8- and MXFP4-activation entry points reject what they cannot
+    run before any HIP call: other formats or shapes the grouped FFN does
+    not take, short workspaces, invalid shapes."""
     L = qm.lib()
+    ws_fn = getattr(L, f"moe_workspace_bytes_mx{bits}")
     s = _shape(T=64, d=512, E=8, k=2, f=256)
-    need = L.moe_workspace_bytes_mx8(ctypes.byref(s))
-    assert need > L.moe_workspace_bytes(ctypes.byref(s))       # plus the quantised token rows
-    assert L.moe_layer_mx8_workspace_bytes(ctypes.byref(s)) > need
-    assert L.moe_workspace_bytes_mx8(ctypes.byref(_shape(k=0))) == 0
+    need = ws_fn(ctypes.byref(s))
+    R = 64 * 2
+    assert need >= 256 + R * (256 + 512) * bits // 8             # header, act and token codes at least
+    assert getattr(L, f"moe_layer_mx{bits}_workspace_bytes")(ctypes.byref(s)) > need
+    assert ws_fn(ctypes.byref(_shape(k=0))) == 0
+    if bits == 4:                                               # half the code bytes of MXFP8
+        assert need < L.moe_workspace_bytes_mx8(ctypes.byref(s))
 
     def mat(fmt=qm.MOE_FMT_MXFP4):
         return qm.moe_qmat(fmt, qm.MOE_LAYOUT_TILES, A16, A16, None)
 
     def ffn(shape, fmt=qm.MOE_FMT_MXFP4, ws_bytes=need):
         ex = qm.moe_experts(mat(fmt), mat(fmt), mat(fmt), None, 8)
-        return L.moe_expert_ffn_mx8(ctypes.byref(shape), A16, ctypes.byref(ex), A16, A16, A16, A16, ws_bytes, None)
+        return getattr(L, f"moe_expert_ffn_mx{bits}")(ctypes.byref(shape), A16, ctypes.byref(ex), A16, A16, A16,
+                                                        A16, ws_bytes, None)
 
     assert ffn(s, qm.MOE_FMT_Q2G32) == qm.MOE_ERR_UNSUPPORTED
     assert ffn(s, qm.MOE_FMT_Q4G32) == qm.MOE_ERR_UNSUPPORTED
     s2 = _shape(T=64, d=256, E=8, k=2, f=256)                    # d not a multiple of 512
-    assert ffn(s2, ws_bytes=L.moe_workspace_bytes_mx8(ctypes.byref(s2))) == qm.MOE_ERR_UNSUPPORTED
+    assert ffn(s2, ws_bytes=ws_fn(ctypes.byref(s2))) == qm.MOE_ERR_UNSUPPORTED
     assert ffn(s, ws_bytes=need - 256) == qm.MOE_ERR_WORKSPACE
     assert ffn(_shape(T=64, d=512, E=8, k=9, f=256)) == qm.MOE_ERR_SHAPE
     assert ffn(_shape(T=0, d=512, E=8, k=2, f=256)) == qm.MOE_OK
@@ -279,6 +285,6 @@ def test_peak_kernels_validation():
     assert L.moe_peak_stream(A16, 1024, -1, A16, None) == qm.MOE_ERR_SHAPE
     assert L.moe_peak_stream(A16 + 8, 1024, 0, A16, None) == qm.MOE_ERR_ALIGN
     assert L.moe_peak_mfma(0, 10, 0, None, None) == qm.MOE_ERR_NULL
-    assert L.moe_peak_mfma(2, 10, 0, A16, None) == qm.MOE_ERR_SHAPE
+    assert L.moe_peak_mfma(3, 10, 0, A16, None) == qm.MOE_ERR_SHAPE
     assert L.moe_peak_mfma(0, 0, 0, A16, None) == qm.MOE_ERR_SHAPE
     assert L.moe_peak_mfma(1, 10, 0, A16 + 2, None) == qm.MOE_ERR_ALIGN

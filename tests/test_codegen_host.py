@@ -54,7 +54,7 @@ def test_grouped_k_loop_never_waits_for_every_copy(tmp_path):
     assert r.returncode == 0, r.stderr[-2000:]
     asm = out.read_text()
     kernels = re.findall(r"^(_ZN5qrmoe26ffn_grouped_chained_kernel\w+):", asm, re.M)
-    assert len(kernels) == 2, kernels                        # bf16 and MXFP8 operands
+    assert len(kernels) == 3, kernels                        # bf16, MXFP8 and MXFP4 operands
     for k in kernels:
         blocks = _mfma_blocks(asm, k)
         assert blocks, k
