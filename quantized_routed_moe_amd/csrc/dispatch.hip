@@ -5,10 +5,12 @@
 //
 // One workgroup of 1024 threads.  Pass 1 counts pairs per expert (LDS
 // integer atomics: the counts do not depend on their order).  An exclusive
-// scan gives offsets.  Pass 2 walks the pairs in tiles of 1024; inside a
-// wave, the lanes holding the same expert are found with seven ballots (one
-// per bit of the id), so a pair's rank among equal ids is a popcount over
-// lower lanes; per-wave totals are scanned across the 16 waves in LDS.
+// scan gives offsets.  Pass 2 walks the pairs in chunks of 4096, as 64
+// sub-tiles of 64 consecutive pairs (four per wave); inside a sub-tile, the
+// lanes holding the same expert are found with seven ballots (one per bit
+// of the id), so a pair's rank among equal ids is a popcount over lower
+// lanes; the per-sub-tile counts are scanned over the sub-tiles in LDS,
+// eight threads per expert, so a chunk takes four barriers.
 // Nothing depends on atomic ordering, so the permutation is deterministic
 // and stable.  Ids outside [0, E) go to an extra bucket E after all valid
 // pairs and raise MOE_DEV_BAD_EXPERT_ID.
