@@ -17,9 +17,7 @@ namespace {
 
 using qrmoe::FfnArgs;
 
-using qrmoe::act_bytes;
 using qrmoe::align256;
-using qrmoe::flag_bytes;
 using qrmoe::kHeader;
 using qrmoe::ffn_ws_bytes;
 using qrmoe::LayerCarve;
@@ -43,7 +41,7 @@ int do_dispatch(const moe_shape& s, const int32_t* ids, int32_t* offsets, int32_
 // layer: the one-call layer, in which an expert mapped to MOE_SLOT_SKIP
 // contributes zero (its y rows are zeroed); moe_expert_ffn leaves them alone.
 FfnArgs ffn_args(const moe_shape& s, const uint16_t* x, const moe_experts* ex, const int32_t* offsets,
-                 const int32_t* perm, float* y, void* ws, bool layer = false) {
+                 const int32_t* perm, float* y, void* ws, bool layer = false, bool shared = false) {
     FfnArgs a{};
     a.zero_skipped = layer;
     a.T = s.T; a.d = s.d; a.E = s.E; a.k = s.k; a.f = s.f;
@@ -58,9 +56,12 @@ FfnArgs ffn_args(const moe_shape& s, const uint16_t* x, const moe_experts* ex, c
         a.codes[i] = static_cast<const uint8_t*>(mats[i]->codes);
         a.scales[i] = static_cast<const uint8_t*>(mats[i]->scales);
     }
-    a.act = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + kHeader);
-    a.flags = flag_bytes(s) ? reinterpret_cast<unsigned long long*>(static_cast<char*>(ws) + kHeader + act_bytes(s))
-                            : nullptr;
+    char* base = static_cast<char*>(ws);
+    const qrmoe::FfnCarve c = qrmoe::ffn_carve(s, shared);
+    a.act = reinterpret_cast<uint16_t*>(base + c.act);
+    a.flags = c.flags ? reinterpret_cast<unsigned long long*>(base + c.flags) : nullptr;
+    a.xsum = c.xsum ? reinterpret_cast<uint32_t*>(base + c.xsum) : nullptr;
+    a.asum = c.asum ? reinterpret_cast<uint32_t*>(base + c.asum) : nullptr;
     a.y = y;
     a.status = static_cast<uint32_t*>(ws);
     a.header = static_cast<const uint32_t*>(ws);
@@ -441,9 +442,7 @@ int moe_layer_shared(const moe_shape* shape, const uint16_t* x, const float* w_r
                                                 stream, true))) != MOE_OK)
             return rc;
     }
-    FfnArgs a = ffn_args(s, x, experts, offsets, perm, y, ws, true);
-    a.flags = flag_bytes(s, true) ? reinterpret_cast<unsigned long long*>(base + kHeader + act_bytes(s, true))
-                                  : nullptr;
+    FfnArgs a = ffn_args(s, x, experts, offsets, perm, y, ws, true, true);
     set_shared(a);
     if ((rc = hip_rc(qrmoe::launch_ffn(s, fmt, a, stream))) != MOE_OK) return rc;
     return hip_rc(qrmoe::launch_combine(s, y, inv, topk_w, out, stream, true));

@@ -62,11 +62,11 @@
 
 #include "chain.hpp"
 #include "common.hpp"
+#include "grouped_sched.hpp"
 #include "kernels.hpp"
 
 namespace qrmoe {
 
-constexpr int kGM = 128;        // token rows per tile
 constexpr int kGN = 512;        // weight rows per tile
 constexpr int kGK = 64;         // K per step
 constexpr int kGWaves = 8;
@@ -75,10 +75,6 @@ constexpr int kStageW = kGN * 32;            // 32 tiles x 32 pieces x 16 B
 constexpr int kStageS = kGN * 2;             // 32 tiles x 32 scale bytes
 constexpr int kLdsBytes = 153600;            // the stage ring (of 160 KB per CU)
 constexpr int kLdsAlloc = kLdsBytes + 16;    // + one word past the ring (the hand-off verdict)
-// Dispatch order: full m-tiles per partial m-tile while both remain.  At the
-// prefill workload (24 full, 44 partial m-tiles) 2 measured 3-4 % faster per
-// FFN call than all full m-tiles first; 1 was 7 % slower, 3 and 4 about even.
-constexpr int kFullPerPart = 2;
 
 // Stage ring of a unit whose valid token rows fill NTT 32-row column tiles:
 // a stage holds the weights, their scales and only the 32*NTT token rows the
@@ -128,75 +124,10 @@ __device__ __forceinline__ void grouped_unit(const FfnArgs& a, int unit, unsigne
     const int NT = MODE == 0 ? a.f / (kGN / 2) : a.d / kGN;
     const int S = K / kGK;
 
-    // ---- schedule: expert / m-tile / n-tile of this workgroup.  Full
-    // 128-row m-tiles (expert-major; matrix-core bound) and partial m-tiles
-    // (at most one per expert, by decreasing row count, ties to the lower
-    // expert id; bound by streaming their weight tile) are dealt in groups
-    // of kFullPerPart full m-tiles and one partial while both kinds remain,
-    // then the rest in the same orders, n-tile fastest within an m-tile.  So
-    // HBM streaming overlaps the matrix-core work from the start, and the
-    // smallest partial m-tiles fill the end of the launch.
-    int cnt = 0;
-    if (lane < a.E) cnt = a.offsets[lane + 1] - a.offsets[lane];
-    const int full = cnt / kGM;          // full m-tiles of expert `lane`
-    const int rem = cnt % kGM;           // rows of its partial m-tile (0: none)
-    int incl = full;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int v = __shfl_up(incl, o);
-        if (lane >= o) incl += v;
-    }
-    const int n_full = lane_value(incl, 63);
-    const uint64_t has_part = __ballot(rem > 0);
-    // the shared expert's m-tiles (rows [T*k, T*k + T)) come first
-    const int n_sh = a.has_shared ? ceil_div(a.T, kGM) : 0;
-    const int total_units = (n_sh + n_full + __popcll(has_part)) * NT;
-    if (unit >= total_units) return;
-    int e, mti, nt;
-    // m-tile position p -> shared m-tile, full m-tile qi or partial m-tile qi
-    const int n_part = __popcll(has_part);
-    const int p = unit / NT - n_sh;
-    nt = unit % NT;
-    const int groups = min(n_full / kFullPerPart, n_part);
-    bool is_full;
-    int qi;
-    if (p < 0) {
-        e = a.E;
-        mti = p + n_sh;
-        is_full = true;
-        qi = 0;
-    } else if (p < groups * (kFullPerPart + 1)) {
-        const int gg = p / (kFullPerPart + 1), rr = p % (kFullPerPart + 1);
-        is_full = rr < kFullPerPart;
-        qi = is_full ? gg * kFullPerPart + rr : gg;
-    } else {
-        const int p2 = p - groups * (kFullPerPart + 1), rf = n_full - groups * kFullPerPart;
-        is_full = p2 < rf;
-        qi = is_full ? groups * kFullPerPart + p2 : groups + (p2 - rf);
-    }
-    if (p < 0) {
-        // shared m-tile: e and mti set above
-    } else if (is_full) {
-        const int q = qi;
-        const int excl = incl - full;
-        const uint64_t below = __ballot(full > 0 && excl <= q);
-        e = 63 - __clzll(static_cast<long long>(below));
-        mti = q - lane_value(excl, e);
-    } else {
-        const int q = qi;
-        int rank = 0;                    // partial tiles longer than this lane's, or as long with a lower id
-        for (int j = 0; j < 64; ++j) {
-            const int rj = lane_value(rem, j);
-            rank += (rj > rem) || (rj == rem && j < lane);
-        }
-        const uint64_t hit = __ballot(rem > 0 && rank == q);
-        e = __ffsll(static_cast<unsigned long long>(hit)) - 1;
-        mti = lane_value(full, e);
-    }
-    const bool sh = e == a.E;
-    const int r_base = (sh ? a.T * a.k : a.offsets[e]) + mti * kGM;
-    const int nvalid = min(kGM, (sh ? a.T * a.k + a.T : a.offsets[e + 1]) - r_base);
-    const int slot = sh ? 0 : a.slot_of_expert ? a.slot_of_expert[e] : e;
+    GroupedUnit gu;
+    if (!grouped_unit_of(a, unit, NT, lane, gu)) return;
+    const int e = gu.e, mti = gu.mti, nt = gu.nt, r_base = gu.r_base, nvalid = gu.nvalid, slot = gu.slot;
+    const bool sh = gu.sh;
     // element-wise selects: choosing between the two pointer arrays would
     // put the kernel argument block in scratch memory
     auto wcodes = [&](int mat) { return sh ? a.sh_codes[mat] : a.codes[mat]; };
@@ -580,18 +511,6 @@ __device__ __forceinline__ void grouped_unit(const FfnArgs& a, int unit, unsigne
     if constexpr (CHAIN && MODE == 0) raise_flag(a.flags + unit, tag);
 }
 
-// Zeroes the y rows past offsets[E] (pairs with an invalid expert id); block
-// `blk` of `nblk` takes every nblk-th float4.
-__device__ __forceinline__ void zero_tail_rows(const FfnArgs& a, int blk, int nblk) {
-    const int r_lo = a.offsets[a.E], r_hi = a.T * a.k;
-    const int n4 = a.d / 4;
-    float4* base = reinterpret_cast<float4*>(a.y + static_cast<size_t>(r_lo) * a.d);
-    const long long total = static_cast<long long>(r_hi - r_lo) * n4;
-    for (long long i = blk * static_cast<long long>(blockDim.x) + threadIdx.x; i < total;
-         i += static_cast<long long>(nblk) * blockDim.x)
-        base[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-}
-
 template <int MODE>
 __global__ __launch_bounds__(kGThreads) void ffn_grouped_kernel(FfnArgs a) {
     __shared__ __align__(16) uint8_t lds[kLdsAlloc];
@@ -616,7 +535,8 @@ __global__ __launch_bounds__(kGThreads) void ffn_grouped_chained_kernel(FfnArgs 
 }
 
 bool grouped_supported(const moe_shape& s, int fmt) {
-    return fmt == MOE_FMT_MXFP4 && s.f % (kGN / 2) == 0 && s.d % kGN == 0;
+    return (fmt == MOE_FMT_MXFP4 || fmt == MOE_FMT_Q2G32 || fmt == MOE_FMT_Q4G32) && s.f % (kGN / 2) == 0 &&
+           s.d % kGN == 0;
 }
 
 static int max_mtiles(const moe_shape& s, bool shared) {

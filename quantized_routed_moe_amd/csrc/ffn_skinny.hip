@@ -510,6 +510,10 @@ bool ffn_uses_grouped(const moe_shape& s, int fmt) {
     return s.T * s.k >= kGroupedMinRows && grouped_supported(s, fmt);
 }
 
+bool grouped_shape(const moe_shape& s) {
+    return s.T * s.k >= kGroupedMinRows && grouped_supported(s, MOE_FMT_MXFP4);
+}
+
 bool routed_ffn_supported(const moe_shape& s, int fmt) {
     // one workgroup per (expert, tile) item, each routing the whole batch:
     // past a few tokens the items of inactive experts (which still route
@@ -530,7 +534,8 @@ hipError_t launch_ffn_routed(const moe_shape& s, int fmt, const FfnArgs& a, hipS
 }
 
 hipError_t launch_ffn(const moe_shape& s, int fmt, const FfnArgs& a, hipStream_t st) {
-    if (ffn_uses_grouped(s, fmt)) return launch_ffn_grouped(s, a, st);
+    if (ffn_uses_grouped(s, fmt))
+        return fmt == MOE_FMT_MXFP4 ? launch_ffn_grouped(s, a, st) : launch_ffn_grouped_q(s, fmt, a, st);
     return launch_two_fmt(s, fmt, a, st, false);
 }
 

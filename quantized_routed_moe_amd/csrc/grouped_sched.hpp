@@ -1,0 +1,118 @@
+// Work units of the single-launch grouped expert FFN (prefill chunks): which
+// expert, 128-row m-tile and n-tile a workgroup computes.  Shared by the
+// MXFP4 kernel (ffn_grouped.hip) and the 2-bit / 4-bit kernel
+// (ffn_grouped_q.hip), so that both deal the work out in the same order.
+//
+// Full 128-row m-tiles (expert-major; matrix-core bound) and partial m-tiles
+// (at most one per expert, by decreasing row count, ties to the lower expert
+// id; bound by streaming their weight tile) are dealt in groups of
+// kFullPerPart full m-tiles and one partial while both kinds remain, then the
+// rest in the same orders, n-tile fastest within an m-tile.  So HBM
+// streaming overlaps the matrix-core work from the start, and the smallest
+// partial m-tiles fill the end of the launch.  A shared expert's m-tiles
+// (rows [T*k, T*k + T)) come first.  Units are derived from offsets on the
+// device; every lane of the calling wave gets the same answer.
+#pragma once
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace qrmoe {
+
+constexpr int kGM = 128;        // token rows per m-tile
+// Dispatch order: full m-tiles per partial m-tile while both remain.  At the
+// prefill workload (24 full, 44 partial m-tiles) 2 measured 3-4 % faster per
+// FFN call than all full m-tiles first; 1 was 7 % slower, 3 and 4 about even.
+constexpr int kFullPerPart = 2;
+
+struct GroupedUnit {
+    int e;          // expert (E: the shared expert)
+    int mti;        // m-tile of the expert
+    int nt;         // n-tile
+    int r_base;     // first sorted row of the m-tile
+    int nvalid;     // its rows (1..128)
+    int slot;       // the expert's slot (slot_of_expert), unchecked
+    bool sh;        // the shared expert
+};
+
+// Unit `unit` of a projection with NT n-tiles; false past the last unit.
+__device__ __forceinline__ bool grouped_unit_of(const FfnArgs& a, int unit, int NT, int lane, GroupedUnit& u) {
+    int cnt = 0;
+    if (lane < a.E) cnt = a.offsets[lane + 1] - a.offsets[lane];
+    const int full = cnt / kGM;          // full m-tiles of expert `lane`
+    const int rem = cnt % kGM;           // rows of its partial m-tile (0: none)
+    int incl = full;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(incl, o);
+        if (lane >= o) incl += v;
+    }
+    const int n_full = lane_value(incl, 63);
+    const uint64_t has_part = __ballot(rem > 0);
+    const int n_sh = a.has_shared ? ceil_div(a.T, kGM) : 0;
+    const int total_units = (n_sh + n_full + __popcll(has_part)) * NT;
+    if (unit >= total_units) return false;
+    int e, mti, nt;
+    // m-tile position p -> shared m-tile, full m-tile qi or partial m-tile qi
+    const int n_part = __popcll(has_part);
+    const int p = unit / NT - n_sh;
+    nt = unit % NT;
+    const int groups = min(n_full / kFullPerPart, n_part);
+    bool is_full;
+    int qi;
+    if (p < 0) {
+        e = a.E;
+        mti = p + n_sh;
+        is_full = true;
+        qi = 0;
+    } else if (p < groups * (kFullPerPart + 1)) {
+        const int gg = p / (kFullPerPart + 1), rr = p % (kFullPerPart + 1);
+        is_full = rr < kFullPerPart;
+        qi = is_full ? gg * kFullPerPart + rr : gg;
+    } else {
+        const int p2 = p - groups * (kFullPerPart + 1), rf = n_full - groups * kFullPerPart;
+        is_full = p2 < rf;
+        qi = is_full ? groups * kFullPerPart + p2 : groups + (p2 - rf);
+    }
+    if (p < 0) {
+        // shared m-tile: e and mti set above
+    } else if (is_full) {
+        const int q = qi;
+        const int excl = incl - full;
+        const uint64_t below = __ballot(full > 0 && excl <= q);
+        e = 63 - __clzll(static_cast<long long>(below));
+        mti = q - lane_value(excl, e);
+    } else {
+        const int q = qi;
+        int rank = 0;                    // partial tiles longer than this lane's, or as long with a lower id
+        for (int j = 0; j < 64; ++j) {
+            const int rj = lane_value(rem, j);
+            rank += (rj > rem) || (rj == rem && j < lane);
+        }
+        const uint64_t hit = __ballot(rem > 0 && rank == q);
+        e = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+        mti = lane_value(full, e);
+    }
+    u.sh = e == a.E;
+    u.e = e;
+    u.mti = mti;
+    u.nt = nt;
+    u.r_base = (u.sh ? a.T * a.k : a.offsets[e]) + mti * kGM;
+    u.nvalid = min(kGM, (u.sh ? a.T * a.k + a.T : a.offsets[e + 1]) - u.r_base);
+    u.slot = u.sh ? 0 : a.slot_of_expert ? a.slot_of_expert[e] : e;
+    return true;
+}
+
+// Zeroes the y rows past offsets[E] (pairs with an invalid expert id); block
+// `blk` of `nblk` takes every nblk-th float4.
+__device__ __forceinline__ void zero_tail_rows(const FfnArgs& a, int blk, int nblk) {
+    const int r_lo = a.offsets[a.E], r_hi = a.T * a.k;
+    const int n4 = a.d / 4;
+    float4* base = reinterpret_cast<float4*>(a.y + static_cast<size_t>(r_lo) * a.d);
+    const long long total = static_cast<long long>(r_hi - r_lo) * n4;
+    for (long long i = blk * static_cast<long long>(blockDim.x) + threadIdx.x; i < total;
+         i += static_cast<long long>(nblk) * blockDim.x)
+        base[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+}  // namespace qrmoe

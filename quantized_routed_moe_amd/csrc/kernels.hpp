@@ -61,6 +61,13 @@ struct FfnArgs {
     uint8_t* aq;
     uint8_t* as;
     int rpad;
+    // 2-bit / 4-bit packs on the grouped path: per 32-element group, the sum
+    // of a row's input values as two fp16 halves (hi | lo << 16, hi + lo =
+    // the fp32 sum to 22 bits): xsum [T][d/32] of the token rows (written by
+    // a pass before the FFN launch), asum [rows][f/32] of the act rows
+    // (written by the gate/up tiles; workspace).
+    uint32_t* xsum;
+    uint32_t* asum;
 };
 
 hipError_t launch_route(const moe_shape& s, const uint16_t* x, const float* wr, const float* bias,
@@ -85,6 +92,13 @@ hipError_t launch_small_route(const moe_shape& s, const uint16_t* x, const float
 bool routed_ffn_supported(const moe_shape& s, int fmt);
 hipError_t launch_ffn_routed(const moe_shape& s, int fmt, const FfnArgs& a, hipStream_t st);
 hipError_t launch_ffn_grouped(const moe_shape& s, const FfnArgs& a, hipStream_t st);
+// The grouped FFN for the 2-bit and 4-bit packs (ffn_grouped_q.hip): the
+// token rows' group sums into a.xsum, then one launch of both projections.
+hipError_t launch_ffn_grouped_q(const moe_shape& s, int fmt, const FfnArgs& a, hipStream_t st);
+// Shapes that take the grouped path at all (any format): T*k rows enough
+// for it and d, f multiples of its tiles.  The workspace then also holds the
+// group sums of the 2-bit / 4-bit path.
+bool grouped_shape(const moe_shape& s);
 // MXFP8 activations: gather + quantise the token rows into a.xq / a.xs, then
 // the single-launch grouped FFN on the block-scaled fp4 x fp8 (bits = 8) or
 // fp4 x fp4 (bits = 4) matrix cores.

@@ -29,8 +29,34 @@ inline size_t flag_bytes(const moe_shape& s, bool shared = false) {
     return align256(static_cast<size_t>(grouped_flag_count(s, shared)) * 8);
 }
 
+// Group sums of the 2-bit / 4-bit grouped FFN (FfnArgs::xsum, ::asum): u32
+// [T][d/32] and [rows][f/32], after the flags; none where the grouped path
+// is never taken.
+inline size_t xsum_bytes(const moe_shape& s) {
+    return grouped_shape(s) ? align256(static_cast<size_t>(s.T) * (s.d / 32) * 4) : 0;
+}
+inline size_t asum_bytes(const moe_shape& s, bool shared = false) {
+    return grouped_shape(s) ? align256(ffn_rows(s, shared) * (s.f / 32) * 4) : 0;
+}
+
 inline size_t ffn_ws_bytes(const moe_shape& s, bool shared = false) {
-    return kHeader + act_bytes(s, shared) + flag_bytes(s, shared);
+    return kHeader + act_bytes(s, shared) + flag_bytes(s, shared) + xsum_bytes(s) + asum_bytes(s, shared);
+}
+
+// Byte offsets of the FFN workspace's arrays (0: not present).
+struct FfnCarve {
+    size_t act, flags, xsum, asum;
+};
+
+inline FfnCarve ffn_carve(const moe_shape& s, bool shared = false) {
+    FfnCarve c;
+    c.act = kHeader;
+    const size_t fl = c.act + act_bytes(s, shared);
+    c.flags = flag_bytes(s, shared) ? fl : 0;
+    const size_t xs = fl + flag_bytes(s, shared);
+    c.xsum = xsum_bytes(s) ? xs : 0;
+    c.asum = asum_bytes(s, shared) ? xs + xsum_bytes(s) : 0;
+    return c;
 }
 
 struct LayerCarve {

@@ -29,6 +29,7 @@ CASES = [
     ((16, 256, 16, 2, 128), "q2"),
     ((12, 256, 8, 3, 128), "mxfp4"),
     ((300, 512, 8, 2, 256), "mxfp4"),
+    ((300, 512, 8, 2, 256), "q2"),
 ]
 
 

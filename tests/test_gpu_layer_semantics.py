@@ -29,6 +29,7 @@ SKIP_CASES = [
     (6, 512, 8, 3, 256, "q2"),
     (24, 512, 16, 3, 256, "q4"),
     (300, 512, 8, 2, 256, "mxfp4"),
+    (300, 512, 8, 2, 256, "q2"),
 ]
 
 
@@ -64,7 +65,7 @@ def test_layer_skipped_expert_contributes_zero(T, d, E, k, f, fmt):
     assert np.array_equal(got[untouched], full.cpu().numpy()[untouched])
 
 
-@pytest.mark.parametrize("T,fmt", [(1, "mxfp4"), (16, "q2"), (5, "q4"), (300, "mxfp4")])
+@pytest.mark.parametrize("T,fmt", [(1, "mxfp4"), (16, "q2"), (5, "q4"), (300, "mxfp4"), (300, "q4")])
 def test_slab_pack_equals_separate_arrays(T, fmt):
     d, f, E = (4096, 2048, 64) if T < 300 else (512, 256, 8)
     case = synthetic.make_case(T, d, E, 2, f, fmt, seed=4500 + T, zipf=1.1)
@@ -77,13 +78,14 @@ def test_slab_pack_equals_separate_arrays(T, fmt):
         assert torch.equal(u, v), n
 
 
-def test_prefill_handoff_timeout_gives_nan_and_status():
+@pytest.mark.parametrize("fmt", ["mxfp4", "q2"])
+def test_prefill_handoff_timeout_gives_nan_and_status(fmt):
     """Workspace header word 32 = 1 makes every down tile of the single-launch
     grouped FFN give up at once: its y rows must be NaN (never a product of
     unfinished act rows), MOE_DEV_CHAIN_TIMEOUT raised, the checked layer
     raises, and a normal call on a fresh workspace is unaffected."""
-    case = synthetic.make_case(300, 512, 8, 2, 256, "mxfp4", seed=4600)
-    _say("forced prefill hand-off timeout: T=300 d=512 E=8 f=256")
+    case = synthetic.make_case(300, 512, 8, 2, 256, fmt, seed=4600)
+    _say(f"forced prefill hand-off timeout: T=300 d=512 E=8 f=256 {fmt}")
     dc = device_case(case)
     s = dc["shape"]
     T, E, k = s.T, s.E, s.k

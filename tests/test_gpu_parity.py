@@ -97,7 +97,7 @@ SHAPES = [
     (1, 32, 1, 1, 32),
     (64, 1024, 32, 2, 512),
     # T*k >= 256 with d % 512 == 0 and f % 256 == 0: the LDS-tiled grouped path
-    # (MXFP4); Q2 and Q4 take the skinny path at these sizes
+    # (ffn_grouped.hip for MXFP4, ffn_grouped_q.hip for Q2 and Q4)
     (300, 512, 8, 2, 256),
     (700, 1024, 16, 2, 512),
     (257, 512, 64, 4, 768),
@@ -133,8 +133,9 @@ def test_one_expert_takes_every_token():
     assert np.all(g["ids"][:, 0] == 5)
 
 
-def test_one_expert_takes_every_token_grouped():
-    base = synthetic.make_case(300, 512, 8, 2, 256, "mxfp4", seed=13)
+@pytest.mark.parametrize("fmt", ["mxfp4", "q2", "q4"])
+def test_one_expert_takes_every_token_grouped(fmt):
+    base = synthetic.make_case(300, 512, 8, 2, 256, fmt, seed=13)
     lg = np.random.default_rng(4).standard_normal((300, 8)).astype(np.float32)
     lg[:, 2] = 40.0
     case = _given(base, lg)

@@ -25,6 +25,8 @@ CASES = [
     (256, 4096, 16, 2, 2048, "mxfp4", 1.1),
     (300, 4096, 16, 2, 2048, "mxfp4", 1.1),
     (2048, 4096, 64, 2, 2048, "mxfp4", 1.1),    # the prefill chunk's shape and routing
+    (300, 4096, 16, 2, 2048, "q2", 1.1),        # the 2-bit / 4-bit grouped path
+    (2048, 4096, 64, 2, 2048, "q4", 1.1),
 ]
 
 
