@@ -296,6 +296,13 @@ __device__ __forceinline__ void grouped_q_unit(const FfnArgs& a, int unit, unsig
                     acc[m][t] = mfma16x16x16_f16(u32x2{xs, xs}, bm, acc[m][t]);
                 }
             }
+            // Per group: the products of token tile t are issued while the
+            // scaling of tile t - 1's products into the accumulators runs, so
+            // the matrix core and the vector ALU work side by side (the
+            // scheduling groups pin the pattern: one product, then the four
+            // multiply-adds of the previous tile's product with the same
+            // weight tile), and the token fragment of tile t + 1 is read
+            // from LDS one tile ahead.
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 bf16x8 wop[4];
@@ -305,16 +312,32 @@ __device__ __forceinline__ void grouped_q_unit(const FfnArgs& a, int unit, unsig
                     wop[m] = q_operand<FMT>(code[m], g, qmask);
                     ks[m] = kQStep<FMT> * fp16_to_f32(smw[m][g]);
                 }
+                auto xfrag = [&](int t) {
+                    return *reinterpret_cast<const bf16x8*>(b + R::xr + (16 * t + (lane & 15)) * 256 +
+                                                            (((4 * g + (lane >> 4)) ^ (lane & 15)) << 4));
+                };
+                bf16x8 xa = xfrag(0);
+                f32x4 cp[4];
 #pragma unroll
-                for (int t = 0; t < NTT; ++t) {
-                    const bf16x8 xa = *reinterpret_cast<const bf16x8*>(
-                        b + R::xr + (16 * t + (lane & 15)) * 256 + (((4 * g + (lane >> 4)) ^ (lane & 15)) << 4));
+                for (int t = 0; t <= NTT; ++t) {
+                    bf16x8 xn = xa;
+                    if (t + 1 < NTT) xn = xfrag(t + 1);
+                    f32x4 cc[4];
 #pragma unroll
                     for (int m = 0; m < 4; ++m) {
-                        const f32x4 c = mfma16x16x32(xa, wop[m], f32x4{0.f, 0.f, 0.f, 0.f});
+                        if (t < NTT) cc[m] = mfma16x16x32(xa, wop[m], f32x4{0.f, 0.f, 0.f, 0.f});
+                        if (t > 0) {
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) acc[m][t][i] = fmaf(ks[m], c[i], acc[m][t][i]);
+                            for (int i = 0; i < 4; ++i) acc[m][t - 1][i] = fmaf(ks[m], cp[m][i], acc[m][t - 1][i]);
+                        }
+                        if (t < NTT && t > 0) {
+                            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one product
+                            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // four multiply-adds
+                        }
                     }
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) cp[m] = cc[m];
+                    xa = xn;
                 }
             }
         }
