@@ -19,18 +19,19 @@ f=2048, MXFP4 experts; by default the same line also carries a `workloads`
 map with every quoted configuration (0-4: tiny, decode, verify, prefill,
 two-bit), each with its own value, roofline and oracle baseline, and
 `measured_peaks`: this box's cold HBM read stream, a decode-sized cold
-stream replayed from a HIP graph, and the dense bf16 and fp4 x fp8 matrix
-loops (include/moe_peak.h), against which every roofline also reports
-`frac_measured`.
+stream replayed from a HIP graph, and the dense bf16, fp4 x fp8 and
+fp4 x fp4 matrix loops (include/moe_peak.h), against which every roofline
+also reports `frac_measured`.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 0..6]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 0..8]
 
 Workloads 0-4 are the configurations the targets are quoted on; 5 and 6
 run the 4-bit group-asymmetric pack at 16 tokens and at 1 token, 7 and 8 the
 2-bit and 4-bit packs at the prefill chunk's size (2048 tokens).  --bank N
 runs the workload through an N-slot expert bank paged from pinned host
 memory instead (its own JSON line: paging included, PCIe roofline);
---shared adds an always-on shared expert (moe_layer_shared; its own JSON line).
+--shared adds an always-on shared expert (moe_layer_shared; its own JSON line);
+--mx8 / --mx4 run the prefill with MXFP8 / MXFP4 activations.
 """
 
 from __future__ import annotations
@@ -739,6 +740,8 @@ def run_workload(c, args, mx=0, peaks=None, cpu=True):
     roof["traffic_unit"] = "HBM bytes per call (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
     roof["kernel"] = (f"moe_expert_ffn_mx{mx} (token quantisation, then one launch of block-scaled fp4 x fp{mx} tiles)" if mx
                       else "moe_expert_ffn (one launch: gate/up + SwiGLU tiles, then down tiles)" if T * k >= 256 and w["fmt"] == "mxfp4"
+                      else "moe_expert_ffn (token group sums, then one launch: gate/up + SwiGLU tiles, then down tiles)"
+                      if T * k >= 256
                       else "moe_expert_ffn (gate/up + SwiGLU kernel, down kernel)")
     roof["algorithmic_bytes_per_launch"] = round(ffn_bytes)
     roof["algorithmic_flop_per_launch"] = round(flops)
