@@ -87,8 +87,9 @@ enum moe_device_status_bits {
                                   (its y rows then hold NaN, never a product of unfinished act rows) */
 };
 
-/* The single-launch prefill FFN (T*k >= 256 with MXFP4 experts, d % 512 == 0
-   and f % 256 == 0, and the MXFP8 entry points) hands act from its gate/up
+/* The single-launch prefill FFN (T*k >= 256 with d % 512 == 0 and
+   f % 256 == 0, every pack format, and the MXFP8 / MXFP4-activation entry
+   points) hands act from its gate/up
    tiles to its down tiles through ready flags with a bounded wait (about a
    third of a second).  A wait that gives up makes that tile's y rows NaN and
    raises MOE_DEV_CHAIN_TIMEOUT; a caller that must not consume such a
@@ -245,7 +246,12 @@ size_t moe_slab_layout(int32_t fmt, int32_t d, int32_t f, size_t* offsets);
    intermediate act[T*k][f], then, when f % 256 == 0, the ready flags of the
    single-launch prefill FFN: 8 bytes per 128-row m-tile and 256 rows of f,
    for the (T*k)/128 + min(E, T*k) m-tiles there can be, rounded up; every
-   launch writes a value of its own into them, so they never need clearing).
+   launch writes a value of its own into them, so they never need clearing;
+   then, for shapes that take that launch (T*k >= 256, d % 512 == 0,
+   f % 256 == 0), the per-32-element group sums the 2-bit and 4-bit packs'
+   launch uses for their min term: u32 [T][d/32] and [T*k][f/32], each word
+   the sum as two fp16 halves, so a group's sum must stay below 65504 in
+   magnitude -- beyond it the outputs become NaN, never finite and wrong).
    Returns 0 for an invalid shape.  The header must be zeroed once before
    first use (moe_workspace_init does it).  A workspace serves one call at a
    time: calls that overlap on one workspace race. */
