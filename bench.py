@@ -55,17 +55,19 @@ METRIC = "MoE layer tokens/s; decode weight-stream GB/s; prefill expert TFLOP/s"
 # HBM bytes per moe_expert_ffn call from rocprofv3 counter runs of the current
 # FFN kernels (--pmc FETCH_SIZE, then --pmc WRITE_SIZE, one dispatch each;
 # FETCH_SIZE x 2.0 and WRITE_SIZE x 1.0 KiB, the factors a plain 256 MiB copy
-# reads), summed over the kernels of the call.  Workloads 3 and 4 route a
+# reads), summed over the kernels of the call.  Workloads 3, 4, 7 and 8 route a
 # different number of experts each step: theirs is the average of the counted
 # steps.  Must be re-measured (or removed) whenever an FFN kernel changes.
 MEASURED_FFN_TRAFFIC = {
-    0: (2 * (209.0 + 112.6) + (2.0 + 8.0)) * 1024,
-    2: (2 * (18725.6 + 8930.0) + (40.0 + 160.0)) * 1024,
-    1: (2 * (13158.5 + 4436.2) + (8.0 + 32.0)) * 1024,
-    3: (2 * 469576.9 + 98466.6) * 1024,
-    4: (2 * (27874.1 + 14211.8) + (128.0 + 512.0)) * 1024,
-    5: (2 * (43130.4 + 19618.4) + (310.9 + 512.0)) * 1024,
-    6: (2 * (15475.2 + 5207.2) + (8.0 + 32.0)) * 1024,
+    0: (2 * (213.0 + 113.0) + (2.0 + 8.0)) * 1024,
+    1: (2 * (13158.0 + 4435.2) + (8.0 + 32.0)) * 1024,
+    2: (2 * (18726.6 + 8928.5) + (40.0 + 160.0)) * 1024,
+    3: (2 * 469613.7 + 98412.2) * 1024,
+    4: (2 * (27882.0 + 14209.4) + (310.9 + 512.0)) * 1024,
+    5: (2 * (43124.4 + 19622.7) + (310.9 + 512.0)) * 1024,
+    6: (2 * (15467.8 + 5203.2) + (8.0 + 32.0)) * 1024,
+    7: (2 * (8211.1 + 366012.1) + (1024.0 + 90128.4)) * 1024,
+    8: (2 * (8211.1 + 529100.3) + (1024.0 + 90129.3)) * 1024,
 }
 
 MX_BYTES_PER_EXPERT = lambda d, f: 3 * d * f // 2 + 3 * d * f // 32      # codes + e8m0 scales

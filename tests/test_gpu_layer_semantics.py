@@ -115,3 +115,24 @@ def test_prefill_handoff_timeout_gives_nan_and_status(fmt):
     r = ref.layer(case["x"], k, case["gate"], case["up"], case["down"], logits=lg.cpu().numpy())
     assert np.array_equal(ids2.cpu().numpy(), r["ids"])
     assert_close(out.cpu().numpy(), r["out"], "out after the forced timeout")
+
+
+def test_q_grouped_group_sum_out_of_range_gives_nan():
+    """The 2-bit / 4-bit grouped FFN keeps each group's input sum as two
+    fp16 halves: a token whose group sum exceeds fp16's range (here 32
+    elements of 4096 in one group) gets NaN in its output row, never a
+    finite wrong value; every other token still matches the oracle."""
+    case = synthetic.make_case(300, 512, 8, 2, 256, "q2", seed=4700)
+    x = case["x"].copy()
+    big = np.float32(4096.0).view(np.uint32) >> 16            # bf16 bits of 4096 (exact)
+    x[5, 64:96] = big
+    case["x"] = x
+    _say("2-bit grouped FFN, one group sum past fp16's range: T=300 d=512 E=8 f=256")
+    dc = device_case(case)
+    out, ids, w, lg = qm.layer(dc["x"], dc["experts"], 2, w_router=dc["w_router"], bias=dc["bias"])
+    out = out.cpu().numpy()
+    assert np.isnan(out[5]).all()
+    r = ref.layer(case["x"], 2, case["gate"], case["up"], case["down"], logits=lg.cpu().numpy())
+    keep = np.arange(300) != 5
+    assert np.array_equal(ids.cpu().numpy(), r["ids"])
+    assert_close(out[keep], r["out"][keep], "out of the other tokens")
