@@ -49,6 +49,7 @@ PAIRS = [
     ((5, 4096, 64, 2, 2048, "mxfp4"), (1, 4096, 64, 2, 2048, "mxfp4")),       # routed small batch
     ((300, 1024, 16, 2, 512, "mxfp4"), (40, 1024, 16, 3, 512, "mxfp4")),      # grouped, then combine kernel
     ((24, 512, 8, 4, 256, "q4"), (3, 512, 8, 4, 256, "q4")),
+    ((300, 1024, 16, 2, 512, "q2"), (140, 512, 8, 2, 256, "q4")),      # the 2-bit / 4-bit grouped launch
 ]
 
 
