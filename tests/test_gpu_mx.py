@@ -161,11 +161,12 @@ def test_mx_ffn_matches_oracle(T, d, E, k, f, zipf, bits):
 
 
 @pytest.mark.parametrize("bits", [8, 4])
-def test_mx_layer_equals_steps(bits):
-    case = synthetic.make_case(100, 1024, 16, 4, 512, "mxfp4", seed=9300, zipf=1.1)
+@pytest.mark.parametrize("T,k", [(100, 4), (300, 2)])
+def test_mx_layer_equals_steps(bits, T, k):
+    case = synthetic.make_case(T, 1024, 16, k, 512, "mxfp4", seed=9300 + T, zipf=1.1)
     dc, g = _run(case, bits)
     layer = qm.layer_mx8 if bits == 8 else qm.layer_mx4
-    out, ids, w, lg = layer(dc["x"], dc["experts"], 4, w_router=dc["w_router"], bias=dc["bias"])
+    out, ids, w, lg = layer(dc["x"], dc["experts"], k, w_router=dc["w_router"], bias=dc["bias"])
     assert np.array_equal(ids.cpu().numpy(), g["ids"])
     assert np.array_equal(out.cpu().numpy(), g["out"])
 
