@@ -523,9 +523,13 @@ int moe_layer_banked(const moe_shape* shape, const uint16_t* x, const float* w_r
 const char* moe_status_str(int status);
 
 /* Synchronises `stream`, then reads the workspace's device status word.
-   Returns MOE_OK, MOE_ERR_DEVICE (some bit set; *bits receives the word when
-   bits != NULL) or MOE_ERR_HIP.  The word stays set until moe_workspace_init. */
-int moe_read_device_status(const void* ws, uint32_t* bits, hipStream_t stream);
+   Returns MOE_OK, MOE_ERR_DEVICE (some bit set) or MOE_ERR_HIP;
+   MOE_ERR_NULL / MOE_ERR_ALIGN for a null or misaligned ws.  The word stays
+   set until moe_workspace_init. */
+int moe_read_device_status(const void* ws, hipStream_t stream);
+/* The same, also storing the word (the MOE_DEV_* bits) in *bits when
+   bits != NULL. */
+int moe_read_device_status_bits(const void* ws, uint32_t* bits, hipStream_t stream);
 
 #ifdef __cplusplus
 }

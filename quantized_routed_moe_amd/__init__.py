@@ -50,7 +50,7 @@ MOE_SLOT_SKIP = -2
 EXPORTS = (
     "moe_workspace_bytes", "moe_workspace_init", "moe_route_topk", "moe_dispatch",
     "moe_expert_ffn", "moe_combine", "moe_layer_workspace_bytes", "moe_layer",
-    "moe_status_str", "moe_read_device_status", "moe_qmat_bytes", "moe_pack_qmat",
+    "moe_status_str", "moe_read_device_status", "moe_read_device_status_bits", "moe_qmat_bytes", "moe_pack_qmat",
     "moe_bank_reset", "moe_bank_plan", "moe_bank_fetch", "moe_layer_banked",
     "moe_layer_shared_workspace_bytes", "moe_layer_shared",
     "moe_workspace_bytes_mx8", "moe_expert_ffn_mx8", "moe_layer_mx8_workspace_bytes", "moe_layer_mx8",
@@ -122,7 +122,8 @@ def lib() -> ctypes.CDLL:
             "moe_combine": (_I, [_P, _P, _P, _P, _P, _P]),
             "moe_layer": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
             "moe_status_str": (ctypes.c_char_p, [_I]),
-            "moe_read_device_status": (_I, [_P, _P, _P]),
+            "moe_read_device_status": (_I, [_P, _P]),
+            "moe_read_device_status_bits": (_I, [_P, _P, _P]),
             "moe_qmat_bytes": (_SZ, [_I, _I, _I, _I, _I, _P, _P, _P]),
             "moe_pack_qmat": (_I, [_P, _P, _I, _I, _I, _P]),
             "moe_layer_shared_workspace_bytes": (_SZ, [_P]),
@@ -448,7 +449,7 @@ def moe_layer_noalloc(shape: Shape, x, w_router, bias, logits, experts: Experts,
 def moe_read_device_status(ws, stream=None) -> int:
     """Synchronises the stream; returns the device status bits (0 = clean)."""
     bits = ctypes.c_uint32(0)
-    rc = lib().moe_read_device_status(_ptr(ws, name="ws"), ctypes.byref(bits), _stream(stream))
+    rc = lib().moe_read_device_status_bits(_ptr(ws, name="ws"), ctypes.byref(bits), _stream(stream))
     if rc not in (MOE_OK, MOE_ERR_DEVICE):
         raise MoeError(rc, "moe_read_device_status")
     return int(bits.value)

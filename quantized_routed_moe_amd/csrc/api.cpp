@@ -505,7 +505,7 @@ const char* moe_status_str(int status) {
     }
 }
 
-int moe_read_device_status(const void* ws, uint32_t* bits, hipStream_t stream) {
+int moe_read_device_status_bits(const void* ws, uint32_t* bits, hipStream_t stream) {
     if (!ws) return MOE_ERR_NULL;
     if (!aligned(ws, 16)) return MOE_ERR_ALIGN;
     uint32_t word = 0;
@@ -513,6 +513,10 @@ int moe_read_device_status(const void* ws, uint32_t* bits, hipStream_t stream) {
     if (hipStreamSynchronize(stream) != hipSuccess) return MOE_ERR_HIP;
     if (bits) *bits = word;
     return word ? MOE_ERR_DEVICE : MOE_OK;
+}
+
+int moe_read_device_status(const void* ws, hipStream_t stream) {
+    return moe_read_device_status_bits(ws, nullptr, stream);
 }
 
 }  // extern "C"

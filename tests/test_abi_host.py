@@ -143,7 +143,9 @@ def test_route_dispatch_combine_validation():
     assert L.moe_combine(ctypes.byref(s), A16, A16, A16, A16 + 4, None) == qm.MOE_ERR_ALIGN
     assert L.moe_workspace_init(None, 256, None) == qm.MOE_ERR_NULL
     assert L.moe_workspace_init(A16, 100, None) == qm.MOE_ERR_WORKSPACE
-    assert L.moe_read_device_status(None, None, None) == qm.MOE_ERR_NULL
+    assert L.moe_read_device_status(None, None) == qm.MOE_ERR_NULL
+    assert L.moe_read_device_status_bits(None, None, None) == qm.MOE_ERR_NULL
+    assert L.moe_read_device_status(A16 + 8, None) == qm.MOE_ERR_ALIGN
 
 
 def test_layer_validation():
