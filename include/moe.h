@@ -47,7 +47,7 @@
  *     buffers are independent.
  *   - Every call only ENQUEUES work on `stream` and returns; buffers must stay
  *     valid until the stream has passed that work.  Nothing synchronises the
- *     host except moe_read_device_status.
+ *     host except moe_read_device_status and moe_read_device_status_bits.
  *   - Host-side validation runs before any HIP call; a negative return code
  *     means nothing was enqueued.  The library never prints, aborts or throws.
  *   - T == 0 is valid and enqueues nothing.
