@@ -234,6 +234,35 @@ def test_dispatch_bad_ids():
     assert np.array_equal(iv[pm], np.arange(10))
 
 
+@pytest.mark.parametrize("T,k,E", [(1, 1, 64), (1, 2, 64), (21, 3, 8), (32, 2, 64), (65, 1, 16), (130, 1, 64)])
+@pytest.mark.parametrize("with_bad", [False, True])
+def test_dispatch_either_side_of_the_one_wave_size(T, k, E, with_bad):
+    """Batches of at most 64 pairs take the one-wave dispatch kernel, larger
+    ones the 1024-thread kernel: both give the stable order by expert id,
+    ids outside [0, E) last in pair order, offsets[E] = number of valid pairs."""
+    rng = np.random.default_rng(T * 7 + k + E)
+    ids = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    if with_bad:
+        ids.flat[rng.choice(T * k, size=max(1, T * k // 5), replace=False)] = rng.choice([-3, E, E + 9])
+    s = qm.Shape(T, 64, E, k, 32)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    perm = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    inv = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    ws = qm.alloc_workspace(s)
+    qm.moe_dispatch(s, torch.from_numpy(ids).cuda(), offsets, perm, inv, ws)
+    assert qm.moe_read_device_status(ws) == (qm.MOE_DEV_BAD_EXPERT_ID if with_bad else 0)
+    flat = ids.reshape(-1)
+    bucket = np.where((flat >= 0) & (flat < E), flat, E)
+    want_perm = np.argsort(bucket, kind="stable")
+    want_off = np.searchsorted(np.sort(bucket), np.arange(E + 1), side="left")
+    assert np.array_equal(offsets.cpu().numpy(), want_off)
+    assert np.array_equal(perm.cpu().numpy(), want_perm)
+    assert np.array_equal(inv.cpu().numpy()[want_perm], np.arange(T * k))
+    if not with_bad:
+        off, pm, iv = ref.dispatch(ids, E)
+        assert np.array_equal(want_off, off) and np.array_equal(want_perm, pm)
+
+
 def test_determinism_and_token_permutation():
     case = synthetic.make_case(29, 512, 16, 2, 256, "mxfp4", seed=9, zipf=1.1)
     dc = device_case(case)
