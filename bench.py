@@ -781,7 +781,7 @@ def main():
         copy_calibration(args.copy_calibration)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+        print(json.dumps({"error": "the layer runs on one GPU; --gpus must be 1 "
                                    "(expert-parallel sharding is designed, not built)"}))
         sys.exit(2)
     if args.bank or args.shared:

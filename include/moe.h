@@ -74,7 +74,7 @@ enum moe_status {
     MOE_ERR_FORMAT = -3,      /* unknown, mixed or mislaid pack format / layout */
     MOE_ERR_ALIGN = -4,       /* a pointer is not aligned as required */
     MOE_ERR_WORKSPACE = -5,   /* ws_bytes < moe_workspace_bytes(shape) */
-    MOE_ERR_UNSUPPORTED = -6, /* valid request this build cannot serve */
+    MOE_ERR_UNSUPPORTED = -6, /* valid request the library cannot serve */
     MOE_ERR_HIP = -7,         /* a HIP call (launch, copy) failed */
     MOE_ERR_DEVICE = -8       /* a kernel flagged bad device data (see below) */
 };
