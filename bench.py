@@ -62,12 +62,12 @@ MEASURED_FFN_TRAFFIC = {
     0: (2 * (213.0 + 113.0) + (2.0 + 8.0)) * 1024,
     1: (2 * (13158.0 + 4435.2) + (8.0 + 32.0)) * 1024,
     2: (2 * (18726.6 + 8928.5) + (40.0 + 160.0)) * 1024,
-    3: (2 * 469613.7 + 98412.2) * 1024,
+    3: (2 * 425002.2 + 98384.7) * 1024,
     4: (2 * (27882.0 + 14209.4) + (310.9 + 512.0)) * 1024,
     5: (2 * (43124.4 + 19622.7) + (310.9 + 512.0)) * 1024,
     6: (2 * (15467.8 + 5203.2) + (8.0 + 32.0)) * 1024,
-    7: (2 * (8211.1 + 366012.1) + (1024.0 + 90128.4)) * 1024,
-    8: (2 * (8211.1 + 529100.3) + (1024.0 + 90129.3)) * 1024,
+    7: (2 * (8211.1 + 297892.9) + (1024.0 + 90128.3)) * 1024,
+    8: (2 * (8211.1 + 486352.0) + (1024.0 + 90129.0)) * 1024,
 }
 
 MX_BYTES_PER_EXPERT = lambda d, f: 3 * d * f // 2 + 3 * d * f // 32      # codes + e8m0 scales

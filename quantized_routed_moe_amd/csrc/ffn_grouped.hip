@@ -51,13 +51,15 @@
 // last row) load a valid row; their output columns are never stored.
 //
 // Schedule: work units (expert, m-tile, n-tile) are enumerated with the n-tile
-// fastest and unit = workgroup id.  Workgroup ids are dealt round-robin over
-// the 8 XCDs, and there are 8 n-tiles at the workload's shape, so an XCD
-// works through one n-tile of every m-tile: consecutive m-tiles of a hot
-// expert reuse the same weight tile from that XCD's L2, and the heavy units
-// of hot experts are spread evenly over all XCDs (handing out contiguous
-// ranges of units per XCD instead put a whole hot expert on one XCD and was
-// measured ~1.5x slower).  Units are derived from offsets on the device.
+// fastest.  Workgroup ids are dealt round-robin over the 8 XCDs, and there
+// are 8 n-tiles at the workload's shape; grouped_unit_index gives each XCD
+// G n-tiles of every G-th m-tile position (G = 2 with bf16 tokens, 4 with
+// MXFP8 / MXFP4 tokens): consecutive m-tiles of a hot expert reuse the same
+// weight tiles from that XCD's L2, an m-tile's token rows are fetched by
+// 8/G XCDs, and the heavy units of hot experts are spread evenly over all
+// XCDs (handing out contiguous ranges of units per XCD instead put a whole
+// hot expert on one XCD and was measured ~1.5x slower).  Units are derived
+// from offsets on the device.
 #include <type_traits>
 
 #include "chain.hpp"
@@ -125,6 +127,7 @@ __device__ __forceinline__ void grouped_unit(const FfnArgs& a, int unit, unsigne
     const int S = K / kGK;
 
     GroupedUnit gu;
+    unit = grouped_unit_index<XQ ? 4 : 2>(unit, NT);
     if (!grouped_unit_of(a, unit, NT, lane, gu)) return;
     const int e = gu.e, mti = gu.mti, nt = gu.nt, r_base = gu.r_base, nvalid = gu.nvalid, slot = gu.slot;
     const bool sh = gu.sh;
@@ -541,7 +544,8 @@ bool grouped_supported(const moe_shape& s, int fmt) {
 
 static int max_mtiles(const moe_shape& s, bool shared) {
     const int pairs = s.T * s.k;
-    return ceil_div(pairs, kGM) + (s.E < pairs ? s.E : pairs) + (shared ? ceil_div(s.T, kGM) : 0);
+    const int m = ceil_div(pairs, kGM) + (s.E < pairs ? s.E : pairs) + (shared ? ceil_div(s.T, kGM) : 0);
+    return (m + kPosBlockMax - 1) / kPosBlockMax * kPosBlockMax;   // whole blocks of grouped_unit_index
 }
 
 int grouped_flag_count(const moe_shape& s, bool shared) {

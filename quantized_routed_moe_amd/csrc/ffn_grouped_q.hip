@@ -138,6 +138,7 @@ __device__ __forceinline__ void grouped_q_unit(const FfnArgs& a, int unit, unsig
     const int G = K / 32;                  // groups per row
 
     GroupedUnit gu;
+    unit = grouped_unit_index<4>(unit, NT);
     if (!grouped_unit_of(a, unit, NT, lane, gu)) return;
     const int nt = gu.nt, r_base = gu.r_base, nvalid = gu.nvalid, slot = gu.slot;
     const bool sh = gu.sh;
@@ -442,7 +443,8 @@ __global__ __launch_bounds__(256) void xsum_kernel(const uint16_t* __restrict__ 
 
 static int q_max_mtiles(const moe_shape& s, bool shared) {
     const int pairs = s.T * s.k;
-    return ceil_div(pairs, kGM) + (s.E < pairs ? s.E : pairs) + (shared ? ceil_div(s.T, kGM) : 0);
+    const int m = ceil_div(pairs, kGM) + (s.E < pairs ? s.E : pairs) + (shared ? ceil_div(s.T, kGM) : 0);
+    return (m + kPosBlockMax - 1) / kPosBlockMax * kPosBlockMax;   // whole blocks of grouped_unit_index
 }
 
 hipError_t launch_ffn_grouped_q(const moe_shape& s, int fmt, const FfnArgs& a, hipStream_t st) {
