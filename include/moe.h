@@ -245,7 +245,8 @@ size_t moe_slab_layout(int32_t fmt, int32_t d, int32_t f, size_t* offsets);
    (a 256-byte header holding the device status word, then the bf16 SwiGLU
    intermediate act[T*k][f], then, when f % 256 == 0, the ready flags of the
    single-launch prefill FFN: 8 bytes per 128-row m-tile and 256 rows of f,
-   for the (T*k)/128 + min(E, T*k) m-tiles there can be, rounded up; every
+   for the ceil(T*k/128) + min(E, T*k) m-tiles there can be, that count
+   rounded up to a multiple of 4; every
    launch writes a value of its own into them, so they never need clearing;
    then, for shapes that take that launch (T*k >= 256, d % 512 == 0,
    f % 256 == 0), the per-32-element group sums the 2-bit and 4-bit packs'
