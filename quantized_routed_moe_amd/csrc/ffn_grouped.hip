@@ -128,7 +128,7 @@ __device__ __forceinline__ void grouped_unit(const FfnArgs& a, int unit, unsigne
 
     GroupedUnit gu;
     unit = grouped_unit_index<XQ ? 4 : 2>(unit, NT);
-    if (!grouped_unit_of(a, unit, NT, lane, gu)) return;
+    if (!grouped_unit_of<kFullPerPartMx>(a, unit, NT, lane, gu)) return;
     const int e = gu.e, mti = gu.mti, nt = gu.nt, r_base = gu.r_base, nvalid = gu.nvalid, slot = gu.slot;
     const bool sh = gu.sh;
     // element-wise selects: choosing between the two pointer arrays would

@@ -139,7 +139,7 @@ __device__ __forceinline__ void grouped_q_unit(const FfnArgs& a, int unit, unsig
 
     GroupedUnit gu;
     unit = grouped_unit_index<4>(unit, NT);
-    if (!grouped_unit_of(a, unit, NT, lane, gu)) return;
+    if (!grouped_unit_of<kFullPerPartQ>(a, unit, NT, lane, gu)) return;
     const int nt = gu.nt, r_base = gu.r_base, nvalid = gu.nvalid, slot = gu.slot;
     const bool sh = gu.sh;
     auto wcodes = [&](int mat) { return sh ? a.sh_codes[mat] : a.codes[mat]; };

@@ -1,12 +1,13 @@
 // Work units of the single-launch grouped expert FFN (prefill chunks): which
 // expert, 128-row m-tile and n-tile a workgroup computes.  Shared by the
 // MXFP4 kernel (ffn_grouped.hip) and the 2-bit / 4-bit kernel
-// (ffn_grouped_q.hip), so that both deal the work out in the same order.
+// (ffn_grouped_q.hip), so that both deal the work out the same way.
 //
 // Full 128-row m-tiles (expert-major; matrix-core bound) and partial m-tiles
 // (at most one per expert, by decreasing row count, ties to the lower expert
 // id; bound by streaming their weight tile) are dealt in groups of
-// kFullPerPart full m-tiles and one partial while both kinds remain, then the
+// kFullPerPart (a template argument) full m-tiles and one partial while both
+// kinds remain, then the
 // rest in the same orders, n-tile fastest within an m-tile.  So HBM
 // streaming overlaps the matrix-core work from the start, and the smallest
 // partial m-tiles fill the end of the launch.  A shared expert's m-tiles
@@ -20,10 +21,15 @@
 namespace qrmoe {
 
 constexpr int kGM = 128;        // token rows per m-tile
-// Dispatch order: full m-tiles per partial m-tile while both remain.  At the
-// prefill workload (24 full, 44 partial m-tiles) 2 measured 3-4 % faster per
-// FFN call than all full m-tiles first; 1 was 7 % slower, 3 and 4 about even.
-constexpr int kFullPerPart = 2;
+// Dispatch order: kFullPerPart full m-tiles per partial m-tile while both
+// remain.  At the prefill workload (24 full, 44 partial m-tiles), measured per
+// FFN call with the XCD mapping below: the MXFP4 launch is fastest at 2 (1
+// is 8-18 % slower, 3 and 4 are 1-4 % slower, for bf16, MXFP8 and MXFP4
+// tokens alike); the 2-bit and 4-bit launch, whose full m-tiles take longer,
+// at 4 or more (2: +9-10 %, 3: +7 %; 4, 8 and all full m-tiles first within
+// 0.5 % of each other).
+constexpr int kFullPerPartMx = 2;
+constexpr int kFullPerPartQ = 4;
 
 struct GroupedUnit {
     int e;          // expert (E: the shared expert)
@@ -36,6 +42,7 @@ struct GroupedUnit {
 };
 
 // Unit `unit` of a projection with NT n-tiles; false past the last unit.
+template <int kFullPerPart>
 __device__ __forceinline__ bool grouped_unit_of(const FfnArgs& a, int unit, int NT, int lane, GroupedUnit& u) {
     int cnt = 0;
     if (lane < a.E) cnt = a.offsets[lane + 1] - a.offsets[lane];
