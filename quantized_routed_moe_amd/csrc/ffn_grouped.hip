@@ -575,16 +575,20 @@ hipError_t launch_ffn_grouped(const moe_shape& s, const FfnArgs& a, hipStream_t 
 // saturated at 448, or E2M1 elements rounded to nearest even and clamped
 // at 6, two per byte, the even element in the low nibble).  xs is
 // block-major, [d/32][rpad], so an m-tile's scale bytes of one block are
-// contiguous.
+// contiguous.  256 threads per workgroup.
 template <int BITS>
 __global__ __launch_bounds__(256) void mxq_gather_quant_kernel(const uint16_t* __restrict__ x,
                                                              const int32_t* __restrict__ perm, int k, int d, int R,
                                                              int rpad, uint8_t* __restrict__ xq,
                                                              uint8_t* __restrict__ xs) {
-    const int nb = d / 32;
-    const long long i = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (i >= static_cast<long long>(R) * nb) return;
-    const int r = static_cast<int>(i / nb), b = static_cast<int>(i % nb);
+    // a workgroup takes 16 rows x 16 blocks, lane i row i % 16 and block
+    // i / 16: the 16 lanes of one block write its 16 scale bytes (block-major
+    // xs) as one contiguous run, and a wave still reads and writes whole
+    // 128-byte runs of each of its 16 rows
+    const int nb = d / 32, nbt = (nb + 15) / 16;
+    const int r = static_cast<int>(blockIdx.x / nbt) * 16 + static_cast<int>(threadIdx.x & 15);
+    const int b = static_cast<int>(blockIdx.x % nbt) * 16 + static_cast<int>(threadIdx.x >> 4);
+    if (r >= R || b >= nb) return;
     const int t = perm[r] / k;
     const u32x4* src = reinterpret_cast<const u32x4*>(x + static_cast<size_t>(t) * d + 32 * b);
     float v[32];
@@ -633,8 +637,7 @@ __global__ __launch_bounds__(256) void mxq_gather_quant_kernel(const uint16_t* _
 
 hipError_t launch_ffn_mxq(const moe_shape& s, const FfnArgs& a, int bits, hipStream_t st) {
     const int R = s.T * s.k;
-    const long long n = static_cast<long long>(R) * (s.d / 32);
-    const unsigned grid = static_cast<unsigned>((n + 255) / 256);
+    const unsigned grid = static_cast<unsigned>(ceil_div(R, 16)) * static_cast<unsigned>(ceil_div(s.d / 32, 16));
     uint8_t* xq = const_cast<uint8_t*>(a.xq);
     uint8_t* xs = const_cast<uint8_t*>(a.xs);
     if (bits == 8) mxq_gather_quant_kernel<8><<<grid, 256, 0, st>>>(a.x, a.perm, s.k, s.d, R, a.rpad, xq, xs);
