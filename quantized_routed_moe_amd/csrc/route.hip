@@ -21,49 +21,54 @@ namespace qrmoe {
 constexpr int kRowsMaxT = 8;
 constexpr int kRowsThreads = 512;
 
-// logits[t][e] for t in [t0, t0 + nt) of one expert, by one workgroup of
-// kRowsThreads threads.  Thread i handles elements 8*i .. 8*i+7 of each
-// 8*512-element chunk of d (one chunk at d = 4096: one round of loads); the
-// partial sums are reduced in a fixed order within each wave (DPP shifts and
-// broadcasts, wave_sum_f32), then across
-// the waves in wave order.
+// logits[t][e] for t in [t0, t0 + nt) of one expert (nt = min(NT, T - t0)),
+// by one workgroup of kRowsThreads threads.  Thread i handles elements
+// 8*i .. 8*i+7 of each 8*512-element chunk of d (one chunk at d = 4096: one
+// round of loads); the loads of all NT token rows are issued together (rows
+// past nt repeat the last one; their sums are never stored), so a batch of
+// tokens costs one load latency, not one per token.  The partial sums are
+// reduced in a fixed order within each wave (DPP shifts and broadcasts,
+// wave_sum_f32), then across the waves in wave order.
+template <int NT>
 __device__ __forceinline__ void router_rows_block(const uint16_t* __restrict__ x, const float* __restrict__ wr,
                                                   const float* __restrict__ bias, float* __restrict__ logits,
                                                   int e, int t0, int T, int d, int E) {
-    const int nt = min(kRowsMaxT, T - t0);
+    const int nt = min(NT, T - t0);
     const float* wrow = wr + static_cast<size_t>(e) * d;
-    float acc[kRowsMaxT];
+    const uint16_t* xrow[NT];
+    float acc[NT];
 #pragma unroll
-    for (int j = 0; j < kRowsMaxT; ++j) acc[j] = 0.f;
+    for (int j = 0; j < NT; ++j) {
+        xrow[j] = x + static_cast<size_t>(t0 + min(j, nt - 1)) * d;
+        acc[j] = 0.f;
+    }
 #pragma unroll 2
     for (int i = threadIdx.x * 8; i < d; i += kRowsThreads * 8) {
         const float4 w0 = *reinterpret_cast<const float4*>(wrow + i);
         const float4 w1 = *reinterpret_cast<const float4*>(wrow + i + 4);
+        u32x4 xv[NT];
 #pragma unroll
-        for (int j = 0; j < kRowsMaxT; ++j) {
-            if (j < nt) {
-                const u32x4 xv = *reinterpret_cast<const u32x4*>(x + static_cast<size_t>(t0 + j) * d + i);
-                float s = acc[j];
-                s = fmaf(bf16lo(xv[0]), w0.x, s);
-                s = fmaf(bf16hi(xv[0]), w0.y, s);
-                s = fmaf(bf16lo(xv[1]), w0.z, s);
-                s = fmaf(bf16hi(xv[1]), w0.w, s);
-                s = fmaf(bf16lo(xv[2]), w1.x, s);
-                s = fmaf(bf16hi(xv[2]), w1.y, s);
-                s = fmaf(bf16lo(xv[3]), w1.z, s);
-                s = fmaf(bf16hi(xv[3]), w1.w, s);
-                acc[j] = s;
-            }
+        for (int j = 0; j < NT; ++j) xv[j] = *reinterpret_cast<const u32x4*>(xrow[j] + i);
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            float s = acc[j];
+            s = fmaf(bf16lo(xv[j][0]), w0.x, s);
+            s = fmaf(bf16hi(xv[j][0]), w0.y, s);
+            s = fmaf(bf16lo(xv[j][1]), w0.z, s);
+            s = fmaf(bf16hi(xv[j][1]), w0.w, s);
+            s = fmaf(bf16lo(xv[j][2]), w1.x, s);
+            s = fmaf(bf16hi(xv[j][2]), w1.y, s);
+            s = fmaf(bf16lo(xv[j][3]), w1.z, s);
+            s = fmaf(bf16hi(xv[j][3]), w1.w, s);
+            acc[j] = s;
         }
     }
     __shared__ float part[kRowsThreads / kWave][kRowsMaxT];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-    for (int j = 0; j < kRowsMaxT; ++j) {
-        if (j < nt) {
-            const float s = wave_sum_f32(acc[j]);
-            if (lane == 0) part[wave][j] = s;
-        }
+    for (int j = 0; j < NT; ++j) {
+        const float s = wave_sum_f32(acc[j]);
+        if (lane == 0) part[wave][j] = s;
     }
     __syncthreads();
     if (threadIdx.x < nt) {
@@ -76,10 +81,11 @@ __device__ __forceinline__ void router_rows_block(const uint16_t* __restrict__ x
     }
 }
 
+template <int NT>
 __global__ __launch_bounds__(kRowsThreads) void router_rows_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ bias,
     float* __restrict__ logits, int T, int d, int E) {
-    router_rows_block(x, wr, bias, logits, blockIdx.x, blockIdx.y * kRowsMaxT, T, d, E);
+    router_rows_block<NT>(x, wr, bias, logits, blockIdx.x, blockIdx.y * NT, T, d, E);
 }
 
 // Large-T router.  Workgroup = 8 waves = 32 tokens x 16 experts, one
@@ -258,10 +264,26 @@ hipError_t launch_small_route(const moe_shape& s, const uint16_t* x, const float
     return hipGetLastError();
 }
 
+template <int NT>
+static void launch_rows(const moe_shape& s, const uint16_t* x, const float* wr, const float* bias, float* logits,
+                        hipStream_t st) {
+    router_rows_kernel<NT><<<dim3(s.E, ceil_div(s.T, NT)), kRowsThreads, 0, st>>>(x, wr, bias, logits, s.T, s.d, s.E);
+}
+
 hipError_t launch_router_logits(const moe_shape& s, const uint16_t* x, const float* wr, const float* bias,
                                 float* logits, hipStream_t st) {
-    dim3 grid(s.E, ceil_div(s.T, kRowsMaxT));
-    router_rows_kernel<<<grid, kRowsThreads, 0, st>>>(x, wr, bias, logits, s.T, s.d, s.E);
+    if (s.T <= 0) return hipSuccess;
+    // token rows per workgroup: the batch itself up to kRowsMaxT
+    switch (s.T < kRowsMaxT ? s.T : kRowsMaxT) {
+        case 1: launch_rows<1>(s, x, wr, bias, logits, st); break;
+        case 2: launch_rows<2>(s, x, wr, bias, logits, st); break;
+        case 3: launch_rows<3>(s, x, wr, bias, logits, st); break;
+        case 4: launch_rows<4>(s, x, wr, bias, logits, st); break;
+        case 5: launch_rows<5>(s, x, wr, bias, logits, st); break;
+        case 6: launch_rows<6>(s, x, wr, bias, logits, st); break;
+        case 7: launch_rows<7>(s, x, wr, bias, logits, st); break;
+        default: launch_rows<kRowsMaxT>(s, x, wr, bias, logits, st); break;
+    }
     return hipGetLastError();
 }
 
