@@ -314,6 +314,33 @@ def test_layer_small_T_fused_path_equals_steps(shape, fmt):
     _assert_layer_equals_steps(lay, g)
 
 
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 6, 7, 8, 9, 17, 32])
+def test_router_every_small_batch_size(T):
+    """The small-batch router runs one kernel instantiation per token count
+    (1 to 8 rows per workgroup; larger batches in groups of 8).  Each token's
+    logits match the float64 oracle within 1e-4 and equal, bit for bit, the
+    logits the same token gets in a batch of its own: a token's sum is formed
+    the same way whatever the batch."""
+    case = synthetic.make_case(T, 4096, 64, 2, 128, "mxfp4", seed=600 + T, zipf=1.1)
+    dc = device_case(case)
+    s = dc["shape"]
+    _say(f"router T={T}")
+    logits = torch.empty((T, s.E), dtype=torch.float32, device="cuda")
+    ids = torch.empty((T, s.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, s.k), dtype=torch.float32, device="cuda")
+    qm.moe_route_topk(s, dc["x"], dc["w_router"], dc["bias"], logits, ids, w)
+    got = logits.cpu().numpy()
+    l64 = ref.router_logits(case["x"], case["w_router"], case["bias"])
+    assert np.abs(got - l64).max() <= 1e-4
+    s1 = qm.Shape(1, s.d, s.E, s.k, s.f)
+    one = torch.empty((1, s.E), dtype=torch.float32, device="cuda")
+    i1 = torch.empty((1, s.k), dtype=torch.int32, device="cuda")
+    w1 = torch.empty((1, s.k), dtype=torch.float32, device="cuda")
+    for t in range(T):
+        qm.moe_route_topk(s1, dc["x"][t:t + 1].contiguous(), dc["w_router"], dc["bias"], one, i1, w1)
+        assert np.array_equal(one.cpu().numpy()[0], got[t]), f"token {t}"
+
+
 def test_layer_repeated_on_one_workspace():
     """Back-to-back moe_layer calls sharing one workspace give identical
     results, leave the device status clean and the rest of the header zero."""
