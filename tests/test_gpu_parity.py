@@ -88,6 +88,36 @@ def test_prefill_chunk_other_formats(fmt):
     _assert_layer_equals_steps(run_layer(dc), g)
 
 
+@pytest.mark.parametrize("fmt", ["mxfp4", "q2"])
+def test_prefill_four_chunks_sampled(fmt):
+    """T=8192 (four prefill chunks at once: 192 m-tile positions, ~130 of
+    them full) on the grouped launch, checked on the rows of 300 random tokens
+    plus the first and last row of every active expert (every m-tile edge
+    the dispatch produces), with the combine checked on the sampled tokens;
+    moe_layer equal to the four calls bit for bit on every row."""
+    T = 8192
+    case = synthetic.make_case(T, 4096, 64, 2, 2048, fmt, seed=8192 + len(fmt), zipf=1.1)
+    _say(f"four prefill chunks T={T} {fmt}, sampled rows")
+    dc = device_case(case)
+    g = run_steps(dc)
+    assert g["status"] == 0
+    rng = np.random.default_rng(11)
+    toks = rng.choice(T, size=300, replace=False)
+    inv = g["inv"]
+    rows = set(int(inv[t * 2 + j]) for t in toks for j in range(2))
+    off = g["offsets"]
+    for e in range(64):
+        if off[e + 1] > off[e]:
+            rows.update((int(off[e]), int(off[e + 1]) - 1))
+            # the first and last row of every 128-row m-tile of the expert
+            for m0 in range(int(off[e]), int(off[e + 1]), 128):
+                rows.update((m0, min(m0 + 127, int(off[e + 1]) - 1)))
+    rows = np.array(sorted(rows))
+    info = check_against_oracle(case, g, rows=rows, strict=True)
+    _say(f"  parity ok on {rows.size} rows {info}")
+    _assert_layer_equals_steps(run_layer(dc), g)
+
+
 SHAPES = [
     # T, d, E, k, f        (d, f multiples of 32 but not of 128: ragged K steps)
     (37, 384, 16, 3, 224),
