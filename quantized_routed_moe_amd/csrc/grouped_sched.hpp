@@ -5,7 +5,8 @@
 //
 // Full 128-row m-tiles (expert-major; matrix-core bound) and partial m-tiles
 // (at most one per expert, by decreasing row count, ties to the lower expert
-// id; bound by streaming their weight tile) are dealt in groups of
+// id; bound by streaming their weight tile; increasing order measured 6 %
+// slower for MXFP4 and 17 % for the 2-bit pack) are dealt in groups of
 // kFullPerPart (a template argument) full m-tiles and one partial while both
 // kinds remain, then the
 // rest in the same orders, n-tile fastest within an m-tile.  So HBM
