@@ -35,7 +35,13 @@ def _cases(n_small=32, n_grouped=16, seed=20261203):
     return out
 
 
-CASES = _cases()
+# one projection with 8 n-tiles (whose workgroups the XCD-aware mapping
+# permutes) and the other without: the down units' flag waits must still
+# find their m-tile's gate/up units
+MIXED = [(300, 1024, 16, 2, 2048, "mxfp4", 1.1), (300, 1024, 16, 2, 2048, "q2", 1.1),
+         (300, 4096, 16, 2, 512, "mxfp4", 1.1), (300, 4096, 16, 2, 512, "q4", 1.1)]
+
+CASES = _cases() + MIXED
 
 
 @pytest.mark.parametrize("case_args", CASES, ids=[f"T{c[0]}-d{c[1]}-E{c[2]}-k{c[3]}-f{c[4]}-{c[5]}" for c in CASES])
