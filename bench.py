@@ -686,15 +686,23 @@ def run_workload(c, args, mx=0, peaks=None, cpu=True):
     elapsed = capture_replay(hip, stream, lambda i: layer_step(args.warmup + i), K)
 
     # Timed region 2 (roofline): the same K steps through the four entry
-    # points, with HIP events around moe_expert_ffn on the same stream.
-    evs = Events(hip, K)
+    # points, with HIP events around moe_expert_ffn on the same stream.  A
+    # hold kernel first keeps the stream busy while the host enqueues the
+    # steps (it is slower per step than the GPU at small T), so the K steps
+    # then run back to back from the queue and each event pair times the
+    # FFN call's kernels, not gaps waiting for the host.  The four-call step
+    # time comes from one more event pair around the whole loop.
+    evs = Events(hip, K + 1)
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    if L.moe_peak_hold(min(1000000, 100 * K + 2000), stream):
+        raise RuntimeError("moe_peak_hold failed")
+    hip.hipEventRecord(evs.ev[K][0], ctypes.c_void_p(stream))
     for i in range(K):
         step(args.warmup + i, evs.ev[i])
+    hip.hipEventRecord(evs.ev[K][1], ctypes.c_void_p(stream))
     torch.cuda.synchronize()
-    steps_elapsed = time.perf_counter() - t1
-    ffn_ms = evs.ms()
+    all_ms = evs.ms()
+    ffn_ms, steps_elapsed = all_ms[:K], all_ms[K] / 1e3
     evs.close()
     assert qm.moe_read_device_status(ws) == 0
 

@@ -11,7 +11,7 @@
  * what a plain kernel reaches on the same box, so that a fraction of the
  * measured peak can sit beside the fraction of the published one.
  *
- * Both only ENQUEUE on `stream`; time them with HIP events on that stream.
+ * Each only ENQUEUES on `stream`; time them with HIP events on that stream.
  * Pointers are device pointers; the caller owns every buffer.  They return
  * MOE_OK (0), MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGN or MOE_ERR_HIP
  * (the codes of include/moe.h).
@@ -49,6 +49,15 @@ int moe_peak_stream(const void* buf, size_t bytes, int32_t workgroups, uint32_t*
    flop = workgroups * 4 * iters * 8 * (flop each); the rate is flop / the
    kernel's duration.  sink holds workgroups * 4 floats. */
 int moe_peak_mfma(int32_t kind, int32_t iters, int32_t workgroups, float* sink, hipStream_t stream);
+
+/* Keeps `stream` busy for `microseconds` (1 .. 1,000,000): one wave reads
+   the GPU's constant 100 MHz clock until that much time has passed, then
+   returns.  Timing code enqueues it ahead of a timed loop so that the host
+   gets ahead of the GPU while it waits: the loop's kernels then run back to
+   back from the queue, and event pairs around them time the kernels rather
+   than the host's launch rate.  Returns MOE_OK, MOE_ERR_SHAPE or
+   MOE_ERR_HIP. */
+int moe_peak_hold(uint32_t microseconds, hipStream_t stream);
 
 #ifdef __cplusplus
 }

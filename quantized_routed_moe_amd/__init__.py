@@ -57,7 +57,7 @@ EXPORTS = (
     "moe_workspace_bytes_mx4", "moe_expert_ffn_mx4", "moe_layer_mx4_workspace_bytes", "moe_layer_mx4",
     "moe_slab_layout", "moe_bank_slots", "moe_layer_noalloc",
     # include/moe_peak.h
-    "moe_peak_stream", "moe_peak_mfma",
+    "moe_peak_stream", "moe_peak_mfma", "moe_peak_hold",
 )
 
 
@@ -145,6 +145,7 @@ def lib() -> ctypes.CDLL:
             "moe_layer_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
             "moe_peak_stream": (_I, [_P, _SZ, ctypes.c_int32, _P, _P]),
             "moe_peak_mfma": (_I, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P]),
+            "moe_peak_hold": (_I, [ctypes.c_uint32, _P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)

@@ -86,6 +86,13 @@ __global__ __launch_bounds__(256) void peak_mfma_kernel(int iters, float* __rest
     if (lane == 0) sink[blockIdx.x * 4 + (threadIdx.x >> 6)] = s;
 }
 
+// One wave waits on the constant 100 MHz clock (s_memrealtime) until
+// `ticks` have passed; the loop ends on time alone.
+__global__ __launch_bounds__(64) void peak_hold_kernel(uint64_t ticks) {
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    while (__builtin_amdgcn_s_memrealtime() - t0 < ticks) __builtin_amdgcn_s_sleep(127);
+}
+
 }  // namespace qrmoe
 
 extern "C" {
@@ -108,6 +115,12 @@ int moe_peak_mfma(int32_t kind, int32_t iters, int32_t workgroups, float* sink, 
     if (kind == 0) qrmoe::peak_mfma_kernel<0><<<g, 256, 0, stream>>>(iters, sink);
     else if (kind == 1) qrmoe::peak_mfma_kernel<1><<<g, 256, 0, stream>>>(iters, sink);
     else qrmoe::peak_mfma_kernel<2><<<g, 256, 0, stream>>>(iters, sink);
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int moe_peak_hold(uint32_t microseconds, hipStream_t stream) {
+    if (microseconds < 1 || microseconds > 1000000) return MOE_ERR_SHAPE;
+    qrmoe::peak_hold_kernel<<<1, 64, 0, stream>>>(static_cast<uint64_t>(microseconds) * 100u);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

@@ -290,3 +290,5 @@ def test_peak_kernels_validation():
     assert L.moe_peak_mfma(3, 10, 0, A16, None) == qm.MOE_ERR_SHAPE
     assert L.moe_peak_mfma(0, 0, 0, A16, None) == qm.MOE_ERR_SHAPE
     assert L.moe_peak_mfma(1, 10, 0, A16 + 2, None) == qm.MOE_ERR_ALIGN
+    assert L.moe_peak_hold(0, None) == qm.MOE_ERR_SHAPE
+    assert L.moe_peak_hold(1000001, None) == qm.MOE_ERR_SHAPE
