@@ -311,10 +311,11 @@ __device__ __forceinline__ void grouped_unit(const FfnArgs& a, int unit, unsigne
             const uint8_t* wb = lds + (s % NST) * SB;
             const uint8_t* sb = wb + kStageW;
             const uint8_t* xb = sb + kStageS;
-            // weight operand first, then the token fragments one sub-step
-            // ahead of the multiplies that use them (the scheduling barriers
-            // keep the compiler from sinking each read next to its use, which
-            // exposed the full LDS latency on every MFMA pair)
+            // weight operand first, then the token fragments and the
+            // weight conversions one sub-step ahead of the multiplies that
+            // use them (the scheduling barriers keep the compiler from
+            // sinking each read next to its use, which exposed the full LDS
+            // latency on every MFMA pair)
             const u32x4 c0 = *reinterpret_cast<const u32x4*>(wb + pc0 * 16);
             const u32x4 c1 = *reinterpret_cast<const u32x4*>(wb + pc1 * 16);
             const uint32_t sc0 = sb[pc0], sc1 = sb[pc1];
@@ -363,23 +364,42 @@ __device__ __forceinline__ void grouped_unit(const FfnArgs& a, int unit, unsigne
             for (int t = 0; t < NTT; ++t) bcur[t] = *reinterpret_cast<const u32x4*>(xb + xswz(32 * t + r32, 4 * h));
             const float s0 = e8m0_to_f32(sc0);
             const float s1 = e8m0_to_f32(sc1);
+            bf16x8 a0 = mxfp4x8_to_bf16(c0[0], s0);
+            bf16x8 a1 = mxfp4x8_to_bf16(c1[0], s1);
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
+                __builtin_amdgcn_sched_barrier(0);
                 if (kk < 3) {
 #pragma unroll
                     for (int t = 0; t < NTT; ++t)
                         bnext[t] = *reinterpret_cast<const u32x4*>(xb + xswz(32 * t + r32, 4 * h + kk + 1));
                 }
-                __builtin_amdgcn_sched_barrier(0);
-                const bf16x8 a0 = mxfp4x8_to_bf16(c0[kk], s0);
-                const bf16x8 a1 = mxfp4x8_to_bf16(c1[kk], s1);
+                bf16x8 n0 = a0, n1 = a1;
+                if (kk < 3) {
+                    n0 = mxfp4x8_to_bf16(c0[kk + 1], s0);
+                    n1 = mxfp4x8_to_bf16(c1[kk + 1], s1);
+                }
 #pragma unroll
                 for (int t = 0; t < NTT; ++t) {
                     const bf16x8 b = bf16x8_from_u32x4(bcur[t]);
                     acc[0][t] = mfma32x32x16(a0, b, acc[0][t]);
                     acc[1][t] = mfma32x32x16(a1, b, acc[1][t]);
                 }
+                // sub-step kk + 1's conversions and token reads placed between
+                // sub-step kk's products (one conversion, and while any remain
+                // one token read, after each product), so a wave keeps
+                // issuing them while its own products run on the matrix core
+                if (kk < 3) {
+#pragma unroll
+                    for (int q = 0; q < 2 * NTT; ++q) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        if (q < 8) __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
+                        if (q < NTT) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    }
+                }
                 __builtin_amdgcn_sched_barrier(0);
+                a0 = n0;
+                a1 = n1;
 #pragma unroll
                 for (int t = 0; t < NTT; ++t) bcur[t] = bnext[t];
             }
