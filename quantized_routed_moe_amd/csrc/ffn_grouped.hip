@@ -307,7 +307,7 @@ __device__ __forceinline__ void grouped_unit(const FfnArgs& a, int unit, unsigne
             // one barrier: every wave's copy of stage s is visible, and every
             // wave is done with stage s - 1, whose buffer stage s + NST - 1 takes
             __builtin_amdgcn_s_barrier();
-            if (s + NST - 1 < S) issue(s + NST - 1, nst_c, sb_c);
+            if (XQ != 0 && s + NST - 1 < S) issue(s + NST - 1, nst_c, sb_c);
             const uint8_t* wb = lds + (s % NST) * SB;
             const uint8_t* sb = wb + kStageW;
             const uint8_t* xb = sb + kStageS;
@@ -362,6 +362,9 @@ __device__ __forceinline__ void grouped_unit(const FfnArgs& a, int unit, unsigne
             u32x4 bcur[NTT], bnext[NTT];
 #pragma unroll
             for (int t = 0; t < NTT; ++t) bcur[t] = *reinterpret_cast<const u32x4*>(xb + xswz(32 * t + r32, 4 * h));
+            __builtin_amdgcn_sched_barrier(0);
+            if (s + NST - 1 < S) issue(s + NST - 1, nst_c, sb_c);
+            __builtin_amdgcn_sched_barrier(0);
             const float s0 = e8m0_to_f32(sc0);
             const float s1 = e8m0_to_f32(sc1);
             bf16x8 a0 = mxfp4x8_to_bf16(c0[0], s0);
