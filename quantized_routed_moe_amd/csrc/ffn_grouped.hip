@@ -285,25 +285,14 @@ __device__ __forceinline__ void grouped_unit(const FfnArgs& a, int unit, unsigne
         const auto nst_c = std::integral_constant<int, NST>{};
         const auto sb_c = std::integral_constant<int, SB>{};
         for (int s = 0; s < NST - 1 && s < S; ++s) issue(s, nst_c, sb_c);
-        for (int s = 0; s < S; ++s) {
+        auto stage = [&](int s, auto l_c) {
             // stage s is in LDS once at most the younger stages issued so far
-            // (up to NST - 2) are in flight; each wave counts its own loads
+            // (up to NST - 2) are in flight; each wave counts its own loads,
+            // L per stage (its role's count, see run below)
+            constexpr int L = decltype(l_c)::value;
             const int younger = min(NST - 2, S - 1 - s);
-            if constexpr (XQ == 8) {     // waves 0 and 1 always hold live rows
-                if (wave <= 1) wait_stages<4, NST - 2>(younger);
-                else if (x_live) wait_stages<3, NST - 2>(younger);
-                else wait_stages<2, NST - 2>(younger);
-            } else if constexpr (XQ == 4) {   // wave 0 always holds live rows
-                if (wave == 0 || (wave == 1 && x_live)) wait_stages<4, NST - 2>(younger);
-                else if (wave == 1 || x_live) wait_stages<3, NST - 2>(younger);
-                else wait_stages<2, NST - 2>(younger);
-            } else if (wave == 0) {
-                if (x_live) wait_stages<5, NST - 2>(younger);
-                else wait_stages<3, NST - 2>(younger);
-            } else {
-                if (x_live) wait_stages<4, NST - 2>(younger);
-                else wait_stages<2, NST - 2>(younger);
-            }
+            if (younger == NST - 2) wait_vmcnt<L * (NST - 2)>();
+            else wait_stages<L, NST - 2>(younger);
             // one barrier: every wave's copy of stage s is visible, and every
             // wave is done with stage s - 1, whose buffer stage s + NST - 1 takes
             __builtin_amdgcn_s_barrier();
@@ -335,7 +324,7 @@ __device__ __forceinline__ void grouped_unit(const FfnArgs& a, int unit, unsigne
                     acc[0][t] = mfma_scale_fp4_fp4(c0, b[t], acc[0][t], static_cast<int>(sc0), bs[t]);
                     acc[1][t] = mfma_scale_fp4_fp4(c1, b[t], acc[1][t], static_cast<int>(sc1), bs[t]);
                 }
-                continue;
+                return;
             } else if constexpr (XQ == 8) {
                 // one block-scaled 32x32x64 product per (weight tile, column
                 // tile): the pieces and their E8M0 bytes go in as they are,
@@ -357,7 +346,7 @@ __device__ __forceinline__ void grouped_unit(const FfnArgs& a, int unit, unsigne
                     acc[0][t] = mfma_scale_fp4_fp8(c0, b[t], acc[0][t], static_cast<int>(sc0), bs[t]);
                     acc[1][t] = mfma_scale_fp4_fp8(c1, b[t], acc[1][t], static_cast<int>(sc1), bs[t]);
                 }
-                continue;
+                return;
             }
             u32x4 bcur[NTT], bnext[NTT];
 #pragma unroll
@@ -406,6 +395,33 @@ __device__ __forceinline__ void grouped_unit(const FfnArgs& a, int unit, unsigne
 #pragma unroll
                 for (int t = 0; t < NTT; ++t) bcur[t] = bnext[t];
             }
+        };
+        // The loads per stage of this wave's role are a compile-time count,
+        // so the steady-state wait is one instruction and not a tree of
+        // scalar branches every stage.  bf16: wave 0 copies the scale bytes
+        // (+1), waves holding live token rows copy two rows of 1 KB (+2).
+        // MXFP8: waves 0 and 1 always hold live rows (one copy), wave 1 the
+        // token scale bytes too.  MXFP4: wave 0 always holds live rows, wave 1
+        // copies the token scale bytes.
+        auto run = [&](auto l_c) {
+            for (int s = 0; s < S; ++s) stage(s, l_c);
+        };
+        if constexpr (XQ == 0) {
+            if (wave == 0) {
+                if (x_live) run(std::integral_constant<int, 5>{});
+                else run(std::integral_constant<int, 3>{});
+            } else {
+                if (x_live) run(std::integral_constant<int, 4>{});
+                else run(std::integral_constant<int, 2>{});
+            }
+        } else if constexpr (XQ == 8) {
+            if (wave <= 1) run(std::integral_constant<int, 4>{});
+            else if (x_live) run(std::integral_constant<int, 3>{});
+            else run(std::integral_constant<int, 2>{});
+        } else {
+            if (wave == 0 || (wave == 1 && x_live)) run(std::integral_constant<int, 4>{});
+            else if (wave == 1 || x_live) run(std::integral_constant<int, 3>{});
+            else run(std::integral_constant<int, 2>{});
         }
     };
 
