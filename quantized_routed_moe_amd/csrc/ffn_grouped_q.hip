@@ -264,7 +264,6 @@ __device__ __forceinline__ void grouped_q_unit(const FfnArgs& a, int unit, unsig
         for (int s = 0; s < S; ++s) {
             q_wait_stages<R::loads, NST - 2>(min(NST - 2, S - 1 - s));
             __builtin_amdgcn_s_barrier();
-            if (s + NST - 1 < S) issue(s + NST - 1);
             const uint8_t* b = lds + (s % NST) * SB;
             // this lane's pieces and scale words of the four weight tiles
             u32x4 code[4], smw[4];
@@ -282,6 +281,11 @@ __device__ __forceinline__ void grouped_q_unit(const FfnArgs& a, int unit, unsig
                 smw[m] = *reinterpret_cast<const u32x4*>(sb);
                 mw[m] = *reinterpret_cast<const uint32_t*>(sb + 4 * (lane >> 4));   // group lane / 16 (the min term)
             }
+            // the next stage's copies go out after this stage's fragment
+            // reads, so the reads are not queued behind them
+            __builtin_amdgcn_sched_barrier(0);
+            if (s + NST - 1 < S) issue(s + NST - 1);
+            __builtin_amdgcn_sched_barrier(0);
             // min term: A' = (X_hi, X_lo, X_hi, X_lo) of the token row's group
             // lane / 16, B' = (min, min, -K scale, -K scale) of the weight row's
 #pragma unroll
