@@ -53,8 +53,7 @@
 // Schedule: work units (expert, m-tile, n-tile) are enumerated with the n-tile
 // fastest.  Workgroup ids are dealt round-robin over the 8 XCDs, and there
 // are 8 n-tiles at the workload's shape; grouped_unit_index gives each XCD
-// G n-tiles of every G-th m-tile position (G = 2 with bf16 tokens, 4 with
-// MXFP8 / MXFP4 tokens): consecutive m-tiles of a hot expert reuse the same
+// G = 4 n-tiles of every fourth m-tile position: consecutive m-tiles of a hot expert reuse the same
 // weight tiles from that XCD's L2, an m-tile's token rows are fetched by
 // 8/G XCDs, and the heavy units of hot experts are spread evenly over all
 // XCDs (handing out contiguous ranges of units per XCD instead put a whole
@@ -127,7 +126,7 @@ __device__ __forceinline__ void grouped_unit(const FfnArgs& a, int unit, unsigne
     const int S = K / kGK;
 
     GroupedUnit gu;
-    unit = grouped_unit_index<XQ ? 4 : 2>(unit, NT);
+    unit = grouped_unit_index<4>(unit, NT);
     if (!grouped_unit_of<kFullPerPartMx>(a, unit, NT, lane, gu)) return;
     const int e = gu.e, mti = gu.mti, nt = gu.nt, r_base = gu.r_base, nvalid = gu.nvalid, slot = gu.slot;
     const bool sh = gu.sh;

@@ -121,7 +121,10 @@ __device__ __forceinline__ bool grouped_unit_of(const FfnArgs& a, int unit, int 
 // G = 1: bf16 tokens -1.6 % at G = 2 (G = 4 and 8 within noise of G = 1);
 // MXFP8 tokens -2.5 / -4.3 / -4.4 % at G = 2 / 4 / 8, MXFP4 tokens -3 % at
 // G = 4; 2-bit packs -1.2 / -4.3 / -4.8 %, 4-bit packs unchanged at G = 2
-// and 4.  The launches round their m-tile count up to a multiple of
+// and 4.  After the K-loop scheduling changes of the MXFP4 kernel, bf16
+// tokens measured G = 4 1.0 % faster than G = 2 and G = 1 0.6 % slower
+// (three alternating runs, one box); every launch now takes G = 4.  The
+// launches round their m-tile count up to a multiple of
 // kPosBlockMax, so every block of positions is whole.
 constexpr int kPosBlockMax = 4;
 template <int G>
