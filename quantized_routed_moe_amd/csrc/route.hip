@@ -189,14 +189,25 @@ __global__ __launch_bounds__(kRouterWaves * 64) void router_mfma_kernel(
         }
     };
     // two register sets: batch b + 1 loads while batch b multiplies (the
-    // loop is unrolled by two so that every set index is a constant)
+    // loop is unrolled by two so that every set index is a constant).  The
+    // loop body holds no load under a branch, so the compiler's waits before
+    // each batch's products count only the loads ahead of it; a batch load
+    // under a branch made them wait for the next batch too (prefill router
+    // 314.8 -> 312.7 us per layer step, four alternating runs, one box)
     load(0, s_beg);
-    for (int sb = s_beg; sb < s_end; sb += 2 * kRouterBatch) {
-        if (sb + kRouterBatch < s_end) load(1, sb + kRouterBatch);
+    int sb = s_beg;
+    for (; sb + 2 * kRouterBatch < s_end; sb += 2 * kRouterBatch) {
+        load(1, sb + kRouterBatch);
         mul(0, sb);
-        if (sb + kRouterBatch >= s_end) break;
-        if (sb + 2 * kRouterBatch < s_end) load(0, sb + 2 * kRouterBatch);
+        load(0, sb + 2 * kRouterBatch);
         mul(1, sb + kRouterBatch);
+    }
+    if (sb + kRouterBatch < s_end) {
+        load(1, sb + kRouterBatch);
+        mul(0, sb);
+        mul(1, sb + kRouterBatch);
+    } else if (sb < s_end) {
+        mul(0, sb);
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) red[wave][h][lane] = acc[h];
