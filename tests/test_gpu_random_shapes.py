@@ -41,7 +41,23 @@ def _cases(n_small=32, n_grouped=16, seed=20261203):
 MIXED = [(300, 1024, 16, 2, 2048, "mxfp4", 1.1), (300, 1024, 16, 2, 2048, "q2", 1.1),
          (300, 4096, 16, 2, 512, "mxfp4", 1.1), (300, 4096, 16, 2, 512, "q4", 1.1)]
 
-CASES = _cases() + MIXED
+# 5 to 8 tokens stage four rows per pass, so an expert with more rows takes
+# a second pass over the weights held in registers; larger E and k make
+# such experts rarer, small E and repeated picks make them common
+def _cases_few_tokens(n=12, seed=777123):
+    rng = random.Random(seed)
+    out = []
+    for _ in range(n):
+        E = rng.choice([2, 4, 8, 16, 33, 64])
+        k = rng.randint(1, min(E, 4))
+        T = rng.choice([5, 6, 7, 8])
+        d = 32 * rng.randint(1, 40)
+        f = 32 * rng.randint(1, 40)
+        out.append((T, d, E, k, f, rng.choice(["mxfp4", "q2", "q4"]), rng.choice([None, 1.1])))
+    return out
+
+
+CASES = _cases() + MIXED + _cases_few_tokens()
 
 
 @pytest.mark.parametrize("case_args", CASES, ids=[f"T{c[0]}-d{c[1]}-E{c[2]}-k{c[3]}-f{c[4]}-{c[5]}" for c in CASES])
