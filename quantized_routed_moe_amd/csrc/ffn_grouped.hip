@@ -41,10 +41,12 @@
 // of the unit's live column tiles, so units with few rows keep more weight
 // bytes in flight); every wave issues its LDS-bound loads of a stage (two
 // weight, up to two token, wave 0 the scales too) NST - 1 stages ahead;
-// before computing stage s it waits (vmcnt, counting its own loads) until
-// only the younger stages are in flight, and one barrier per stage makes
-// every wave's copy visible and frees the buffer of stage s-1 for stage
-// s+NST-1.  No register
+// before computing stage s it waits (vmcnt, counting its own loads, a
+// compile-time count per wave role) until only the younger stages are in
+// flight, and one barrier per stage makes every wave's copy visible and
+// frees the buffer of stage s-1 for stage s+NST-1, whose copies go out right
+// after the barrier (MX tokens) or after the stage's fragment reads (bf16
+// tokens).  No register
 // ring and no LDS store pass: the registers go to the accumulators and to the
 // B fragments, which are all read at the start of a stage so that their LDS
 // latency overlaps the multiplies.  Padding token rows (past the expert's
