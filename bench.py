@@ -62,7 +62,7 @@ MEASURED_FFN_TRAFFIC = {
     0: (2 * (213.0 + 113.0) + (2.0 + 8.0)) * 1024,
     1: (2 * (13158.0 + 4435.2) + (8.0 + 32.0)) * 1024,
     2: (2 * (18469.3 + 9103.3) + (40.0 + 160.0)) * 1024,
-    3: (2 * 423348.5 + 98329.2) * 1024,
+    3: (2 * 422740.3 + 98328.8) * 1024,
     4: (2 * (27882.0 + 14209.4) + (310.9 + 512.0)) * 1024,
     5: (2 * (43124.4 + 19622.7) + (310.9 + 512.0)) * 1024,
     6: (2 * (15467.8 + 5203.2) + (8.0 + 32.0)) * 1024,
