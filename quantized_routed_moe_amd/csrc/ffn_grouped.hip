@@ -40,14 +40,13 @@
 // Pipeline: a ring of NST stages (4 to 7: a stage holds only the token rows
 // of the unit's live column tiles, so units with few rows keep more weight
 // bytes in flight); every wave issues its LDS-bound loads of a stage (two
-// weight, up to two token, wave 0 the scales too) NST - 1 stages ahead;
-// before computing stage s it waits (vmcnt, counting its own loads, a
-// compile-time count per wave role) until only the younger stages are in
-// flight, and one barrier per stage makes every wave's copy visible and
-// frees the buffer of stage s-1 for stage s+NST-1, whose copies go out right
-// after the barrier (MX tokens).  With bf16 tokens one barrier covers a pair
-// of stages, and the pair's first stage issues two stages' copies after its
-// fragment reads (see the K loop).  No register
+// weight, up to two token, wave 0 the scales too) NST - 2 or NST - 1 stages
+// ahead; the stages go in pairs: before a pair it waits (vmcnt, counting its
+// own loads, a compile-time count per wave role) until only the younger
+// stages are in flight, and one barrier per pair makes every wave's copies
+// visible and frees the previous pair's buffers for the copies of the next
+// two stages, issued right after the barrier (MX tokens) or after the first
+// stage's fragment reads (bf16 tokens).  No register
 // ring and no LDS store pass: the registers go to the accumulators and to the
 // B fragments, which are all read at the start of a stage so that their LDS
 // latency overlaps the multiplies.  Padding token rows (past the expert's
@@ -286,34 +285,30 @@ __device__ __forceinline__ void grouped_unit(const FfnArgs& a, int unit, unsigne
         constexpr int NST = Ring<NTT, XQ>::count, SB = Ring<NTT, XQ>::stage;
         const auto nst_c = std::integral_constant<int, NST>{};
         const auto sb_c = std::integral_constant<int, SB>{};
-        for (int s = 0; s < NST - (XQ == 0 ? 2 : 1) && s < S; ++s) issue(s, nst_c, sb_c);
+        for (int s = 0; s < NST - 2 && s < S; ++s) issue(s, nst_c, sb_c);
         auto stage = [&](int s, auto l_c, auto m_c) {
             constexpr int L = decltype(l_c)::value;
-            // M = 0: one stage per barrier (MX tokens).  M = 1, 2: the first
-            // and second stage of a pair under one barrier (bf16 tokens): the
-            // pair's wait leaves NST - 4 stages in flight, and the first
-            // stage issues the copies of stages s + NST - 2 and s + NST - 1,
-            // into the buffers of the previous pair.  Half the barriers, one
-            // stage less of prefetch for half the stages (FFN call -1.3 %,
-            // three alternating runs, one box).
+            // One barrier per pair of stages: M = 1 is the pair's first stage,
+            // M = 2 its second.  The pair's wait leaves NST - 4 stages in
+            // flight (each wave counts its own loads, L per stage: its role's
+            // count, see run below); after the barrier every wave's copies of
+            // both stages are visible and every wave is done with the
+            // previous pair, whose buffers stages s + NST - 2 and s + NST - 1
+            // take: MX tokens issue their copies right after the barrier,
+            // bf16 tokens after the first stage's fragment reads.  Against
+            // one barrier per stage: bf16 FFN call -1.3 to -1.5 % (two
+            // boxes), MXFP8 -1.7 %, MXFP4 -2.6 % (alternating runs).
             constexpr int M = decltype(m_c)::value;
-            if constexpr (M == 0) {
-                // stage s is in LDS once at most the younger stages issued so
-                // far (up to NST - 2) are in flight; each wave counts its own
-                // loads, L per stage (its role's count, see run below)
-                const int younger = min(NST - 2, S - 1 - s);
-                if (younger == NST - 2) wait_vmcnt<L * (NST - 2)>();
-                else wait_stages<L, NST - 2>(younger);
-                // one barrier: every wave's copy of stage s is visible, and every
-                // wave is done with stage s - 1, whose buffer stage s + NST - 1 takes
-                __builtin_amdgcn_s_barrier();
-            } else if constexpr (M == 1) {
+            if constexpr (M == 1) {
                 const int younger = min(S - 1, s + NST - 3) - min(s + 1, S - 1);
                 if (younger == NST - 4) wait_vmcnt<L * (NST - 4)>();
                 else wait_stages<L, NST - 4>(younger);
                 __builtin_amdgcn_s_barrier();
+                if constexpr (XQ != 0) {
+                    if (s + NST - 2 < S) issue(s + NST - 2, nst_c, sb_c);
+                    if (s + NST - 1 < S) issue(s + NST - 1, nst_c, sb_c);
+                }
             }
-            if (XQ != 0 && s + NST - 1 < S) issue(s + NST - 1, nst_c, sb_c);
             const uint8_t* wb = lds + (s % NST) * SB;
             const uint8_t* sb = wb + kStageW;
             const uint8_t* xb = sb + kStageS;
@@ -424,13 +419,9 @@ __device__ __forceinline__ void grouped_unit(const FfnArgs& a, int unit, unsigne
         // token scale bytes too.  MXFP4: wave 0 always holds live rows, wave 1
         // copies the token scale bytes.
         auto run = [&](auto l_c) {
-            if constexpr (XQ == 0) {
-                for (int s = 0; s < S; s += 2) {
-                    stage(s, l_c, std::integral_constant<int, 1>{});
-                    if (s + 1 < S) stage(s + 1, l_c, std::integral_constant<int, 2>{});
-                }
-            } else {
-                for (int s = 0; s < S; ++s) stage(s, l_c, std::integral_constant<int, 0>{});
+            for (int s = 0; s < S; s += 2) {
+                stage(s, l_c, std::integral_constant<int, 1>{});
+                if (s + 1 < S) stage(s + 1, l_c, std::integral_constant<int, 2>{});
             }
         };
         if constexpr (XQ == 0) {
