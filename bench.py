@@ -66,8 +66,8 @@ MEASURED_FFN_TRAFFIC = {
     4: (2 * (27882.0 + 14209.4) + (310.9 + 512.0)) * 1024,
     5: (2 * (43124.4 + 19622.7) + (310.9 + 512.0)) * 1024,
     6: (2 * (15467.8 + 5203.2) + (8.0 + 32.0)) * 1024,
-    7: (2 * (8211.1 + 292669.3) + (1024.0 + 90128.3)) * 1024,
-    8: (2 * (8211.1 + 484356.0) + (1024.0 + 90129.0)) * 1024,
+    7: (2 * (8211.1 + 292317.6) + (1024.0 + 90128.4)) * 1024,
+    8: (2 * (8211.2 + 483074.4) + (1024.0 + 90129.0)) * 1024,
 }
 
 MX_BYTES_PER_EXPERT = lambda d, f: 3 * d * f // 2 + 3 * d * f // 32      # codes + e8m0 scales
